@@ -1,0 +1,204 @@
+"""Benchmark: batched speculative-decoding verification on one MI355X.
+
+One step = one spec_verify call over the whole batch of the concurrent-batch
+workload (B=32 sequences, K=7 drafted positions, V=151936, bf16 target / f32
+draft logits, temperature 0.7, top-p 0.9), inputs resident in HBM.  Several
+copies of the inputs are rotated so that the 256 MB Infinity Cache cannot
+serve a step from the previous one.
+
+Prints one JSON line with the headline metric (verified draft positions/s),
+the roofline of the dominant (streaming) kernel measured with HIP events on
+the call's stream, and the CPU oracle timed on the host as a baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936, 1 GPU"
+PEAK_HBM_GBS = 8000.0
+MALL_BYTES = 256 << 20
+
+
+def _hip():
+    for name in ("libamdhip64.so", "/opt/rocm/lib/libamdhip64.so"):
+        try:
+            L = ctypes.CDLL(name)
+            break
+        except OSError:
+            continue
+    else:
+        raise RuntimeError("libamdhip64.so not found")
+    L.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    L.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                      ctypes.c_void_p]
+    L.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return L
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "draft_verification_02_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        if f.endswith((".h", ".hip")):
+            with open(os.path.join(csrc, f), "rb") as fh:
+                h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(config_name: str, src_hash: str):
+    """HBM bytes per launch from the committed PMC summary, only while the
+    kernel sources still match the ones the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "k_rowstats_c3_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != src_hash or d.get("workload") != config_name:
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, max_seqs: int):
+    import oracle  # CPU baseline leg only
+
+    seqs = list(range(min(w.B, max_seqs)))
+    t0 = time.perf_counter()
+    for b in seqs:
+        oracle.verify(w.target[b:b + 1], w.draft[b:b + 1], w.tokens[b:b + 1],
+                      float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p)),
+                      w.seed, seq_base=b, diagnostics=False)
+    dt = time.perf_counter() - t0
+    return {"value": round(len(seqs) * w.K / dt, 3), "unit": "verified draft positions/s",
+            "cores": 1, "kind": "oracle",
+            "sample": f"{len(seqs)} of {w.B} sequences of the same workload, single-threaded "
+                      f"fp64 C++ oracle, {dt:.2f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
+    ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the verifier is data-parallel over sequences and "
+              "this build runs on a single MI355X; run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from draft_verification_02_amd import binding, workloads as wl
+
+    w = wl.config(args.config)
+    if w.greedy:
+        raise SystemExit("the headline workload is a sampling workload")
+    dev = torch.device("cuda:0")
+    ideal = w.ideal_bytes()
+    n_sets = args.sets or max(4, int(np.ceil(2.5 * MALL_BYTES / ideal)))
+
+    def up(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(a).to(dev)
+
+    sets = [(up(w.target), up(w.draft), up(w.tokens)) for _ in range(n_sets)]
+    out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((w.B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        t, d, k = sets[i % n_sets]
+        binding.spec_verify(t, d, k, w.temperature, w.top_k, w.top_p, w.seed, out_t, out_n,
+                            stream=stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+
+    # headline: K back-to-back steps between two events on the call stream
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t_wall = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter() - t_wall
+    ms = e0.elapsed_time(e1) / args.steps
+
+    # dominant kernel: the library records a HIP event pair around its
+    # streaming kernel, once per step, on the same stream
+    hip = _hip()
+    n_ev = args.steps
+    evs = []
+    for _ in range(2 * n_ev):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        evs.append(h)
+    torch.cuda.synchronize()
+    for i in range(n_ev):
+        binding.profile_events(evs[2 * i].value, evs[2 * i + 1].value)
+        step(i)
+    torch.cuda.synchronize()
+    durs = []
+    for i in range(n_ev):
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), evs[2 * i], evs[2 * i + 1]) == 0
+        durs.append(f.value)
+    for h in evs:
+        hip.hipEventDestroy(h)
+    k_ms = float(np.mean(durs))
+
+    src_hash = kernel_source_hash()
+    achieved = ideal / (k_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(w.name, src_hash)
+    positions = w.B * w.K
+    value = positions / (ms * 1e-3)
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32+f64",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "K": w.K, "V": w.V, "target": "bf16",
+                   "draft": "f32", "temperature": w.temperature, "top_k": w.top_k,
+                   "top_p": w.top_p, "input_sets_rotated": n_sets, "ideal_bytes": ideal},
+        "hbm_gbs_step": round(ideal / (ms * 1e-3) / 1e9, 1),
+        "pct_peak_step": round(100 * ideal / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
+        "roofline": {"bound": "hbm", "kernel": "k_rowstats", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": traffic, "kernel_ms": round(k_ms, 5),
+                     "kernel_source_hash": src_hash},
+        "wall_s_timed": round(t_wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,195 @@
+"""Thin Python binding of libspecverify.so (argument marshalling only).
+
+Every step of the verification runs in the library's HIP kernels; this module
+checks shapes and dtypes of torch tensors, passes device pointers and the
+current HIP stream through ctypes, and raises on a non-zero status.  It raises
+ImportError-style RuntimeError when the library has not been built: there is
+no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from ._build import LIB
+
+SPEC_DTYPE_F32 = 0
+SPEC_DTYPE_BF16 = 1
+
+ROW_FILTERED = 0x1
+ROW_EXACT_PATH = 0x2
+
+# Layout of spec_row_stats_t (32 bytes), for viewing a stats tensor from numpy.
+ROW_STATS_FIELDS = [("max_logit", "<f4"), ("thresh", "<f4"), ("n_kept", "<i4"),
+                    ("flags", "<i4"), ("z_kept", "<f8"), ("prob_at_token", "<f8")]
+ROW_STATS_BYTES = 32
+
+EXPORTS = ["spec_verify", "spec_verify_greedy", "spec_verify_stats", "spec_rng_uniforms",
+           "spec_profile_events", "spec_status_string", "spec_release_workspace"]
+
+_lib = None
+
+
+class SpecVerifyError(RuntimeError):
+    pass
+
+
+def load(path: str = LIB) -> ctypes.CDLL:
+    """Load the HIP library (fails loudly when it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"HIP library {path} is not built; run __graft_entry__.build() "
+            "(hipcc --offload-arch=gfx950) first")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, u64, f64p = (ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_uint64,
+                               ctypes.c_void_p)
+    L.spec_verify.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32, i32]
+    L.spec_verify.restype = i32
+    L.spec_verify_greedy.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32]
+    L.spec_verify_greedy.restype = i32
+    L.spec_verify_stats.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp,
+                                    i32, i32, vp, vp]
+    L.spec_verify_stats.restype = i32
+    L.spec_rng_uniforms.argtypes = [u64, i32, i32, f64p, f64p, vp]
+    L.spec_rng_uniforms.restype = i32
+    L.spec_profile_events.argtypes = [vp, vp]
+    L.spec_profile_events.restype = i32
+    L.spec_status_string.argtypes = [i32]
+    L.spec_status_string.restype = ctypes.c_char_p
+    L.spec_release_workspace.argtypes = []
+    L.spec_release_workspace.restype = None
+    _lib = L
+    return L
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        msg = load().spec_status_string(rc).decode()
+        raise SpecVerifyError(f"spec_verify status {rc}: {msg}")
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return SPEC_DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return SPEC_DTYPE_BF16
+    raise TypeError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_handle(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _outputs(B, K, device, out_tokens, out_num):
+    if out_tokens is None:
+        out_tokens = torch.empty((B, K + 1), dtype=torch.int32, device=device)
+    if out_num is None:
+        out_num = torch.empty((B,), dtype=torch.int32, device=device)
+    assert out_tokens.dtype == torch.int32 and out_tokens.numel() == B * (K + 1)
+    assert out_num.dtype == torch.int32 and out_num.numel() == B
+    _dev(out_tokens, "out_tokens")
+    _dev(out_num, "out_num_accepted")
+    return out_tokens, out_num
+
+
+def _shapes(target, draft, tokens, need_draft=True):
+    _dev(target, "target_logits")
+    B, K1, V = target.shape
+    K = K1 - 1
+    if K > 0:
+        if need_draft:
+            assert draft is not None and tuple(draft.shape) == (B, K, V), "draft must be [B, K, V]"
+            _dev(draft, "draft_logits")
+        assert tokens is not None and tokens.dtype == torch.int32 and tuple(tokens.shape) == (B, K)
+        _dev(tokens, "draft_tokens")
+    return B, K, V
+
+
+def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor | None,
+                temperature: float, top_k: int = 0, top_p: float = 1.0, seed: int = 0,
+                out_tokens=None, out_num_accepted=None, stream=None):
+    """Verify a batch: target [B, K+1, V], draft [B, K, V] (bf16 or f32),
+    tokens [B, K] int32.  Returns (out_tokens [B, K+1], out_num_accepted [B])."""
+    B, K, V = _shapes(target, draft, tokens, need_draft=temperature > 0)
+    out_tokens, out_num = _outputs(B, K, target.device, out_tokens, out_num_accepted)
+    use_draft = draft is not None and K > 0 and temperature > 0
+    ddt = _dtype_code(draft) if use_draft else SPEC_DTYPE_F32
+    rc = load().spec_verify(_ptr(target), _ptr(draft) if use_draft else None,
+                            _ptr(tokens) if K > 0 else None, B, K, V, float(temperature),
+                            int(top_k), float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                            _ptr(out_tokens), _ptr(out_num), _stream_handle(stream),
+                            _dtype_code(target), ddt)
+    _check(rc)
+    return out_tokens, out_num
+
+
+def spec_verify_greedy(target: torch.Tensor, tokens: torch.Tensor | None, out_tokens=None,
+                       out_num_accepted=None, stream=None):
+    _dev(target, "target_logits")
+    B, K1, V = target.shape
+    K = K1 - 1
+    if K > 0:
+        assert tokens is not None and tokens.dtype == torch.int32 and tuple(tokens.shape) == (B, K)
+        _dev(tokens, "draft_tokens")
+    out_tokens, out_num = _outputs(B, K, target.device, out_tokens, out_num_accepted)
+    rc = load().spec_verify_greedy(_ptr(target), _ptr(tokens) if K > 0 else None, B, K, V,
+                                   _ptr(out_tokens), _ptr(out_num), _stream_handle(stream),
+                                   _dtype_code(target))
+    _check(rc)
+    return out_tokens, out_num
+
+
+def spec_verify_stats(target, draft, tokens, temperature, top_k=0, top_p=1.0, seed=0,
+                      stream=None):
+    """spec_verify plus per-row intermediates.  Returns
+    (out_tokens, out_num_accepted, target_stats uint8[B, K+1, 32], draft_stats uint8[B, K, 32])."""
+    B, K, V = _shapes(target, draft, tokens)
+    out_tokens, out_num = _outputs(B, K, target.device, None, None)
+    ts = torch.empty((B, K + 1, ROW_STATS_BYTES), dtype=torch.uint8, device=target.device)
+    ds = torch.empty((B, max(K, 0), ROW_STATS_BYTES), dtype=torch.uint8, device=target.device)
+    ddt = _dtype_code(draft) if (draft is not None and K > 0) else SPEC_DTYPE_F32
+    rc = load().spec_verify_stats(_ptr(target), _ptr(draft) if K > 0 else None,
+                                  _ptr(tokens) if K > 0 else None, B, K, V, float(temperature),
+                                  int(top_k), float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                  _ptr(out_tokens), _ptr(out_num), _stream_handle(stream),
+                                  _dtype_code(target), ddt, _ptr(ts),
+                                  _ptr(ds) if K > 0 else None)
+    _check(rc)
+    return out_tokens, out_num, ts, ds
+
+
+def rng_uniforms(seed: int, B: int, K: int, device="cuda", stream=None):
+    ua = torch.empty((B, K), dtype=torch.float64, device=device)
+    us = torch.empty((B, K + 1), dtype=torch.float64, device=device)
+    rc = load().spec_rng_uniforms(int(seed) & 0xFFFFFFFFFFFFFFFF, B, K,
+                                  _ptr(ua) if K > 0 else None, _ptr(us), _stream_handle(stream))
+    _check(rc)
+    return ua, us
+
+
+def profile_events(before, after) -> None:
+    """Arm the measurement hook with two hipEvent_t handles (ints) or clear it."""
+    _check(load().spec_profile_events(ctypes.c_void_p(before) if before else None,
+                                      ctypes.c_void_p(after) if after else None))
+
+
+def release_workspace() -> None:
+    load().spec_release_workspace()

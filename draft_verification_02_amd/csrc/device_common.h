@@ -1,0 +1,124 @@
+// device_common.h — small device helpers shared by the verification kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sv {
+
+constexpr int kBlock = 256;       // threads per workgroup (4 wave64)
+constexpr int kWaves = kBlock / 64;
+constexpr int kEPT = 32;          // elements per thread per streaming tile
+constexpr int kTile = kBlock * kEPT;  // 8192 elements per streaming tile
+
+enum { DT_F32 = 0, DT_BF16 = 1 };
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load marked non-temporal (data is read once).
+__device__ __forceinline__ u32x4 ld16_nt(const void* p) {
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// One stored logit, widened to float (exact for both formats).
+__device__ __forceinline__ float load_logit(const char* row, int dt, long long i) {
+    if (dt == DT_F32) return reinterpret_cast<const float*>(row)[i];
+    const uint32_t h = reinterpret_cast<const uint16_t*>(row)[i];
+    return __uint_as_float(h << 16);
+}
+
+// Order-preserving 32-bit key of a float: a < b  <=>  key(a) < key(b) for
+// non-NaN values; -0 and +0 map to the same key.
+__device__ __forceinline__ uint32_t fkey(float f) {
+    uint32_t u = __float_as_uint(f);
+    u = (u == 0x80000000u) ? 0u : u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_to_float(uint32_t k) {
+    const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// ---- wave64 reductions (fixed combination order, hence deterministic) ----
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const unsigned long long o = __shfl_xor(v, off, 64);
+        v = o > v ? o : v;
+    }
+    return v;
+}
+
+// Block-wide max / sum over kBlock threads through LDS (fixed order).
+__device__ __forceinline__ float block_max(float v, float* s4) {
+    v = wave_max(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) s4[wid] = v;
+    __syncthreads();
+    float r = s4[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r = fmaxf(r, s4[w]);
+    return r;
+}
+__device__ __forceinline__ double block_sum(double v, double* s4) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) s4[wid] = v;
+    __syncthreads();
+    double r = s4[0];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) r += s4[w];
+    return r;
+}
+
+// ---- Philox4x32-10 -------------------------------------------------------
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11): ten rounds; each multiplies counter words 0 and 2 by the round
+// constants, splits the products into high and low halves and mixes the high
+// halves with words 1 and 3 and the key; the key advances by the Weyl
+// constants between rounds.
+struct U4 { uint32_t x, y, z, w; };
+
+__device__ __forceinline__ U4 philox4x32_10(U4 c, uint32_t k0, uint32_t k1) {
+    constexpr uint32_t M0 = 0xD2511F53u, M1 = 0xCD9E8D57u;
+    constexpr uint32_t W0 = 0x9E3779B9u, W1 = 0xBB67AE85u;
+#pragma unroll
+    for (int r = 0; r < 10; ++r) {
+        const uint32_t hi0 = __umulhi(M0, c.x), lo0 = M0 * c.x;
+        const uint32_t hi1 = __umulhi(M1, c.z), lo1 = M1 * c.z;
+        c = U4{hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0};
+        k0 += W0;
+        k1 += W1;
+    }
+    return c;
+}
+
+enum { PURPOSE_ACCEPT = 0, PURPOSE_SAMPLE = 1 };
+
+__device__ __forceinline__ U4 draw_block(uint64_t seed, uint32_t b, uint32_t k, uint32_t purpose) {
+    return philox4x32_10(U4{b, k, purpose, 0u}, static_cast<uint32_t>(seed),
+                         static_cast<uint32_t>(seed >> 32));
+}
+// 24-bit uniform in [0, 1) from word 0.
+__device__ __forceinline__ double uniform24(U4 w) { return (double)(w.x >> 8) * 0x1p-24; }
+// 53-bit uniform in [0, 1) from words 0 and 1 (27 + 26 bits).
+__device__ __forceinline__ double uniform53(U4 w) {
+    return ((double)(w.x >> 5) * 67108864.0 + (double)(w.y >> 6)) * 0x1p-53;
+}
+
+}  // namespace sv

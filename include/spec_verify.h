@@ -1,0 +1,180 @@
+/*
+ * spec_verify.h — batched speculative-decoding verification on MI355X (gfx950).
+ *
+ * One call verifies B sequences.  For sequence b the caller passes the target
+ * model's logits at K+1 positions and the drafter's logits at K positions,
+ * plus the K drafted token ids.  The library
+ *   1. applies temperature, then top-k, then top-p (on the renormalised top-k
+ *      set) identically to every target and draft row, and normalises them to
+ *      p_0..p_K and q_0..q_{K-1};
+ *   2. accepts drafted token d_k while u_k * q_k(d_k) < p_k(d_k), i.e. with
+ *      probability min(1, p/q), and stops at the first rejection j;
+ *   3. emits d_0..d_{j-1} and then one more token: after a rejection a draw
+ *      from max(0, p_j - q_j) normalised, or, when all K drafts are accepted,
+ *      the bonus token drawn from p_K.
+ * Greedy mode instead accepts the longest prefix with d_k == argmax p_k and
+ * emits the target argmax at the first mismatch.
+ *
+ * Where these steps are defined:
+ *  - accept test, stop at the first rejection, residual distribution and the
+ *    identity that makes the output distribution equal to p: "FlashMap: Flow
+ *    Map Speculative Decoding and the Mathematical Elimination of Suffix
+ *    Decay", section 4 (The Rejection Sampling Invariant); "Speculative
+ *    decoding and multi-token prediction: how LLMs generate faster", sections
+ *    "Draft and verify" and "Why the output is identical";
+ *  - K+1 target distributions, bonus token, greedy longest-prefix mode:
+ *    "DFlash", section 4 (inference and distribution equivalence);
+ *  - logits / temperature before the softmax: FlashMap page, section 5;
+ *  - top-k and top-p applied the same way to both distributions:
+ *    threatfrontier page, "Why the output is identical".
+ *
+ * Readings of points the pages leave open (all documented in the repository
+ * design notes): accept on u * q < p with u in [0, 1) (so p = 0 is never
+ * accepted and p >= q always is); top-k keeps every token whose logit is at
+ * least the k-th largest (ties kept); top-p keeps a group of equal logits
+ * while the mass of all strictly larger logits is below top_p (the top group
+ * is always kept, the crossing group whole); when rounding leaves no
+ * residual mass after a rejection the token is drawn from p_j; draws use
+ * the inverse CDF in ascending token order.
+ *
+ * Random numbers: Philox4x32-10 (Salmon et al., SC'11) with key
+ * (seed low 32 bits, seed high 32 bits) and counter (b, k, purpose, 0);
+ * purpose 0 = accept test at position k, uniform (w0 >> 8) * 2^-24;
+ * purpose 1 = draw at stop position j, uniform
+ * ((w0 >> 5) * 2^26 + (w1 >> 6)) * 2^-53.  A call is a pure function of its
+ * inputs and seed: repeated calls give identical outputs.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller.  Inputs must
+ *    stay alive and unmodified, and outputs untouched, until the stream has
+ *    reached the end of the call.
+ *  - Calls are asynchronous and stream-ordered on `stream` (a hipStream_t;
+ *    NULL means the null stream).  No call synchronises the device, except
+ *    that the first call on a (device, stream) pair, or one that needs a larger
+ *    workspace, allocates library-owned scratch memory (hipMalloc) and waits
+ *    for the stream before releasing a smaller one.
+ *  - Layouts are row-major and contiguous: target [B][K+1][V], draft
+ *    [B][K][V], draft_tokens [B][K], out_tokens [B][K+1], out_num_accepted [B].
+ *    Rows whose byte address is 16-byte aligned take the vector load path;
+ *    other alignments are correct but slower.
+ *  - Return values report host-checkable problems only (SPEC_E_*); device-side
+ *    preconditions are documented and not checked: no NaN or +inf logits, and
+ *    every row has at least one finite logit that survives its filters.
+ *  - A drafted id outside [0, V) has p = q = 0 and is rejected.
+ *  - out_tokens[b] holds d_0..d_{j-1}, then the emitted token, then -1 up to
+ *    K+1 entries; out_num_accepted[b] = j in [0, K].
+ *  - The library keeps one workspace per (device, stream): concurrent calls on
+ *    the same stream from several host threads must be serialised by the
+ *    caller; calls on different streams may overlap.
+ */
+#ifndef SPEC_VERIFY_H
+#define SPEC_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Storage formats of logits. */
+typedef enum { SPEC_DTYPE_F32 = 0, SPEC_DTYPE_BF16 = 1 } spec_dtype_t;
+
+/* Status codes. */
+typedef enum {
+    SPEC_OK = 0,
+    SPEC_E_INVALID = 1,     /* bad pointer, size, temperature, top_p, ... */
+    SPEC_E_UNSUPPORTED = 2, /* unknown dtype code                         */
+    SPEC_E_NOMEM = 3,       /* workspace allocation failed                */
+    SPEC_E_LAUNCH = 4       /* a HIP runtime call or kernel launch failed */
+} spec_status_t;
+
+/* Per-row intermediates written by spec_verify_stats (32 bytes). */
+typedef struct {
+    float max_logit;       /* M: largest raw logit of the row (always kept)   */
+    float thresh;          /* keep threshold: kept <=> x >= thresh (-inf: all) */
+    int32_t n_kept;        /* number of kept tokens                           */
+    int32_t flags;         /* SPEC_ROW_* bits                                 */
+    double z_kept;         /* sum over kept tokens of exp((x - M) / T)        */
+    double prob_at_token;  /* p_k(d_k) or q_k(d_k); 0 for an out-of-range id;
+                              unused (NaN) for the bonus row p_K              */
+} spec_row_stats_t;
+
+#define SPEC_ROW_FILTERED 0x1  /* top-k or top-p active on this row          */
+#define SPEC_ROW_EXACT_PATH 0x2 /* resolved by re-reading the row            */
+
+/*
+ * Sampling-mode verification (temperature > 0), or greedy semantics when
+ * temperature == 0 (then draft_logits and draft_dtype are not used and may be
+ * NULL / any value).
+ *   target_logits  [B][K+1][V] in target_dtype
+ *   draft_logits   [B][K][V]   in draft_dtype (may be NULL when K == 0)
+ *   draft_tokens   [B][K] int32 (may be NULL when K == 0)
+ *   B >= 0 (B == 0 is a no-op), K >= 0, V >= 1, B*(2K+1)*V < 2^40
+ *   temperature    finite, >= 0
+ *   top_k          <= 0 or >= V: disabled; otherwise keep logits >= the
+ *                  top_k-th largest
+ *   top_p          in (0, 1]; 1 disables it
+ *   seed           key of the random stream
+ *   out_tokens     [B][K+1] int32, out_num_accepted [B] int32
+ *   stream         hipStream_t or NULL
+ *   target_dtype, draft_dtype: spec_dtype_t codes
+ * Returns SPEC_OK or an error code; on error nothing is launched.
+ */
+int spec_verify(const void* target_logits, const void* draft_logits,
+                const int32_t* draft_tokens, int B, int K, int V,
+                float temperature, int top_k, float top_p, uint64_t seed,
+                int32_t* out_tokens, int32_t* out_num_accepted, void* stream,
+                int target_dtype, int draft_dtype);
+
+/*
+ * Greedy verification: g_k = argmax of target row k (lowest index among equal
+ * maxima), accept while d_k == g_k, emit g_j at the first mismatch j (or the
+ * bonus argmax g_K).  Reads target logits only.  Same conventions as
+ * spec_verify.
+ */
+int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens,
+                       int B, int K, int V, int32_t* out_tokens,
+                       int32_t* out_num_accepted, void* stream,
+                       int target_dtype);
+
+/*
+ * spec_verify plus the per-row intermediates: target_stats [B][K+1] and
+ * draft_stats [B][K] (device arrays of spec_row_stats_t, either may be NULL).
+ * Sampling mode only (temperature > 0).  Outputs are identical to
+ * spec_verify's for the same arguments.
+ */
+int spec_verify_stats(const void* target_logits, const void* draft_logits,
+                      const int32_t* draft_tokens, int B, int K, int V,
+                      float temperature, int top_k, float top_p, uint64_t seed,
+                      int32_t* out_tokens, int32_t* out_num_accepted,
+                      void* stream, int target_dtype, int draft_dtype,
+                      spec_row_stats_t* target_stats,
+                      spec_row_stats_t* draft_stats);
+
+/*
+ * Diagnostic: the uniforms the verifier draws for `seed`, computed by the
+ * same device generator: u_accept [B][K] (purpose 0) and u_sample [B][K+1]
+ * (purpose 1), as doubles in device memory.  Either pointer may be NULL.
+ */
+int spec_rng_uniforms(uint64_t seed, int B, int K, double* u_accept,
+                      double* u_sample, void* stream);
+
+/*
+ * Measurement hook: when both are non-NULL hipEvent_t handles, the next
+ * sampling-mode call records `before` on its stream just before launching its
+ * streaming (dominant) kernel and `after` just after it; the hook is then
+ * cleared.  Passing NULLs clears it.  Not thread-safe with concurrent calls.
+ */
+int spec_profile_events(void* before, void* after);
+
+/* Human-readable text for a status code (static storage). */
+const char* spec_status_string(int status);
+
+/* Free every workspace the library holds (waits for their streams). */
+void spec_release_workspace(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPEC_VERIFY_H */

@@ -1,0 +1,175 @@
+"""Helpers for comparing the HIP library with the CPU oracle.
+
+Tolerances (spec bar):
+  * greedy: token ids and accepted counts bit-exact;
+  * sampling: token ids exact, except where the first differing decision is
+    ambiguous in floating point: an accept test with |u*q - p| <= 1e-5 * q,
+    a nucleus boundary within 1e-6 of top_p on a row that decides it, or an
+    inverse-CDF draw within 1e-12 * S of a cumulative boundary.  Such
+    mismatches are counted and must stay at or below 1e-6 of the decisions;
+  * intermediates: z_kept and p(d_k) / q(d_k) within 1e-5 relative, except on
+    rows whose nucleus boundary is ambiguous (they may keep a different set).
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+from draft_verification_02_amd import binding
+from draft_verification_02_amd import workloads as wl
+
+ACCEPT_BAND = 1e-5
+NUCLEUS_BAND = 1e-6
+SAMPLE_BAND = 1e-12
+PROB_RTOL = 1e-5
+
+STATS_DTYPE = np.dtype(binding.ROW_STATS_FIELDS)
+
+
+def to_device(a: np.ndarray, dev="cuda") -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def upload(w: wl.Workload, dev="cuda"):
+    t = to_device(w.target, dev)
+    d = to_device(w.draft, dev) if w.draft is not None else None
+    k = torch.from_numpy(np.ascontiguousarray(w.tokens)).to(dev)
+    return t, d, k
+
+
+def f32(x) -> float:
+    """The float32 value the C ABI receives for a float argument."""
+    return float(np.float32(x))
+
+
+def stats_np(ts: torch.Tensor) -> np.ndarray:
+    return ts.cpu().numpy().reshape(-1).view(STATS_DTYPE).reshape(ts.shape[:-1])
+
+
+def run_oracle(w: wl.Workload, seqs=None):
+    """Oracle on all sequences, or on the listed ones (each with its own
+    global sequence index so that the draws match)."""
+    if seqs is None:
+        seqs = range(w.B)
+    outs = []
+    for b in seqs:
+        outs.append(oracle.verify(w.target[b:b + 1], None if w.draft is None else w.draft[b:b + 1],
+                                  w.tokens[b:b + 1], f32(w.temperature), w.top_k, f32(w.top_p),
+                                  w.seed, seq_base=int(b)))
+    return list(seqs), outs
+
+
+class Report:
+    def __init__(self):
+        self.decisions = 0
+        self.mismatch_tolerated = 0
+        self.rows_checked = 0
+        self.rows_ambiguous = 0
+        self.details = []
+
+    def __repr__(self):
+        return (f"Report(decisions={self.decisions}, tolerated={self.mismatch_tolerated}, "
+                f"rows={self.rows_checked}, ambiguous_rows={self.rows_ambiguous})")
+
+
+def compare_sampling(w: wl.Workload, g_tok, g_num, g_ts, g_ds, seqs, outs, report=None,
+                     check_stats=True) -> Report:
+    """Compare GPU outputs (numpy) for the listed sequences with oracle results."""
+    rep = report or Report()
+    K = w.K
+    invT = 1.0 / f32(w.temperature)
+    for b, r in zip(seqs, outs):
+        ti, di = r["target_info"][0], r["draft_info"][0]
+        j_o = int(r["num_accepted"][0])
+        j_g = int(g_num[b])
+        rep.decisions += j_o + (1 if j_o < K else 0) + 1
+        amb_t = ti["nucleus_margin"] <= NUCLEUS_BAND
+        amb_d = di["nucleus_margin"] <= NUCLEUS_BAND if K > 0 else np.zeros(0, bool)
+        if check_stats:
+            gt = g_ts[b]
+            gd = g_ds[b] if K > 0 else None
+            for k in range(K + 1):
+                rep.rows_checked += 1
+                if amb_t[k]:
+                    rep.rows_ambiguous += 1
+                    continue
+                _check_row(gt[k], ti[k], invT, k < K, f"b{b} target row {k}")
+            for k in range(K):
+                rep.rows_checked += 1
+                if amb_d[k]:
+                    rep.rows_ambiguous += 1
+                    continue
+                _check_row(gd[k], di[k], invT, True, f"b{b} draft row {k}")
+        if j_g == j_o and np.array_equal(g_tok[b], r["tokens"][0]):
+            continue
+        # first differing decision must be ambiguous
+        m = min(j_g, j_o)
+        if j_g != j_o:
+            am = r["accept_margin"][0, m]
+            ok = (am <= ACCEPT_BAND) or amb_t[m] or (m < K and amb_d[m])
+            why = f"accept at position {m}: margin {am:.3g}"
+        else:
+            sm = r["sample_margin"][0]
+            ok = (sm <= SAMPLE_BAND) or amb_t[m] or (m < K and amb_d[m])
+            why = f"draw at position {m}: margin {sm:.3g}"
+        assert ok, (f"sequence {b}: GPU {g_tok[b].tolist()} (j={j_g}) vs oracle "
+                    f"{r['tokens'][0].tolist()} (j={j_o}); {why} is outside every band")
+        rep.mismatch_tolerated += 1
+        rep.details.append((b, why))
+    assert rep.mismatch_tolerated <= 1e-6 * rep.decisions, rep
+    return rep
+
+
+def _check_row(g, o, invT, has_token, where):
+    # the row max is always kept, so both sides report the same element
+    ms = float(np.float64(g["max_logit"]) * invT)
+    assert abs(ms - o["max_scaled"]) <= 1e-12 * max(1.0, abs(o["max_scaled"])), where
+    assert _rel(g["z_kept"], o["z_kept"]) <= PROB_RTOL, (where, g["z_kept"], o["z_kept"])
+    assert int(g["n_kept"]) == int(o["n_kept"]), (where, g["n_kept"], o["n_kept"])
+    if int(g["flags"]) & binding.ROW_FILTERED:
+        assert np.float64(g["thresh"]) == o["thresh"], (where, g["thresh"], o["thresh"])
+    if has_token:
+        po, pg = o["prob_at_token"], g["prob_at_token"]
+        if np.isnan(po):  # out-of-range token
+            assert pg == 0.0, where
+        else:
+            assert (po == 0.0 and pg == 0.0) or _rel(pg, po) <= PROB_RTOL, (where, pg, po)
+
+
+def _rel(a, b):
+    a, b = float(a), float(b)
+    if a == b:
+        return 0.0
+    return abs(a - b) / max(abs(b), 1e-300)
+
+
+def gpu_sampling(w: wl.Workload, dev="cuda", stats=True):
+    t, d, k = upload(w, dev)
+    if stats:
+        tok, num, ts, ds = binding.spec_verify_stats(t, d, k, w.temperature, w.top_k, w.top_p, w.seed)
+        torch.cuda.synchronize()
+        return tok.cpu().numpy(), num.cpu().numpy(), stats_np(ts), (stats_np(ds) if w.K > 0 else None)
+    tok, num = binding.spec_verify(t, d, k, w.temperature, w.top_k, w.top_p, w.seed)
+    torch.cuda.synchronize()
+    return tok.cpu().numpy(), num.cpu().numpy(), None, None
+
+
+def check_sampling(w: wl.Workload, seqs=None, report=None, check_stats=True) -> Report:
+    g_tok, g_num, g_ts, g_ds = gpu_sampling(w, stats=check_stats)
+    s, outs = run_oracle(w, seqs)
+    return compare_sampling(w, g_tok, g_num, g_ts, g_ds, s, outs, report, check_stats)
+
+
+def check_greedy(w: wl.Workload, via_verify=False):
+    t, _, k = upload(w)
+    if via_verify:
+        tok, num = binding.spec_verify(t, None, k, 0.0)
+    else:
+        tok, num = binding.spec_verify_greedy(t, k)
+    torch.cuda.synchronize()
+    ref = oracle.verify_greedy(w.target, w.tokens)
+    np.testing.assert_array_equal(num.cpu().numpy(), ref["num_accepted"])
+    np.testing.assert_array_equal(tok.cpu().numpy(), ref["tokens"])

@@ -1,0 +1,72 @@
+"""CPU checks of the C-ABI library: it loads, exports every function that
+include/spec_verify.h declares, and rejects bad arguments on the host (these
+calls return before any device work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from draft_verification_02_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "spec_verify.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_\s\*]*?\b(spec_[a-z_]+)\s*\(", text,
+                       flags=re.M)
+    return sorted(set(names))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB):
+        from draft_verification_02_amd import _build
+        _build.build()
+    return binding.load()
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    assert names == sorted(binding.EXPORTS), names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings(lib):
+    assert lib.spec_status_string(0) == b"ok"
+    assert b"invalid" in lib.spec_status_string(1)
+    assert lib.spec_status_string(12345) == b"unknown status"
+
+
+def _call(lib, **kw):
+    a = dict(target=ctypes.c_void_p(16), draft=ctypes.c_void_p(16), tokens=ctypes.c_void_p(16),
+             B=1, K=1, V=4, T=1.0, top_k=0, top_p=1.0, seed=0, out=ctypes.c_void_p(16),
+             num=ctypes.c_void_p(16), stream=None, tdt=0, ddt=0)
+    a.update(kw)
+    return lib.spec_verify(a["target"], a["draft"], a["tokens"], a["B"], a["K"], a["V"], a["T"],
+                           a["top_k"], a["top_p"], a["seed"], a["out"], a["num"], a["stream"],
+                           a["tdt"], a["ddt"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1.0), 1), (dict(T=float("nan")), 1), (dict(T=float("inf")), 1),
+    (dict(top_p=0.0), 1), (dict(top_p=1.5), 1), (dict(top_p=float("nan")), 1),
+    (dict(B=-1), 1), (dict(K=-1), 1), (dict(V=0), 1),
+    (dict(tdt=7), 2), (dict(ddt=9), 2),
+    (dict(target=None), 1), (dict(out=None), 1), (dict(draft=None), 1), (dict(tokens=None), 1),
+    (dict(T=1e-39), 1),
+])
+def test_invalid_arguments_rejected_on_host(lib, kw, code):
+    assert _call(lib, **kw) == code
+
+
+def test_empty_batch_returns_ok_without_device_work(lib):
+    assert _call(lib, B=0, target=None, draft=None, tokens=None, out=None, num=None) == 0
+    assert lib.spec_verify_greedy(None, None, 0, 3, 10, None, None, None, 1) == 0

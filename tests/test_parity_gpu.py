@@ -1,0 +1,223 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle.
+
+Workloads are the five measured configurations (full size; the oracle checks
+every sequence where it finishes in seconds, otherwise a fixed sample of
+sequences computed one by one) plus smaller cases with the same generators
+that span several tiles and a ragged tail, and the degenerate cases.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_verification_02_amd import binding
+from draft_verification_02_amd import workloads as wl
+
+from parity import check_greedy, check_sampling, f32, gpu_sampling, upload
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(name):
+    print(f"[case] {name}", flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Random numbers
+# ---------------------------------------------------------------------------
+
+def test_device_uniforms_match_oracle_bitwise():
+    _print_case("uniforms")
+    seed, B, K = 0xC0FFEE0300000007, 300, 15
+    ua, us = binding.rng_uniforms(seed, B, K)
+    ua, us = ua.cpu().numpy(), us.cpu().numpy()
+    for b in range(B):
+        for k in range(K):
+            assert ua[b, k] == oracle.u24(seed, b, k, 0)
+        for k in range(K + 1):
+            assert us[b, k] == oracle.u53(seed, b, k, 1)
+
+
+# ---------------------------------------------------------------------------
+# The five measured workloads
+# ---------------------------------------------------------------------------
+
+def test_c1_tiny_all_rounds():
+    _print_case("c1 x256 rounds")
+    from parity import Report
+    rep = Report()
+    for rnd in range(wl.C1_ROUNDS):
+        w = wl.config(1, rnd)
+        check_sampling(w, report=rep)
+    print(rep)
+
+
+def test_c2_block16_single_stream():
+    _print_case("c2 full")
+    w = wl.config(2)
+    print(check_sampling(w))
+
+
+def test_c2_many_seeds_small_vocab():
+    """c2's generator at V=20000 over many seeds: more accept decisions."""
+    _print_case("c2-like V=20000 x16 seeds")
+    from parity import Report
+    rep = Report()
+    for rnd in range(16):
+        w = wl.config(2, rnd, V=20000, B=4)
+        check_sampling(w, report=rep)
+    print(rep)
+
+
+def test_c3_concurrent_batch_full_size_sampled():
+    _print_case("c3 full, 6 sequences checked")
+    w = wl.config(3)
+    print(check_sampling(w, seqs=[0, 5, 11, 17, 26, 31]))
+
+
+def test_c3_generator_small_batch_all_sequences():
+    _print_case("c3-like B=8 V=40000")
+    w = wl.config(3, 1, B=8, V=40000)
+    print(check_sampling(w))
+
+
+def test_c4_greedy_full():
+    _print_case("c4 greedy full")
+    w = wl.config(4)
+    check_greedy(w)
+    check_greedy(w, via_verify=True)
+
+
+def test_c5_large_batch_full_size_sampled():
+    _print_case("c5 full, 24 sequences checked")
+    w = wl.config(5)
+    print(check_sampling(w, seqs=list(range(0, 256, 11))))
+
+
+# ---------------------------------------------------------------------------
+# Edge cases
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("V", [1, 2, 7, 8191, 8192, 8193, 12347])
+@pytest.mark.parametrize("tdt,ddt", [(wl.F32, wl.F32), (wl.BF16, wl.F32), (wl.BF16, wl.BF16)])
+def test_ragged_vocab_and_dtypes(V, tdt, ddt):
+    _print_case(f"ragged V={V} dtypes={tdt},{ddt}")
+    w = wl.make(3, 4, V, target_dtype=tdt, draft_dtype=ddt, temperature=1.0, rho=0.9,
+                seed=V * 7 + tdt, vseed=V + 99)
+    check_sampling(w)
+
+
+@pytest.mark.parametrize("top_k,top_p", [(1, 1.0), (5, 1.0), (50, 0.95), (0, 0.5), (0, 0.99),
+                                         (3000, 1.0), (100000, 0.9), (0, 1e-6)])
+def test_filters(top_k, top_p):
+    _print_case(f"filters top_k={top_k} top_p={top_p}")
+    w = wl.make(4, 5, 30011, temperature=0.9, top_k=top_k, top_p=top_p, rho=0.8, n_boost=3,
+                seed=top_k + 17, vseed=top_k + 5)
+    check_sampling(w)
+
+
+def test_ties_at_filter_thresholds():
+    """Quantised logits: heavy ties at the top-k value and inside nucleus groups."""
+    _print_case("ties")
+    rng = np.random.default_rng(9)
+    B, K, V = 6, 3, 5000
+    x = rng.integers(-8, 9, size=(B, K + 1, V)).astype(np.float32) * np.float32(0.5)
+    d = rng.integers(-8, 9, size=(B, K, V)).astype(np.float32) * np.float32(0.5)
+    toks = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    for top_k, top_p in [(7, 1.0), (40, 0.8), (0, 0.7)]:
+        w = wl.Workload("ties", B, K, V, wl.f32_to_bf16_bits(x), d, toks, 1.0, top_k, top_p, 77)
+        check_sampling(w)
+
+
+def test_neg_inf_logits_and_out_of_range_tokens():
+    _print_case("-inf and out-of-range")
+    rng = np.random.default_rng(10)
+    B, K, V = 5, 4, 9000
+    x = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    x[:, :, ::3] = -np.inf
+    d = (0.7 * x[:, :K] + rng.standard_normal((B, K, V))).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    toks[0, 0] = -1
+    toks[1, 1] = V
+    toks[2, 0] = 3  # a -inf target logit
+    for top_k, top_p in [(0, 1.0), (20, 0.9)]:
+        w = wl.Workload("neginf", B, K, V, x, d, toks, 1.0, top_k, top_p, 5)
+        check_sampling(w)
+
+
+def test_k0_bonus_only_and_identical_distributions():
+    _print_case("K=0 and identical rows")
+    w = wl.make(7, 0, 20000, seed=3, vseed=4)
+    check_sampling(w)
+    rng = np.random.default_rng(2)
+    B, K, V = 4, 6, 10000
+    x = (rng.standard_normal((B, K + 1, V)) * 3).astype(np.float32)
+    toks = rng.integers(0, V, size=(B, K)).astype(np.int32)
+    w = wl.Workload("same", B, K, V, x, x[:, :K].copy(), toks, 1.3, 0, 1.0, 8)
+    g_tok, g_num, _, _ = gpu_sampling(w, stats=False)
+    assert (g_num == K).all()
+    check_sampling(w)
+
+
+@pytest.mark.parametrize("T", [0.05, 0.37, 2.5])
+def test_temperatures(T):
+    _print_case(f"T={T}")
+    w = wl.make(3, 5, 16385, temperature=T, rho=0.9, n_boost=2, seed=int(T * 100), vseed=1)
+    check_sampling(w)
+
+
+def test_greedy_edge_cases():
+    _print_case("greedy edges")
+    rng = np.random.default_rng(12)
+    for (B, K, V) in [(3, 0, 100), (5, 7, 1), (4, 6, 8193), (9, 3, 12347)]:
+        x = rng.integers(-3, 4, size=(B, K + 1, V)).astype(np.float32)  # ties
+        g = x.argmax(-1).astype(np.int32)
+        toks = g[:, :K].copy()
+        if K > 0:
+            toks[::2, K // 2] = (toks[::2, K // 2] + 1) % max(V, 1)
+        for tgt in (x, wl.f32_to_bf16_bits(x)):
+            w = wl.Workload("g", B, K, V, tgt, None, toks, 0.0, 0, 1.0, 0)
+            check_greedy(w)
+
+
+def test_unaligned_rows():
+    """bf16 rows of odd length start at 2-byte offsets: element-wise load path."""
+    _print_case("unaligned")
+    w = wl.make(3, 3, 9999, target_dtype=wl.BF16, draft_dtype=wl.BF16, temperature=1.0,
+                top_p=0.9, seed=31, vseed=32)
+    check_sampling(w)
+    w.temperature = 0.0
+    check_greedy(w)
+
+
+def test_deterministic_and_workspace_reuse():
+    _print_case("determinism")
+    big = wl.make(6, 5, 50000, top_p=0.9, temperature=0.8, seed=41, vseed=42)
+    small = wl.make(2, 2, 3000, seed=43, vseed=44)
+    r1 = gpu_sampling(big, stats=False)
+    r2 = gpu_sampling(small, stats=False)
+    r3 = gpu_sampling(big, stats=False)
+    r4 = gpu_sampling(small, stats=False)
+    np.testing.assert_array_equal(r1[0], r3[0])
+    np.testing.assert_array_equal(r2[0], r4[0])
+    check_sampling(big)
+    check_sampling(small)
+
+
+def test_empty_batch_is_noop():
+    _print_case("B=0")
+    t = torch.zeros((0, 3, 10), device="cuda")
+    d = torch.zeros((0, 2, 10), device="cuda")
+    k = torch.zeros((0, 2), dtype=torch.int32, device="cuda")
+    out, n = binding.spec_verify(t, d, k, 1.0)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 3) and n.shape == (0,)
+
+
+def test_stats_entry_matches_plain_entry():
+    _print_case("stats == plain")
+    w = wl.make(5, 4, 20000, top_p=0.9, top_k=100, temperature=0.7, seed=50, vseed=51)
+    a = gpu_sampling(w, stats=True)
+    b = gpu_sampling(w, stats=False)
+    np.testing.assert_array_equal(a[0], b[0])
+    np.testing.assert_array_equal(a[1], b[1])

@@ -1,0 +1,1018 @@
+// row_kernels.h — per-row kernels: one 512-thread workgroup streams one whole
+// logit row from HBM exactly once.
+//
+//  k_row     : sampling mode.  Running per-thread max / sum of exp((x-M)/T);
+//              for filtered rows (top-k or top-p) a candidate reservoir in
+//              LDS holds every logit at or above a threshold set from the
+//              row's first tile, from which the row's kept set is resolved
+//              exactly at the end; if the reservoir cannot decide (too few
+//              candidates, overflow) the workgroup falls back to an exact
+//              resolution by re-reading the row.  Writes the row record
+//              (M, Z, threshold, p(d_k) or q(d_k)) and, for target rows, the
+//              kept tokens sorted by index.
+//  k_row_argmax : greedy mode, lowest-index argmax of a target row.
+//
+// Row numbering: rows [0, B*(K+1)) are target rows b*(K+1)+k, rows
+// [B*(K+1), B*(2K+1)) are draft rows b*K+k.
+#pragma once
+
+#include <type_traits>
+
+#include "device_common.h"
+#include "../../include/spec_verify.h"
+
+namespace sv {
+
+typedef unsigned long long u64;
+
+constexpr int kRB = 512;                 // threads per row workgroup
+constexpr int kRW = kRB / 64;            // waves per row workgroup
+constexpr int kREPT = 16;                // logits per thread per tile
+constexpr int kRTile = kRB * kREPT;      // 8192 logits per tile
+constexpr int kCap = 5120;               // reservoir slots
+constexpr int kOwn = kCap / kRB;         // reservoir slots per thread (10)
+constexpr int kSeg = kCap / kRW;         // reservoir slots owned by one wave (640)
+constexpr int kR0 = 64;                  // rank among thread maxima for the first threshold
+constexpr int kListMax = 4096;           // longest kept list stored for the draw
+
+struct RowRec {
+    spec_row_stats_t s;
+    double z_all;  // sum over all tokens of exp((x - M)/T), before filters
+    double pad;
+};
+static_assert(sizeof(spec_row_stats_t) == 32, "row stats layout");
+
+struct Shape {
+    const char* target;
+    const char* draft;
+    const int32_t* tokens;
+    int B, K, V;
+    int tdt, ddt;
+    int tsz, dsz;
+    int n_trows, n_drows;
+};
+
+__device__ __forceinline__ const char* row_ptr(const Shape& sh, int row) {
+    if (row < sh.n_trows) return sh.target + (size_t)row * sh.V * sh.tsz;
+    return sh.draft + (size_t)(row - sh.n_trows) * sh.V * sh.dsz;
+}
+__device__ __forceinline__ int row_dt(const Shape& sh, int row) {
+    return row < sh.n_trows ? sh.tdt : sh.ddt;
+}
+__device__ __forceinline__ bool row_has_token(const Shape& sh, int row) {
+    return row >= sh.n_trows || (row % (sh.K + 1)) < sh.K;
+}
+__device__ __forceinline__ int row_token(const Shape& sh, int row) {
+    if (row < sh.n_trows) {
+        const int b = row / (sh.K + 1), k = row % (sh.K + 1);
+        return sh.tokens[(size_t)b * sh.K + k];
+    }
+    return sh.tokens[row - sh.n_trows];
+}
+
+// ---------------------------------------------------------------------------
+// Block helpers for kRB threads (fixed combination order: deterministic).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float rb_max(float v, float* s) {
+    v = wave_max(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+    __syncthreads();
+    float r = s[0];
+#pragma unroll
+    for (int w = 1; w < kRW; ++w) r = fmaxf(r, s[w]);
+    return r;
+}
+__device__ __forceinline__ double rb_sum(double v, double* s) {
+    v = wave_sum(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+    __syncthreads();
+    double r = s[0];
+#pragma unroll
+    for (int w = 1; w < kRW; ++w) r += s[w];
+    return r;
+}
+__device__ __forceinline__ u64 wave_sum_u64(u64 v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+__device__ __forceinline__ u64 rb_sum_u64(u64 v, u64* s) {
+    v = wave_sum_u64(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+    __syncthreads();
+    u64 r = 0;
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) r += s[w];
+    return r;
+}
+__device__ __forceinline__ u64 rb_max_u64(u64 v, u64* s) {
+    v = wave_max_u64(v);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) s[threadIdx.x >> 6] = v;
+    __syncthreads();
+    u64 r = s[0];
+#pragma unroll
+    for (int w = 1; w < kRW; ++w) r = s[w] > r ? s[w] : r;
+    return r;
+}
+
+// One wave scans 256 histogram bins from bin 255 down and returns the first
+// bin d where (sum of bins above d) + hist[d] >= target, with the sum above d.
+// bin = -1 when the total stays below target (then above = total).
+__device__ __forceinline__ void wave_find_from_top(const u64* hist, u64 target, int& bin, u64& above) {
+    const int lane = threadIdx.x & 63;
+    u64 c[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
+    const u64 ls = c[0] + c[1] + c[2] + c[3];
+    u64 incl = ls;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const u64 t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+    }
+    const u64 excl = incl - ls;
+    const u64 m = __ballot(incl >= target);
+    if (m == 0) {
+        bin = -1;
+        above = __shfl(incl, 63, 64);
+        return;
+    }
+    const int L = __ffsll((long long)m) - 1;
+    int d = 0;
+    u64 run = excl;
+    if (lane == L) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (run + c[i] >= target) {
+                d = 255 - 4 * lane - i;
+                break;
+            }
+            run += c[i];
+        }
+    }
+    bin = __shfl(d, L, 64);
+    above = __shfl(run, L, 64);
+}
+
+// Result of a block-wide selection from the top.
+struct Sel {
+    uint32_t key;     // selected group (exact key)
+    u64 above;        // weight of entries with a larger key
+    u64 group;        // weight of the selected group
+    uint32_t cnt_above, cnt_group;
+    int ok;           // 0: the total weight stays below the target
+};
+
+// Complete a key known in its top 16 bits, for widened bf16 values whose low
+// 16 bits are zero: key low half is 0 for x >= 0 and 0xFFFF for x < 0.
+__device__ __forceinline__ uint32_t bf16_key_fill(uint32_t k) {
+    return (k & 0x80000000u) ? (k & 0xFFFF0000u) : (k | 0x0000FFFFu);
+}
+
+// ---------------------------------------------------------------------------
+// Row streaming: 16-byte non-temporal loads, groups g = t*kRB*NL + j*kRB + tid
+// (each load instruction of the workgroup covers 8 KiB contiguous).  The
+// logit at slot s = j*per + q of tile t has index per*g + q.  Groups past the
+// end, the partial last group and unaligned rows use element loads.
+// ---------------------------------------------------------------------------
+template <int DT>
+struct RowStream {
+    static constexpr int esz = DT == DT_BF16 ? 2 : 4;
+    static constexpr int per = 16 / esz;
+    static constexpr int NL = kREPT / per;  // 16-byte loads per thread per tile
+    const char* rowp;
+    int V;
+    int gfull;     // groups that can be read with one 16-byte load
+    int nt;        // tiles
+    int nfull;     // leading tiles whose every group is a full 16-byte load
+
+    __device__ RowStream(const char* p, int v) : rowp(p), V(v) {
+        const bool aligned = (((uintptr_t)p) & 15) == 0;
+        gfull = aligned ? V / per : 0;
+        const int ng = (V + per - 1) / per;
+        nt = (ng + kRB * NL - 1) / (kRB * NL);
+        nfull = gfull / (kRB * NL);
+    }
+    __device__ __forceinline__ int group(int t, int j) const {
+        return t * kRB * NL + j * kRB + (int)threadIdx.x;
+    }
+    __device__ __forceinline__ int index(int t, int s) const {
+        return group(t, s / per) * per + s % per;
+    }
+    // tile t < nfull: every load in bounds, no checks
+    __device__ __forceinline__ void issue_full(int t, u32x4 (&raw)[NL]) const {
+        const char* base = rowp + (size_t)t * (kRB * NL * 16);
+        const uint32_t lane_off = threadIdx.x * 16u;
+#pragma unroll
+        for (int j = 0; j < NL; ++j) raw[j] = ld16_nt(base + j * (kRB * 16) + lane_off);
+    }
+    __device__ __forceinline__ void issue(int t, u32x4 (&raw)[NL]) const {
+        if (t < nfull) {
+            issue_full(t, raw);
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int g = group(t, j);
+            if (g < gfull) raw[j] = ld16_nt(rowp + (size_t)g * 16);
+        }
+    }
+    __device__ __forceinline__ static void unpack_full(const u32x4 (&raw)[NL], float (&v)[kREPT]) {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (DT == DT_BF16) {
+                    v[j * 8 + 2 * q] = bf16_lo(w[q]);
+                    v[j * 8 + 2 * q + 1] = bf16_hi(w[q]);
+                } else {
+                    v[j * 4 + q] = __uint_as_float(w[q]);
+                }
+            }
+        }
+    }
+    __device__ __forceinline__ void unpack(int t, const u32x4 (&raw)[NL], float (&v)[kREPT]) const {
+        if (t < nfull) {
+            unpack_full(raw, v);
+            return;
+        }
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int g = group(t, j);
+            if (g < gfull) {
+                const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    if (DT == DT_BF16) {
+                        v[j * 8 + 2 * q] = bf16_lo(w[q]);
+                        v[j * 8 + 2 * q + 1] = bf16_hi(w[q]);
+                    } else {
+                        v[j * 4 + q] = __uint_as_float(w[q]);
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int q = 0; q < per; ++q) {
+                    const int idx = g * per + q;
+                    v[j * per + q] = idx < V ? load_logit(rowp, DT, idx) : -INFINITY;
+                }
+            }
+        }
+    }
+};
+
+// ---------------------------------------------------------------------------
+// k_row
+// ---------------------------------------------------------------------------
+constexpr int kNB = 512;                 // value bins used to resolve filters
+constexpr int kBinMax = 512;             // largest bin resolved pairwise
+
+struct RowArgs {
+    Shape sh;
+    float c_hi, c_lo;   // log2(e)/T = c_hi + c_lo, c_hi with 12 significant bits
+    float c;            // log2(e)/T rounded to float
+    double inv_T;
+    int top_k;          // active iff use_k
+    float top_p;        // active iff use_p
+    int use_k, use_p;
+    int fx_shift;       // fixed-point scale 2^fx_shift for weights <= 1
+    RowRec* rec;
+    uint2* kept;        // [n_trows][kListMax] (index, logit bits), ascending index
+    int* kept_n;        // [n_trows]; -1 when the list was not stored
+};
+
+struct RowShared {
+    u64 buf[kCap];          // reservoir: kRW segments of kSeg entries (logit bits << 32) | index
+    u64 hm[kNB];            // per-bin fixed-point mass
+    uint32_t hc[kNB];       // per-bin count
+    uint32_t bkey[kBinMax]; // entries of one bin
+    u64 bw[kBinMax];
+    Sel sel;
+    double red_d[kRW];
+    float red_f[kRW];
+    u64 red_u[kRW];
+    int n;                  // reservoir entries after compaction (> kCap: overflow)
+    int wfill[kRW];         // per-wave segment fill
+    int wovf[kRW];          // per-wave overflow flag
+    int nbin;
+    int nlist;
+    int ibin;
+    u64 ubefore;
+    uint32_t cbefore;
+    float tau;              // capture threshold
+};
+
+__device__ __forceinline__ float rb_min(float v, float* s) { return -rb_max(-v, s); }
+
+// One wave (wave 0) scans bins 0..kNB-1 in order and finds the first bin at
+// which the running sum of val(b) reaches target; returns it with the sum of
+// the bins before it (bin = -1 and before = total when it is never reached).
+template <class F>
+__device__ __forceinline__ void wave_first_reach(F&& val, u64 target, int& bin, u64& before) {
+    constexpr int per = kNB / 64;
+    const int lane = threadIdx.x & 63;
+    u64 c[per];
+    u64 ls = 0ull;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        c[i] = val(per * lane + i);
+        ls += c[i];
+    }
+    u64 incl = ls;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const u64 t = __shfl_up(incl, off, 64);
+        if (lane >= off) incl += t;
+    }
+    const u64 m = __ballot(incl >= target);
+    if (m == 0) {
+        bin = -1;
+        before = __shfl(incl, 63, 64);
+        return;
+    }
+    const int L = __ffsll((long long)m) - 1;
+    int d = 0;
+    u64 run = incl - ls;
+    if (lane == L) {
+#pragma unroll
+        for (int i = 0; i < per; ++i) {
+            if (run + c[i] >= target) {
+                d = per * lane + i;
+                break;
+            }
+            run += c[i];
+        }
+    }
+    bin = __shfl(d, L, 64);
+    before = __shfl(run, L, 64);
+}
+
+// Reservoir append for one tile.  Every wave owns a segment of kSeg slots
+// and a uniform fill count (kept in a scalar register), so an append costs a
+// ballot per slot and, for slots with captures, a prefix count and one LDS
+// store; no atomics.  Entries are (logit bits << 32) | token index.
+template <int DT>
+__device__ __forceinline__ void capture_tile(RowShared& S, const RowStream<DT>& st, int t,
+                                             const float (&v)[kREPT], float tau, int& fill,
+                                             int& ovf) {
+    const int wave = threadIdx.x >> 6;
+    uint2* seg = reinterpret_cast<uint2*>(S.buf) + wave * kSeg;
+    const int idx0 = st.index(t, 0);
+    constexpr int per = RowStream<DT>::per;
+#pragma unroll
+    for (int s = 0; s < kREPT; ++s) {
+        const bool hit = v[s] >= tau;
+        const u64 m = __builtin_amdgcn_ballot_w64(hit);
+        if (m != 0ull) {
+            const int c = __popcll(m);
+            if (fill + c <= kSeg) {
+                if (hit) {
+                    const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    seg[fill + r] = make_uint2((uint32_t)(idx0 + (s / per) * kRB * per + s % per),
+                                               __float_as_uint(v[s]));
+                }
+                fill += c;
+            } else {
+                ovf = 1;
+            }
+        }
+    }
+}
+
+// First capture threshold, from tile 0: about the rank-th largest thread
+// maximum (binned over the range of thread maxima), so that at least `rank`
+// logits of tile 0 are captured.
+__device__ __forceinline__ float first_threshold(RowShared& S, float tm, int rank) {
+    const float M0 = rb_max(tm, S.red_f);
+    const bool fin = tm != -INFINITY;
+    const float mn = rb_min(fin ? tm : INFINITY, S.red_f);
+    const float span = M0 - mn;
+    const float bscale = span > 0.f ? (float)(kNB - 1) / span : 0.f;
+    for (int i = threadIdx.x; i < kNB; i += kRB) S.hc[i] = 0u;
+    __syncthreads();
+    const int b = fin ? min(kNB - 1, (int)((M0 - tm) * bscale)) : kNB;
+    if (fin) atomicAdd(&S.hc[b], 1u);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        int bin;
+        u64 before;
+        wave_first_reach([&](int i) { return (u64)S.hc[i]; }, (u64)rank, bin, before);
+        if (threadIdx.x == 0) S.ibin = bin;
+    }
+    __syncthreads();
+    const int b0 = S.ibin;
+    // fewer finite thread maxima than `rank`: capture everything
+    const float tau = b0 < 0 ? -INFINITY : rb_min((fin && b <= b0) ? tm : INFINITY, S.red_f);
+    return tau;
+}
+
+// Resolve top-k / top-p from the reservoir.  Entries (kOwn per thread) hold
+// every logit >= the capture threshold.  Returns false when the reservoir
+// cannot decide (the caller then re-reads the row).
+__device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S, float M, double Z,
+                                                  int n, double scale, uint32_t& thr_key,
+                                                  double& z_kept, int& n_kept) {
+    const int tid = threadIdx.x;
+    uint32_t key[kOwn];
+    u64 wt[kOwn];
+    int bin[kOwn];
+    float xmin = INFINITY;
+#pragma unroll
+    for (int i = 0; i < kOwn; ++i) {
+        const int slot = tid + i * kRB;
+        key[i] = 0u;
+        wt[i] = 0ull;
+        if (slot < n) {
+            const float x = __uint_as_float((uint32_t)(S.buf[slot] >> 32));
+            key[i] = fkey(x);
+            wt[i] = (u64)(exp(((double)x - (double)M) * a.inv_T) * scale);
+            xmin = fminf(xmin, x);
+        }
+    }
+    const float lo = rb_min(xmin, S.red_f);
+    const float span = M - lo;
+    const float bscale = span > 0.f ? (float)(kNB - 1) / span : 0.f;
+    for (int i = tid; i < kNB; i += kRB) {
+        S.hc[i] = 0u;
+        S.hm[i] = 0ull;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < kOwn; ++i) {
+        bin[i] = kNB;
+        if (tid + i * kRB < n) {
+            bin[i] = min(kNB - 1, (int)((M - key_to_float(key[i])) * bscale));
+            atomicAdd(&S.hc[bin[i]], 1u);
+            atomicAdd(&S.hm[bin[i]], wt[i]);
+        }
+    }
+    __syncthreads();
+
+    // Exact decision inside one bin: every entry of the bin (with key >=
+    // floor) learns how many entries and how much mass of the bin lie
+    // strictly above it; `keep(rank_or_excl)` decides, and the block gets the
+    // smallest kept key, the kept count and the kept mass of the bin.
+    auto resolve_bin = [&](int b, uint32_t floor_key, u64 base, bool by_count, u64 limit,
+                           uint32_t& kmin, uint32_t& kcnt, u64& kmass) -> bool {
+        if (tid == 0) S.nbin = 0;
+        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < kOwn; ++i) {
+            if (bin[i] == b && key[i] >= floor_key) {
+                const int slot = atomicAdd(&S.nbin, 1);
+                if (slot < kBinMax) {
+                    S.bkey[slot] = key[i];
+                    S.bw[slot] = wt[i];
+                }
+            }
+        }
+        __syncthreads();
+        const int nb = S.nbin;
+        if (nb > kBinMax) return false;
+        uint32_t my_k = 0u, my_c = 0u;
+        u64 my_m = 0ull;
+        uint32_t my_min = 0xFFFFFFFFu;
+        for (int i = tid; i < nb; i += kRB) {
+            const uint32_t ki = S.bkey[i];
+            uint32_t cgt = 0u;
+            u64 mgt = 0ull;
+            for (int jj = 0; jj < nb; ++jj) {
+                const uint32_t kj = S.bkey[jj];
+                if (kj > ki) {
+                    ++cgt;
+                    mgt += S.bw[jj];
+                }
+            }
+            const bool kept = by_count ? (base + cgt < limit) : (base + mgt < limit);
+            if (kept) {
+                ++my_c;
+                my_m += S.bw[i];
+                my_min = min(my_min, ki);
+            }
+        }
+        (void)my_k;
+        kcnt = (uint32_t)rb_sum_u64(my_c, S.red_u);
+        kmass = rb_sum_u64(my_m, S.red_u);
+        kmin = 0xFFFFFFFFu - (uint32_t)rb_max_u64(0xFFFFFFFFu - my_min, S.red_u);
+        return true;
+    };
+
+    // top-k: the bin holding the top_k-th largest logit, then exact ranks in it
+    int bk = kNB;
+    uint32_t tau_k = 0u, in_k_cnt = 0u;
+    u64 in_k_mass = 0ull;
+    u64 cb_k = 0ull, mb_k = 0ull;
+    if (a.use_k) {
+        if (tid < 64) {
+            int b;
+            u64 before;
+            wave_first_reach([&](int i) { return (u64)S.hc[i]; }, (u64)a.top_k, b, before);
+            if (tid == 0) {
+                S.ibin = b;
+                S.cbefore = (uint32_t)before;
+                u64 mb = 0ull;
+                for (int i = 0; i < (b < 0 ? 0 : b); ++i) mb += S.hm[i];
+                S.ubefore = mb;
+            }
+        }
+        __syncthreads();
+        bk = S.ibin;
+        cb_k = S.cbefore;
+        mb_k = S.ubefore;
+        __syncthreads();
+        if (bk < 0) return false;  // fewer than top_k entries captured
+        if (!resolve_bin(bk, 0u, cb_k, true, (u64)a.top_k, tau_k, in_k_cnt, in_k_mass)) return false;
+    }
+    const u64 zk = a.use_k ? mb_k + in_k_mass : 0ull;
+    if (!a.use_p) {
+        thr_key = tau_k;
+        n_kept = (int)(cb_k + in_k_cnt);
+        z_kept = (double)zk / scale;
+        return true;
+    }
+    // top-p on the (top-k) kept set: kept <=> excl < ceil(top_p * Z * 2^s)
+    const double zbase = a.use_k ? (double)zk / scale : Z;
+    u64 target = (u64)ceil((double)a.top_p * zbase * scale);
+    if (target == 0ull) target = 1ull;
+    if (a.use_k && target > zk) target = zk;  // rounding: keep the whole top-k set
+    if (tid < 64) {
+        int b;
+        u64 before;
+        wave_first_reach([&](int i) -> u64 { return i < bk ? S.hm[i] : (i == bk ? in_k_mass : 0ull); },
+                         target, b, before);
+        if (tid == 0) {
+            S.ibin = b;
+            S.ubefore = before;
+            uint32_t cb = 0u;
+            for (int i = 0; i < (b < 0 ? 0 : b); ++i) cb += S.hc[i];
+            S.cbefore = cb;
+        }
+    }
+    __syncthreads();
+    const int bp = S.ibin;
+    const u64 mb_p = S.ubefore;
+    const uint32_t cb_p = S.cbefore;
+    __syncthreads();
+    if (bp < 0) return false;  // the crossing lies below the reservoir
+    uint32_t kmin, kcnt;
+    u64 kmass;
+    if (!resolve_bin(bp, bp == bk ? tau_k : 0u, mb_p, false, target, kmin, kcnt, kmass)) return false;
+    thr_key = kmin;
+    n_kept = (int)(cb_p + kcnt);
+    z_kept = (double)(mb_p + kmass) / scale;
+    return true;
+}
+
+// Exact resolution by re-reading the row: radix selection over every logit
+// of the row (counts for top-k, fixed-point masses for top-p).
+template <int DT, class F>
+__device__ __forceinline__ void row_for_each(const char* rowp, int V, F&& f) {
+    constexpr int esz = DT == DT_BF16 ? 2 : 4;
+    constexpr int per = 16 / esz;
+    if ((((uintptr_t)rowp) & 15) == 0) {
+        const int ng = V / per;
+        for (int g = threadIdx.x; g < ng; g += kRB) {
+            const u32x4 raw = ld16_nt(rowp + (size_t)g * 16);
+            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                if (DT == DT_BF16) {
+                    f(g * per + 2 * q, bf16_lo(w[q]));
+                    f(g * per + 2 * q + 1, bf16_hi(w[q]));
+                } else {
+                    f(g * per + q, __uint_as_float(w[q]));
+                }
+            }
+        }
+        for (int i = ng * per + threadIdx.x; i < V; i += kRB) f(i, load_logit(rowp, DT, i));
+    } else {
+        for (int i = threadIdx.x; i < V; i += kRB) f(i, load_logit(rowp, DT, i));
+    }
+}
+
+template <int DT>
+__device__ __forceinline__ Sel row_select_exact(RowShared& S, const char* rowp, int V, float M, double inv_T,
+                                                uint32_t floor_key, bool by_count, u64 target, double scale) {
+    const int nlev = DT == DT_BF16 ? 2 : 4;
+    uint32_t prefix = 0u, mask = 0u;
+    u64 A = 0ull;
+    uint32_t C = 0u;
+    for (int lvl = 0; lvl < nlev; ++lvl) {
+        const int shift = 24 - 8 * lvl;
+        for (int i = threadIdx.x; i < 256; i += kRB) {
+            S.hm[i] = 0ull;
+            S.hc[i] = 0u;
+        }
+        __syncthreads();
+        row_for_each<DT>(rowp, V, [&](int, float x) {
+            const uint32_t k = fkey(x);
+            if (k >= floor_key && (k & mask) == prefix) {
+                const uint32_t d = (k >> shift) & 255u;
+                const u64 w = by_count ? 1ull
+                                       : (u64)(exp(((double)x - (double)M) * inv_T) * scale);
+                atomicAdd(&S.hm[d], w);
+                atomicAdd(&S.hc[d], 1u);
+            }
+        });
+        __syncthreads();
+        if (threadIdx.x < 64) {
+            int bin;
+            u64 above;
+            wave_find_from_top(S.hm, target - A, bin, above);
+            if (threadIdx.x == 0) {
+                Sel r;
+                if (bin < 0) {
+                    r.ok = 0;
+                } else {
+                    uint32_t ca = 0u;
+                    for (int d = 255; d > bin; --d) ca += S.hc[d];
+                    r.ok = 1;
+                    r.key = prefix | ((uint32_t)bin << shift);
+                    r.above = A + above;
+                    r.group = S.hm[bin];
+                    r.cnt_above = C + ca;
+                    r.cnt_group = S.hc[bin];
+                }
+                S.sel = r;
+            }
+        }
+        __syncthreads();
+        const Sel r = S.sel;
+        if (!r.ok) return r;
+        prefix = r.key;
+        mask |= 0xFFu << shift;
+        A = r.above;
+        C = r.cnt_above;
+        __syncthreads();
+    }
+    Sel r = S.sel;
+    if (nlev == 2) r.key = bf16_key_fill(r.key);
+    return r;
+}
+
+template <int DT, bool FILT>
+__device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row) {
+    const char* rowp = row_ptr(a.sh, row);
+    const int V = a.sh.V;
+    constexpr bool filtered = FILT;
+    const RowStream<DT> st(rowp, V);
+    constexpr int NL = RowStream<DT>::NL;
+
+    // the drafted token's logit, fetched while the row streams
+    int d_tok = -1;
+    float xd = -INFINITY;
+    if (threadIdx.x == 0 && row_has_token(a.sh, row)) {
+        d_tok = row_token(a.sh, row);
+        if (d_tok >= 0 && d_tok < V) xd = load_logit(rowp, DT, d_tok);
+    }
+    float m_th = -INFINITY;
+    double z_th = 0.0;
+    float tau = INFINITY;
+    int fill = 0, ovf = 0;  // this wave's reservoir segment (uniform per wave)
+
+    // One tile: running max / sum of exp, and the reservoir capture.  FULL
+    // tiles take the unchecked unpack; tile 0 also sets the capture threshold.
+    auto process = [&](int t, const u32x4 (&raw)[NL], auto full_tag, bool first) {
+        constexpr bool FULL = decltype(full_tag)::value;
+        float v[kREPT];
+        if (FULL)
+            RowStream<DT>::unpack_full(raw, v);
+        else
+            st.unpack(t, raw, v);
+        float tm = v[0];
+#pragma unroll
+        for (int s = 1; s < kREPT; ++s) tm = fmaxf(tm, v[s]);
+        if (tm > m_th) {
+            if (m_th != -INFINITY) z_th *= exp(((double)m_th - (double)tm) * a.inv_T);
+            m_th = tm;
+        }
+        if (m_th != -INFINITY) {
+            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < kREPT; ++s) {
+                const float y = v[s] - m_th;
+                // filtered rows use Z only in the top-p test (ambiguity band
+                // 1e-6): one product; otherwise the split constant keeps the
+                // exponent free of the rounding of log2(e)/T
+                const float e = FILT ? y * a.c : fmaf(y, a.c_hi, y * a.c_lo);
+                acc[s & 3] += __builtin_amdgcn_exp2f(e);
+            }
+            z_th += ((double)acc[0] + (double)acc[1]) + ((double)acc[2] + (double)acc[3]);
+        }
+        if (filtered) {
+            if (first)
+                tau = V <= kCap ? -INFINITY
+                                : first_threshold(S, tm, max(kR0, a.use_k ? min(a.top_k, kRB) : 0));
+            capture_tile<DT>(S, st, t, v, tau, fill, ovf);
+        }
+    };
+    using FullT = std::integral_constant<bool, true>;
+    using AnyT = std::integral_constant<bool, false>;
+
+    {
+        // Steady state: three full tiles of loads in flight in rotating
+        // registers, straight-line code so that each tile waits only for its
+        // own loads.  Then the drain, then the remaining tiles one by one.
+        u32x4 rA[NL], rB[NL], rC[NL];
+        const int nf = st.nfull;
+        int t = 0;
+        if (nf >= 4) {
+            st.issue_full(0, rA);
+            st.issue_full(1, rB);
+            st.issue_full(2, rC);
+            process(0, rA, FullT{}, true);
+            st.issue_full(3, rA);
+            t = 1;
+            for (; t + 5 < nf; t += 3) {
+                process(t, rB, FullT{}, false);
+                st.issue_full(t + 3, rB);
+                process(t + 1, rC, FullT{}, false);
+                st.issue_full(t + 4, rC);
+                process(t + 2, rA, FullT{}, false);
+                st.issue_full(t + 5, rA);
+            }
+            process(t, rB, FullT{}, false);
+            process(t + 1, rC, FullT{}, false);
+            process(t + 2, rA, FullT{}, false);
+            t += 3;
+        }
+        for (; t < st.nt; ++t) {
+            st.issue(t, rA);
+            process(t, rA, AnyT{}, t == 0);
+        }
+    }
+
+    if (filtered) {
+        // compact the per-wave reservoir segments into buf[0, n)
+        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+        if (lane == 0) {
+            S.wfill[wave] = fill;
+            S.wovf[wave] = ovf;
+        }
+        u64 ent[kSeg / 64];
+#pragma unroll
+        for (int i = 0; i < kSeg / 64; ++i) {
+            const int k = lane + 64 * i;
+            ent[i] = k < fill ? S.buf[wave * kSeg + k] : 0ull;
+        }
+        __syncthreads();
+        int P = 0, total = 0, any_ovf = 0;
+#pragma unroll
+        for (int w = 0; w < kRW; ++w) {
+            P += w < wave ? S.wfill[w] : 0;
+            total += S.wfill[w];
+            any_ovf |= S.wovf[w];
+        }
+#pragma unroll
+        for (int i = 0; i < kSeg / 64; ++i) {
+            const int k = lane + 64 * i;
+            if (k < fill) S.buf[P + k] = ent[i];
+        }
+        if (threadIdx.x == 0) S.n = any_ovf ? kCap + 1 : total;
+        __syncthreads();
+    }
+
+    // ---- merge the row: M and Z over all logits (fixed-order reductions) ----
+    const float M = rb_max(m_th, S.red_f);
+    const double zc = (m_th == -INFINITY) ? 0.0 : z_th * exp(((double)m_th - (double)M) * a.inv_T);
+    const double Z = rb_sum(zc, S.red_d);
+
+    float thr = -INFINITY;
+    double z_kept = Z;
+    int n_kept = V;
+    int flags = 0;
+
+    if (filtered) {
+        flags = SPEC_ROW_FILTERED;
+        const double scale = ldexp(1.0, a.fx_shift);
+        const int n_res = S.n;
+        uint32_t thr_key = 0u;
+        bool fast = n_res <= kCap &&
+                    resolve_reservoir(a, S, M, Z, n_res, scale, thr_key, z_kept, n_kept);
+        if (fast) {
+            thr = key_to_float(thr_key);
+        } else {
+            flags |= SPEC_ROW_EXACT_PATH;
+            __syncthreads();
+            uint32_t tk = 0u;
+            uint32_t cnt = (uint32_t)V;
+            if (a.use_k) {
+                const Sel sk = row_select_exact<DT>(S, rowp, V, M, a.inv_T, 0u, true, (u64)a.top_k, scale);
+                tk = sk.key;
+                cnt = sk.cnt_above + sk.cnt_group;
+            }
+            u64 part = 0ull;
+            row_for_each<DT>(rowp, V, [&](int, float x) {
+                if (fkey(x) >= tk) part += (u64)(exp(((double)x - (double)M) * a.inv_T) * scale);
+            });
+            const u64 tot = rb_sum_u64(part, S.red_u);
+            uint32_t thk = tk;
+            u64 zfx = tot;
+            if (a.use_p) {
+                const double zbase = a.use_k ? (double)tot / scale : Z;
+                u64 target = (u64)ceil((double)a.top_p * zbase * scale);
+                if (target == 0ull) target = 1ull;
+                if (target > tot) target = tot;  // rounding: keep the whole top-k range
+                const Sel sp = row_select_exact<DT>(S, rowp, V, M, a.inv_T, tk, false, target, scale);
+                if (sp.ok) {
+                    thk = sp.key;
+                    zfx = sp.above + sp.group;
+                    cnt = sp.cnt_above + sp.cnt_group;
+                }
+            }
+            thr = key_to_float(thk);
+            z_kept = (double)zfx / scale;
+            n_kept = (int)cnt;
+        }
+        // kept list of a target row, sorted by token index: gather the kept
+        // logits (reservoir entries >= thr, or a pass over the row on the
+        // exact path) into LDS, then bucket them by tile and rank each entry
+        // inside its bucket, which gives a deterministic order.
+        if (row < a.sh.n_trows) {
+            const int list_n = (n_kept <= kListMax && st.nt <= kNB) ? n_kept : -1;
+            if (list_n >= 0) {
+                u64 own[kOwn];
+                if (fast) {
+#pragma unroll
+                    for (int i = 0; i < kOwn; ++i) {
+                        const int slot = threadIdx.x + i * kRB;
+                        own[i] = slot < n_res ? S.buf[slot] : 0ull;
+                    }
+                }
+                __syncthreads();
+                if (threadIdx.x == 0) S.nlist = 0;
+                __syncthreads();
+                const uint32_t tk = fkey(thr);
+                if (fast) {
+#pragma unroll
+                    for (int i = 0; i < kOwn; ++i) {
+                        const int slot = threadIdx.x + i * kRB;
+                        if (slot < n_res && fkey(__uint_as_float((uint32_t)(own[i] >> 32))) >= tk) {
+                            const int p = atomicAdd(&S.nlist, 1);
+                            if (p < kCap) S.buf[p] = own[i];
+                        }
+                    }
+                } else {
+                    row_for_each<DT>(rowp, V, [&](int i, float x) {
+                        if (x >= thr) {
+                            const int p = atomicAdd(&S.nlist, 1);
+                            if (p < kCap) S.buf[p] = ((u64)__float_as_uint(x) << 32) | (uint32_t)i;
+                        }
+                    });
+                }
+                __syncthreads();
+                const int nk = min(S.nlist, list_n);
+                // bucket = streaming tile of the token
+                for (int i = threadIdx.x; i < kNB; i += kRB) {
+                    S.hc[i] = 0u;
+                    S.bkey[i] = 0u;
+                }
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) {
+                    const int slot = threadIdx.x + i * kRB;
+                    own[i] = slot < nk ? S.buf[slot] : 0ull;
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i)
+                    if (threadIdx.x + i * kRB < nk) atomicAdd(&S.hc[(uint32_t)own[i] / kRTile], 1u);
+                __syncthreads();
+                if (threadIdx.x < 64) {
+                    // exclusive prefix of bucket counts, bucket starts into hm
+                    constexpr int per = kNB / 64;
+                    const int lane = threadIdx.x;
+                    u64 c[per];
+                    u64 ls = 0ull;
+#pragma unroll
+                    for (int q = 0; q < per; ++q) {
+                        c[q] = S.hc[per * lane + q];
+                        ls += c[q];
+                    }
+                    u64 incl = ls;
+#pragma unroll
+                    for (int off = 1; off < 64; off <<= 1) {
+                        const u64 t = __shfl_up(incl, off, 64);
+                        if (lane >= off) incl += t;
+                    }
+                    u64 run = incl - ls;
+#pragma unroll
+                    for (int q = 0; q < per; ++q) {
+                        S.hm[per * lane + q] = run;
+                        run += c[q];
+                    }
+                }
+                __syncthreads();
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) {
+                    if (threadIdx.x + i * kRB < nk) {
+                        const uint32_t bkt = (uint32_t)own[i] / kRTile;
+                        const uint32_t p = (uint32_t)S.hm[bkt] + atomicAdd(&S.bkey[bkt], 1u);
+                        S.buf[p] = own[i];
+                    }
+                }
+                __syncthreads();
+                uint2* out = a.kept + (size_t)row * kListMax;
+                for (int e = threadIdx.x; e < nk; e += kRB) {
+                    const u64 me = S.buf[e];
+                    const uint32_t idx = (uint32_t)me;
+                    const uint32_t bkt = idx / kRTile;
+                    const int s0 = (int)S.hm[bkt], len = (int)S.hc[bkt];
+                    int rank = 0;
+                    for (int q = s0; q < s0 + len; ++q) rank += ((uint32_t)S.buf[q] < idx) ? 1 : 0;
+                    out[s0 + rank] = make_uint2(idx, (uint32_t)(me >> 32));
+                }
+            }
+            if (threadIdx.x == 0) a.kept_n[row] = list_n;
+        }
+    }
+
+    if (threadIdx.x == 0) {
+        RowRec r;
+        r.s.max_logit = M;
+        r.z_all = Z;
+        r.pad = 0.0;
+        r.s.thresh = thr;
+        r.s.n_kept = n_kept;
+        r.s.flags = flags;
+        r.s.z_kept = z_kept;
+        double prob = __builtin_nan("");
+        if (row_has_token(a.sh, row)) {
+            prob = 0.0;
+            if (d_tok >= 0 && d_tok < V && xd >= thr)
+                prob = exp(((double)xd - (double)M) * a.inv_T) / z_kept;
+        }
+        r.s.prob_at_token = prob;
+        a.rec[row] = r;
+    }
+}
+
+__global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
+    __shared__ RowShared S;
+    const int row = blockIdx.x;
+    const bool bf = row_dt(a.sh, row) == DT_BF16;
+    if (a.use_k || a.use_p) {
+        if (bf)
+            row_body<DT_BF16, true>(a, S, row);
+        else
+            row_body<DT_F32, true>(a, S, row);
+    } else {
+        if (bf)
+            row_body<DT_BF16, false>(a, S, row);
+        else
+            row_body<DT_F32, false>(a, S, row);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// k_row_argmax: lowest-index argmax of a target row (greedy mode).
+// ---------------------------------------------------------------------------
+template <int DT>
+__device__ __forceinline__ void argmax_body(const Shape& sh, int row, int32_t* gidx, u64* s_red) {
+    const char* rowp = row_ptr(sh, row);
+    const RowStream<DT> st(rowp, sh.V);
+    constexpr int NL = RowStream<DT>::NL;
+    float best = -INFINITY;
+    int bidx = -1;
+    auto process = [&](int t, const u32x4 (&raw)[NL]) {
+        float v[kREPT];
+        st.unpack(t, raw, v);
+        // slots of one thread are in increasing index order across tiles
+#pragma unroll
+        for (int s = 0; s < kREPT; ++s) {
+            const int idx = st.index(t, s);
+            if (idx < sh.V && (bidx < 0 || v[s] > best)) {
+                best = v[s];
+                bidx = idx;
+            }
+        }
+    };
+    u32x4 r0[NL], r1[NL];
+    st.issue(0, r0);
+    for (int t = 0; t < st.nt; t += 2) {
+        if (t + 1 < st.nt) st.issue(t + 1, r1);
+        process(t, r0);
+        if (t + 2 < st.nt) st.issue(t + 2, r0);
+        if (t + 1 < st.nt) process(t + 1, r1);
+    }
+    const u64 key = bidx < 0 ? 0ull
+                             : (((u64)fkey(best) << 32) | (u64)(0xFFFFFFFFu - (uint32_t)bidx));
+    const u64 k = rb_max_u64(key, s_red);
+    if (threadIdx.x == 0) gidx[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+}
+
+__global__ void __launch_bounds__(kRB) k_row_argmax(Shape sh, int32_t* gidx) {
+    __shared__ u64 s_red[kRW];
+    const int row = blockIdx.x;
+    if (sh.tdt == DT_BF16)
+        argmax_body<DT_BF16>(sh, row, gidx, s_red);
+    else
+        argmax_body<DT_F32>(sh, row, gidx, s_red);
+}
+
+}  // namespace sv

@@ -1,0 +1,444 @@
+// seq_kernels.h — per-sequence kernels: the accept scan over K drafted
+// positions and the draw of the stop token.
+//
+//  k_seq_filtered : filtered rows (top-k / top-p).  p_j is nonzero only on the
+//                   stop target row's kept set, stored sorted by index by
+//                   k_row, so the residual max(0, p_j - q_j) is evaluated on
+//                   that list (draft logits gathered by index).
+//  k_draw_sums / k_draw_pick : unfiltered rows.  The residual is spread over
+//                   the whole vocabulary: chunk sums over the stop row pair in
+//                   fp64, then one workgroup per sequence locates the draw.
+//  k_greedy_prefix : greedy prefix match from the per-row argmax.
+#pragma once
+
+#include "row_kernels.h"
+
+namespace sv {
+
+constexpr int kSB = 256;                 // threads per sequence workgroup
+constexpr int kChunk = 8192;             // tokens per draw chunk
+constexpr int kCPT = kChunk / kSB;       // 32 contiguous tokens per thread
+
+struct SeqArgs {
+    Shape sh;
+    double inv_T;
+    uint64_t seed;
+    const RowRec* rec;
+    const uint2* kept;
+    const int* kept_n;
+    double2* chunk_sum;   // [B][n_chunks] (.x residual, .y p)
+    int n_chunks;
+    int32_t* out_tokens;
+    int32_t* out_num;
+};
+
+// Stop position of sequence b: first k with !(u_k * q_k(d_k) < p_k(d_k)),
+// or K.  Executed by one wave; every lane returns it.
+__device__ __forceinline__ int first_rejection(const SeqArgs& a, int b) {
+    const int lane = threadIdx.x & 63;
+    const int K = a.sh.K;
+    for (int k0 = 0; k0 < K; k0 += 64) {
+        const int k = k0 + lane;
+        bool reject = false;
+        if (k < K) {
+            const double p = a.rec[(size_t)b * (K + 1) + k].s.prob_at_token;
+            const double q = a.rec[a.sh.n_trows + (size_t)b * K + k].s.prob_at_token;
+            const double u = uniform24(draw_block(a.seed, (uint32_t)b, (uint32_t)k, PURPOSE_ACCEPT));
+            reject = !(u * q < p);
+        }
+        const unsigned long long m = __ballot(reject);
+        if (m) return k0 + __ffsll((long long)m) - 1;
+    }
+    return K;
+}
+
+// The stop row pair of a sequence: target row j, draft row j when j < K.
+struct StopRow {
+    const char* tp;
+    const char* dp;
+    int tdt, ddt;
+    float Mt, Md, thr_t, thr_d;
+    double zt, zd;
+    bool has_draft;
+};
+
+__device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
+    StopRow s;
+    const int K = a.sh.K;
+    const int rt = b * (K + 1) + j;
+    const RowRec& Rt = a.rec[rt];
+    s.tp = row_ptr(a.sh, rt);
+    s.tdt = a.sh.tdt;
+    s.Mt = Rt.s.max_logit;
+    s.thr_t = Rt.s.thresh;
+    s.zt = Rt.s.z_kept;
+    s.has_draft = j < K;
+    if (s.has_draft) {
+        const int rd = a.sh.n_trows + b * K + j;
+        const RowRec& Rd = a.rec[rd];
+        s.dp = row_ptr(a.sh, rd);
+        s.ddt = a.sh.ddt;
+        s.Md = Rd.s.max_logit;
+        s.thr_d = Rd.s.thresh;
+        s.zd = Rd.s.z_kept;
+    } else {
+        s.dp = nullptr;
+        s.ddt = 0;
+        s.Md = 0.f;
+        s.thr_d = 0.f;
+        s.zd = 1.0;
+    }
+    return s;
+}
+
+// p_j(i) and the residual max(0, p_j(i) - q_j(i)) in fp64, given the target
+// logit xt of token i.
+__device__ __forceinline__ void stop_terms_x(const StopRow& s, double inv_T, int i, float xt,
+                                             double& p, double& r) {
+    p = xt >= s.thr_t ? exp(((double)xt - (double)s.Mt) * inv_T) / s.zt : 0.0;
+    double q = 0.0;
+    if (s.has_draft) {
+        const float xd = load_logit(s.dp, s.ddt, i);
+        q = xd >= s.thr_d ? exp(((double)xd - (double)s.Md) * inv_T) / s.zd : 0.0;
+    }
+    const double d = p - q;
+    r = d > 0.0 ? d : 0.0;
+}
+__device__ __forceinline__ void stop_terms(const StopRow& s, double inv_T, int i, double& p, double& r) {
+    stop_terms_x(s, inv_T, i, load_logit(s.tp, s.tdt, i), p, r);
+}
+
+// Deterministic exclusive scan of one double per thread (thread order) over
+// kSB threads; also returns the total.  The same code produces chunk totals
+// and search prefixes, so both see identical values.
+__device__ __forceinline__ void seq_excl_scan(double v, double* s_val, double* s_excl, double* s_total, double& excl,
+                              double& total) {
+    const int tid = threadIdx.x;
+    s_val[tid] = v;
+    __syncthreads();
+    if (tid < 64) {
+        const double v0 = s_val[4 * tid], v1 = s_val[4 * tid + 1];
+        const double v2 = s_val[4 * tid + 2], v3 = s_val[4 * tid + 3];
+        const double ls = ((v0 + v1) + v2) + v3;
+        double incl = ls;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const double t = __shfl_up(incl, off, 64);
+            if (tid >= off) incl += t;
+        }
+        double e = __shfl_up(incl, 1, 64);
+        if (tid == 0) e = 0.0;
+        s_excl[4 * tid] = e;
+        e += v0;
+        s_excl[4 * tid + 1] = e;
+        e += v1;
+        s_excl[4 * tid + 2] = e;
+        e += v2;
+        s_excl[4 * tid + 3] = e;
+        if (tid == 63) *s_total = incl;
+    }
+    __syncthreads();
+    excl = s_excl[tid];
+    total = *s_total;
+    __syncthreads();
+}
+
+// The thread whose range holds the draw point t: the last thread with
+// positive mass whose range starts at or before t (or, if rounding put t
+// before every positive range, the first one with positive mass).
+__device__ __forceinline__ int pick_thread(double mine, double run_excl, double t, int* s_tau) {
+    if (threadIdx.x == 0) *s_tau = -1;
+    __syncthreads();
+    if (mine > 0.0 && run_excl <= t) atomicMax(s_tau, (int)threadIdx.x);
+    __syncthreads();
+    int tau = *s_tau;
+    if (tau < 0) {
+        __syncthreads();
+        if (threadIdx.x == 0) *s_tau = kSB;
+        __syncthreads();
+        if (mine > 0.0) atomicMin(s_tau, (int)threadIdx.x);
+        __syncthreads();
+        tau = *s_tau;
+    }
+    __syncthreads();
+    return tau;
+}
+
+__device__ __forceinline__ void write_outputs(const SeqArgs& a, int b, int j, int y) {
+    const int K = a.sh.K;
+    int32_t* out = a.out_tokens + (size_t)b * (K + 1);
+    for (int k = 0; k < j; ++k) out[k] = a.sh.tokens[(size_t)b * K + k];
+    out[j] = y;
+    for (int k = j + 1; k <= K; ++k) out[k] = -1;
+    a.out_num[b] = j;
+}
+
+// Draw over the whole stop row pair with one workgroup (thread-contiguous
+// token ranges).  Used when no kept list is available.
+__device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, double* s_val, double* s_excl,
+                              double* s_total, int* s_tau) {
+    const StopRow s = stop_row(a, b, j);
+    const int V = a.sh.V;
+    const int per = (V + kSB - 1) / kSB;
+    const int lo = threadIdx.x * per, hi = min(lo + per, V);
+    double sr = 0.0, sp = 0.0;
+    for (int i = lo; i < hi; ++i) {
+        double p, r;
+        stop_terms(s, a.inv_T, i, p, r);
+        sr += r;
+        sp += p;
+    }
+    double er, tr, ep, tp;
+    seq_excl_scan(sr, s_val, s_excl, s_total, er, tr);
+    seq_excl_scan(sp, s_val, s_excl, s_total, ep, tp);
+    const bool usep = (j == a.sh.K) || !(tr > 0.0);
+    const double S = usep ? tp : tr;
+    const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
+    const double mine = usep ? sp : sr;
+    const double ex = usep ? ep : er;
+    const int tau = pick_thread(mine, ex, t, s_tau);
+    if ((int)threadIdx.x == tau) {
+        double acc = ex;
+        int y = -1, last = -1;
+        for (int i = lo; i < hi; ++i) {
+            double p, r;
+            stop_terms(s, a.inv_T, i, p, r);
+            const double w = usep ? p : r;
+            if (w > 0.0) {
+                last = i;
+                acc += w;
+                if (acc > t) {
+                    y = i;
+                    break;
+                }
+            }
+        }
+        write_outputs(a, b, j, y >= 0 ? y : last);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Filtered: one workgroup per sequence.
+// ---------------------------------------------------------------------------
+constexpr int kListPT = kListMax / kSB;  // kept-list entries per thread (16)
+
+__global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
+    __shared__ double s_val[kSB], s_excl[kSB], s_total;
+    __shared__ int s_j, s_tau;
+    const int b = blockIdx.x;
+    const int K = a.sh.K;
+    if (threadIdx.x < 64) {
+        const int j = first_rejection(a, b);
+        if (threadIdx.x == 0) s_j = j;
+    }
+    __syncthreads();
+    const int j = s_j;
+    const int rt = b * (K + 1) + j;
+    const int n = a.kept_n[rt];
+    if (n < 0) {
+        draw_full_row(a, b, j, s_val, s_excl, &s_total, &s_tau);
+        return;
+    }
+    const StopRow s = stop_row(a, b, j);
+    const uint2* L = a.kept + (size_t)rt * kListMax;
+    // thread-contiguous slices of the index-sorted kept list
+    const int per = (n + kSB - 1) / kSB;
+    const int lo = threadIdx.x * per, hi = min(lo + per, n);
+    double pr[kListPT], rr[kListPT];
+    int ix[kListPT];
+    double sr = 0.0, sp = 0.0;
+#pragma unroll
+    for (int e = 0; e < kListPT; ++e) {
+        pr[e] = 0.0;
+        rr[e] = 0.0;
+        ix[e] = -1;
+        const int i = lo + e;
+        if (e < per && i < hi) {
+            const uint2 ent = L[i];
+            ix[e] = (int)ent.x;
+            stop_terms_x(s, a.inv_T, (int)ent.x, __uint_as_float(ent.y), pr[e], rr[e]);
+            sr += rr[e];
+            sp += pr[e];
+        }
+    }
+    double er, tr, ep, tp;
+    seq_excl_scan(sr, s_val, s_excl, &s_total, er, tr);
+    seq_excl_scan(sp, s_val, s_excl, &s_total, ep, tp);
+    const bool usep = (j == K) || !(tr > 0.0);
+    const double S = usep ? tp : tr;
+    const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
+    const double mine = usep ? sp : sr;
+    const double ex = usep ? ep : er;
+    const int tau = pick_thread(mine, ex, t, &s_tau);
+    if ((int)threadIdx.x == tau) {
+        double acc = ex;
+        int y = -1, last = -1;
+#pragma unroll
+        for (int e = 0; e < kListPT; ++e) {
+            const double w = usep ? pr[e] : rr[e];
+            if (y < 0 && ix[e] >= 0 && w > 0.0) {
+                last = ix[e];
+                acc += w;
+                if (acc > t) y = ix[e];
+            }
+        }
+        write_outputs(a, b, j, y >= 0 ? y : last);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Unfiltered: chunk sums, then the pick.
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
+    __shared__ double s_val[kSB], s_excl[kSB], s_total;
+    __shared__ int s_j;
+    const int b = blockIdx.x / a.n_chunks;
+    const int c = blockIdx.x % a.n_chunks;
+    if (threadIdx.x < 64) {
+        const int j = first_rejection(a, b);
+        if (threadIdx.x == 0) s_j = j;
+    }
+    __syncthreads();
+    const StopRow s = stop_row(a, b, s_j);
+    const int lo = c * kChunk + threadIdx.x * kCPT;
+    const int hi = min(lo + kCPT, a.sh.V);
+    double sr = 0.0, sp = 0.0;
+    for (int i = lo; i < hi; ++i) {
+        double p, r;
+        stop_terms(s, a.inv_T, i, p, r);
+        sr += r;
+        sp += p;
+    }
+    double e, tr, tp;
+    seq_excl_scan(sr, s_val, s_excl, &s_total, e, tr);
+    seq_excl_scan(sp, s_val, s_excl, &s_total, e, tp);
+    if (threadIdx.x == 0) a.chunk_sum[(size_t)b * a.n_chunks + c] = make_double2(tr, tp);
+}
+
+__global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
+    __shared__ double s_val[kSB], s_excl[kSB], s_total;
+    __shared__ int s_j, s_cstar, s_tau, s_usep;
+    __shared__ double s_run, s_t;
+    const int b = blockIdx.x;
+    const int K = a.sh.K, V = a.sh.V;
+    if (threadIdx.x < 64) {
+        const int j = first_rejection(a, b);
+        if (threadIdx.x == 0) s_j = j;
+    }
+    __syncthreads();
+    const int j = s_j;
+    if (threadIdx.x == 0) {
+        const double2* cs = a.chunk_sum + (size_t)b * a.n_chunks;
+        double Sr = 0.0, Sp = 0.0;
+        for (int cc = 0; cc < a.n_chunks; ++cc) {
+            Sr += cs[cc].x;
+            Sp += cs[cc].y;
+        }
+        const int usep = (j == K) || !(Sr > 0.0);
+        const double S = usep ? Sp : Sr;
+        const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
+        double run = 0.0, run_last = 0.0;
+        int cstar = -1, last_nz = 0;
+        for (int cc = 0; cc < a.n_chunks; ++cc) {
+            const double sc = usep ? cs[cc].y : cs[cc].x;
+            if (sc > 0.0) {
+                if (run + sc > t) {
+                    cstar = cc;
+                    break;
+                }
+                last_nz = cc;
+                run_last = run;
+            }
+            run += sc;
+        }
+        if (cstar < 0) {
+            cstar = last_nz;
+            run = run_last;
+        }
+        s_cstar = cstar;
+        s_run = run;
+        s_t = t;
+        s_usep = usep;
+    }
+    __syncthreads();
+    const StopRow s = stop_row(a, b, j);
+    const int cstar = s_cstar;
+    const double run = s_run, t = s_t;
+    const bool usep = s_usep != 0;
+    const int lo = cstar * kChunk + threadIdx.x * kCPT;
+    const int hi = min(lo + kCPT, V);
+    double sr = 0.0, sp = 0.0;
+    for (int i = lo; i < hi; ++i) {
+        double p, r;
+        stop_terms(s, a.inv_T, i, p, r);
+        sr += r;
+        sp += p;
+    }
+    const double mine = usep ? sp : sr;
+    double excl, total;
+    seq_excl_scan(mine, s_val, s_excl, &s_total, excl, total);
+    const int tau = pick_thread(mine, run + excl, t, &s_tau);
+    if ((int)threadIdx.x == tau) {
+        double acc = run + excl;
+        int y = -1, last = -1;
+        for (int i = lo; i < hi; ++i) {
+            double p, r;
+            stop_terms(s, a.inv_T, i, p, r);
+            const double w = usep ? p : r;
+            if (w > 0.0) {
+                last = i;
+                acc += w;
+                if (acc > t) {
+                    y = i;
+                    break;
+                }
+            }
+        }
+        write_outputs(a, b, j, y >= 0 ? y : last);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Greedy prefix match: one thread per sequence.
+// ---------------------------------------------------------------------------
+__global__ void k_greedy_prefix(Shape sh, const int32_t* gidx, int32_t* out_tokens, int32_t* out_num) {
+    const int b = blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= sh.B) return;
+    const int K = sh.K;
+    const int32_t* g = gidx + (size_t)b * (K + 1);
+    const int32_t* d = sh.tokens + (size_t)b * K;
+    int j = K;
+    for (int k = 0; k < K; ++k)
+        if (d[k] != g[k]) {
+            j = k;
+            break;
+        }
+    int32_t* out = out_tokens + (size_t)b * (K + 1);
+    for (int k = 0; k < j; ++k) out[k] = d[k];
+    out[j] = g[j];
+    for (int k = j + 1; k <= K; ++k) out[k] = -1;
+    out_num[b] = j;
+}
+
+// Copy row records to the caller's stats arrays.
+__global__ void k_copy_stats(const RowRec* rec, int n_trows, int n_drows, spec_row_stats_t* tstats,
+                             spec_row_stats_t* dstats) {
+    const int i = blockIdx.x * blockDim.x + threadIdx.x;
+    if (i < n_trows) {
+        if (tstats) tstats[i] = rec[i].s;
+    } else if (i < n_trows + n_drows) {
+        if (dstats) dstats[i - n_trows] = rec[i].s;
+    }
+}
+
+// Diagnostic: uniforms of the accept tests and draws.
+__global__ void k_uniforms(uint64_t seed, int B, int K, double* ua, double* us) {
+    const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long long na = (long long)B * K, ns = (long long)B * (K + 1);
+    if (ua && i < na)
+        ua[i] = uniform24(draw_block(seed, (uint32_t)(i / K), (uint32_t)(i % K), PURPOSE_ACCEPT));
+    if (us && i < ns)
+        us[i] = uniform53(draw_block(seed, (uint32_t)(i / (K + 1)), (uint32_t)(i % (K + 1)), PURPOSE_SAMPLE));
+}
+
+}  // namespace sv

@@ -9,27 +9,24 @@
 #include <utility>
 
 #include "../../include/spec_verify.h"
-#include "kernels.h"
+#include "seq_kernels.h"
 
 namespace {
 
 using namespace sv;
 
-// Library-owned scratch for one (device, stream): tile partials, row records,
-// sampling chunk sums, counters (kept at zero between calls by the kernels
-// that use them) and greedy argmax slots (likewise).
+// Library-owned scratch for one (device, stream): row records, kept lists of
+// filtered target rows, greedy argmax indices and draw chunk sums.  Every
+// kernel writes what it later reads within the same call, so nothing needs
+// clearing between calls.
 struct Workspace {
     void* base = nullptr;
-    size_t bytes = 0;
-    size_t cap_tiles = 0, cap_rows = 0, cap_chunks = 0, cap_seqs = 0, cap_trows = 0;
-    float* tile_m = nullptr;
-    double* tile_z = nullptr;
+    size_t cap_rows = 0, cap_trows = 0, cap_chunks = 0;
     RowRec* rec = nullptr;
+    uint2* kept = nullptr;
+    int* kept_n = nullptr;
+    int32_t* gidx = nullptr;
     double2* chunk_sum = nullptr;
-    unsigned* row_cnt = nullptr;
-    unsigned* seq_cnt = nullptr;
-    unsigned* gseq_cnt = nullptr;
-    unsigned long long* gkey = nullptr;
 };
 
 std::mutex g_mu;
@@ -39,59 +36,38 @@ void* g_ev_after = nullptr;
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-// Returns SPEC_OK and a workspace with at least the requested capacities.
-int get_workspace(hipStream_t stream, size_t tiles, size_t rows, size_t chunks, size_t seqs,
-                  size_t trows, Workspace** out) {
+int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, Workspace** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_LAUNCH;
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace& w = g_ws[{dev, stream}];
-    if (w.base && tiles <= w.cap_tiles && rows <= w.cap_rows && chunks <= w.cap_chunks &&
-        seqs <= w.cap_seqs && trows <= w.cap_trows) {
+    if (w.base && rows <= w.cap_rows && trows <= w.cap_trows && chunks <= w.cap_chunks) {
         *out = &w;
         return SPEC_OK;
     }
     Workspace nw;
-    nw.cap_tiles = std::max(tiles, w.cap_tiles);
     nw.cap_rows = std::max(rows, w.cap_rows);
-    nw.cap_chunks = std::max(chunks, w.cap_chunks);
-    nw.cap_seqs = std::max(seqs, w.cap_seqs);
     nw.cap_trows = std::max(trows, w.cap_trows);
+    nw.cap_chunks = std::max(chunks, w.cap_chunks);
     size_t off = 0;
-    const size_t o_tm = off; off = align_up(off + nw.cap_tiles * sizeof(float));
-    const size_t o_tz = off; off = align_up(off + nw.cap_tiles * sizeof(double));
     const size_t o_rec = off; off = align_up(off + nw.cap_rows * sizeof(RowRec));
+    const size_t o_kept = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(uint2));
+    const size_t o_kn = off; off = align_up(off + nw.cap_trows * sizeof(int));
+    const size_t o_g = off; off = align_up(off + nw.cap_trows * sizeof(int32_t));
     const size_t o_cs = off; off = align_up(off + nw.cap_chunks * sizeof(double2));
-    const size_t o_zero = off;  // counters and slots that must start at zero
-    const size_t o_rc = off; off = align_up(off + nw.cap_rows * sizeof(unsigned));
-    const size_t o_sc = off; off = align_up(off + nw.cap_seqs * sizeof(unsigned));
-    const size_t o_gsc = off; off = align_up(off + nw.cap_seqs * sizeof(unsigned));
-    const size_t o_gk = off; off = align_up(off + nw.cap_trows * sizeof(unsigned long long));
-    nw.bytes = off;
     if (w.base) {
         // the old buffer may still be in use by work queued on this stream
         if (hipStreamSynchronize(stream) != hipSuccess) return SPEC_E_LAUNCH;
         (void)hipFree(w.base);
-        w.base = nullptr;
-    }
-    if (hipMalloc(&nw.base, nw.bytes) != hipSuccess) {
         w = Workspace();
-        return SPEC_E_NOMEM;
     }
+    if (hipMalloc(&nw.base, std::max<size_t>(off, 256)) != hipSuccess) return SPEC_E_NOMEM;
     char* b = static_cast<char*>(nw.base);
-    if (hipMemsetAsync(b + o_zero, 0, nw.bytes - o_zero, stream) != hipSuccess) {
-        (void)hipFree(nw.base);
-        w = Workspace();
-        return SPEC_E_LAUNCH;
-    }
-    nw.tile_m = reinterpret_cast<float*>(b + o_tm);
-    nw.tile_z = reinterpret_cast<double*>(b + o_tz);
     nw.rec = reinterpret_cast<RowRec*>(b + o_rec);
+    nw.kept = reinterpret_cast<uint2*>(b + o_kept);
+    nw.kept_n = reinterpret_cast<int*>(b + o_kn);
+    nw.gidx = reinterpret_cast<int32_t*>(b + o_g);
     nw.chunk_sum = reinterpret_cast<double2*>(b + o_cs);
-    nw.row_cnt = reinterpret_cast<unsigned*>(b + o_rc);
-    nw.seq_cnt = reinterpret_cast<unsigned*>(b + o_sc);
-    nw.gseq_cnt = reinterpret_cast<unsigned*>(b + o_gsc);
-    nw.gkey = reinterpret_cast<unsigned long long*>(b + o_gk);
     w = nw;
     *out = &w;
     return SPEC_OK;
@@ -103,21 +79,25 @@ bool dtype_size(int dt, int* sz) {
     return false;
 }
 
-int ceil_div(long long a, long long b) { return (int)((a + b - 1) / b); }
+long long ceil_div(long long a, long long b) { return (a + b - 1) / b; }
 
 int check_sizes(int B, int K, int V) {
     if (B < 0 || K < 0 || V < 1) return SPEC_E_INVALID;
     const long long rows = (long long)B * (2LL * K + 1);
-    if (rows > (1LL << 30)) return SPEC_E_INVALID;
+    if (rows >= (1LL << 31)) return SPEC_E_INVALID;
     if (rows * (long long)V >= (1LL << 40)) return SPEC_E_INVALID;
-    if ((long long)V >= (1LL << 31) - kTile) return SPEC_E_INVALID;
-    // grid sizes: tiles of every row must fit a 32-bit grid
-    if (rows * (long long)ceil_div(V, kTile) >= (1LL << 31)) return SPEC_E_INVALID;
+    if ((long long)V >= (1LL << 30)) return SPEC_E_INVALID;
+    if ((long long)B * ceil_div(V, kChunk) >= (1LL << 31)) return SPEC_E_INVALID;
     return SPEC_OK;
 }
 
-int launch_status() {
-    return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_E_LAUNCH;
+int launch_status() { return hipGetLastError() == hipSuccess ? SPEC_OK : SPEC_E_LAUNCH; }
+
+void take_events(void** evb, void** eva) {
+    std::lock_guard<std::mutex> lock(g_mu);
+    *evb = g_ev_before;
+    *eva = g_ev_after;
+    g_ev_before = g_ev_after = nullptr;
 }
 
 int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, int32_t* out_tokens,
@@ -128,26 +108,26 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     if (rc) return rc;
     if (B == 0) return SPEC_OK;
     if (!target || !out_tokens || !out_num || (K > 0 && !tokens)) return SPEC_E_INVALID;
-    const int nt = ceil_div(V, kTile);
     const int n_trows = B * (K + 1);
     Workspace* ws;
-    rc = get_workspace(stream, 0, 0, 0, B, n_trows, &ws);
+    rc = get_workspace(stream, 0, n_trows, 0, &ws);
     if (rc) return rc;
-    GreedyArgs a;
-    a.sh = Shape{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0,
-                 n_trows, 0, nt};
-    a.gkey = ws->gkey;
-    a.seq_cnt = ws->gseq_cnt;
-    a.out_tokens = out_tokens;
-    a.out_num = out_num;
-    hipLaunchKernelGGL(k_greedy, dim3((unsigned)((long long)n_trows * nt)), dim3(kBlock), 0, stream, a);
+    const Shape sh{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0, n_trows, 0};
+    void *evb, *eva;
+    take_events(&evb, &eva);
+    if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
+    hipLaunchKernelGGL(k_row_argmax, dim3(n_trows), dim3(kRB), 0, stream, sh, ws->gidx);
+    if ((rc = launch_status())) return rc;
+    if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
+    hipLaunchKernelGGL(k_greedy_prefix, dim3((unsigned)ceil_div(B, 256)), dim3(256), 0, stream, sh,
+                       (const int32_t*)ws->gidx, out_tokens, out_num);
     return launch_status();
 }
 
 int run_sampling(const void* target, const void* draft, const int32_t* tokens, int B, int K, int V,
                  float temperature, int top_k, float top_p, uint64_t seed, int32_t* out_tokens,
-                 int32_t* out_num, hipStream_t stream, int tdt, int ddt,
-                 spec_row_stats_t* tstats, spec_row_stats_t* dstats) {
+                 int32_t* out_num, hipStream_t stream, int tdt, int ddt, spec_row_stats_t* tstats,
+                 spec_row_stats_t* dstats) {
     int tsz, dsz = 4;
     if (!dtype_size(tdt, &tsz)) return SPEC_E_UNSUPPORTED;
     if (K > 0 && !dtype_size(ddt, &dsz)) return SPEC_E_UNSUPPORTED;
@@ -161,76 +141,69 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     if (!target || !out_tokens || !out_num) return SPEC_E_INVALID;
     if (K > 0 && (!draft || !tokens)) return SPEC_E_INVALID;
 
-    const int nt = ceil_div(V, kTile);
     const int n_trows = B * (K + 1);
     const int n_drows = B * K;
     const int rows = n_trows + n_drows;
-    const int n_chunks = ceil_div(V, kChunk);
+    const bool use_k = top_k > 0 && top_k < V;
+    const bool use_p = top_p < 1.0f;
+    const bool filtered = use_k || use_p;
+    const int n_chunks = (int)ceil_div(V, kChunk);
     Workspace* ws;
-    rc = get_workspace(stream, (size_t)rows * nt, rows, (size_t)B * n_chunks, B, 0, &ws);
+    rc = get_workspace(stream, rows, filtered ? n_trows : 0, filtered ? 0 : (size_t)B * n_chunks, &ws);
     if (rc) return rc;
 
     const Shape sh{static_cast<const char*>(target), static_cast<const char*>(draft), tokens, B, K, V,
-                   tdt, ddt, tsz, dsz, n_trows, n_drows, nt};
-    const bool use_k = top_k > 0 && top_k < V;
-    const bool use_p = top_p < 1.0f;
-
-    StreamArgs sa;
-    sa.sh = sh;
-    // c = c_hi + c_lo with c_hi carrying 12 significant bits, so that
-    // (x - M) * c_hi is exact for the 8-bit (bf16) and most f32 differences
+                   tdt, ddt, tsz, dsz, n_trows, n_drows};
+    RowArgs ra;
+    ra.sh = sh;
+    // c = c_hi + c_lo, c_hi with 12 significant bits so that (x - m) * c_hi
+    // is exact for bf16 differences
     const float c_full = (float)c;
     const float c_hi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, c_full) & 0xFFFFF800u);
-    sa.c_hi = c_hi;
-    sa.c_lo = (float)(c - (double)c_hi);
-    sa.inv_T = inv_T;
-    sa.filtered = use_k || use_p;
-    sa.tile_m = ws->tile_m;
-    sa.tile_z = ws->tile_z;
-    sa.row_cnt = ws->row_cnt;
-    sa.rec = ws->rec;
+    ra.c_hi = c_hi;
+    ra.c_lo = (float)(c - (double)c_hi);
+    ra.c = c_full;
+    ra.inv_T = inv_T;
+    ra.top_k = top_k;
+    ra.top_p = top_p;
+    ra.use_k = use_k;
+    ra.use_p = use_p;
+    int lg = 0;
+    while ((1LL << lg) < (long long)V + 1) ++lg;
+    ra.fx_shift = 62 - lg;
+    ra.rec = ws->rec;
+    ra.kept = ws->kept;
+    ra.kept_n = ws->kept_n;
 
-    void* evb = nullptr;
-    void* eva = nullptr;
-    {
-        std::lock_guard<std::mutex> lock(g_mu);
-        std::swap(evb, g_ev_before);
-        std::swap(eva, g_ev_after);
-    }
+    void *evb, *eva;
+    take_events(&evb, &eva);
     if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
-    hipLaunchKernelGGL(k_rowstats, dim3((unsigned)((long long)rows * nt)), dim3(kBlock), 0, stream, sa);
+    hipLaunchKernelGGL(k_row, dim3(rows), dim3(kRB), 0, stream, ra);
     if ((rc = launch_status())) return rc;
     if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
 
-    if (sa.filtered) {
-        ResolveArgs ra;
-        ra.sh = sh;
-        ra.inv_T = inv_T;
-        ra.top_k = top_k;
-        ra.top_p = top_p;
-        int lg = 0;
-        while ((1LL << lg) < (long long)V + 1) ++lg;
-        ra.fx_shift = 62 - lg;
-        ra.rec = ws->rec;
-        hipLaunchKernelGGL(k_resolve, dim3(rows), dim3(kBlock), 0, stream, ra);
+    SeqArgs sa;
+    sa.sh = sh;
+    sa.inv_T = inv_T;
+    sa.seed = seed;
+    sa.rec = ws->rec;
+    sa.kept = ws->kept;
+    sa.kept_n = ws->kept_n;
+    sa.chunk_sum = ws->chunk_sum;
+    sa.n_chunks = n_chunks;
+    sa.out_tokens = out_tokens;
+    sa.out_num = out_num;
+    if (filtered) {
+        hipLaunchKernelGGL(k_seq_filtered, dim3(B), dim3(kSB), 0, stream, sa);
+        if ((rc = launch_status())) return rc;
+    } else {
+        hipLaunchKernelGGL(k_draw_sums, dim3((unsigned)((long long)B * n_chunks)), dim3(kSB), 0, stream, sa);
+        if ((rc = launch_status())) return rc;
+        hipLaunchKernelGGL(k_draw_pick, dim3(B), dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
     }
-
-    SampleArgs pa;
-    pa.sh = sh;
-    pa.inv_T = inv_T;
-    pa.seed = seed;
-    pa.n_chunks = n_chunks;
-    pa.rec = ws->rec;
-    pa.chunk_sum = ws->chunk_sum;
-    pa.seq_cnt = ws->seq_cnt;
-    pa.out_tokens = out_tokens;
-    pa.out_num = out_num;
-    hipLaunchKernelGGL(k_sample, dim3((unsigned)((long long)B * n_chunks)), dim3(kBlock), 0, stream, pa);
-    if ((rc = launch_status())) return rc;
-
     if (tstats || dstats) {
-        hipLaunchKernelGGL(k_copy_stats, dim3(ceil_div(rows, 256)), dim3(256), 0, stream,
+        hipLaunchKernelGGL(k_copy_stats, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, stream,
                            (const RowRec*)ws->rec, n_trows, n_drows, tstats, dstats);
         if ((rc = launch_status())) return rc;
     }
@@ -277,6 +250,7 @@ int spec_verify_stats(const void* target_logits, const void* draft_logits,
 int spec_rng_uniforms(uint64_t seed, int B, int K, double* u_accept, double* u_sample,
                       void* stream) {
     if (B < 0 || K < 0 || (long long)B * (K + 1) >= (1LL << 31)) return SPEC_E_INVALID;
+    if (B > 0 && !u_sample && !(K > 0 && u_accept)) return SPEC_OK;
     if (B == 0) return SPEC_OK;
     const long long n = (long long)B * (K + 1);
     hipLaunchKernelGGL(k_uniforms, dim3((unsigned)((n + 255) / 256)), dim3(256), 0,

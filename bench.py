@@ -59,7 +59,7 @@ def kernel_source_hash() -> str:
 def traffic_from_profiles(config_name: str, src_hash: str):
     """HBM bytes per launch from the committed PMC summary, only while the
     kernel sources still match the ones the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", "k_rowstats_c3_traffic.json")
+    path = os.path.join(ROOT, "profiles", "k_row_c3_traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -94,7 +94,20 @@ def main():
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0,
+                    help="only run a plain device copy of this many bytes (3 times), for "
+                         "calibrating HBM traffic counters, then exit")
     args = ap.parse_args()
+
+    if args.copy_probe:
+        import torch
+        src = torch.empty(args.copy_probe, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}))
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verifier is data-parallel over sequences and "
@@ -189,7 +202,7 @@ def main():
                    "top_p": w.top_p, "input_sets_rotated": n_sets, "ideal_bytes": ideal},
         "hbm_gbs_step": round(ideal / (ms * 1e-3) / 1e9, 1),
         "pct_peak_step": round(100 * ideal / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "k_rowstats", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_row", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": traffic, "kernel_ms": round(k_ms, 5),
                      "kernel_source_hash": src_hash},

@@ -1,15 +1,20 @@
 // row_kernels.h — per-row kernels: one 512-thread workgroup streams one whole
 // logit row from HBM exactly once.
 //
-//  k_row     : sampling mode.  Running per-thread max / sum of exp((x-M)/T);
-//              for filtered rows (top-k or top-p) a candidate reservoir in
-//              LDS holds every logit at or above a threshold set from the
-//              row's first tile, from which the row's kept set is resolved
-//              exactly at the end; if the reservoir cannot decide (too few
-//              candidates, overflow) the workgroup falls back to an exact
-//              resolution by re-reading the row.  Writes the row record
-//              (M, Z, threshold, p(d_k) or q(d_k)) and, for target rows, the
-//              kept tokens sorted by index.
+//  k_row     : sampling mode.  Three row modes:
+//                plain   (no filter)      running max / sum of exp((x-M)/T);
+//                nucleus (top-p only)     the same sums, plus candidate capture;
+//                top-k   (top-k active)   candidate capture only: the kept set
+//                                         and its mass come from the top-k
+//                                         candidates, so no sum over the row.
+//              Capture: every 16-byte load (8 bf16 or 4 fp32 logits) whose
+//              maximum reaches a threshold set from the row's first tile is
+//              appended, raw, to its wave's LDS segment.  After the stream
+//              the segments are expanded into (logit, index) candidates, the
+//              kept set is resolved exactly from them and, if they cannot
+//              decide (overflow, too few), by re-reading the row.  Writes the
+//              row record (M, Z, threshold, p(d_k) or q(d_k)) and, for target
+//              rows, the kept tokens sorted by index.
 //  k_row_argmax : greedy mode, lowest-index argmax of a target row.
 //
 // Row numbering: rows [0, B*(K+1)) are target rows b*(K+1)+k, rows
@@ -29,11 +34,18 @@ constexpr int kRB = 512;                 // threads per row workgroup
 constexpr int kRW = kRB / 64;            // waves per row workgroup
 constexpr int kREPT = 16;                // logits per thread per tile
 constexpr int kRTile = kRB * kREPT;      // 8192 logits per tile
-constexpr int kCap = 5120;               // reservoir slots
-constexpr int kOwn = kCap / kRB;         // reservoir slots per thread (10)
-constexpr int kSeg = kCap / kRW;         // reservoir slots owned by one wave (640)
+constexpr int kSegU = 256;               // captured 16-byte units per wave segment
+constexpr int kUnits = kSegU * kRW;      // 2048 units per workgroup
+constexpr int kUPL = kSegU / 64;         // units per lane when a wave expands its segment
+constexpr int kCap = 4096;               // candidates (logit, index) after expansion
+constexpr int kOwn = kCap / kRB;         // candidates per thread during resolution (8)
 constexpr int kR0 = 64;                  // rank among thread maxima for the first threshold
 constexpr int kListMax = 4096;           // longest kept list stored for the draw
+
+enum { MODE_PLAIN = 0, MODE_NUCLEUS = 1, MODE_TOPK = 2 };
+
+constexpr int kBufWord3 = 0x00020000;    // raw buffer descriptor, word 3, for gfx9-family parts
+constexpr int kLoadNT = 2;               // cache policy of streaming loads: non-temporal
 
 struct RowRec {
     spec_row_stats_t s;
@@ -189,6 +201,7 @@ struct RowStream {
     int gfull;     // groups that can be read with one 16-byte load
     int nt;        // tiles
     int nfull;     // leading tiles whose every group is a full 16-byte load
+    __amdgpu_buffer_rsrc_t rsrc;  // the row as a raw buffer (full tiles load through it)
 
     __device__ RowStream(const char* p, int v) : rowp(p), V(v) {
         const bool aligned = (((uintptr_t)p) & 15) == 0;
@@ -196,6 +209,7 @@ struct RowStream {
         const int ng = (V + per - 1) / per;
         nt = (ng + kRB * NL - 1) / (kRB * NL);
         nfull = gfull / (kRB * NL);
+        rsrc = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(p), 0, V * esz, kBufWord3);
     }
     __device__ __forceinline__ int group(int t, int j) const {
         return t * kRB * NL + j * kRB + (int)threadIdx.x;
@@ -203,12 +217,23 @@ struct RowStream {
     __device__ __forceinline__ int index(int t, int s) const {
         return group(t, s / per) * per + s % per;
     }
-    // tile t < nfull: every load in bounds, no checks
+    // tile t < nfull: every load in bounds, no checks.  The tile and load
+    // offsets are uniform (scalar offset), the lane's offset is the same for
+    // every load, so no per-load address arithmetic.
     __device__ __forceinline__ void issue_full(int t, u32x4 (&raw)[NL]) const {
-        const char* base = rowp + (size_t)t * (kRB * NL * 16);
-        const uint32_t lane_off = threadIdx.x * 16u;
 #pragma unroll
-        for (int j = 0; j < NL; ++j) raw[j] = ld16_nt(base + j * (kRB * 16) + lane_off);
+        for (int j = 0; j < NL; ++j)
+            raw[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   rsrc, (int)(threadIdx.x * 16u), (t * NL + j) * (kRB * 16),
+                                                   kLoadNT));
+    }
+    // any tile: groups past the full ones load group 0 instead (needs gfull > 0)
+    __device__ __forceinline__ void issue_clamped(int t, u32x4 (&raw)[NL]) const {
+#pragma unroll
+        for (int j = 0; j < NL; ++j) {
+            const int g = group(t, j);
+            raw[j] = ld16_nt(rowp + (size_t)(g < gfull ? g : 0) * 16);
+        }
     }
     __device__ __forceinline__ void issue(int t, u32x4 (&raw)[NL]) const {
         if (t < nfull) {
@@ -264,6 +289,31 @@ struct RowStream {
             }
         }
     }
+    // Group j of a tile in its stored 16-byte form, rebuilt from the widened
+    // values (slots past the end of the row hold -inf).
+    __device__ __forceinline__ static u32x4 repack(const float (&v)[kREPT], int j) {
+        u32x4 u;
+        if (DT == DT_BF16) {
+            u.x = (__float_as_uint(v[j * 8 + 1]) & 0xFFFF0000u) | (__float_as_uint(v[j * 8 + 0]) >> 16);
+            u.y = (__float_as_uint(v[j * 8 + 3]) & 0xFFFF0000u) | (__float_as_uint(v[j * 8 + 2]) >> 16);
+            u.z = (__float_as_uint(v[j * 8 + 5]) & 0xFFFF0000u) | (__float_as_uint(v[j * 8 + 4]) >> 16);
+            u.w = (__float_as_uint(v[j * 8 + 7]) & 0xFFFF0000u) | (__float_as_uint(v[j * 8 + 6]) >> 16);
+        } else {
+            u.x = __float_as_uint(v[j * 4 + 0]);
+            u.y = __float_as_uint(v[j * 4 + 1]);
+            u.z = __float_as_uint(v[j * 4 + 2]);
+            u.w = __float_as_uint(v[j * 4 + 3]);
+        }
+        return u;
+    }
+    // Logit q of a stored 16-byte group, widened.
+    __device__ __forceinline__ static float unit_value(const u32x4& u, int q) {
+        if (DT == DT_BF16) {
+            const uint32_t w = (q >> 1) == 0 ? u.x : (q >> 1) == 1 ? u.y : (q >> 1) == 2 ? u.z : u.w;
+            return (q & 1) ? bf16_hi(w) : bf16_lo(w);
+        }
+        return __uint_as_float(q == 0 ? u.x : q == 1 ? u.y : q == 2 ? u.z : u.w);
+    }
 };
 
 // ---------------------------------------------------------------------------
@@ -274,8 +324,9 @@ constexpr int kBinMax = 512;             // largest bin resolved pairwise
 
 struct RowArgs {
     Shape sh;
-    float c_hi, c_lo;   // log2(e)/T = c_hi + c_lo, c_hi with 12 significant bits
-    float c;            // log2(e)/T rounded to float
+    float c_hi, c_lo;   // log2(e)/T = c_hi + c_lo to about 2^-48 relative, c_hi < log2(e)/T, c_lo > 0
+    double c64;         // log2(e)/T
+    float c8;           // log2(e)/(8 T), rounded
     double inv_T;
     int top_k;          // active iff use_k
     float top_p;        // active iff use_p
@@ -287,102 +338,221 @@ struct RowArgs {
 };
 
 struct RowShared {
-    u64 buf[kCap];          // reservoir: kRW segments of kSeg entries (logit bits << 32) | index
-    u64 hm[kNB];            // per-bin fixed-point mass
-    uint32_t hc[kNB];       // per-bin count
-    uint32_t bkey[kBinMax]; // entries of one bin
-    u64 bw[kBinMax];
+    union {
+        struct {                      // while the row streams: one segment per wave
+            u32x4 raw[kUnits + 64];   // captured 16-byte groups, as stored (+ a scratch slot per lane)
+            uint32_t grp[kUnits + 64];  // their group numbers
+        } st;
+        struct {                      // after the stream
+            u64 buf[kCap + kRB];      // candidates (logit bits << 32) | index in per-thread
+                                      // columns (row kOwn: scratch), later the kept list
+            u64 hm[kNB];              // per-bin fixed-point mass
+            uint32_t hc[kNB];         // per-bin count
+            uint32_t bkey[kBinMax];   // entries of one bin
+            u64 bw[kBinMax];
+        } fz;
+    } u;
+    uint32_t th_hc[kNB];      // histogram of the first threshold
     Sel sel;
     double red_d[kRW];
     float red_f[kRW];
     u64 red_u[kRW];
-    int n;                  // reservoir entries after compaction (> kCap: overflow)
-    int wfill[kRW];         // per-wave segment fill
-    int wovf[kRW];          // per-wave overflow flag
+    int red_i[kRW];
+    uint32_t red_k[kRW];
     int nbin;
     int nlist;
     int ibin;
     u64 ubefore;
     uint32_t cbefore;
-    float tau;              // capture threshold
 };
 
 __device__ __forceinline__ float rb_min(float v, float* s) { return -rb_max(-v, s); }
 
-// One wave (wave 0) scans bins 0..kNB-1 in order and finds the first bin at
-// which the running sum of val(b) reaches target; returns it with the sum of
-// the bins before it (bin = -1 and before = total when it is never reached).
-template <class F>
-__device__ __forceinline__ void wave_first_reach(F&& val, u64 target, int& bin, u64& before) {
-    constexpr int per = kNB / 64;
-    const int lane = threadIdx.x & 63;
-    u64 c[per];
-    u64 ls = 0ull;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-        c[i] = val(per * lane + i);
-        ls += c[i];
-    }
-    u64 incl = ls;
+// Exclusive prefix of one int per thread in thread order; also the total.
+__device__ __forceinline__ int rb_excl_scan(int v, int* s, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    int incl = v;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
-        const u64 t = __shfl_up(incl, off, 64);
+        const int t = __shfl_up(incl, off, 64);
         if (lane >= off) incl += t;
     }
-    const u64 m = __ballot(incl >= target);
+    __syncthreads();
+    if (lane == 63) s[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) {
+        before += w < wave ? s[w] : 0;
+        total += s[w];
+    }
+    return before + incl - v;
+}
+
+// Block-wide (sum, sum, min) of a count, a mass and a key, in one exchange.
+__device__ __forceinline__ void rb_count_mass_min(uint32_t& c, u64& m, uint32_t& k, RowShared& S) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        c += __shfl_xor(c, off, 64);
+        m += __shfl_xor(m, off, 64);
+        k = min(k, (uint32_t)__shfl_xor(k, off, 64));
+    }
+    __syncthreads();
+    if (lane == 0) {
+        S.red_i[wave] = (int)c;
+        S.red_u[wave] = m;
+        S.red_k[wave] = k;
+    }
+    __syncthreads();
+    c = 0u;
+    m = 0ull;
+    k = 0xFFFFFFFFu;
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) {
+        c += (uint32_t)S.red_i[w];
+        m += S.red_u[w];
+        k = min(k, S.red_k[w]);
+    }
+}
+
+// One wave (wave 0) scans bins 0..kNB-1 in order and finds the first bin at
+// which the running sum of va(b) reaches target; returns it with the sums of
+// va and vb over the bins before it (bin = -1 and the totals when target is
+// never reached).
+template <class FA, class FB>
+__device__ __forceinline__ void wave_first_reach(FA&& va, FB&& vb, u64 target, int& bin, u64& before_a,
+                                                 u64& before_b) {
+    constexpr int per = kNB / 64;
+    const int lane = threadIdx.x & 63;
+    u64 c[per], d[per];
+    u64 la = 0ull, lb = 0ull;
+#pragma unroll
+    for (int i = 0; i < per; ++i) {
+        c[i] = va(per * lane + i);
+        d[i] = vb(per * lane + i);
+        la += c[i];
+        lb += d[i];
+    }
+    u64 ia = la, ib = lb;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const u64 ta = __shfl_up(ia, off, 64);
+        const u64 tb = __shfl_up(ib, off, 64);
+        if (lane >= off) {
+            ia += ta;
+            ib += tb;
+        }
+    }
+    const u64 m = __ballot(ia >= target);
     if (m == 0) {
         bin = -1;
-        before = __shfl(incl, 63, 64);
+        before_a = __shfl(ia, 63, 64);
+        before_b = __shfl(ib, 63, 64);
         return;
     }
     const int L = __ffsll((long long)m) - 1;
-    int d = 0;
-    u64 run = incl - ls;
+    int dbin = 0;
+    u64 ra = ia - la, rb = ib - lb;
     if (lane == L) {
 #pragma unroll
         for (int i = 0; i < per; ++i) {
-            if (run + c[i] >= target) {
-                d = per * lane + i;
+            if (ra + c[i] >= target) {
+                dbin = per * lane + i;
                 break;
             }
-            run += c[i];
+            ra += c[i];
+            rb += d[i];
         }
     }
-    bin = __shfl(d, L, 64);
-    before = __shfl(run, L, 64);
+    bin = __shfl(dbin, L, 64);
+    before_a = __shfl(ra, L, 64);
+    before_b = __shfl(rb, L, 64);
 }
 
-// Reservoir append for one tile.  Every wave owns a segment of kSeg slots
-// and a uniform fill count (kept in a scalar register), so an append costs a
-// ballot per slot and, for slots with captures, a prefix count and one LDS
-// store; no atomics.  Entries are (logit bits << 32) | token index.
-template <int DT>
-__device__ __forceinline__ void capture_tile(RowShared& S, const RowStream<DT>& st, int t,
-                                             const float (&v)[kREPT], float tau, int& fill,
-                                             int& ovf) {
-    const int wave = threadIdx.x >> 6;
-    uint2* seg = reinterpret_cast<uint2*>(S.buf) + wave * kSeg;
-    const int idx0 = st.index(t, 0);
-    constexpr int per = RowStream<DT>::per;
+// Capture for one tile.  Every wave owns a segment of kSegU slots and a
+// uniform fill count (a scalar register).  The ballots of the tile's loads
+// are taken first; if they all fit, the lanes whose group maximum reaches tau
+// store their 16 bytes and group number at fill + (rank among the hits),
+// otherwise the segment stops growing and ovf is raised.  No atomics, no
+// branches and no exec-mask changes.
+template <int NL>
+__device__ __forceinline__ void capture_units(RowShared& S, int t, const u32x4 (&unit)[NL],
+                                              const float (&gm)[NL], float tau, int& fill, int& ovf) {
+    const int seg0 = (threadIdx.x >> 6) * kSegU;
+    u64 m[NL];
+    int c[NL];
+    int tot = 0;
 #pragma unroll
-    for (int s = 0; s < kREPT; ++s) {
-        const bool hit = v[s] >= tau;
-        const u64 m = __builtin_amdgcn_ballot_w64(hit);
-        if (m != 0ull) {
-            const int c = __popcll(m);
-            if (fill + c <= kSeg) {
-                if (hit) {
-                    const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
-                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
-                    seg[fill + r] = make_uint2((uint32_t)(idx0 + (s / per) * kRB * per + s % per),
-                                               __float_as_uint(v[s]));
-                }
-                fill += c;
-            } else {
-                ovf = 1;
+    for (int j = 0; j < NL; ++j) {
+        m[j] = __builtin_amdgcn_ballot_w64(gm[j] >= tau);
+        c[j] = __popcll(m[j]);
+        tot += c[j];
+    }
+    const bool ok = fill + tot <= kSegU;
+    const int lane = threadIdx.x & 63;
+    int f = fill;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) {
+        // lanes without a hit (or all lanes once the segment is full) store
+        // into their own scratch slot past the segments, so every lane
+        // stores and nothing branches
+        const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m[j] >> 32),
+                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m[j], 0u));
+        const int mine = (ok && gm[j] >= tau) ? 1 : 0;
+        const int pos = kUnits + lane + mine * (seg0 + f + r - kUnits - lane);
+        S.u.st.raw[pos] = unit[j];
+        S.u.st.grp[pos] = (uint32_t)(t * (kRB * NL) + j * kRB) + threadIdx.x;
+        f += c[j];
+    }
+    fill = __builtin_amdgcn_readfirstlane(ok ? f : fill);
+    ovf = __builtin_amdgcn_readfirstlane(ok ? ovf : 1);
+}
+
+// Expands the wave segments into candidates, every logit >= tau of every
+// captured group, as (logit bits << 32) | index.  Each thread keeps its
+// candidates in its own column of S.u.fz.buf (slots tid + i * kRB, i < n_own);
+// row kOwn of the buffer takes the writes of non-candidates and overflow, so
+// the loop has no branches.  Returns the block's candidate count, or kCap + 1
+// when a segment or a column overflowed.
+template <int DT>
+__device__ __forceinline__ int expand_units(RowShared& S, int V, float tau, int fill, int ovf, int& n_own) {
+    constexpr int per = RowStream<DT>::per;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    u32x4 ur[kUPL];
+    uint32_t ug[kUPL];
+#pragma unroll
+    for (int i = 0; i < kUPL; ++i) {
+        const int k = lane + 64 * i;
+        ur[i] = u32x4{0u, 0u, 0u, 0u};
+        ug[i] = 0u;
+        if (k < fill) {
+            ur[i] = S.u.st.raw[wave * kSegU + k];
+            ug[i] = S.u.st.grp[wave * kSegU + k];
+        }
+    }
+    __syncthreads();  // segments read: the union now belongs to the candidates
+    int n = 0;
+#pragma unroll
+    for (int i = 0; i < kUPL; ++i) {
+        if (64 * i < fill) {  // uniform: some lane of the wave holds unit i
+            const bool have = lane + 64 * i < fill;
+            const int lim = have ? V - (int)ug[i] * per : 0;  // slots of the unit inside the row
+#pragma unroll
+            for (int q = 0; q < per; ++q) {
+                const float x = RowStream<DT>::unit_value(ur[i], q);
+                const bool hit = q < lim && x >= tau;
+                S.u.fz.buf[threadIdx.x + min(n, kOwn) * kRB] =
+                    ((u64)__float_as_uint(x) << 32) | (ug[i] * per + q);
+                n += hit ? 1 : 0;
             }
         }
     }
+    n_own = min(n, kOwn);
+    const u64 flags = (u64)n | ((u64)((n > kOwn ? 1 : 0) | ovf) << 32);
+    const u64 tot = rb_sum_u64(flags, S.red_u);  // its barriers also publish the candidates
+    return (tot >> 32) ? kCap + 1 : (int)(uint32_t)tot;
 }
 
 // First capture threshold, from tile 0: about the rank-th largest thread
@@ -394,15 +564,16 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
     const float mn = rb_min(fin ? tm : INFINITY, S.red_f);
     const float span = M0 - mn;
     const float bscale = span > 0.f ? (float)(kNB - 1) / span : 0.f;
-    for (int i = threadIdx.x; i < kNB; i += kRB) S.hc[i] = 0u;
+    for (int i = threadIdx.x; i < kNB; i += kRB) S.th_hc[i] = 0u;
     __syncthreads();
     const int b = fin ? min(kNB - 1, (int)((M0 - tm) * bscale)) : kNB;
-    if (fin) atomicAdd(&S.hc[b], 1u);
+    if (fin) atomicAdd(&S.th_hc[b], 1u);
     __syncthreads();
     if (threadIdx.x < 64) {
         int bin;
-        u64 before;
-        wave_first_reach([&](int i) { return (u64)S.hc[i]; }, (u64)rank, bin, before);
+        u64 before, unused;
+        wave_first_reach([&](int i) { return (u64)S.th_hc[i]; }, [](int) { return 0ull; }, (u64)rank, bin,
+                         before, unused);
         if (threadIdx.x == 0) S.ibin = bin;
     }
     __syncthreads();
@@ -412,11 +583,11 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
     return tau;
 }
 
-// Resolve top-k / top-p from the reservoir.  Entries (kOwn per thread) hold
+// Resolve top-k / top-p from the candidates.  Entries (kOwn per thread) hold
 // every logit >= the capture threshold.  Returns false when the reservoir
 // cannot decide (the caller then re-reads the row).
 __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S, float M, double Z,
-                                                  int n, double scale, uint32_t& thr_key,
+                                                  int n_own, float tau, double scale, uint32_t& thr_key,
                                                   double& z_kept, int& n_kept) {
     const int tid = threadIdx.x;
     uint32_t key[kOwn];
@@ -425,31 +596,31 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     float xmin = INFINITY;
 #pragma unroll
     for (int i = 0; i < kOwn; ++i) {
-        const int slot = tid + i * kRB;
         key[i] = 0u;
         wt[i] = 0ull;
-        if (slot < n) {
-            const float x = __uint_as_float((uint32_t)(S.buf[slot] >> 32));
+        if (i < n_own) {
+            const float x = __uint_as_float((uint32_t)(S.u.fz.buf[tid + i * kRB] >> 32));
             key[i] = fkey(x);
             wt[i] = (u64)(exp(((double)x - (double)M) * a.inv_T) * scale);
             xmin = fminf(xmin, x);
         }
     }
-    const float lo = rb_min(xmin, S.red_f);
+    // every candidate is >= tau; a row captured whole has tau = -inf
+    const float lo = tau != -INFINITY ? tau : rb_min(xmin, S.red_f);
     const float span = M - lo;
     const float bscale = span > 0.f ? (float)(kNB - 1) / span : 0.f;
     for (int i = tid; i < kNB; i += kRB) {
-        S.hc[i] = 0u;
-        S.hm[i] = 0ull;
+        S.u.fz.hc[i] = 0u;
+        S.u.fz.hm[i] = 0ull;
     }
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kOwn; ++i) {
         bin[i] = kNB;
-        if (tid + i * kRB < n) {
+        if (i < n_own) {
             bin[i] = min(kNB - 1, (int)((M - key_to_float(key[i])) * bscale));
-            atomicAdd(&S.hc[bin[i]], 1u);
-            atomicAdd(&S.hm[bin[i]], wt[i]);
+            atomicAdd(&S.u.fz.hc[bin[i]], 1u);
+            atomicAdd(&S.u.fz.hm[bin[i]], wt[i]);
         }
     }
     __syncthreads();
@@ -460,46 +631,46 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     // smallest kept key, the kept count and the kept mass of the bin.
     auto resolve_bin = [&](int b, uint32_t floor_key, u64 base, bool by_count, u64 limit,
                            uint32_t& kmin, uint32_t& kcnt, u64& kmass) -> bool {
-        if (tid == 0) S.nbin = 0;
-        __syncthreads();
+        int mine = 0;
+#pragma unroll
+        for (int i = 0; i < kOwn; ++i) mine += (bin[i] == b && key[i] >= floor_key) ? 1 : 0;
+        int nb;
+        int p = rb_excl_scan(mine, S.red_i, nb);
+        if (nb > kBinMax) return false;
 #pragma unroll
         for (int i = 0; i < kOwn; ++i) {
             if (bin[i] == b && key[i] >= floor_key) {
-                const int slot = atomicAdd(&S.nbin, 1);
-                if (slot < kBinMax) {
-                    S.bkey[slot] = key[i];
-                    S.bw[slot] = wt[i];
-                }
+                S.u.fz.bkey[p] = key[i];
+                S.u.fz.bw[p] = wt[i];
+                ++p;
             }
         }
         __syncthreads();
-        const int nb = S.nbin;
-        if (nb > kBinMax) return false;
-        uint32_t my_k = 0u, my_c = 0u;
+        uint32_t my_c = 0u;
         u64 my_m = 0ull;
         uint32_t my_min = 0xFFFFFFFFu;
         for (int i = tid; i < nb; i += kRB) {
-            const uint32_t ki = S.bkey[i];
+            const uint32_t ki = S.u.fz.bkey[i];
             uint32_t cgt = 0u;
             u64 mgt = 0ull;
             for (int jj = 0; jj < nb; ++jj) {
-                const uint32_t kj = S.bkey[jj];
+                const uint32_t kj = S.u.fz.bkey[jj];
                 if (kj > ki) {
                     ++cgt;
-                    mgt += S.bw[jj];
+                    mgt += S.u.fz.bw[jj];
                 }
             }
             const bool kept = by_count ? (base + cgt < limit) : (base + mgt < limit);
             if (kept) {
                 ++my_c;
-                my_m += S.bw[i];
+                my_m += S.u.fz.bw[i];
                 my_min = min(my_min, ki);
             }
         }
-        (void)my_k;
-        kcnt = (uint32_t)rb_sum_u64(my_c, S.red_u);
-        kmass = rb_sum_u64(my_m, S.red_u);
-        kmin = 0xFFFFFFFFu - (uint32_t)rb_max_u64(0xFFFFFFFFu - my_min, S.red_u);
+        rb_count_mass_min(my_c, my_m, my_min, S);
+        kcnt = my_c;
+        kmass = my_m;
+        kmin = my_min;
         return true;
     };
 
@@ -511,14 +682,13 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     if (a.use_k) {
         if (tid < 64) {
             int b;
-            u64 before;
-            wave_first_reach([&](int i) { return (u64)S.hc[i]; }, (u64)a.top_k, b, before);
+            u64 before_c, before_m;
+            wave_first_reach([&](int i) { return (u64)S.u.fz.hc[i]; }, [&](int i) { return S.u.fz.hm[i]; },
+                             (u64)a.top_k, b, before_c, before_m);
             if (tid == 0) {
                 S.ibin = b;
-                S.cbefore = (uint32_t)before;
-                u64 mb = 0ull;
-                for (int i = 0; i < (b < 0 ? 0 : b); ++i) mb += S.hm[i];
-                S.ubefore = mb;
+                S.cbefore = (uint32_t)before_c;
+                S.ubefore = before_m;
             }
         }
         __syncthreads();
@@ -543,15 +713,14 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     if (a.use_k && target > zk) target = zk;  // rounding: keep the whole top-k set
     if (tid < 64) {
         int b;
-        u64 before;
-        wave_first_reach([&](int i) -> u64 { return i < bk ? S.hm[i] : (i == bk ? in_k_mass : 0ull); },
-                         target, b, before);
+        u64 before_m, before_c;
+        wave_first_reach([&](int i) -> u64 { return i < bk ? S.u.fz.hm[i] : (i == bk ? in_k_mass : 0ull); },
+                         [&](int i) -> u64 { return i < bk ? S.u.fz.hc[i] : (i == bk ? in_k_cnt : 0u); },
+                         target, b, before_m, before_c);
         if (tid == 0) {
             S.ibin = b;
-            S.ubefore = before;
-            uint32_t cb = 0u;
-            for (int i = 0; i < (b < 0 ? 0 : b); ++i) cb += S.hc[i];
-            S.cbefore = cb;
+            S.ubefore = before_m;
+            S.cbefore = (uint32_t)before_c;
         }
     }
     __syncthreads();
@@ -606,8 +775,8 @@ __device__ __forceinline__ Sel row_select_exact(RowShared& S, const char* rowp, 
     for (int lvl = 0; lvl < nlev; ++lvl) {
         const int shift = 24 - 8 * lvl;
         for (int i = threadIdx.x; i < 256; i += kRB) {
-            S.hm[i] = 0ull;
-            S.hc[i] = 0u;
+            S.u.fz.hm[i] = 0ull;
+            S.u.fz.hc[i] = 0u;
         }
         __syncthreads();
         row_for_each<DT>(rowp, V, [&](int, float x) {
@@ -616,28 +785,28 @@ __device__ __forceinline__ Sel row_select_exact(RowShared& S, const char* rowp, 
                 const uint32_t d = (k >> shift) & 255u;
                 const u64 w = by_count ? 1ull
                                        : (u64)(exp(((double)x - (double)M) * inv_T) * scale);
-                atomicAdd(&S.hm[d], w);
-                atomicAdd(&S.hc[d], 1u);
+                atomicAdd(&S.u.fz.hm[d], w);
+                atomicAdd(&S.u.fz.hc[d], 1u);
             }
         });
         __syncthreads();
         if (threadIdx.x < 64) {
             int bin;
             u64 above;
-            wave_find_from_top(S.hm, target - A, bin, above);
+            wave_find_from_top(S.u.fz.hm, target - A, bin, above);
             if (threadIdx.x == 0) {
                 Sel r;
                 if (bin < 0) {
                     r.ok = 0;
                 } else {
                     uint32_t ca = 0u;
-                    for (int d = 255; d > bin; --d) ca += S.hc[d];
+                    for (int d = 255; d > bin; --d) ca += S.u.fz.hc[d];
                     r.ok = 1;
                     r.key = prefix | ((uint32_t)bin << shift);
                     r.above = A + above;
-                    r.group = S.hm[bin];
+                    r.group = S.u.fz.hm[bin];
                     r.cnt_above = C + ca;
-                    r.cnt_group = S.hc[bin];
+                    r.cnt_group = S.u.fz.hc[bin];
                 }
                 S.sel = r;
             }
@@ -656,13 +825,22 @@ __device__ __forceinline__ Sel row_select_exact(RowShared& S, const char* rowp, 
     return r;
 }
 
-template <int DT, bool FILT>
+// One row.  MODE_PLAIN / MODE_NUCLEUS keep, per thread, the sum of
+// 2^(x * log2(e) / T - 8 k) over the thread's logits, where the reference
+// 8 k is the smallest multiple of 8 at or above the thread's largest
+// x * log2(e) / T so far: every term is at most 1, a change of reference is
+// an exact power-of-two rescale (ldexp), and -8 k is an exact float.  The
+// exponent is two FMAs, x * c_lo + (x * c_hi - 8 k), so the rounding of
+// log2(e)/T to a float adds no systematic error.
+template <int DT, int MODE>
 __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row) {
     const char* rowp = row_ptr(a.sh, row);
     const int V = a.sh.V;
-    constexpr bool filtered = FILT;
+    constexpr bool kFilt = MODE != MODE_PLAIN;
+    constexpr bool kSum = MODE != MODE_TOPK;
     const RowStream<DT> st(rowp, V);
     constexpr int NL = RowStream<DT>::NL;
+    constexpr int per = RowStream<DT>::per;
 
     // the drafted token's logit, fetched while the row streams
     int d_tok = -1;
@@ -671,13 +849,15 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         d_tok = row_token(a.sh, row);
         if (d_tok >= 0 && d_tok < V) xd = load_logit(rowp, DT, d_tok);
     }
-    float m_th = -INFINITY;
-    double z_th = 0.0;
-    float tau = INFINITY;
-    int fill = 0, ovf = 0;  // this wave's reservoir segment (uniform per wave)
+    float m_th = -INFINITY;  // running maximum of this thread's logits
+    float k_th = -INFINITY;  // reference index k (a whole number, as a float)
+    double z_th = 0.0;       // sum of 2^(x * log2(e) / T - 8 k_th) over this thread's logits
+    float tau = INFINITY;    // capture threshold
+    float m_run = -INFINITY; // running maximum for threshold refreshes (top-k rows)
+    int fill = 0, ovf = 0;   // this wave's segment (uniform per wave)
 
-    // One tile: running max / sum of exp, and the reservoir capture.  FULL
-    // tiles take the unchecked unpack; tile 0 also sets the capture threshold.
+    // One tile: group maxima, running max / sum, capture.  FULL tiles take
+    // the unchecked unpack; tile 0 also sets the capture threshold.
     auto process = [&](int t, const u32x4 (&raw)[NL], auto full_tag, bool first) {
         constexpr bool FULL = decltype(full_tag)::value;
         float v[kREPT];
@@ -685,31 +865,57 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             RowStream<DT>::unpack_full(raw, v);
         else
             st.unpack(t, raw, v);
-        float tm = v[0];
+        float gm[NL];
 #pragma unroll
-        for (int s = 1; s < kREPT; ++s) tm = fmaxf(tm, v[s]);
-        if (tm > m_th) {
-            if (m_th != -INFINITY) z_th *= exp(((double)m_th - (double)tm) * a.inv_T);
-            m_th = tm;
+        for (int j = 0; j < NL; ++j) {
+            float g = v[j * per];
+#pragma unroll
+            for (int q = 1; q < per; ++q) g = fmaxf(g, v[j * per + q]);
+            gm[j] = g;
         }
-        if (m_th != -INFINITY) {
-            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+        float tm = gm[0];
 #pragma unroll
-            for (int s = 0; s < kREPT; ++s) {
-                const float y = v[s] - m_th;
-                // filtered rows use Z only in the top-p test (ambiguity band
-                // 1e-6): one product; otherwise the split constant keeps the
-                // exponent free of the rounding of log2(e)/T
-                const float e = FILT ? y * a.c : fmaf(y, a.c_hi, y * a.c_lo);
-                acc[s & 3] += __builtin_amdgcn_exp2f(e);
+        for (int j = 1; j < NL; ++j) tm = fmaxf(tm, gm[j]);
+        if (kSum) {
+            m_th = fmaxf(m_th, tm);
+            // k of this tile: ceil(tm * log2(e) / (8 T)); a float rounding
+            // that lands one short only lets terms exceed 1 by a hair
+            const float kt = ceilf(tm * a.c8);
+            if (kt > k_th) {
+                // new reference: rescale by 2^(8 (k_th - kt)), exact (z_th is
+                // still 0 while no finite logit has been seen)
+                z_th = k_th == -INFINITY ? 0.0 : ldexp(z_th, (int)fmaxf(8.f * (k_th - kt), -4096.f));
+                k_th = kt;
             }
-            z_th += ((double)acc[0] + (double)acc[1]) + ((double)acc[2] + (double)acc[3]);
+            if (k_th != -INFINITY) {
+                const float nmc = -8.f * k_th;
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < kREPT; ++s) {
+                    const float e = fmaf(v[s], a.c_lo, fmaf(v[s], a.c_hi, nmc));
+                    acc[s & 3] += __builtin_amdgcn_exp2f(e);
+                }
+                z_th += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
+            }
         }
-        if (filtered) {
-            if (first)
+        if (kFilt) {
+            // Threshold from the first tile: the kR0-th (nucleus) or top_k-th
+            // (top-k) largest thread maximum, so that at least that many logits
+            // are captured.  Top-k rows raise it after tiles 3 and 15 from the
+            // running thread maxima: any value with top_k logits at or above
+            // it is a lower bound of the row's top_k-th largest.  It only
+            // rises, so every logit at or above the final threshold is held.
+            if (MODE == MODE_TOPK) m_run = fmaxf(m_run, tm);
+            if (first) {
                 tau = V <= kCap ? -INFINITY
-                                : first_threshold(S, tm, max(kR0, a.use_k ? min(a.top_k, kRB) : 0));
-            capture_tile<DT>(S, st, t, v, tau, fill, ovf);
+                                : first_threshold(S, tm, MODE == MODE_TOPK ? max(1, min(a.top_k, kRB)) : kR0);
+            } else if (MODE == MODE_TOPK && (t == 3 || t == 15)) {
+                tau = fmaxf(tau, first_threshold(S, m_run, max(1, min(a.top_k, kRB))));
+            }
+            u32x4 unit[NL];
+#pragma unroll
+            for (int j = 0; j < NL; ++j) unit[j] = FULL ? raw[j] : RowStream<DT>::repack(v, j);
+            capture_units<NL>(S, t, unit, gm, tau, fill, ovf);
         }
     };
     using FullT = std::integral_constant<bool, true>;
@@ -718,7 +924,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     {
         // Steady state: three full tiles of loads in flight in rotating
         // registers, straight-line code so that each tile waits only for its
-        // own loads.  Then the drain, then the remaining tiles one by one.
+        // own loads.  Rows with fewer than four full tiles go tile by tile.
         u32x4 rA[NL], rB[NL], rC[NL];
         const int nf = st.nfull;
         int t = 0;
@@ -729,6 +935,10 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             process(0, rA, FullT{}, true);
             st.issue_full(3, rA);
             t = 1;
+            // Every scalar load is complete here (lgkmcnt(0), other counters
+            // left alone): without it the compiler waits on lgkmcnt inside the
+            // loop, and with capture stores in flight that wait is for the LDS.
+            __builtin_amdgcn_s_waitcnt(0xC07F);
             for (; t + 5 < nf; t += 3) {
                 process(t, rB, FullT{}, false);
                 st.issue_full(t + 3, rB);
@@ -737,10 +947,19 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                 process(t + 2, rA, FullT{}, false);
                 st.issue_full(t + 5, rA);
             }
+            // drain: the rest of the row (at most three more tiles, the last
+            // possibly partial) rides the same rotation with clamped loads
             process(t, rB, FullT{}, false);
+            st.issue_clamped(t + 3, rB);
             process(t + 1, rC, FullT{}, false);
+            st.issue_clamped(t + 4, rC);
             process(t + 2, rA, FullT{}, false);
+            st.issue_clamped(t + 5, rA);
             t += 3;
+            if (t < st.nt) process(t, rB, AnyT{}, false);
+            if (t + 1 < st.nt) process(t + 1, rC, AnyT{}, false);
+            if (t + 2 < st.nt) process(t + 2, rA, AnyT{}, false);
+            t = st.nt;
         }
         for (; t < st.nt; ++t) {
             st.issue(t, rA);
@@ -748,53 +967,30 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         }
     }
 
-    if (filtered) {
-        // compact the per-wave reservoir segments into buf[0, n)
-        const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-        if (lane == 0) {
-            S.wfill[wave] = fill;
-            S.wovf[wave] = ovf;
-        }
-        u64 ent[kSeg / 64];
-#pragma unroll
-        for (int i = 0; i < kSeg / 64; ++i) {
-            const int k = lane + 64 * i;
-            ent[i] = k < fill ? S.buf[wave * kSeg + k] : 0ull;
-        }
-        __syncthreads();
-        int P = 0, total = 0, any_ovf = 0;
-#pragma unroll
-        for (int w = 0; w < kRW; ++w) {
-            P += w < wave ? S.wfill[w] : 0;
-            total += S.wfill[w];
-            any_ovf |= S.wovf[w];
-        }
-#pragma unroll
-        for (int i = 0; i < kSeg / 64; ++i) {
-            const int k = lane + 64 * i;
-            if (k < fill) S.buf[P + k] = ent[i];
-        }
-        if (threadIdx.x == 0) S.n = any_ovf ? kCap + 1 : total;
-        __syncthreads();
+    // ---- merge the row (fixed-order reductions) ----
+    float M = -INFINITY;
+    double Z = 0.0;
+    int n_res = 0, n_own = 0;
+    if (kFilt) n_res = expand_units<DT>(S, V, tau, fill, ovf, n_own);
+    if (MODE == MODE_TOPK) M = rb_max(m_run, S.red_f);
+    if (kSum) {
+        M = rb_max(m_th, S.red_f);
+        // z_th * 2^(8 k_th - M log2(e) / T): the thread's sum relative to the row maximum
+        const double zc = (k_th == -INFINITY) ? 0.0 : z_th * exp2(8.0 * (double)k_th - (double)M * a.c64);
+        Z = rb_sum(zc, S.red_d);
     }
-
-    // ---- merge the row: M and Z over all logits (fixed-order reductions) ----
-    const float M = rb_max(m_th, S.red_f);
-    const double zc = (m_th == -INFINITY) ? 0.0 : z_th * exp(((double)m_th - (double)M) * a.inv_T);
-    const double Z = rb_sum(zc, S.red_d);
 
     float thr = -INFINITY;
     double z_kept = Z;
     int n_kept = V;
     int flags = 0;
 
-    if (filtered) {
+    if (kFilt) {
         flags = SPEC_ROW_FILTERED;
         const double scale = ldexp(1.0, a.fx_shift);
-        const int n_res = S.n;
         uint32_t thr_key = 0u;
         bool fast = n_res <= kCap &&
-                    resolve_reservoir(a, S, M, Z, n_res, scale, thr_key, z_kept, n_kept);
+                    resolve_reservoir(a, S, M, Z, n_own, tau, scale, thr_key, z_kept, n_kept);
         if (fast) {
             thr = key_to_float(thr_key);
         } else {
@@ -831,7 +1027,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             n_kept = (int)cnt;
         }
         // kept list of a target row, sorted by token index: gather the kept
-        // logits (reservoir entries >= thr, or a pass over the row on the
+        // logits (candidates >= thr, or a pass over the row on the
         // exact path) into LDS, then bucket them by tile and rank each entry
         // inside its bucket, which gives a deterministic order.
         if (row < a.sh.n_trows) {
@@ -840,10 +1036,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                 u64 own[kOwn];
                 if (fast) {
 #pragma unroll
-                    for (int i = 0; i < kOwn; ++i) {
-                        const int slot = threadIdx.x + i * kRB;
-                        own[i] = slot < n_res ? S.buf[slot] : 0ull;
-                    }
+                    for (int i = 0; i < kOwn; ++i) own[i] = i < n_own ? S.u.fz.buf[threadIdx.x + i * kRB] : 0ull;
                 }
                 __syncthreads();
                 if (threadIdx.x == 0) S.nlist = 0;
@@ -852,17 +1045,16 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                 if (fast) {
 #pragma unroll
                     for (int i = 0; i < kOwn; ++i) {
-                        const int slot = threadIdx.x + i * kRB;
-                        if (slot < n_res && fkey(__uint_as_float((uint32_t)(own[i] >> 32))) >= tk) {
+                        if (i < n_own && fkey(__uint_as_float((uint32_t)(own[i] >> 32))) >= tk) {
                             const int p = atomicAdd(&S.nlist, 1);
-                            if (p < kCap) S.buf[p] = own[i];
+                            if (p < kCap) S.u.fz.buf[p] = own[i];
                         }
                     }
                 } else {
                     row_for_each<DT>(rowp, V, [&](int i, float x) {
                         if (x >= thr) {
                             const int p = atomicAdd(&S.nlist, 1);
-                            if (p < kCap) S.buf[p] = ((u64)__float_as_uint(x) << 32) | (uint32_t)i;
+                            if (p < kCap) S.u.fz.buf[p] = ((u64)__float_as_uint(x) << 32) | (uint32_t)i;
                         }
                     });
                 }
@@ -870,18 +1062,18 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                 const int nk = min(S.nlist, list_n);
                 // bucket = streaming tile of the token
                 for (int i = threadIdx.x; i < kNB; i += kRB) {
-                    S.hc[i] = 0u;
-                    S.bkey[i] = 0u;
+                    S.u.fz.hc[i] = 0u;
+                    S.u.fz.bkey[i] = 0u;
                 }
 #pragma unroll
                 for (int i = 0; i < kOwn; ++i) {
                     const int slot = threadIdx.x + i * kRB;
-                    own[i] = slot < nk ? S.buf[slot] : 0ull;
+                    own[i] = slot < nk ? S.u.fz.buf[slot] : 0ull;
                 }
                 __syncthreads();
 #pragma unroll
                 for (int i = 0; i < kOwn; ++i)
-                    if (threadIdx.x + i * kRB < nk) atomicAdd(&S.hc[(uint32_t)own[i] / kRTile], 1u);
+                    if (threadIdx.x + i * kRB < nk) atomicAdd(&S.u.fz.hc[(uint32_t)own[i] / kRTile], 1u);
                 __syncthreads();
                 if (threadIdx.x < 64) {
                     // exclusive prefix of bucket counts, bucket starts into hm
@@ -891,7 +1083,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                     u64 ls = 0ull;
 #pragma unroll
                     for (int q = 0; q < per; ++q) {
-                        c[q] = S.hc[per * lane + q];
+                        c[q] = S.u.fz.hc[per * lane + q];
                         ls += c[q];
                     }
                     u64 incl = ls;
@@ -903,7 +1095,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                     u64 run = incl - ls;
 #pragma unroll
                     for (int q = 0; q < per; ++q) {
-                        S.hm[per * lane + q] = run;
+                        S.u.fz.hm[per * lane + q] = run;
                         run += c[q];
                     }
                 }
@@ -912,19 +1104,19 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                 for (int i = 0; i < kOwn; ++i) {
                     if (threadIdx.x + i * kRB < nk) {
                         const uint32_t bkt = (uint32_t)own[i] / kRTile;
-                        const uint32_t p = (uint32_t)S.hm[bkt] + atomicAdd(&S.bkey[bkt], 1u);
-                        S.buf[p] = own[i];
+                        const uint32_t p = (uint32_t)S.u.fz.hm[bkt] + atomicAdd(&S.u.fz.bkey[bkt], 1u);
+                        S.u.fz.buf[p] = own[i];
                     }
                 }
                 __syncthreads();
                 uint2* out = a.kept + (size_t)row * kListMax;
                 for (int e = threadIdx.x; e < nk; e += kRB) {
-                    const u64 me = S.buf[e];
+                    const u64 me = S.u.fz.buf[e];
                     const uint32_t idx = (uint32_t)me;
                     const uint32_t bkt = idx / kRTile;
-                    const int s0 = (int)S.hm[bkt], len = (int)S.hc[bkt];
+                    const int s0 = (int)S.u.fz.hm[bkt], len = (int)S.u.fz.hc[bkt];
                     int rank = 0;
-                    for (int q = s0; q < s0 + len; ++q) rank += ((uint32_t)S.buf[q] < idx) ? 1 : 0;
+                    for (int q = s0; q < s0 + len; ++q) rank += ((uint32_t)S.u.fz.buf[q] < idx) ? 1 : 0;
                     out[s0 + rank] = make_uint2(idx, (uint32_t)(me >> 32));
                 }
             }
@@ -935,13 +1127,13 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     if (threadIdx.x == 0) {
         RowRec r;
         r.s.max_logit = M;
-        r.z_all = Z;
+        r.z_all = kSum ? Z : __longlong_as_double(0x7FF8000000000000LL);  // NaN: not computed
         r.pad = 0.0;
         r.s.thresh = thr;
         r.s.n_kept = n_kept;
         r.s.flags = flags;
         r.s.z_kept = z_kept;
-        double prob = __builtin_nan("");
+        double prob = __longlong_as_double(0x7FF8000000000000LL);  // NaN: no drafted token
         if (row_has_token(a.sh, row)) {
             prob = 0.0;
             if (d_tok >= 0 && d_tok < V && xd >= thr)
@@ -956,16 +1148,21 @@ __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
     __shared__ RowShared S;
     const int row = blockIdx.x;
     const bool bf = row_dt(a.sh, row) == DT_BF16;
-    if (a.use_k || a.use_p) {
+    if (a.use_k) {
         if (bf)
-            row_body<DT_BF16, true>(a, S, row);
+            row_body<DT_BF16, MODE_TOPK>(a, S, row);
         else
-            row_body<DT_F32, true>(a, S, row);
+            row_body<DT_F32, MODE_TOPK>(a, S, row);
+    } else if (a.use_p) {
+        if (bf)
+            row_body<DT_BF16, MODE_NUCLEUS>(a, S, row);
+        else
+            row_body<DT_F32, MODE_NUCLEUS>(a, S, row);
     } else {
         if (bf)
-            row_body<DT_BF16, false>(a, S, row);
+            row_body<DT_BF16, MODE_PLAIN>(a, S, row);
         else
-            row_body<DT_F32, false>(a, S, row);
+            row_body<DT_F32, MODE_PLAIN>(a, S, row);
     }
 }
 

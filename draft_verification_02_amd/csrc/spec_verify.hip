@@ -156,13 +156,15 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
                    tdt, ddt, tsz, dsz, n_trows, n_drows};
     RowArgs ra;
     ra.sh = sh;
-    // c = c_hi + c_lo, c_hi with 12 significant bits so that (x - m) * c_hi
-    // is exact for bf16 differences
-    const float c_full = (float)c;
-    const float c_hi = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, c_full) & 0xFFFFF800u);
+    // c = c_hi + c_lo with c_hi the largest float below c, so that c_lo > 0:
+    // for x = -inf both products are -inf and their sum stays -inf (a c_lo of
+    // the other sign, or zero, would give NaN).
+    float c_hi = (float)c;
+    if ((double)c_hi >= c) c_hi = std::nextafter(c_hi, 0.0f);
     ra.c_hi = c_hi;
     ra.c_lo = (float)(c - (double)c_hi);
-    ra.c = c_full;
+    ra.c64 = c;
+    ra.c8 = (float)(c * 0.125);
     ra.inv_T = inv_T;
     ra.top_k = top_k;
     ra.top_p = top_p;

@@ -42,24 +42,110 @@ __device__ __forceinline__ float key_to_float(uint32_t k) {
     return __uint_as_float(u);
 }
 
+// ---- cross-lane moves within a wave64, by DPP (no LDS round trip) --------
+// Every helper below expects all 64 lanes active.
+enum : int {
+    kDppQuadXor1 = 0xB1,       // quad_perm [1,0,3,2]: lane ^ 1
+    kDppQuadXor2 = 0x4E,       // quad_perm [2,3,0,1]: lane ^ 2
+    kDppRowMirror = 0x140,     // lane 15 - i within a row of 16
+    kDppRowHalfMirror = 0x141, // lane 7 - i within a half row of 8
+    kDppRowShr1 = 0x111,
+    kDppRowShr2 = 0x112,
+    kDppRowShr4 = 0x114,
+    kDppRowShr8 = 0x118,
+    kDppRowBcast15 = 0x142,    // lane 15 of each row to the next row
+    kDppRowBcast31 = 0x143,    // lane 31 to rows 2 and 3
+    kDppWaveShr1 = 0x138,      // lane i - 1 of the whole wave
+};
+
+template <int CTRL, int ROWS = 0xF, bool ZERO = true>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+    // lanes outside ROWS, or whose source lies outside the row, read 0
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xF, ZERO);
+}
+template <int CTRL, int ROWS = 0xF, bool ZERO = true>
+__device__ __forceinline__ unsigned long long dpp_u64(unsigned long long v) {
+    const uint32_t lo = dpp_u32<CTRL, ROWS, ZERO>((uint32_t)v);
+    const uint32_t hi = dpp_u32<CTRL, ROWS, ZERO>((uint32_t)(v >> 32));
+    return ((unsigned long long)hi << 32) | lo;
+}
+template <int CTRL, int ROWS = 0xF, bool ZERO = true>
+__device__ __forceinline__ float dpp_move(float v) {
+    return __uint_as_float(dpp_u32<CTRL, ROWS, ZERO>(__float_as_uint(v)));
+}
+template <int CTRL, int ROWS = 0xF, bool ZERO = true>
+__device__ __forceinline__ int dpp_move(int v) {
+    return (int)dpp_u32<CTRL, ROWS, ZERO>((uint32_t)v);
+}
+template <int CTRL, int ROWS = 0xF, bool ZERO = true>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t v) {
+    return dpp_u32<CTRL, ROWS, ZERO>(v);
+}
+template <int CTRL, int ROWS = 0xF, bool ZERO = true>
+__device__ __forceinline__ unsigned long long dpp_move(unsigned long long v) {
+    return dpp_u64<CTRL, ROWS, ZERO>(v);
+}
+template <int CTRL, int ROWS = 0xF, bool ZERO = true>
+__device__ __forceinline__ double dpp_move(double v) {
+    return __longlong_as_double((long long)dpp_u64<CTRL, ROWS, ZERO>((unsigned long long)__double_as_longlong(v)));
+}
+
+// The value of `lane` (a wave-uniform lane number) in every lane.
+__device__ __forceinline__ uint32_t lane_read(uint32_t v, int lane) {
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, lane);
+}
+__device__ __forceinline__ int lane_read(int v, int lane) { return __builtin_amdgcn_readlane(v, lane); }
+__device__ __forceinline__ float lane_read(float v, int lane) {
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), lane));
+}
+__device__ __forceinline__ unsigned long long lane_read(unsigned long long v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((unsigned long long)hi << 32) | lo;
+}
+__device__ __forceinline__ double lane_read(double v, int lane) {
+    return __longlong_as_double((long long)lane_read((unsigned long long)__double_as_longlong(v), lane));
+}
+
+// op over the wave, the same value in every lane: butterflies inside each
+// row of 16 (commutative steps, so every lane of a row ends equal), then the
+// four row values combined in a fixed order.
+template <class T, class Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+    v = op(v, dpp_move<kDppQuadXor1>(v));
+    v = op(v, dpp_move<kDppQuadXor2>(v));
+    v = op(v, dpp_move<kDppRowHalfMirror>(v));
+    v = op(v, dpp_move<kDppRowMirror>(v));
+    return op(op(lane_read(v, 0), lane_read(v, 16)), op(lane_read(v, 32), lane_read(v, 48)));
+}
+
+// Inclusive prefix sum in lane order (within rows by doubling, then across
+// rows by broadcasts); a fixed order of additions.
+template <class T>
+__device__ __forceinline__ T wave_incl_scan(T x) {
+    x = x + dpp_move<kDppRowShr1>(x);
+    x = x + dpp_move<kDppRowShr2>(x);
+    x = x + dpp_move<kDppRowShr4>(x);
+    x = x + dpp_move<kDppRowShr8>(x);
+    x = x + dpp_move<kDppRowBcast15, 0xA>(x);
+    x = x + dpp_move<kDppRowBcast31, 0xC>(x);
+    return x;
+}
+// The previous lane's value (0 in lane 0).
+template <class T>
+__device__ __forceinline__ T wave_shift_up1(T x) {
+    return dpp_move<kDppWaveShr1>(x);
+}
+
 // ---- wave64 reductions (fixed combination order, hence deterministic) ----
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+    return wave_allreduce(v, [](float a, float b) { return fmaxf(a, b); });
 }
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    return wave_allreduce(v, [](double a, double b) { return a + b; });
 }
 __device__ __forceinline__ unsigned long long wave_max_u64(unsigned long long v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const unsigned long long o = __shfl_xor(v, off, 64);
-        v = o > v ? o : v;
-    }
-    return v;
+    return wave_allreduce(v, [](unsigned long long a, unsigned long long b) { return a > b ? a : b; });
 }
 
 // Block-wide max / sum over kBlock threads through LDS (fixed order).

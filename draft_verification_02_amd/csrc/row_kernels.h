@@ -106,9 +106,7 @@ __device__ __forceinline__ double rb_sum(double v, double* s) {
     return r;
 }
 __device__ __forceinline__ u64 wave_sum_u64(u64 v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    return wave_allreduce(v, [](u64 a, u64 b) { return a + b; });
 }
 __device__ __forceinline__ u64 rb_sum_u64(u64 v, u64* s) {
     v = wave_sum_u64(v);
@@ -140,17 +138,12 @@ __device__ __forceinline__ void wave_find_from_top(const u64* hist, u64 target, 
 #pragma unroll
     for (int i = 0; i < 4; ++i) c[i] = hist[255 - 4 * lane - i];
     const u64 ls = c[0] + c[1] + c[2] + c[3];
-    u64 incl = ls;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const u64 t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-    }
+    const u64 incl = wave_incl_scan(ls);
     const u64 excl = incl - ls;
     const u64 m = __ballot(incl >= target);
     if (m == 0) {
         bin = -1;
-        above = __shfl(incl, 63, 64);
+        above = lane_read(incl, 63);
         return;
     }
     const int L = __ffsll((long long)m) - 1;
@@ -166,8 +159,8 @@ __device__ __forceinline__ void wave_find_from_top(const u64* hist, u64 target, 
             run += c[i];
         }
     }
-    bin = __shfl(d, L, 64);
-    above = __shfl(run, L, 64);
+    bin = lane_read(d, L);
+    above = lane_read(run, L);
 }
 
 // Result of a block-wide selection from the top.
@@ -201,7 +194,7 @@ struct RowStream {
     int gfull;     // groups that can be read with one 16-byte load
     int nt;        // tiles
     int nfull;     // leading tiles whose every group is a full 16-byte load
-    __amdgpu_buffer_rsrc_t rsrc;  // the row as a raw buffer (full tiles load through it)
+    __amdgpu_buffer_rsrc_t rsrc;  // the row as a raw buffer
 
     __device__ RowStream(const char* p, int v) : rowp(p), V(v) {
         const bool aligned = (((uintptr_t)p) & 15) == 0;
@@ -359,6 +352,7 @@ struct RowShared {
     u64 red_u[kRW];
     int red_i[kRW];
     uint32_t red_k[kRW];
+    float red_kf[kRW];
     int nbin;
     int nlist;
     int ibin;
@@ -371,12 +365,7 @@ __device__ __forceinline__ float rb_min(float v, float* s) { return -rb_max(-v, 
 // Exclusive prefix of one int per thread in thread order; also the total.
 __device__ __forceinline__ int rb_excl_scan(int v, int* s, int& total) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const int t = __shfl_up(incl, off, 64);
-        if (lane >= off) incl += t;
-    }
+    const int incl = wave_incl_scan(v);
     __syncthreads();
     if (lane == 63) s[wave] = incl;
     __syncthreads();
@@ -393,12 +382,9 @@ __device__ __forceinline__ int rb_excl_scan(int v, int* s, int& total) {
 // Block-wide (sum, sum, min) of a count, a mass and a key, in one exchange.
 __device__ __forceinline__ void rb_count_mass_min(uint32_t& c, u64& m, uint32_t& k, RowShared& S) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        c += __shfl_xor(c, off, 64);
-        m += __shfl_xor(m, off, 64);
-        k = min(k, (uint32_t)__shfl_xor(k, off, 64));
-    }
+    c = wave_allreduce(c, [](uint32_t a, uint32_t b) { return a + b; });
+    m = wave_allreduce(m, [](u64 a, u64 b) { return a + b; });
+    k = wave_allreduce(k, [](uint32_t a, uint32_t b) { return a < b ? a : b; });
     __syncthreads();
     if (lane == 0) {
         S.red_i[wave] = (int)c;
@@ -435,21 +421,12 @@ __device__ __forceinline__ void wave_first_reach(FA&& va, FB&& vb, u64 target, i
         la += c[i];
         lb += d[i];
     }
-    u64 ia = la, ib = lb;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const u64 ta = __shfl_up(ia, off, 64);
-        const u64 tb = __shfl_up(ib, off, 64);
-        if (lane >= off) {
-            ia += ta;
-            ib += tb;
-        }
-    }
+    const u64 ia = wave_incl_scan(la), ib = wave_incl_scan(lb);
     const u64 m = __ballot(ia >= target);
     if (m == 0) {
         bin = -1;
-        before_a = __shfl(ia, 63, 64);
-        before_b = __shfl(ib, 63, 64);
+        before_a = lane_read(ia, 63);
+        before_b = lane_read(ib, 63);
         return;
     }
     const int L = __ffsll((long long)m) - 1;
@@ -466,9 +443,9 @@ __device__ __forceinline__ void wave_first_reach(FA&& va, FB&& vb, u64 target, i
             rb += d[i];
         }
     }
-    bin = __shfl(dbin, L, 64);
-    before_a = __shfl(ra, L, 64);
-    before_b = __shfl(rb, L, 64);
+    bin = lane_read(dbin, L);
+    before_a = lane_read(ra, L);
+    before_b = lane_read(rb, L);
 }
 
 // Capture for one tile.  Every wave owns a segment of kSegU slots and a
@@ -478,8 +455,8 @@ __device__ __forceinline__ void wave_first_reach(FA&& va, FB&& vb, u64 target, i
 // otherwise the segment stops growing and ovf is raised.  No atomics, no
 // branches and no exec-mask changes.
 template <int NL>
-__device__ __forceinline__ void capture_units(RowShared& S, int t, const u32x4 (&unit)[NL],
-                                              const float (&gm)[NL], float tau, int& fill, int& ovf) {
+__device__ __forceinline__ void capture_units(RowShared& S, const u32x4 (&unit)[NL], const float (&gm)[NL],
+                                              int gbase, int gstride, float tau, int& fill, int& ovf) {
     const int seg0 = (threadIdx.x >> 6) * kSegU;
     u64 m[NL];
     int c[NL];
@@ -503,7 +480,7 @@ __device__ __forceinline__ void capture_units(RowShared& S, int t, const u32x4 (
         const int mine = (ok && gm[j] >= tau) ? 1 : 0;
         const int pos = kUnits + lane + mine * (seg0 + f + r - kUnits - lane);
         S.u.st.raw[pos] = unit[j];
-        S.u.st.grp[pos] = (uint32_t)(t * (kRB * NL) + j * kRB) + threadIdx.x;
+        S.u.st.grp[pos] = (uint32_t)(gbase + j * gstride);
         f += c[j];
     }
     fill = __builtin_amdgcn_readfirstlane(ok ? f : fill);
@@ -514,10 +491,10 @@ __device__ __forceinline__ void capture_units(RowShared& S, int t, const u32x4 (
 // captured group, as (logit bits << 32) | index.  Each thread keeps its
 // candidates in its own column of S.u.fz.buf (slots tid + i * kRB, i < n_own);
 // row kOwn of the buffer takes the writes of non-candidates and overflow, so
-// the loop has no branches.  Returns the block's candidate count, or kCap + 1
-// when a segment or a column overflowed.
+// the loop has no branches.  Returns this thread's candidate count, with
+// bit 32 set when its segment or its column overflowed.
 template <int DT>
-__device__ __forceinline__ int expand_units(RowShared& S, int V, float tau, int fill, int ovf, int& n_own) {
+__device__ __forceinline__ u64 expand_units(RowShared& S, int V, float tau, int fill, int ovf, int& n_own) {
     constexpr int per = RowStream<DT>::per;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     u32x4 ur[kUPL];
@@ -550,9 +527,54 @@ __device__ __forceinline__ int expand_units(RowShared& S, int V, float tau, int 
         }
     }
     n_own = min(n, kOwn);
-    const u64 flags = (u64)n | ((u64)((n > kOwn ? 1 : 0) | ovf) << 32);
-    const u64 tot = rb_sum_u64(flags, S.red_u);  // its barriers also publish the candidates
-    return (tot >> 32) ? kCap + 1 : (int)(uint32_t)tot;
+    return (u64)n | ((u64)((n > kOwn ? 1 : 0) | ovf) << 32);
+}
+
+// A row's totals, combined over the block in one exchange: the largest
+// logit, the per-thread sums taken to the largest grid reference k (exact
+// power-of-two rescales) and added, and a 64-bit count.  Every combine step
+// is commutative, so the butterfly leaves the same value in every lane and
+// the result does not depend on timing.
+struct RowTot {
+    float m, k;
+    double z;
+    u64 c;
+};
+__device__ __forceinline__ RowTot row_tot_combine(const RowTot& a, const RowTot& b) {
+    RowTot r;
+    r.m = fmaxf(a.m, b.m);
+    r.k = fmaxf(a.k, b.k);
+    const double za = a.k == -INFINITY ? 0.0 : ldexp(a.z, (int)fmaxf(8.f * (a.k - r.k), -4096.f));
+    const double zb = b.k == -INFINITY ? 0.0 : ldexp(b.z, (int)fmaxf(8.f * (b.k - r.k), -4096.f));
+    r.z = za + zb;
+    r.c = a.c + b.c;
+    return r;
+}
+__device__ __forceinline__ RowTot rb_row_totals(RowTot t, RowShared& S) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    auto step = [&](RowTot o) { t = row_tot_combine(t, o); };
+    step(RowTot{dpp_move<kDppQuadXor1>(t.m), dpp_move<kDppQuadXor1>(t.k), dpp_move<kDppQuadXor1>(t.z),
+                dpp_move<kDppQuadXor1>(t.c)});
+    step(RowTot{dpp_move<kDppQuadXor2>(t.m), dpp_move<kDppQuadXor2>(t.k), dpp_move<kDppQuadXor2>(t.z),
+                dpp_move<kDppQuadXor2>(t.c)});
+    step(RowTot{dpp_move<kDppRowHalfMirror>(t.m), dpp_move<kDppRowHalfMirror>(t.k),
+                dpp_move<kDppRowHalfMirror>(t.z), dpp_move<kDppRowHalfMirror>(t.c)});
+    step(RowTot{dpp_move<kDppRowMirror>(t.m), dpp_move<kDppRowMirror>(t.k), dpp_move<kDppRowMirror>(t.z),
+                dpp_move<kDppRowMirror>(t.c)});
+    auto row = [&](int l) { return RowTot{lane_read(t.m, l), lane_read(t.k, l), lane_read(t.z, l), lane_read(t.c, l)}; };
+    t = row_tot_combine(row_tot_combine(row(0), row(16)), row_tot_combine(row(32), row(48)));
+    __syncthreads();
+    if (lane == 0) {
+        S.red_f[wave] = t.m;
+        S.red_kf[wave] = t.k;
+        S.red_d[wave] = t.z;
+        S.red_u[wave] = t.c;
+    }
+    __syncthreads();
+    RowTot r{S.red_f[0], S.red_kf[0], S.red_d[0], S.red_u[0]};
+#pragma unroll
+    for (int w = 1; w < kRW; ++w) r = row_tot_combine(r, RowTot{S.red_f[w], S.red_kf[w], S.red_d[w], S.red_u[w]});
+    return r;
 }
 
 // First capture threshold, from tile 0: about the rank-th largest thread
@@ -852,19 +874,17 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     float m_th = -INFINITY;  // running maximum of this thread's logits
     float k_th = -INFINITY;  // reference index k (a whole number, as a float)
     double z_th = 0.0;       // sum of 2^(x * log2(e) / T - 8 k_th) over this thread's logits
-    float tau = INFINITY;    // capture threshold
+    float tau = INFINITY;    // capture threshold of this wave
+    float tau0 = INFINITY;   // the first (block-wide) threshold: at or below every wave's
     float m_run = -INFINITY; // running maximum for threshold refreshes (top-k rows)
     int fill = 0, ovf = 0;   // this wave's segment (uniform per wave)
 
-    // One tile: group maxima, running max / sum, capture.  FULL tiles take
-    // the unchecked unpack; tile 0 also sets the capture threshold.
-    auto process = [&](int t, const u32x4 (&raw)[NL], auto full_tag, bool first) {
-        constexpr bool FULL = decltype(full_tag)::value;
-        float v[kREPT];
-        if (FULL)
-            RowStream<DT>::unpack_full(raw, v);
-        else
-            st.unpack(t, raw, v);
+    // One tile of kREPT logits per thread (NL groups of `per`; group j of this
+    // thread is gbase + j * gstride): group maxima, running max and sum,
+    // capture.  The first tile also sets the capture threshold: the kR0-th
+    // (nucleus) or top_k-th (top-k) largest thread maximum of the block, so
+    // at least that many logits are captured.
+    auto core = [&](const float (&v)[kREPT], const u32x4 (&unit)[NL], int gbase, int gstride, bool first) {
         float gm[NL];
 #pragma unroll
         for (int j = 0; j < NL; ++j) {
@@ -899,28 +919,40 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             }
         }
         if (kFilt) {
-            // Threshold from the first tile: the kR0-th (nucleus) or top_k-th
-            // (top-k) largest thread maximum, so that at least that many logits
-            // are captured.  Top-k rows raise it after tiles 3 and 15 from the
-            // running thread maxima: any value with top_k logits at or above
-            // it is a lower bound of the row's top_k-th largest.  It only
-            // rises, so every logit at or above the final threshold is held.
             if (MODE == MODE_TOPK) m_run = fmaxf(m_run, tm);
             if (first) {
                 tau = V <= kCap ? -INFINITY
                                 : first_threshold(S, tm, MODE == MODE_TOPK ? max(1, min(a.top_k, kRB)) : kR0);
-            } else if (MODE == MODE_TOPK && (t == 3 || t == 15)) {
-                tau = fmaxf(tau, first_threshold(S, m_run, max(1, min(a.top_k, kRB))));
+                tau0 = tau;
             }
-            u32x4 unit[NL];
-#pragma unroll
-            for (int j = 0; j < NL; ++j) unit[j] = FULL ? raw[j] : RowStream<DT>::repack(v, j);
-            capture_units<NL>(S, t, unit, gm, tau, fill, ovf);
+            capture_units<NL>(S, unit, gm, gbase, gstride, tau, fill, ovf);
         }
     };
-    using FullT = std::integral_constant<bool, true>;
-    using AnyT = std::integral_constant<bool, false>;
 
+    // Top-k rows raise the threshold after tiles 3 and 15 from the running
+    // thread maxima: any value with top_k logits at or above it bounds the
+    // row's top_k-th largest from below; it only rises, so every logit at or
+    // above the final threshold is held.
+    auto refresh = [&](int t) {
+        if (MODE == MODE_TOPK && (t == 3 || t == 15)) {
+            tau = fmaxf(tau, first_threshold(S, m_run, max(1, min(a.top_k, kRB))));
+        }
+    };
+    auto full_tile = [&](int t, const u32x4 (&raw)[NL]) {
+        float v[kREPT];
+        RowStream<DT>::unpack_full(raw, v);
+        core(v, raw, t * (kRB * NL) + (int)threadIdx.x, kRB, t == 0);
+        refresh(t);
+    };
+    auto any_tile = [&](int t, const u32x4 (&raw)[NL]) {
+        float v[kREPT];
+        st.unpack(t, raw, v);
+        u32x4 unit[NL];
+#pragma unroll
+        for (int j = 0; j < NL; ++j) unit[j] = RowStream<DT>::repack(v, j);
+        core(v, unit, t * (kRB * NL) + (int)threadIdx.x, kRB, t == 0);
+        refresh(t);
+    };
     {
         // Steady state: three full tiles of loads in flight in rotating
         // registers, straight-line code so that each tile waits only for its
@@ -932,7 +964,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             st.issue_full(0, rA);
             st.issue_full(1, rB);
             st.issue_full(2, rC);
-            process(0, rA, FullT{}, true);
+            full_tile(0, rA);
             st.issue_full(3, rA);
             t = 1;
             // Every scalar load is complete here (lgkmcnt(0), other counters
@@ -940,45 +972,43 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             // loop, and with capture stores in flight that wait is for the LDS.
             __builtin_amdgcn_s_waitcnt(0xC07F);
             for (; t + 5 < nf; t += 3) {
-                process(t, rB, FullT{}, false);
+                full_tile(t, rB);
                 st.issue_full(t + 3, rB);
-                process(t + 1, rC, FullT{}, false);
+                full_tile(t + 1, rC);
                 st.issue_full(t + 4, rC);
-                process(t + 2, rA, FullT{}, false);
+                full_tile(t + 2, rA);
                 st.issue_full(t + 5, rA);
             }
             // drain: the rest of the row (at most three more tiles, the last
             // possibly partial) rides the same rotation with clamped loads
-            process(t, rB, FullT{}, false);
+            full_tile(t, rB);
             st.issue_clamped(t + 3, rB);
-            process(t + 1, rC, FullT{}, false);
+            full_tile(t + 1, rC);
             st.issue_clamped(t + 4, rC);
-            process(t + 2, rA, FullT{}, false);
+            full_tile(t + 2, rA);
             st.issue_clamped(t + 5, rA);
             t += 3;
-            if (t < st.nt) process(t, rB, AnyT{}, false);
-            if (t + 1 < st.nt) process(t + 1, rC, AnyT{}, false);
-            if (t + 2 < st.nt) process(t + 2, rA, AnyT{}, false);
+            if (t < st.nt) any_tile(t, rB);
+            if (t + 1 < st.nt) any_tile(t + 1, rC);
+            if (t + 2 < st.nt) any_tile(t + 2, rA);
             t = st.nt;
         }
         for (; t < st.nt; ++t) {
             st.issue(t, rA);
-            process(t, rA, AnyT{}, t == 0);
+            any_tile(t, rA);
         }
     }
 
     // ---- merge the row (fixed-order reductions) ----
-    float M = -INFINITY;
-    double Z = 0.0;
-    int n_res = 0, n_own = 0;
-    if (kFilt) n_res = expand_units<DT>(S, V, tau, fill, ovf, n_own);
-    if (MODE == MODE_TOPK) M = rb_max(m_run, S.red_f);
-    if (kSum) {
-        M = rb_max(m_th, S.red_f);
-        // z_th * 2^(8 k_th - M log2(e) / T): the thread's sum relative to the row maximum
-        const double zc = (k_th == -INFINITY) ? 0.0 : z_th * exp2(8.0 * (double)k_th - (double)M * a.c64);
-        Z = rb_sum(zc, S.red_d);
-    }
+    int n_own = 0;
+    u64 cflags = 0ull;
+    if (kFilt) cflags = expand_units<DT>(S, V, tau, fill, ovf, n_own);
+    const RowTot tot =
+        rb_row_totals(RowTot{MODE == MODE_TOPK ? m_run : m_th, kSum ? k_th : -INFINITY, z_th, cflags}, S);
+    const float M = tot.m;
+    // the row sum relative to the row maximum: z * 2^(8 k - M log2(e) / T)
+    const double Z = (kSum && tot.k != -INFINITY) ? tot.z * exp2(8.0 * (double)tot.k - (double)M * a.c64) : 0.0;
+    const int n_res = (tot.c >> 32) ? kCap + 1 : (int)(uint32_t)tot.c;
 
     float thr = -INFINITY;
     double z_kept = Z;
@@ -990,7 +1020,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         const double scale = ldexp(1.0, a.fx_shift);
         uint32_t thr_key = 0u;
         bool fast = n_res <= kCap &&
-                    resolve_reservoir(a, S, M, Z, n_own, tau, scale, thr_key, z_kept, n_kept);
+                    resolve_reservoir(a, S, M, Z, n_own, tau0, scale, thr_key, z_kept, n_kept);
         if (fast) {
             thr = key_to_float(thr_key);
         } else {
@@ -1086,13 +1116,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                         c[q] = S.u.fz.hc[per * lane + q];
                         ls += c[q];
                     }
-                    u64 incl = ls;
-#pragma unroll
-                    for (int off = 1; off < 64; off <<= 1) {
-                        const u64 t = __shfl_up(incl, off, 64);
-                        if (lane >= off) incl += t;
-                    }
-                    u64 run = incl - ls;
+                    u64 run = wave_incl_scan(ls) - ls;
 #pragma unroll
                     for (int q = 0; q < per; ++q) {
                         S.u.fz.hm[per * lane + q] = run;

@@ -4,7 +4,8 @@
 //  k_seq_filtered : filtered rows (top-k / top-p).  p_j is nonzero only on the
 //                   stop target row's kept set, stored sorted by index by
 //                   k_row, so the residual max(0, p_j - q_j) is evaluated on
-//                   that list (draft logits gathered by index).
+//                   that list (draft logits gathered by index).  One
+//                   workgroup per (sequence, possible stop position).
 //  k_draw_sums / k_draw_pick : unfiltered rows.  The residual is spread over
 //                   the whole vocabulary: chunk sums over the stop row pair in
 //                   fp64, then one workgroup per sequence locates the draw.
@@ -120,14 +121,8 @@ __device__ __forceinline__ void seq_excl_scan(double v, double* s_val, double* s
         const double v0 = s_val[4 * tid], v1 = s_val[4 * tid + 1];
         const double v2 = s_val[4 * tid + 2], v3 = s_val[4 * tid + 3];
         const double ls = ((v0 + v1) + v2) + v3;
-        double incl = ls;
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-            const double t = __shfl_up(incl, off, 64);
-            if (tid >= off) incl += t;
-        }
-        double e = __shfl_up(incl, 1, 64);
-        if (tid == 0) e = 0.0;
+        const double incl = wave_incl_scan(ls);
+        double e = wave_shift_up1(incl);
         s_excl[4 * tid] = e;
         e += v0;
         s_excl[4 * tid + 1] = e;
@@ -217,31 +212,13 @@ __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, do
     }
 }
 
-// ---------------------------------------------------------------------------
-// Filtered: one workgroup per sequence.
-// ---------------------------------------------------------------------------
-constexpr int kListPT = kListMax / kSB;  // kept-list entries per thread (16)
+// Draw over a kept list longer than the speculative load: thread-contiguous
+// slices of up to kListMax / kSB entries, read and gathered now.
+constexpr int kListPT = kListMax / kSB;  // 16
 
-__global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
-    __shared__ double s_val[kSB], s_excl[kSB], s_total;
-    __shared__ int s_j, s_tau;
-    const int b = blockIdx.x;
-    const int K = a.sh.K;
-    if (threadIdx.x < 64) {
-        const int j = first_rejection(a, b);
-        if (threadIdx.x == 0) s_j = j;
-    }
-    __syncthreads();
-    const int j = s_j;
-    const int rt = b * (K + 1) + j;
-    const int n = a.kept_n[rt];
-    if (n < 0) {
-        draw_full_row(a, b, j, s_val, s_excl, &s_total, &s_tau);
-        return;
-    }
-    const StopRow s = stop_row(a, b, j);
-    const uint2* L = a.kept + (size_t)rt * kListMax;
-    // thread-contiguous slices of the index-sorted kept list
+__device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, int n, const uint2* L,
+                                               const StopRow& s, double* s_val, double* s_excl,
+                                               double* s_total, int* s_tau) {
     const int per = (n + kSB - 1) / kSB;
     const int lo = threadIdx.x * per, hi = min(lo + per, n);
     double pr[kListPT], rr[kListPT];
@@ -262,14 +239,14 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         }
     }
     double er, tr, ep, tp;
-    seq_excl_scan(sr, s_val, s_excl, &s_total, er, tr);
-    seq_excl_scan(sp, s_val, s_excl, &s_total, ep, tp);
-    const bool usep = (j == K) || !(tr > 0.0);
+    seq_excl_scan(sr, s_val, s_excl, s_total, er, tr);
+    seq_excl_scan(sp, s_val, s_excl, s_total, ep, tp);
+    const bool usep = (j == a.sh.K) || !(tr > 0.0);
     const double S = usep ? tp : tr;
     const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
     const double mine = usep ? sp : sr;
     const double ex = usep ? ep : er;
-    const int tau = pick_thread(mine, ex, t, &s_tau);
+    const int tau = pick_thread(mine, ex, t, s_tau);
     if ((int)threadIdx.x == tau) {
         double acc = ex;
         int y = -1, last = -1;
@@ -284,6 +261,151 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         }
         write_outputs(a, b, j, y >= 0 ? y : last);
     }
+}
+
+// ---------------------------------------------------------------------------
+// Filtered: one workgroup per (sequence, candidate stop position j).  Every
+// workgroup loads, in one round, the accept-test inputs of its sequence, the
+// records of row pair j and the first kSpec entries of target row j's kept
+// list; the workgroup whose j is the stop position then gathers the draft
+// logits of the listed tokens and draws, the others exit.  This puts two
+// dependent memory rounds, not four, between the row kernel and the output.
+// ---------------------------------------------------------------------------
+constexpr int kLPT = 4;                  // kept-list entries per thread
+constexpr int kSpec = kLPT * kSB;        // entries loaded before the stop is known (1024)
+
+// Exclusive prefix sums of two doubles over the kSB threads in thread order
+// (wave scans, then the wave totals), and their totals.
+__device__ __forceinline__ void seq_excl_scan2(double a, double b, double* s_wa, double* s_wb, double& ea,
+                                               double& eb, double& ta, double& tb) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const double ia = wave_incl_scan(a), ib = wave_incl_scan(b);
+    const double xa = wave_shift_up1(ia), xb = wave_shift_up1(ib);
+    if (lane == 63) {
+        s_wa[wave] = ia;
+        s_wb[wave] = ib;
+    }
+    __syncthreads();
+    double pa = 0.0, pb = 0.0;
+    ta = 0.0;
+    tb = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSB / 64; ++w) {
+        if (w < wave) {
+            pa += s_wa[w];
+            pb += s_wb[w];
+        }
+        ta += s_wa[w];
+        tb += s_wb[w];
+    }
+    ea = pa + xa;
+    eb = pb + xb;
+}
+
+__global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
+    __shared__ double s_val[kSB], s_excl[kSB], s_total;
+    __shared__ double s_wa[kSB / 64], s_wb[kSB / 64];
+    __shared__ int s_j, s_tau, s_y;
+    __shared__ int s_last[kSB / 64], s_first[kSB / 64];
+    const int K = a.sh.K;
+    const int b = blockIdx.x / (K + 1), jc = blockIdx.x % (K + 1);
+    const int rt = b * (K + 1) + jc;
+    const int n = a.kept_n[rt];
+    const uint2* L = a.kept + (size_t)rt * kListMax;
+    // thread-contiguous slices, so thread order is token order
+    uint2 ent[kLPT];
+#pragma unroll
+    for (int e = 0; e < kLPT; ++e) ent[e] = L[threadIdx.x * kLPT + e];
+    const StopRow s = stop_row(a, b, jc);
+    // the accepted drafted tokens, one per thread, for the output row
+    const int tok = (int)threadIdx.x < jc ? a.sh.tokens[(size_t)b * K + threadIdx.x] : -1;
+    if (threadIdx.x < 64) {
+        const int j = first_rejection(a, b);
+        if (threadIdx.x == 0) s_j = j;
+    }
+    __syncthreads();
+    if (s_j != jc) return;
+    if (n < 0) {
+        draw_full_row(a, b, jc, s_val, s_excl, &s_total, &s_tau);
+        return;
+    }
+    if (n > kSpec) {
+        draw_long_list(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
+        return;
+    }
+    float xd[kLPT];
+#pragma unroll
+    for (int e = 0; e < kLPT; ++e) {
+        const int i = threadIdx.x * kLPT + e;
+        xd[e] = -INFINITY;
+        if (s.has_draft && i < n) xd[e] = load_logit(s.dp, s.ddt, (int)ent[e].x);
+    }
+    double pr[kLPT], rr[kLPT];
+    double sr = 0.0, sp = 0.0;
+#pragma unroll
+    for (int e = 0; e < kLPT; ++e) {
+        const int i = threadIdx.x * kLPT + e;
+        pr[e] = 0.0;
+        rr[e] = 0.0;
+        if (i < n) {
+            const float xt = __uint_as_float(ent[e].y);
+            const double p = xt >= s.thr_t ? exp(((double)xt - (double)s.Mt) * a.inv_T) / s.zt : 0.0;
+            const double q = (s.has_draft && xd[e] >= s.thr_d)
+                                 ? exp(((double)xd[e] - (double)s.Md) * a.inv_T) / s.zd
+                                 : 0.0;
+            const double d = p - q;
+            pr[e] = p;
+            rr[e] = d > 0.0 ? d : 0.0;
+            sr += rr[e];
+            sp += pr[e];
+        }
+    }
+    double er, ep, tr, tp;
+    seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
+    const bool usep = (jc == K) || !(tr > 0.0);
+    const double S = usep ? tp : tr;
+    const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)jc, PURPOSE_SAMPLE)) * S;
+    const double mine = usep ? sp : sr;
+    const double ex = usep ? ep : er;
+    // the thread whose range holds t: the last one with mass whose range
+    // starts at or before t (prefixes are non-decreasing in thread order);
+    // if rounding put t before all of them, the first one with mass
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
+    const unsigned long long mf = __ballot(mine > 0.0);
+    if (lane == 0) {
+        s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
+        s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
+    }
+    __syncthreads();
+    int tau = -1, first = kSB;
+#pragma unroll
+    for (int w = 0; w < kSB / 64; ++w) {
+        tau = max(tau, s_last[w]);
+        first = min(first, s_first[w]);
+    }
+    if (tau < 0) tau = first;
+    if ((int)threadIdx.x == tau) {
+        double acc = ex;
+        int y = -1, last = -1;
+#pragma unroll
+        for (int e = 0; e < kLPT; ++e) {
+            const int i = threadIdx.x * kLPT + e;
+            const double w = usep ? pr[e] : rr[e];
+            if (y < 0 && i < n && w > 0.0) {
+                last = (int)ent[e].x;
+                acc += w;
+                if (acc > t) y = (int)ent[e].x;
+            }
+        }
+        s_y = y >= 0 ? y : last;
+    }
+    __syncthreads();
+    // output row: accepted drafts, the drawn token, then -1
+    int32_t* out = a.out_tokens + (size_t)b * (K + 1);
+    for (int k = threadIdx.x; k <= K; k += kSB)
+        out[k] = k < jc ? (k < kSB ? tok : a.sh.tokens[(size_t)b * K + k]) : (k == jc ? s_y : -1);
+    if (threadIdx.x == 0) a.out_num[b] = jc;
 }
 
 // ---------------------------------------------------------------------------

@@ -196,7 +196,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     sa.out_tokens = out_tokens;
     sa.out_num = out_num;
     if (filtered) {
-        hipLaunchKernelGGL(k_seq_filtered, dim3(B), dim3(kSB), 0, stream, sa);
+        hipLaunchKernelGGL(k_seq_filtered, dim3((unsigned)((long long)B * (K + 1))), dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
     } else {
         hipLaunchKernelGGL(k_draw_sums, dim3((unsigned)((long long)B * n_chunks)), dim3(kSB), 0, stream, sa);

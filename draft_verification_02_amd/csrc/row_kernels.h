@@ -354,6 +354,7 @@ struct RowShared {
     uint32_t red_k[kRW];
     float red_kf[kRW];
     int nbin;
+    int nbin2[2];             // gather counters of the two bin resolutions
     int nlist;
     int ibin;
     u64 ubefore;
@@ -403,7 +404,7 @@ __device__ __forceinline__ void rb_count_mass_min(uint32_t& c, u64& m, uint32_t&
     }
 }
 
-// One wave (wave 0) scans bins 0..kNB-1 in order and finds the first bin at
+// A wave scans bins 0..kNB-1 in order and finds the first bin at
 // which the running sum of va(b) reaches target; returns it with the sums of
 // va and vb over the bins before it (bin = -1 and the totals when target is
 // never reached).
@@ -510,6 +511,12 @@ __device__ __forceinline__ u64 expand_units(RowShared& S, int V, float tau, int 
         }
     }
     __syncthreads();  // segments read: the union now belongs to the candidates
+    // bins of the resolution, cleared now; the next barriers publish it
+    for (int i = threadIdx.x; i < kNB; i += kRB) {
+        S.u.fz.hc[i] = 0u;
+        S.u.fz.hm[i] = 0ull;
+    }
+    if (threadIdx.x < 2) S.nbin2[threadIdx.x] = 0;
     int n = 0;
 #pragma unroll
     for (int i = 0; i < kUPL; ++i) {
@@ -606,12 +613,20 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
 }
 
 // Resolve top-k / top-p from the candidates.  Entries (kOwn per thread) hold
-// every logit >= the capture threshold.  Returns false when the reservoir
+// every logit >= the capture threshold.  Returns false when the candidates
 // cannot decide (the caller then re-reads the row).
+//
+// The candidates are binned by value (kNB bins over [lo, M]) with their
+// count and fixed-point mass.  Every wave scans the bins itself, so the
+// crossing bin needs no broadcast; inside that bin the entries are gathered
+// and every entry learns the count and mass of the bin's entries with a
+// strictly larger key (within one wave when the bin holds at most 64).
+// The bins and the gather counters were cleared before the candidates were
+// published (expand_units).
 __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S, float M, double Z,
                                                   int n_own, float tau, double scale, uint32_t& thr_key,
                                                   double& z_kept, int& n_kept) {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     uint32_t key[kOwn];
     u64 wt[kOwn];
     int bin[kOwn];
@@ -631,11 +646,6 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     const float lo = tau != -INFINITY ? tau : rb_min(xmin, S.red_f);
     const float span = M - lo;
     const float bscale = span > 0.f ? (float)(kNB - 1) / span : 0.f;
-    for (int i = tid; i < kNB; i += kRB) {
-        S.u.fz.hc[i] = 0u;
-        S.u.fz.hm[i] = 0ull;
-    }
-    __syncthreads();
 #pragma unroll
     for (int i = 0; i < kOwn; ++i) {
         bin[i] = kNB;
@@ -647,45 +657,64 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     }
     __syncthreads();
 
-    // Exact decision inside one bin: every entry of the bin (with key >=
-    // floor) learns how many entries and how much mass of the bin lie
-    // strictly above it; `keep(rank_or_excl)` decides, and the block gets the
-    // smallest kept key, the kept count and the kept mass of the bin.
-    auto resolve_bin = [&](int b, uint32_t floor_key, u64 base, bool by_count, u64 limit,
+    // Exact decision inside bin b (entries with key >= floor_key): kept
+    // <=> base + (count or mass of the bin's entries with a larger key) <
+    // limit.  Returns the smallest kept key, the kept count and mass.
+    auto resolve_bin = [&](int b, int call, uint32_t floor_key, u64 base, bool by_count, u64 limit,
                            uint32_t& kmin, uint32_t& kcnt, u64& kmass) -> bool {
-        int mine = 0;
-#pragma unroll
-        for (int i = 0; i < kOwn; ++i) mine += (bin[i] == b && key[i] >= floor_key) ? 1 : 0;
-        int nb;
-        int p = rb_excl_scan(mine, S.red_i, nb);
-        if (nb > kBinMax) return false;
+        // gather (contention only among the bin's own entries)
+        u64* bw = call == 0 ? S.u.fz.bw : S.u.fz.bw + kBinMax / 2;
+        uint32_t* bk = call == 0 ? S.u.fz.bkey : S.u.fz.bkey + kBinMax / 2;
+        constexpr int cap = kBinMax / 2;
 #pragma unroll
         for (int i = 0; i < kOwn; ++i) {
             if (bin[i] == b && key[i] >= floor_key) {
-                S.u.fz.bkey[p] = key[i];
-                S.u.fz.bw[p] = wt[i];
-                ++p;
+                const int slot = atomicAdd(&S.nbin2[call], 1);
+                if (slot < cap) {
+                    bk[slot] = key[i];
+                    bw[slot] = wt[i];
+                }
             }
         }
         __syncthreads();
+        const int nb = S.nbin2[call];
+        if (nb > cap) return false;
+        if (nb <= 64) {
+            // one entry per lane; every wave computes the same result
+            const uint32_t k = lane < nb ? bk[lane] : 0u;
+            const u64 w = lane < nb ? bw[lane] : 0ull;
+            uint32_t cgt = 0u;
+            u64 mgt = 0ull;
+            for (int jj = 0; jj < nb; ++jj) {
+                const uint32_t kj = lane_read(k, jj);
+                const u64 wj = lane_read(w, jj);
+                cgt += kj > k ? 1u : 0u;
+                mgt += kj > k ? wj : 0ull;
+            }
+            const bool kept = lane < nb && (by_count ? base + cgt < limit : base + mgt < limit);
+            kcnt = (uint32_t)__popcll(__ballot(kept));
+            kmass = wave_allreduce(kept ? w : 0ull, [](u64 x, u64 y) { return x + y; });
+            kmin = wave_allreduce(kept ? k : 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+            return true;
+        }
         uint32_t my_c = 0u;
         u64 my_m = 0ull;
         uint32_t my_min = 0xFFFFFFFFu;
         for (int i = tid; i < nb; i += kRB) {
-            const uint32_t ki = S.u.fz.bkey[i];
+            const uint32_t ki = bk[i];
             uint32_t cgt = 0u;
             u64 mgt = 0ull;
             for (int jj = 0; jj < nb; ++jj) {
-                const uint32_t kj = S.u.fz.bkey[jj];
+                const uint32_t kj = bk[jj];
                 if (kj > ki) {
                     ++cgt;
-                    mgt += S.u.fz.bw[jj];
+                    mgt += bw[jj];
                 }
             }
             const bool kept = by_count ? (base + cgt < limit) : (base + mgt < limit);
             if (kept) {
                 ++my_c;
-                my_m += S.u.fz.bw[i];
+                my_m += bw[i];
                 my_min = min(my_min, ki);
             }
         }
@@ -702,24 +731,10 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     u64 in_k_mass = 0ull;
     u64 cb_k = 0ull, mb_k = 0ull;
     if (a.use_k) {
-        if (tid < 64) {
-            int b;
-            u64 before_c, before_m;
-            wave_first_reach([&](int i) { return (u64)S.u.fz.hc[i]; }, [&](int i) { return S.u.fz.hm[i]; },
-                             (u64)a.top_k, b, before_c, before_m);
-            if (tid == 0) {
-                S.ibin = b;
-                S.cbefore = (uint32_t)before_c;
-                S.ubefore = before_m;
-            }
-        }
-        __syncthreads();
-        bk = S.ibin;
-        cb_k = S.cbefore;
-        mb_k = S.ubefore;
-        __syncthreads();
+        wave_first_reach([&](int i) { return (u64)S.u.fz.hc[i]; }, [&](int i) { return S.u.fz.hm[i]; },
+                         (u64)a.top_k, bk, cb_k, mb_k);
         if (bk < 0) return false;  // fewer than top_k entries captured
-        if (!resolve_bin(bk, 0u, cb_k, true, (u64)a.top_k, tau_k, in_k_cnt, in_k_mass)) return false;
+        if (!resolve_bin(bk, 0, 0u, cb_k, true, (u64)a.top_k, tau_k, in_k_cnt, in_k_mass)) return false;
     }
     const u64 zk = a.use_k ? mb_k + in_k_mass : 0ull;
     if (!a.use_p) {
@@ -733,27 +748,15 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     u64 target = (u64)ceil((double)a.top_p * zbase * scale);
     if (target == 0ull) target = 1ull;
     if (a.use_k && target > zk) target = zk;  // rounding: keep the whole top-k set
-    if (tid < 64) {
-        int b;
-        u64 before_m, before_c;
-        wave_first_reach([&](int i) -> u64 { return i < bk ? S.u.fz.hm[i] : (i == bk ? in_k_mass : 0ull); },
-                         [&](int i) -> u64 { return i < bk ? S.u.fz.hc[i] : (i == bk ? in_k_cnt : 0u); },
-                         target, b, before_m, before_c);
-        if (tid == 0) {
-            S.ibin = b;
-            S.ubefore = before_m;
-            S.cbefore = (uint32_t)before_c;
-        }
-    }
-    __syncthreads();
-    const int bp = S.ibin;
-    const u64 mb_p = S.ubefore;
-    const uint32_t cb_p = S.cbefore;
-    __syncthreads();
-    if (bp < 0) return false;  // the crossing lies below the reservoir
+    int bp;
+    u64 mb_p, cb_p;
+    wave_first_reach([&](int i) -> u64 { return i < bk ? S.u.fz.hm[i] : (i == bk ? in_k_mass : 0ull); },
+                     [&](int i) -> u64 { return i < bk ? S.u.fz.hc[i] : (i == bk ? in_k_cnt : 0u); },
+                     target, bp, mb_p, cb_p);
+    if (bp < 0) return false;  // the crossing lies below the candidates
     uint32_t kmin, kcnt;
     u64 kmass;
-    if (!resolve_bin(bp, bp == bk ? tau_k : 0u, mb_p, false, target, kmin, kcnt, kmass)) return false;
+    if (!resolve_bin(bp, 1, bp == bk ? tau_k : 0u, mb_p, false, target, kmin, kcnt, kmass)) return false;
     thr_key = kmin;
     n_kept = (int)(cb_p + kcnt);
     z_kept = (double)(mb_p + kmass) / scale;
@@ -954,43 +957,49 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         refresh(t);
     };
     {
-        // Steady state: three full tiles of loads in flight in rotating
+        // Steady state: four full tiles of loads in flight in rotating
         // registers, straight-line code so that each tile waits only for its
-        // own loads.  Rows with fewer than four full tiles go tile by tile.
-        u32x4 rA[NL], rB[NL], rC[NL];
+        // own loads.  Rows with fewer than five full tiles go tile by tile.
+        u32x4 rA[NL], rB[NL], rC[NL], rD[NL];
         const int nf = st.nfull;
         int t = 0;
-        if (nf >= 4) {
+        if (nf >= 5) {
             st.issue_full(0, rA);
             st.issue_full(1, rB);
             st.issue_full(2, rC);
+            st.issue_full(3, rD);
             full_tile(0, rA);
-            st.issue_full(3, rA);
+            st.issue_full(4, rA);
             t = 1;
             // Every scalar load is complete here (lgkmcnt(0), other counters
             // left alone): without it the compiler waits on lgkmcnt inside the
             // loop, and with capture stores in flight that wait is for the LDS.
             __builtin_amdgcn_s_waitcnt(0xC07F);
-            for (; t + 5 < nf; t += 3) {
+            for (; t + 7 < nf; t += 4) {
                 full_tile(t, rB);
-                st.issue_full(t + 3, rB);
+                st.issue_full(t + 4, rB);
                 full_tile(t + 1, rC);
-                st.issue_full(t + 4, rC);
-                full_tile(t + 2, rA);
-                st.issue_full(t + 5, rA);
+                st.issue_full(t + 5, rC);
+                full_tile(t + 2, rD);
+                st.issue_full(t + 6, rD);
+                full_tile(t + 3, rA);
+                st.issue_full(t + 7, rA);
             }
-            // drain: the rest of the row (at most three more tiles, the last
+            // drain: the rest of the row (at most four more tiles, the last
             // possibly partial) rides the same rotation with clamped loads
             full_tile(t, rB);
-            st.issue_clamped(t + 3, rB);
+            st.issue_clamped(t + 4, rB);
             full_tile(t + 1, rC);
-            st.issue_clamped(t + 4, rC);
-            full_tile(t + 2, rA);
-            st.issue_clamped(t + 5, rA);
-            t += 3;
+            st.issue_clamped(t + 5, rC);
+            full_tile(t + 2, rD);
+            st.issue_clamped(t + 6, rD);
+            full_tile(t + 3, rA);
+            st.issue_clamped(t + 7, rA);
+            t += 4;
             if (t < st.nt) any_tile(t, rB);
             if (t + 1 < st.nt) any_tile(t + 1, rC);
-            if (t + 2 < st.nt) any_tile(t + 2, rA);
+            if (t + 2 < st.nt) any_tile(t + 2, rD);
+            if (t + 3 < st.nt) any_tile(t + 3, rA);
             t = st.nt;
         }
         for (; t < st.nt; ++t) {

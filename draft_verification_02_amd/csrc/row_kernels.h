@@ -37,8 +37,9 @@ constexpr int kRTile = kRB * kREPT;      // 8192 logits per tile
 constexpr int kSegU = 256;               // captured 16-byte units per wave segment
 constexpr int kUnits = kSegU * kRW;      // 2048 units per workgroup
 constexpr int kUPL = kSegU / 64;         // units per lane when a wave expands its segment
-constexpr int kCap = 4096;               // candidates (logit, index) after expansion
-constexpr int kOwn = kCap / kRB;         // candidates per thread during resolution (8)
+constexpr int kCW = 320;                 // candidates (logit, index) per wave after expansion
+constexpr int kCap = kCW * kRW;          // candidates per workgroup (2560)
+constexpr int kOwn = (kCW + 63) / 64;    // candidates per thread during resolution (5)
 constexpr int kR0 = 64;                  // rank among thread maxima for the first threshold
 constexpr int kListMax = 4096;           // longest kept list stored for the draw
 
@@ -336,15 +337,13 @@ struct RowShared {
             u32x4 raw[kUnits + 64];   // captured 16-byte groups, as stored (+ a scratch slot per lane)
             uint32_t grp[kUnits + 64];  // their group numbers
         } st;
-        struct {                      // after the stream
-            u64 buf[kCap + kRB];      // candidates (logit bits << 32) | index in per-thread
-                                      // columns (row kOwn: scratch), later the kept list
-            u64 hm[kNB];              // per-bin fixed-point mass
-            uint32_t hc[kNB];         // per-bin count
-            uint32_t bkey[kBinMax];   // entries of one bin
-            u64 bw[kBinMax];
-        } fz;
+        u64 list[kListMax];           // after every wave expanded its segment: the kept list
     } u;
+    u64 cand[kCap + 64];      // per-wave candidates (logit bits << 32) | index (+ a scratch slot per lane)
+    u64 hm[kNB];              // per-bin fixed-point mass
+    uint32_t hc[kNB];         // per-bin count
+    uint32_t bkey[kBinMax];   // entries of one bin
+    u64 bw[kBinMax];
     uint32_t th_hc[kNB];      // histogram of the first threshold
     Sel sel;
     double red_d[kRW];
@@ -488,53 +487,61 @@ __device__ __forceinline__ void capture_units(RowShared& S, const u32x4 (&unit)[
     ovf = __builtin_amdgcn_readfirstlane(ok ? ovf : 1);
 }
 
-// Expands the wave segments into candidates, every logit >= tau of every
-// captured group, as (logit bits << 32) | index.  Each thread keeps its
-// candidates in its own column of S.u.fz.buf (slots tid + i * kRB, i < n_own);
-// row kOwn of the buffer takes the writes of non-candidates and overflow, so
-// the loop has no branches.  Returns this thread's candidate count, with
-// bit 32 set when its segment or its column overflowed.
+// Expands this wave's segment into candidates, every logit >= tau of every
+// captured group, as (logit bits << 32) | index, packed in the wave's own
+// region S.cand[wave * kCW, ...) in segment order.  Only this wave's segment and region are touched, so a wave
+// expands as soon as its own stream ends.  Candidates past kCW, and the
+// values that are no candidates, go to the lane's scratch slot, so nothing
+// branches.  Returns the wave's candidate count (uniform) with bit 32 set
+// when the segment or the region overflowed.
 template <int DT>
-__device__ __forceinline__ u64 expand_units(RowShared& S, int V, float tau, int fill, int ovf, int& n_own) {
+__device__ __forceinline__ u64 wave_expand(RowShared& S, int V, float tau, int fill, int ovf) {
     constexpr int per = RowStream<DT>::per;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     u32x4 ur[kUPL];
     uint32_t ug[kUPL];
+    int lim[kUPL];
+    // hits of unit i in 16-bit field i (at most 8 per unit, 512 per wave)
+    u64 c = 0ull;
 #pragma unroll
     for (int i = 0; i < kUPL; ++i) {
         const int k = lane + 64 * i;
         ur[i] = u32x4{0u, 0u, 0u, 0u};
         ug[i] = 0u;
+        lim[i] = 0;
         if (k < fill) {
             ur[i] = S.u.st.raw[wave * kSegU + k];
             ug[i] = S.u.st.grp[wave * kSegU + k];
+            lim[i] = V - (int)ug[i] * per;  // slots of the unit inside the row
         }
+        int ci = 0;
+#pragma unroll
+        for (int q = 0; q < per; ++q) ci += (q < lim[i] && RowStream<DT>::unit_value(ur[i], q) >= tau) ? 1 : 0;
+        c |= (u64)ci << (16 * i);
     }
-    __syncthreads();  // segments read: the union now belongs to the candidates
-    // bins of the resolution, cleared now; the next barriers publish it
-    for (int i = threadIdx.x; i < kNB; i += kRB) {
-        S.u.fz.hc[i] = 0u;
-        S.u.fz.hm[i] = 0ull;
-    }
-    if (threadIdx.x < 2) S.nbin2[threadIdx.x] = 0;
+    // candidates go in segment order (unit lane + 64 i: i, then lane), which
+    // is ascending token index
+    const u64 incl = wave_incl_scan(c);
+    const u64 tot = lane_read(incl, 63);
+    const u64 excl = incl - c;
+    u64* region = S.cand + wave * kCW;
     int n = 0;
 #pragma unroll
     for (int i = 0; i < kUPL; ++i) {
+        int p = n + (int)((excl >> (16 * i)) & 0xFFFFu);
+        n += (int)((tot >> (16 * i)) & 0xFFFFu);
         if (64 * i < fill) {  // uniform: some lane of the wave holds unit i
-            const bool have = lane + 64 * i < fill;
-            const int lim = have ? V - (int)ug[i] * per : 0;  // slots of the unit inside the row
 #pragma unroll
             for (int q = 0; q < per; ++q) {
                 const float x = RowStream<DT>::unit_value(ur[i], q);
-                const bool hit = q < lim && x >= tau;
-                S.u.fz.buf[threadIdx.x + min(n, kOwn) * kRB] =
-                    ((u64)__float_as_uint(x) << 32) | (ug[i] * per + q);
-                n += hit ? 1 : 0;
+                const bool hit = q < lim[i] && x >= tau;
+                u64* slot = (hit && p < kCW) ? region + p : S.cand + kCap + lane;
+                *slot = ((u64)__float_as_uint(x) << 32) | (ug[i] * per + q);
+                p += hit ? 1 : 0;
             }
         }
     }
-    n_own = min(n, kOwn);
-    return (u64)n | ((u64)((n > kOwn ? 1 : 0) | ovf) << 32);
+    return (u64)min(n, kCW) | ((u64)((n > kCW ? 1 : 0) | ovf) << 32);
 }
 
 // A row's totals, combined over the block in one exchange: the largest
@@ -612,8 +619,8 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
     return tau;
 }
 
-// Resolve top-k / top-p from the candidates.  Entries (kOwn per thread) hold
-// every logit >= the capture threshold.  Returns false when the candidates
+// Resolve top-k / top-p from the candidates.  Entries (up to kOwn per thread:
+// its wave's candidates lane + 64 i) hold every logit >= the capture threshold.  Returns false when the candidates
 // cannot decide (the caller then re-reads the row).
 //
 // The candidates are binned by value (kNB bins over [lo, M]) with their
@@ -621,12 +628,12 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
 // crossing bin needs no broadcast; inside that bin the entries are gathered
 // and every entry learns the count and mass of the bin's entries with a
 // strictly larger key (within one wave when the bin holds at most 64).
-// The bins and the gather counters were cleared before the candidates were
-// published (expand_units).
+// The bins and the gather counters were cleared when the row started.
 __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S, float M, double Z,
                                                   int n_own, float tau, double scale, uint32_t& thr_key,
                                                   double& z_kept, int& n_kept) {
     const int tid = threadIdx.x, lane = tid & 63;
+    const u64* mine = S.cand + (tid >> 6) * kCW + lane;  // this thread's candidates: mine[64 i], i < n_own
     uint32_t key[kOwn];
     u64 wt[kOwn];
     int bin[kOwn];
@@ -636,7 +643,7 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         key[i] = 0u;
         wt[i] = 0ull;
         if (i < n_own) {
-            const float x = __uint_as_float((uint32_t)(S.u.fz.buf[tid + i * kRB] >> 32));
+            const float x = __uint_as_float((uint32_t)(mine[64 * i] >> 32));
             key[i] = fkey(x);
             wt[i] = (u64)(exp(((double)x - (double)M) * a.inv_T) * scale);
             xmin = fminf(xmin, x);
@@ -651,8 +658,8 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         bin[i] = kNB;
         if (i < n_own) {
             bin[i] = min(kNB - 1, (int)((M - key_to_float(key[i])) * bscale));
-            atomicAdd(&S.u.fz.hc[bin[i]], 1u);
-            atomicAdd(&S.u.fz.hm[bin[i]], wt[i]);
+            atomicAdd(&S.hc[bin[i]], 1u);
+            atomicAdd(&S.hm[bin[i]], wt[i]);
         }
     }
     __syncthreads();
@@ -663,8 +670,8 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     auto resolve_bin = [&](int b, int call, uint32_t floor_key, u64 base, bool by_count, u64 limit,
                            uint32_t& kmin, uint32_t& kcnt, u64& kmass) -> bool {
         // gather (contention only among the bin's own entries)
-        u64* bw = call == 0 ? S.u.fz.bw : S.u.fz.bw + kBinMax / 2;
-        uint32_t* bk = call == 0 ? S.u.fz.bkey : S.u.fz.bkey + kBinMax / 2;
+        u64* bw = call == 0 ? S.bw : S.bw + kBinMax / 2;
+        uint32_t* bk = call == 0 ? S.bkey : S.bkey + kBinMax / 2;
         constexpr int cap = kBinMax / 2;
 #pragma unroll
         for (int i = 0; i < kOwn; ++i) {
@@ -731,7 +738,7 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     u64 in_k_mass = 0ull;
     u64 cb_k = 0ull, mb_k = 0ull;
     if (a.use_k) {
-        wave_first_reach([&](int i) { return (u64)S.u.fz.hc[i]; }, [&](int i) { return S.u.fz.hm[i]; },
+        wave_first_reach([&](int i) { return (u64)S.hc[i]; }, [&](int i) { return S.hm[i]; },
                          (u64)a.top_k, bk, cb_k, mb_k);
         if (bk < 0) return false;  // fewer than top_k entries captured
         if (!resolve_bin(bk, 0, 0u, cb_k, true, (u64)a.top_k, tau_k, in_k_cnt, in_k_mass)) return false;
@@ -750,8 +757,8 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     if (a.use_k && target > zk) target = zk;  // rounding: keep the whole top-k set
     int bp;
     u64 mb_p, cb_p;
-    wave_first_reach([&](int i) -> u64 { return i < bk ? S.u.fz.hm[i] : (i == bk ? in_k_mass : 0ull); },
-                     [&](int i) -> u64 { return i < bk ? S.u.fz.hc[i] : (i == bk ? in_k_cnt : 0u); },
+    wave_first_reach([&](int i) -> u64 { return i < bk ? S.hm[i] : (i == bk ? in_k_mass : 0ull); },
+                     [&](int i) -> u64 { return i < bk ? S.hc[i] : (i == bk ? in_k_cnt : 0u); },
                      target, bp, mb_p, cb_p);
     if (bp < 0) return false;  // the crossing lies below the candidates
     uint32_t kmin, kcnt;
@@ -800,8 +807,8 @@ __device__ __forceinline__ Sel row_select_exact(RowShared& S, const char* rowp, 
     for (int lvl = 0; lvl < nlev; ++lvl) {
         const int shift = 24 - 8 * lvl;
         for (int i = threadIdx.x; i < 256; i += kRB) {
-            S.u.fz.hm[i] = 0ull;
-            S.u.fz.hc[i] = 0u;
+            S.hm[i] = 0ull;
+            S.hc[i] = 0u;
         }
         __syncthreads();
         row_for_each<DT>(rowp, V, [&](int, float x) {
@@ -810,28 +817,28 @@ __device__ __forceinline__ Sel row_select_exact(RowShared& S, const char* rowp, 
                 const uint32_t d = (k >> shift) & 255u;
                 const u64 w = by_count ? 1ull
                                        : (u64)(exp(((double)x - (double)M) * inv_T) * scale);
-                atomicAdd(&S.u.fz.hm[d], w);
-                atomicAdd(&S.u.fz.hc[d], 1u);
+                atomicAdd(&S.hm[d], w);
+                atomicAdd(&S.hc[d], 1u);
             }
         });
         __syncthreads();
         if (threadIdx.x < 64) {
             int bin;
             u64 above;
-            wave_find_from_top(S.u.fz.hm, target - A, bin, above);
+            wave_find_from_top(S.hm, target - A, bin, above);
             if (threadIdx.x == 0) {
                 Sel r;
                 if (bin < 0) {
                     r.ok = 0;
                 } else {
                     uint32_t ca = 0u;
-                    for (int d = 255; d > bin; --d) ca += S.u.fz.hc[d];
+                    for (int d = 255; d > bin; --d) ca += S.hc[d];
                     r.ok = 1;
                     r.key = prefix | ((uint32_t)bin << shift);
                     r.above = A + above;
-                    r.group = S.u.fz.hm[bin];
+                    r.group = S.hm[bin];
                     r.cnt_above = C + ca;
-                    r.cnt_group = S.u.fz.hc[bin];
+                    r.cnt_group = S.hc[bin];
                 }
                 S.sel = r;
             }
@@ -881,6 +888,14 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     float tau0 = INFINITY;   // the first (block-wide) threshold: at or below every wave's
     float m_run = -INFINITY; // running maximum for threshold refreshes (top-k rows)
     int fill = 0, ovf = 0;   // this wave's segment (uniform per wave)
+    if (kFilt) {
+        // bins of the candidate resolution (first used after many barriers)
+        for (int i = threadIdx.x; i < kNB; i += kRB) {
+            S.hm[i] = 0ull;
+            S.hc[i] = 0u;
+        }
+        if (threadIdx.x < 2) S.nbin2[threadIdx.x] = 0;
+    }
 
     // One tile of kREPT logits per thread (NL groups of `per`; group j of this
     // thread is gbase + j * gstride): group maxima, running max and sum,
@@ -924,7 +939,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         if (kFilt) {
             if (MODE == MODE_TOPK) m_run = fmaxf(m_run, tm);
             if (first) {
-                tau = V <= kCap ? -INFINITY
+                tau = V <= kCW ? -INFINITY
                                 : first_threshold(S, tm, MODE == MODE_TOPK ? max(1, min(a.top_k, kRB)) : kR0);
                 tau0 = tau;
             }
@@ -1011,7 +1026,13 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     // ---- merge the row (fixed-order reductions) ----
     int n_own = 0;
     u64 cflags = 0ull;
-    if (kFilt) cflags = expand_units<DT>(S, V, tau, fill, ovf, n_own);
+    if (kFilt) {
+        const u64 w = wave_expand<DT>(S, V, tau, fill, ovf);
+        const int nw = (int)(uint32_t)w;
+        n_own = min(kOwn, max(0, (nw - (int)(threadIdx.x & 63) + 63) / 64));
+        cflags = (threadIdx.x & 63) == 0 ? w : 0ull;  // one contribution per wave
+    }
+    // the barriers of the block totals also end every wave's use of its segment
     const RowTot tot =
         rb_row_totals(RowTot{MODE == MODE_TOPK ? m_run : m_th, kSum ? k_th : -INFINITY, z_th, cflags}, S);
     const float M = tot.m;
@@ -1065,54 +1086,108 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             z_kept = (double)zfx / scale;
             n_kept = (int)cnt;
         }
-        // kept list of a target row, sorted by token index: gather the kept
-        // logits (candidates >= thr, or a pass over the row on the
-        // exact path) into LDS, then bucket them by tile and rank each entry
-        // inside its bucket, which gives a deterministic order.
+        // kept list of a target row, sorted by token index.  Fast path: every
+        // wave's candidates are in index order (a wave captures its groups in
+        // ascending order), so each wave packs its kept ones in place and an
+        // entry's place in the merged list is its place in its own wave's
+        // list plus, for every other wave, the number of that wave's kept
+        // indices below it.  Exact path: gather the kept logits in a pass over
+        // the row, bucket them by tile and rank each inside its bucket.  Both
+        // orders are deterministic.
         if (row < a.sh.n_trows) {
             const int list_n = (n_kept <= kListMax && st.nt <= kNB) ? n_kept : -1;
-            if (list_n >= 0) {
+            const uint32_t tk = fkey(thr);
+            uint2* out = a.kept + (size_t)row * kListMax;
+            if (list_n >= 0 && fast) {
+                const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                u64* region = S.cand + wave * kCW;
                 u64 own[kOwn];
-                if (fast) {
 #pragma unroll
-                    for (int i = 0; i < kOwn; ++i) own[i] = i < n_own ? S.u.fz.buf[threadIdx.x + i * kRB] : 0ull;
+                for (int i = 0; i < kOwn; ++i) own[i] = i < n_own ? region[lane + 64 * i] : 0ull;
+                __builtin_amdgcn_wave_barrier();
+                int p = 0;
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) {
+                    const bool keep = i < n_own && fkey(__uint_as_float((uint32_t)(own[i] >> 32))) >= tk;
+                    const u64 m = __builtin_amdgcn_ballot_w64(keep);
+                    const int r = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    if (keep) region[p + r] = own[i];
+                    p += __popcll(m);
                 }
+                if (lane == 0) S.red_i[wave] = p;
+                __syncthreads();
+                int kw[kRW], off[kRW];
+                int nk = 0;
+#pragma unroll
+                for (int w = 0; w < kRW; ++w) {
+                    kw[w] = S.red_i[w];
+                    off[w] = nk;
+                    nk += kw[w];
+                }
+                nk = min(nk, list_n);
+                for (int e = threadIdx.x; e < nk; e += kRB) {
+                    int w0 = 0;
+#pragma unroll
+                    for (int w = 1; w < kRW; ++w) w0 = e >= off[w] ? w : w0;
+                    const u64 me = S.cand[w0 * kCW + (e - off[w0])];
+                    const uint32_t idx = (uint32_t)me;
+                    // kept indices below idx in every wave's list (its own
+                    // included, where that is its position), by binary
+                    // searches run side by side
+                    const uint32_t* L = reinterpret_cast<const uint32_t*>(S.cand);
+                    int lo[kRW];
+#pragma unroll
+                    for (int w = 0; w < kRW; ++w) lo[w] = 0;
+                    static_assert(kCW <= 511, "the search covers lists of up to 511 entries");
+#pragma unroll
+                    for (int step = 256; step >= 1; step >>= 1) {
+                        // all eight probes are read before any is used (one
+                        // LDS round trip per step); a probe at the list's
+                        // end repeats its last entry, which never moves lo
+                        int probe[kRW];
+                        uint32_t val[kRW];
+#pragma unroll
+                        for (int w = 0; w < kRW; ++w) {
+                            probe[w] = min(lo[w] + step, kw[w]);
+                            val[w] = L[2 * (w * kCW + max(probe[w], 1) - 1)];
+                        }
+#pragma unroll
+                        for (int w = 0; w < kRW; ++w) lo[w] = (probe[w] > lo[w] && val[w] < idx) ? probe[w] : lo[w];
+                    }
+                    int rank = 0;
+#pragma unroll
+                    for (int w = 0; w < kRW; ++w) rank += lo[w];
+                    if (rank < nk) out[rank] = make_uint2(idx, (uint32_t)(me >> 32));
+                }
+            } else if (list_n >= 0) {
+                constexpr int kLPT = kListMax / kRB;
+                u64 own[kLPT];
                 __syncthreads();
                 if (threadIdx.x == 0) S.nlist = 0;
                 __syncthreads();
-                const uint32_t tk = fkey(thr);
-                if (fast) {
-#pragma unroll
-                    for (int i = 0; i < kOwn; ++i) {
-                        if (i < n_own && fkey(__uint_as_float((uint32_t)(own[i] >> 32))) >= tk) {
-                            const int p = atomicAdd(&S.nlist, 1);
-                            if (p < kCap) S.u.fz.buf[p] = own[i];
-                        }
+                row_for_each<DT>(rowp, V, [&](int i, float x) {
+                    if (x >= thr) {
+                        const int p = atomicAdd(&S.nlist, 1);
+                        if (p < kListMax) S.u.list[p] = ((u64)__float_as_uint(x) << 32) | (uint32_t)i;
                     }
-                } else {
-                    row_for_each<DT>(rowp, V, [&](int i, float x) {
-                        if (x >= thr) {
-                            const int p = atomicAdd(&S.nlist, 1);
-                            if (p < kCap) S.u.fz.buf[p] = ((u64)__float_as_uint(x) << 32) | (uint32_t)i;
-                        }
-                    });
-                }
+                });
                 __syncthreads();
                 const int nk = min(S.nlist, list_n);
                 // bucket = streaming tile of the token
                 for (int i = threadIdx.x; i < kNB; i += kRB) {
-                    S.u.fz.hc[i] = 0u;
-                    S.u.fz.bkey[i] = 0u;
+                    S.hc[i] = 0u;
+                    S.bkey[i] = 0u;
                 }
 #pragma unroll
-                for (int i = 0; i < kOwn; ++i) {
+                for (int i = 0; i < kLPT; ++i) {
                     const int slot = threadIdx.x + i * kRB;
-                    own[i] = slot < nk ? S.u.fz.buf[slot] : 0ull;
+                    own[i] = slot < nk ? S.u.list[slot] : 0ull;
                 }
                 __syncthreads();
 #pragma unroll
-                for (int i = 0; i < kOwn; ++i)
-                    if (threadIdx.x + i * kRB < nk) atomicAdd(&S.u.fz.hc[(uint32_t)own[i] / kRTile], 1u);
+                for (int i = 0; i < kLPT; ++i)
+                    if (threadIdx.x + i * kRB < nk) atomicAdd(&S.hc[(uint32_t)own[i] / kRTile], 1u);
                 __syncthreads();
                 if (threadIdx.x < 64) {
                     // exclusive prefix of bucket counts, bucket starts into hm
@@ -1122,34 +1197,33 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                     u64 ls = 0ull;
 #pragma unroll
                     for (int q = 0; q < per; ++q) {
-                        c[q] = S.u.fz.hc[per * lane + q];
+                        c[q] = S.hc[per * lane + q];
                         ls += c[q];
                     }
                     u64 run = wave_incl_scan(ls) - ls;
 #pragma unroll
                     for (int q = 0; q < per; ++q) {
-                        S.u.fz.hm[per * lane + q] = run;
+                        S.hm[per * lane + q] = run;
                         run += c[q];
                     }
                 }
                 __syncthreads();
 #pragma unroll
-                for (int i = 0; i < kOwn; ++i) {
+                for (int i = 0; i < kLPT; ++i) {
                     if (threadIdx.x + i * kRB < nk) {
                         const uint32_t bkt = (uint32_t)own[i] / kRTile;
-                        const uint32_t p = (uint32_t)S.u.fz.hm[bkt] + atomicAdd(&S.u.fz.bkey[bkt], 1u);
-                        S.u.fz.buf[p] = own[i];
+                        const uint32_t p = (uint32_t)S.hm[bkt] + atomicAdd(&S.bkey[bkt], 1u);
+                        S.u.list[p] = own[i];
                     }
                 }
                 __syncthreads();
-                uint2* out = a.kept + (size_t)row * kListMax;
                 for (int e = threadIdx.x; e < nk; e += kRB) {
-                    const u64 me = S.u.fz.buf[e];
+                    const u64 me = S.u.list[e];
                     const uint32_t idx = (uint32_t)me;
                     const uint32_t bkt = idx / kRTile;
-                    const int s0 = (int)S.u.fz.hm[bkt], len = (int)S.u.fz.hc[bkt];
+                    const int s0 = (int)S.hm[bkt], len = (int)S.hc[bkt];
                     int rank = 0;
-                    for (int q = s0; q < s0 + len; ++q) rank += ((uint32_t)S.u.fz.buf[q] < idx) ? 1 : 0;
+                    for (int q = s0; q < s0 + len; ++q) rank += ((uint32_t)S.u.list[q] < idx) ? 1 : 0;
                     out[s0 + rank] = make_uint2(idx, (uint32_t)(me >> 32));
                 }
             }

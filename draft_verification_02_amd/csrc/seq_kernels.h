@@ -12,6 +12,8 @@
 //  k_greedy_prefix : greedy prefix match from the per-row argmax.
 #pragma once
 
+#include <type_traits>
+
 #include "row_kernels.h"
 
 namespace sv {
@@ -333,79 +335,92 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         draw_long_list(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
         return;
     }
-    float xd[kLPT];
-#pragma unroll
-    for (int e = 0; e < kLPT; ++e) {
-        const int i = threadIdx.x * kLPT + e;
-        xd[e] = -INFINITY;
-        if (s.has_draft && i < n) xd[e] = load_logit(s.dp, s.ddt, (int)ent[e].x);
-    }
-    double pr[kLPT], rr[kLPT];
-    double sr = 0.0, sp = 0.0;
-#pragma unroll
-    for (int e = 0; e < kLPT; ++e) {
-        const int i = threadIdx.x * kLPT + e;
-        pr[e] = 0.0;
-        rr[e] = 0.0;
-        if (i < n) {
-            const float xt = __uint_as_float(ent[e].y);
-            const double p = xt >= s.thr_t ? exp(((double)xt - (double)s.Mt) * a.inv_T) / s.zt : 0.0;
-            const double q = (s.has_draft && xd[e] >= s.thr_d)
-                                 ? exp(((double)xd[e] - (double)s.Md) * a.inv_T) / s.zd
-                                 : 0.0;
-            const double d = p - q;
-            pr[e] = p;
-            rr[e] = d > 0.0 ? d : 0.0;
-            sr += rr[e];
-            sp += pr[e];
-        }
-    }
-    double er, ep, tr, tp;
-    seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
-    const bool usep = (jc == K) || !(tr > 0.0);
-    const double S = usep ? tp : tr;
-    const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)jc, PURPOSE_SAMPLE)) * S;
-    const double mine = usep ? sp : sr;
-    const double ex = usep ? ep : er;
-    // the thread whose range holds t: the last one with mass whose range
-    // starts at or before t (prefixes are non-decreasing in thread order);
-    // if rounding put t before all of them, the first one with mass
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
-    const unsigned long long mf = __ballot(mine > 0.0);
-    if (lane == 0) {
-        s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
-        s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
-    }
-    __syncthreads();
-    int tau = -1, first = kSB;
-#pragma unroll
-    for (int w = 0; w < kSB / 64; ++w) {
-        tau = max(tau, s_last[w]);
-        first = min(first, s_first[w]);
-    }
-    if (tau < 0) tau = first;
-    if ((int)threadIdx.x == tau) {
-        double acc = ex;
-        int y = -1, last = -1;
+    // The rest is straight-line per draft dtype, so that the gathers of a
+    // thread are in flight together while p is computed.
+    auto finish = [&](auto ddt_tag) {
+        constexpr int DDT = decltype(ddt_tag)::value;
+        // raw draft elements, decoded where used (after p).  Without a draft
+        // row the loads read the target row (at least as many bytes) and are
+        // ignored, so no branch makes the gathers wait early.
+        const char* dp = s.has_draft ? s.dp : s.tp;
+        uint32_t xraw[kLPT];
 #pragma unroll
         for (int e = 0; e < kLPT; ++e) {
-            const int i = threadIdx.x * kLPT + e;
-            const double w = usep ? pr[e] : rr[e];
-            if (y < 0 && i < n && w > 0.0) {
-                last = (int)ent[e].x;
-                acc += w;
-                if (acc > t) y = (int)ent[e].x;
-            }
+            const uint32_t ix = threadIdx.x * kLPT + e < n ? ent[e].x : 0u;
+            xraw[e] = DDT == DT_F32 ? reinterpret_cast<const uint32_t*>(dp)[ix]
+                                    : (uint32_t)reinterpret_cast<const uint16_t*>(dp)[ix];
         }
-        s_y = y >= 0 ? y : last;
-    }
-    __syncthreads();
-    // output row: accepted drafts, the drawn token, then -1
-    int32_t* out = a.out_tokens + (size_t)b * (K + 1);
-    for (int k = threadIdx.x; k <= K; k += kSB)
-        out[k] = k < jc ? (k < kSB ? tok : a.sh.tokens[(size_t)b * K + k]) : (k == jc ? s_y : -1);
-    if (threadIdx.x == 0) a.out_num[b] = jc;
+        const double inv_zt = 1.0 / s.zt, inv_zd = 1.0 / s.zd;
+        double pr[kLPT], rr[kLPT];
+        double sr = 0.0, sp = 0.0;
+#pragma unroll
+        for (int e = 0; e < kLPT; ++e) {
+            const float xt = __uint_as_float(ent[e].y);
+            pr[e] = (threadIdx.x * kLPT + e < n && xt >= s.thr_t)
+                        ? exp(((double)xt - (double)s.Mt) * a.inv_T) * inv_zt
+                        : 0.0;
+            sp += pr[e];
+        }
+#pragma unroll
+        for (int e = 0; e < kLPT; ++e) {
+            const float xd = s.has_draft ? __uint_as_float(DDT == DT_F32 ? xraw[e] : xraw[e] << 16) : -INFINITY;
+            const bool qd = threadIdx.x * kLPT + e < n && xd >= s.thr_d;
+            const double q = qd ? exp(((double)xd - (double)s.Md) * a.inv_T) * inv_zd : 0.0;
+            const double d = pr[e] - q;
+            rr[e] = d > 0.0 ? d : 0.0;
+            sr += rr[e];
+        }
+        double er, ep, tr, tp;
+        seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
+        const bool usep = (jc == K) || !(tr > 0.0);
+        const double S = usep ? tp : tr;
+        const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)jc, PURPOSE_SAMPLE)) * S;
+        const double mine = usep ? sp : sr;
+        const double ex = usep ? ep : er;
+        // the thread whose range holds t: the last one with mass whose range
+        // starts at or before t (prefixes are non-decreasing in thread order);
+        // if rounding put t before all of them, the first one with mass
+        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+        const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
+        const unsigned long long mf = __ballot(mine > 0.0);
+        if (lane == 0) {
+            s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
+            s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
+        }
+        __syncthreads();
+        int tau = -1, first = kSB;
+#pragma unroll
+        for (int w = 0; w < kSB / 64; ++w) {
+            tau = max(tau, s_last[w]);
+            first = min(first, s_first[w]);
+        }
+        if (tau < 0) tau = first;
+        if ((int)threadIdx.x == tau) {
+            double acc = ex;
+            int y = -1, last = -1;
+#pragma unroll
+            for (int e = 0; e < kLPT; ++e) {
+                const int i = threadIdx.x * kLPT + e;
+                const double w = usep ? pr[e] : rr[e];
+                if (y < 0 && i < n && w > 0.0) {
+                    last = (int)ent[e].x;
+                    acc += w;
+                    if (acc > t) y = (int)ent[e].x;
+                }
+            }
+            s_y = y >= 0 ? y : last;
+        }
+        __syncthreads();
+        // output row: accepted drafts, the drawn token, then -1
+        int32_t* out = a.out_tokens + (size_t)b * (K + 1);
+        for (int k = threadIdx.x; k <= K; k += kSB)
+            out[k] = k < jc ? (k < kSB ? tok : a.sh.tokens[(size_t)b * K + k]) : (k == jc ? s_y : -1);
+        if (threadIdx.x == 0) a.out_num[b] = jc;
+    };
+    if (s.has_draft && s.ddt == DT_F32)
+        finish(std::integral_constant<int, DT_F32>());
+    else
+        finish(std::integral_constant<int, DT_BF16>());
 }
 
 // ---------------------------------------------------------------------------

@@ -19,8 +19,8 @@
 namespace sv {
 
 constexpr int kSB = 256;                 // threads per sequence workgroup
-constexpr int kChunk = 8192;             // tokens per draw chunk
-constexpr int kCPT = kChunk / kSB;       // 32 contiguous tokens per thread
+constexpr int kChunk = 1024;             // tokens per draw chunk
+constexpr int kCPT = kChunk / kSB;       // 4 contiguous tokens per thread
 
 struct SeqArgs {
     Shape sh;
@@ -426,8 +426,57 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
 // ---------------------------------------------------------------------------
 // Unfiltered: chunk sums, then the pick.
 // ---------------------------------------------------------------------------
+// The kCPT logits of row `row` from token lo on (-inf past V): the loads of
+// a thread are issued together and decoded after.
+template <int DT>
+__device__ __forceinline__ void load_run(const char* row, int lo, int V, float (&x)[kCPT]) {
+    uint32_t raw[kCPT];
+#pragma unroll
+    for (int e = 0; e < kCPT; ++e) {
+        const int i = min(lo + e, V - 1);
+        raw[e] = DT == DT_F32 ? reinterpret_cast<const uint32_t*>(row)[i]
+                              : (uint32_t)reinterpret_cast<const uint16_t*>(row)[i];
+    }
+#pragma unroll
+    for (int e = 0; e < kCPT; ++e)
+        x[e] = lo + e < V ? __uint_as_float(DT == DT_F32 ? raw[e] : raw[e] << 16) : -INFINITY;
+}
+
+// p_j and the residual max(0, p_j - q_j) of the kCPT tokens from lo on, in
+// fp64 (the same arithmetic wherever a chunk is summed or searched).
+template <int TDT, int DDT>
+__device__ __forceinline__ void run_terms(const StopRow& s, double inv_T, int lo, int V, double (&p)[kCPT],
+                                          double (&r)[kCPT]) {
+    float xt[kCPT], xd[kCPT];
+    load_run<TDT>(s.tp, lo, V, xt);
+    // without a draft row the target row is read again and ignored
+    load_run<DDT>(s.has_draft ? s.dp : s.tp, lo, V, xd);
+    const double inv_zt = 1.0 / s.zt, inv_zd = 1.0 / s.zd;
+#pragma unroll
+    for (int e = 0; e < kCPT; ++e) {
+        p[e] = xt[e] >= s.thr_t ? exp(((double)xt[e] - (double)s.Mt) * inv_T) * inv_zt : 0.0;
+        const double q = (s.has_draft && xd[e] >= s.thr_d) ? exp(((double)xd[e] - (double)s.Md) * inv_T) * inv_zd : 0.0;
+        const double d = p[e] - q;
+        r[e] = d > 0.0 ? d : 0.0;
+    }
+}
+
+// Calls f(integral_constant TDT, integral_constant DDT) for the row pair's
+// dtypes (uniform over the workgroup).
+template <class F>
+__device__ __forceinline__ void with_dtypes(const StopRow& s, F&& f) {
+    const int ddt = s.has_draft ? s.ddt : s.tdt;
+    if (s.tdt == DT_F32) {
+        if (ddt == DT_F32) f(std::integral_constant<int, DT_F32>(), std::integral_constant<int, DT_F32>());
+        else f(std::integral_constant<int, DT_F32>(), std::integral_constant<int, DT_BF16>());
+    } else {
+        if (ddt == DT_F32) f(std::integral_constant<int, DT_BF16>(), std::integral_constant<int, DT_F32>());
+        else f(std::integral_constant<int, DT_BF16>(), std::integral_constant<int, DT_BF16>());
+    }
+}
+
 __global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
-    __shared__ double s_val[kSB], s_excl[kSB], s_total;
+    __shared__ double s_wa[kSB / 64], s_wb[kSB / 64];
     __shared__ int s_j;
     const int b = blockIdx.x / a.n_chunks;
     const int c = blockIdx.x % a.n_chunks;
@@ -438,45 +487,80 @@ __global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
     __syncthreads();
     const StopRow s = stop_row(a, b, s_j);
     const int lo = c * kChunk + threadIdx.x * kCPT;
-    const int hi = min(lo + kCPT, a.sh.V);
     double sr = 0.0, sp = 0.0;
-    for (int i = lo; i < hi; ++i) {
-        double p, r;
-        stop_terms(s, a.inv_T, i, p, r);
-        sr += r;
-        sp += p;
-    }
-    double e, tr, tp;
-    seq_excl_scan(sr, s_val, s_excl, &s_total, e, tr);
-    seq_excl_scan(sp, s_val, s_excl, &s_total, e, tp);
+    with_dtypes(s, [&](auto tt, auto dt) {
+        double p[kCPT], r[kCPT];
+        run_terms<decltype(tt)::value, decltype(dt)::value>(s, a.inv_T, lo, a.sh.V, p, r);
+#pragma unroll
+        for (int e = 0; e < kCPT; ++e) {
+            sr += r[e];
+            sp += p[e];
+        }
+    });
+    double er, ep, tr, tp;
+    seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
     if (threadIdx.x == 0) a.chunk_sum[(size_t)b * a.n_chunks + c] = make_double2(tr, tp);
 }
 
+// One workgroup per sequence: the chunk holding the draw point (chunk sums
+// in chunk order, thread t holding chunks t, t + kSB, ...), then the token
+// inside it from the same per-thread terms.
 __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
-    __shared__ double s_val[kSB], s_excl[kSB], s_total;
-    __shared__ int s_j, s_cstar, s_tau, s_usep;
-    __shared__ double s_run, s_t;
+    __shared__ double s_wa[kSB / 64], s_wb[kSB / 64], s_run;
+    __shared__ int s_j, s_cstar;
+    __shared__ int s_last[kSB / 64], s_first[kSB / 64];
     const int b = blockIdx.x;
     const int K = a.sh.K, V = a.sh.V;
     if (threadIdx.x < 64) {
         const int j = first_rejection(a, b);
-        if (threadIdx.x == 0) s_j = j;
-    }
-    __syncthreads();
-    const int j = s_j;
-    if (threadIdx.x == 0) {
-        const double2* cs = a.chunk_sum + (size_t)b * a.n_chunks;
-        double Sr = 0.0, Sp = 0.0;
-        for (int cc = 0; cc < a.n_chunks; ++cc) {
-            Sr += cs[cc].x;
-            Sp += cs[cc].y;
+        if (threadIdx.x == 0) {
+            s_j = j;
+            s_cstar = 0;  // stays if no chunk holds mass
+            s_run = 0.0;
         }
-        const int usep = (j == K) || !(Sr > 0.0);
-        const double S = usep ? Sp : Sr;
-        const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
-        double run = 0.0, run_last = 0.0;
-        int cstar = -1, last_nz = 0;
-        for (int cc = 0; cc < a.n_chunks; ++cc) {
+    }
+    const double2* cs = a.chunk_sum + (size_t)b * a.n_chunks;
+    // this thread's chunks are contiguous: [c0, c1)
+    const int per = (a.n_chunks + kSB - 1) / kSB;
+    const int c0 = min((int)threadIdx.x * per, a.n_chunks), c1 = min(c0 + per, a.n_chunks);
+    double mr = 0.0, mp = 0.0;
+    for (int cc = c0; cc < c1; ++cc) {
+        const double2 v = cs[cc];
+        mr += v.x;
+        mp += v.y;
+    }
+    double er, ep, tr, tp;
+    seq_excl_scan2(mr, mp, s_wa, s_wb, er, ep, tr, tp);  // (its barrier also publishes s_j)
+    const int j = s_j;
+    const bool usep = (j == K) || !(tr > 0.0);
+    const double S = usep ? tp : tr;
+    const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    // the thread whose chunk range holds t (the last with mass starting at or
+    // before t; else the first with mass), then the chunk inside its range
+    auto locate = [&](double mine, double ex) {
+        const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
+        const unsigned long long mf = __ballot(mine > 0.0);
+        __syncthreads();
+        if (lane == 0) {
+            s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
+            s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
+        }
+        __syncthreads();
+        int tau = -1, first = kSB;
+#pragma unroll
+        for (int w = 0; w < kSB / 64; ++w) {
+            tau = max(tau, s_last[w]);
+            first = min(first, s_first[w]);
+        }
+        return tau >= 0 ? tau : first;
+    };
+    const int tc = locate(usep ? mp : mr, usep ? ep : er);
+    if ((int)threadIdx.x == tc) {
+        double run = usep ? ep : er;
+        int cstar = -1, last_nz = c0;
+        double run_last = run;
+        for (int cc = c0; cc < c1; ++cc) {
             const double sc = usep ? cs[cc].y : cs[cc].x;
             if (sc > 0.0) {
                 if (run + sc > t) {
@@ -494,45 +578,41 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
         }
         s_cstar = cstar;
         s_run = run;
-        s_t = t;
-        s_usep = usep;
     }
     __syncthreads();
-    const StopRow s = stop_row(a, b, j);
     const int cstar = s_cstar;
-    const double run = s_run, t = s_t;
-    const bool usep = s_usep != 0;
+    const double run = s_run;
+    const StopRow s = stop_row(a, b, j);
     const int lo = cstar * kChunk + threadIdx.x * kCPT;
-    const int hi = min(lo + kCPT, V);
-    double sr = 0.0, sp = 0.0;
-    for (int i = lo; i < hi; ++i) {
-        double p, r;
-        stop_terms(s, a.inv_T, i, p, r);
-        sr += r;
-        sp += p;
-    }
-    const double mine = usep ? sp : sr;
-    double excl, total;
-    seq_excl_scan(mine, s_val, s_excl, &s_total, excl, total);
-    const int tau = pick_thread(mine, run + excl, t, &s_tau);
-    if ((int)threadIdx.x == tau) {
-        double acc = run + excl;
-        int y = -1, last = -1;
-        for (int i = lo; i < hi; ++i) {
-            double p, r;
-            stop_terms(s, a.inv_T, i, p, r);
-            const double w = usep ? p : r;
-            if (w > 0.0) {
-                last = i;
-                acc += w;
-                if (acc > t) {
-                    y = i;
-                    break;
+    with_dtypes(s, [&](auto tt, auto dt) {
+        double p[kCPT], r[kCPT];
+        run_terms<decltype(tt)::value, decltype(dt)::value>(s, a.inv_T, lo, V, p, r);
+        double sr = 0.0, sp = 0.0;
+#pragma unroll
+        for (int e = 0; e < kCPT; ++e) {
+            sr += r[e];
+            sp += p[e];
+        }
+        double er2, ep2, tr2, tp2;
+        seq_excl_scan2(sr, sp, s_wa, s_wb, er2, ep2, tr2, tp2);
+        const double mine = usep ? sp : sr;
+        const double ex = run + (usep ? ep2 : er2);
+        const int tau = locate(mine, ex);
+        if ((int)threadIdx.x == tau) {
+            double acc = ex;
+            int y = -1, last = -1;
+#pragma unroll
+            for (int e = 0; e < kCPT; ++e) {
+                const double w = usep ? p[e] : r[e];
+                if (y < 0 && w > 0.0) {
+                    last = lo + e;
+                    acc += w;
+                    if (acc > t) y = lo + e;
                 }
             }
+            write_outputs(a, b, j, y >= 0 ? y : last);
         }
-        write_outputs(a, b, j, y >= 0 ? y : last);
-    }
+    });
 }
 
 // ---------------------------------------------------------------------------

@@ -619,8 +619,22 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
     return tau;
 }
 
+// Fixed-point weight 2^(x c - 8 kref) * 2^fx of a candidate (kref: the row's
+// power-of-two reference, so the weight is at most 2^fx).  The exponent is
+// formed in fp64 and split into whole and fractional parts, so the fp32 exp2
+// of the fraction carries the only rounding (relative error near 2^-23,
+// the same as the streaming terms of Z).
+__device__ __forceinline__ u64 grid_weight(float x, float kref, double c, int fx) {
+    const double y = fmax(fma((double)x, c, -8.0 * (double)kref), -2000.0);
+    const double n = floor(y);
+    const float w = __builtin_amdgcn_exp2f((float)(y - n));  // in [1, 2)
+    return (u64)ldexp((double)w, (int)n + fx);
+}
+
 // Resolve top-k / top-p from the candidates.  Entries (up to kOwn per thread:
-// its wave's candidates lane + 64 i) hold every logit >= the capture threshold.  Returns false when the candidates
+// its wave's candidates lane + 64 i) hold every logit >= the capture threshold.
+// Masses are in units of 2^(8 kref) / scale (Zg: the row sum in units of
+// 2^(8 kref)); z_kept is returned in units of 2^(8 kref).  Returns false when the candidates
 // cannot decide (the caller then re-reads the row).
 //
 // The candidates are binned by value (kNB bins over [lo, M]) with their
@@ -629,7 +643,7 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
 // and every entry learns the count and mass of the bin's entries with a
 // strictly larger key (within one wave when the bin holds at most 64).
 // The bins and the gather counters were cleared when the row started.
-__device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S, float M, double Z,
+__device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S, float M, float kref, double Zg,
                                                   int n_own, float tau, double scale, uint32_t& thr_key,
                                                   double& z_kept, int& n_kept) {
     const int tid = threadIdx.x, lane = tid & 63;
@@ -645,7 +659,7 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         if (i < n_own) {
             const float x = __uint_as_float((uint32_t)(mine[64 * i] >> 32));
             key[i] = fkey(x);
-            wt[i] = (u64)(exp(((double)x - (double)M) * a.inv_T) * scale);
+            wt[i] = grid_weight(x, kref, a.c64, a.fx_shift);
             xmin = fminf(xmin, x);
         }
     }
@@ -751,7 +765,7 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         return true;
     }
     // top-p on the (top-k) kept set: kept <=> excl < ceil(top_p * Z * 2^s)
-    const double zbase = a.use_k ? (double)zk / scale : Z;
+    const double zbase = a.use_k ? (double)zk / scale : Zg;
     u64 target = (u64)ceil((double)a.top_p * zbase * scale);
     if (target == 0ull) target = 1ull;
     if (a.use_k && target > zk) target = zk;  // rounding: keep the whole top-k set
@@ -1045,14 +1059,25 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     int n_kept = V;
     int flags = 0;
 
+    // exp of the drafted token's logit against the row maximum, ahead of the
+    // resolution's barriers (thread 0 writes the record)
+    double e_tok = 0.0;
+    if (threadIdx.x == 0 && d_tok >= 0 && d_tok < V) e_tok = exp(((double)xd - (double)M) * a.inv_T);
+
     if (kFilt) {
         flags = SPEC_ROW_FILTERED;
         const double scale = ldexp(1.0, a.fx_shift);
         uint32_t thr_key = 0u;
+        // power-of-two reference of the row: the streaming sums use the same
+        // (a thread's reference is ceil(its max * c / 8))
+        const float kref = M != -INFINITY ? ceilf(M * a.c8) : 0.f;
+        const double Zg = (kSum && tot.k != -INFINITY) ? ldexp(tot.z, (int)(8.f * (tot.k - kref))) : 0.0;
+        double zk_grid = 0.0;
         bool fast = n_res <= kCap &&
-                    resolve_reservoir(a, S, M, Z, n_own, tau0, scale, thr_key, z_kept, n_kept);
+                    resolve_reservoir(a, S, M, kref, Zg, n_own, tau0, scale, thr_key, zk_grid, n_kept);
         if (fast) {
             thr = key_to_float(thr_key);
+            z_kept = zk_grid * exp2(8.0 * (double)kref - (double)M * a.c64);
         } else {
             flags |= SPEC_ROW_EXACT_PATH;
             __syncthreads();
@@ -1243,8 +1268,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         double prob = __longlong_as_double(0x7FF8000000000000LL);  // NaN: no drafted token
         if (row_has_token(a.sh, row)) {
             prob = 0.0;
-            if (d_tok >= 0 && d_tok < V && xd >= thr)
-                prob = exp(((double)xd - (double)M) * a.inv_T) / z_kept;
+            if (d_tok >= 0 && d_tok < V && xd >= thr) prob = e_tok / z_kept;
         }
         r.s.prob_at_token = prob;
         a.rec[row] = r;

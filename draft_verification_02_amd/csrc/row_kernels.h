@@ -487,56 +487,45 @@ __device__ __forceinline__ void capture_units(RowShared& S, const u32x4 (&unit)[
     ovf = __builtin_amdgcn_readfirstlane(ok ? ovf : 1);
 }
 
-// Expands this wave's segment into candidates, every logit >= tau of every
-// captured group, as (logit bits << 32) | index, packed in the wave's own
-// region S.cand[wave * kCW, ...) in segment order.  Only this wave's segment and region are touched, so a wave
-// expands as soon as its own stream ends.  Candidates past kCW, and the
-// values that are no candidates, go to the lane's scratch slot, so nothing
-// branches.  Returns the wave's candidate count (uniform) with bit 32 set
-// when the segment or the region overflowed.
+// Expands the units [0, fill) of this wave's segment into candidates, every
+// logit >= tau of every captured group, as (logit bits << 32) | index,
+// appended in segment order (unit lane + 64 i: i, then lane, which is
+// ascending token index) to the wave's own region S.cand[wave * kCW, ...)
+// after its first `base` entries.  One unit per lane at a time, so that it
+// needs few registers.  Candidates past kCW, and the values that are no
+// candidates, go to the lane's scratch slot, so nothing branches.  Returns
+// the wave's candidate count (uniform, base included) with bit 32 set when
+// the segment or the region overflowed.
 template <int DT>
-__device__ __forceinline__ u64 wave_expand(RowShared& S, int V, float tau, int fill, int ovf) {
+__device__ __forceinline__ u64 wave_expand(RowShared& S, int V, float tau, int fill, int ovf, int base) {
     constexpr int per = RowStream<DT>::per;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    u32x4 ur[kUPL];
-    uint32_t ug[kUPL];
-    int lim[kUPL];
-    // hits of unit i in 16-bit field i (at most 8 per unit, 512 per wave)
-    u64 c = 0ull;
-#pragma unroll
-    for (int i = 0; i < kUPL; ++i) {
-        const int k = lane + 64 * i;
-        ur[i] = u32x4{0u, 0u, 0u, 0u};
-        ug[i] = 0u;
-        lim[i] = 0;
-        if (k < fill) {
-            ur[i] = S.u.st.raw[wave * kSegU + k];
-            ug[i] = S.u.st.grp[wave * kSegU + k];
-            lim[i] = V - (int)ug[i] * per;  // slots of the unit inside the row
-        }
-        int ci = 0;
-#pragma unroll
-        for (int q = 0; q < per; ++q) ci += (q < lim[i] && RowStream<DT>::unit_value(ur[i], q) >= tau) ? 1 : 0;
-        c |= (u64)ci << (16 * i);
-    }
-    // candidates go in segment order (unit lane + 64 i: i, then lane), which
-    // is ascending token index
-    const u64 incl = wave_incl_scan(c);
-    const u64 tot = lane_read(incl, 63);
-    const u64 excl = incl - c;
     u64* region = S.cand + wave * kCW;
-    int n = 0;
+    int n = base;
 #pragma unroll
     for (int i = 0; i < kUPL; ++i) {
-        int p = n + (int)((excl >> (16 * i)) & 0xFFFFu);
-        n += (int)((tot >> (16 * i)) & 0xFFFFu);
         if (64 * i < fill) {  // uniform: some lane of the wave holds unit i
+            const int k = lane + 64 * i;
+            u32x4 ur = u32x4{0u, 0u, 0u, 0u};
+            uint32_t ug = 0u;
+            int lim = 0;
+            if (k < fill) {
+                ur = S.u.st.raw[wave * kSegU + k];
+                ug = S.u.st.grp[wave * kSegU + k];
+                lim = V - (int)ug * per;  // slots of the unit inside the row
+            }
+            int c = 0;
+#pragma unroll
+            for (int q = 0; q < per; ++q) c += (q < lim && RowStream<DT>::unit_value(ur, q) >= tau) ? 1 : 0;
+            const int incl = wave_incl_scan(c);
+            int p = n + incl - c;
+            n += lane_read(incl, 63);
 #pragma unroll
             for (int q = 0; q < per; ++q) {
-                const float x = RowStream<DT>::unit_value(ur[i], q);
-                const bool hit = q < lim[i] && x >= tau;
+                const float x = RowStream<DT>::unit_value(ur, q);
+                const bool hit = q < lim && x >= tau;
                 u64* slot = (hit && p < kCW) ? region + p : S.cand + kCap + lane;
-                *slot = ((u64)__float_as_uint(x) << 32) | (ug[i] * per + q);
+                *slot = ((u64)__float_as_uint(x) << 32) | (ug * per + q);
                 p += hit ? 1 : 0;
             }
         }
@@ -970,6 +959,17 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             tau = fmaxf(tau, first_threshold(S, m_run, max(1, min(a.top_k, kRB))));
         }
     };
+    // Expands the captured units so far into the wave's candidates and
+    // empties the segment.
+    int n_w = 0;  // this wave's candidates (uniform per wave)
+    auto expand_now = [&]() {
+        if (kFilt) {
+            const u64 w = wave_expand<DT>(S, V, tau, fill, ovf, n_w);
+            n_w = (int)(uint32_t)w;
+            ovf = (int)(w >> 32);
+            fill = 0;
+        }
+    };
     auto full_tile = [&](int t, const u32x4 (&raw)[NL]) {
         float v[kREPT];
         RowStream<DT>::unpack_full(raw, v);
@@ -1041,10 +1041,10 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     int n_own = 0;
     u64 cflags = 0ull;
     if (kFilt) {
-        const u64 w = wave_expand<DT>(S, V, tau, fill, ovf);
-        const int nw = (int)(uint32_t)w;
-        n_own = min(kOwn, max(0, (nw - (int)(threadIdx.x & 63) + 63) / 64));
-        cflags = (threadIdx.x & 63) == 0 ? w : 0ull;  // one contribution per wave
+        expand_now();
+        n_own = min(kOwn, max(0, (n_w - (int)(threadIdx.x & 63) + 63) / 64));
+        // one contribution per wave: count | overflow << 32
+        cflags = (threadIdx.x & 63) == 0 ? ((u64)n_w | ((u64)(ovf ? 1 : 0) << 32)) : 0ull;
     }
     // the barriers of the block totals also end every wave's use of its segment
     const RowTot tot =

@@ -877,6 +877,9 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     constexpr int NL = RowStream<DT>::NL;
     constexpr int per = RowStream<DT>::per;
 
+    // Streaming waves issue ahead of waves of a co-resident workgroup that
+    // are already finishing their row (priority drops again below).
+    __builtin_amdgcn_s_setprio(1);
     // the drafted token's logit, fetched while the row streams
     int d_tok = -1;
     float xd = -INFINITY;
@@ -1037,6 +1040,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         }
     }
 
+    __builtin_amdgcn_s_setprio(0);
     // ---- merge the row (fixed-order reductions) ----
     int n_own = 0;
     u64 cflags = 0ull;

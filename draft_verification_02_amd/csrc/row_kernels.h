@@ -1127,7 +1127,63 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             const int list_n = (n_kept <= kListMax && st.nt <= kNB) ? n_kept : -1;
             const uint32_t tk = fkey(thr);
             uint2* out = a.kept + (size_t)row * kListMax;
-            if (list_n >= 0 && fast) {
+            // Tokens come in blocks of 64 groups (64 * per tokens) that each
+            // belong to one wave (block b to wave b mod kRW), and a wave's
+            // list holds its blocks' entries contiguously in block order.  So
+            // an entry's rank is the number of kept entries in all earlier
+            // blocks plus its place within its block's run.
+            constexpr int kBlkShift = DT == DT_BF16 ? 9 : 8;  // log2(64 * per)
+            const int nblk = (V + (1 << kBlkShift) - 1) >> kBlkShift;
+            if (list_n >= 0 && fast && nblk <= kNB) {
+                const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+                u64* region = S.cand + wave * kCW;
+                // per block: kept count (th_hc), then its exclusive prefix;
+                // first list position of its run (hm)
+                for (int i = threadIdx.x; i < nblk; i += kRB) {
+                    S.th_hc[i] = 0u;
+                    S.hm[i] = ~0ull;
+                }
+                u64 own[kOwn];
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) own[i] = i < n_own ? region[lane + 64 * i] : 0ull;
+                __builtin_amdgcn_wave_barrier();
+                int p = 0;
+                int kpos[kOwn];  // list position of this lane's kept entries, or -1
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) {
+                    const bool keep = i < n_own && fkey(__uint_as_float((uint32_t)(own[i] >> 32))) >= tk;
+                    const u64 m = __builtin_amdgcn_ballot_w64(keep);
+                    const int r = p + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                     __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                    kpos[i] = keep ? r : -1;
+                    p += __popcll(m);
+                }
+                __syncthreads();  // the bins are cleared
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) {
+                    if (kpos[i] >= 0) {
+                        const uint32_t blk = (uint32_t)own[i] >> kBlkShift;
+                        atomicAdd(&S.th_hc[blk], 1u);
+                        atomicMin(&S.hm[blk], (u64)kpos[i]);
+                    }
+                }
+                __syncthreads();
+                int nk_all = 0;
+                const int cnt = (int)threadIdx.x < nblk ? (int)S.th_hc[threadIdx.x] : 0;
+                const int before = rb_excl_scan(cnt, S.red_i, nk_all);
+                if ((int)threadIdx.x < nblk) S.th_hc[threadIdx.x] = (uint32_t)before;
+                __syncthreads();
+                const int nk = min(nk_all, list_n);
+#pragma unroll
+                for (int i = 0; i < kOwn; ++i) {
+                    if (kpos[i] >= 0) {
+                        const uint32_t idx = (uint32_t)own[i];
+                        const uint32_t blk = idx >> kBlkShift;
+                        const int rank = (int)S.th_hc[blk] + kpos[i] - (int)S.hm[blk];
+                        if (rank < nk) out[rank] = make_uint2(idx, (uint32_t)(own[i] >> 32));
+                    }
+                }
+            } else if (list_n >= 0 && fast) {
                 const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
                 u64* region = S.cand + wave * kCW;
                 u64 own[kOwn];

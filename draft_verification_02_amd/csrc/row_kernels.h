@@ -329,6 +329,7 @@ struct RowArgs {
     RowRec* rec;
     uint2* kept;        // [n_trows][kListMax] (index, logit bits), ascending index
     int* kept_n;        // [n_trows]; -1 when the list was not stored
+    float* kept_d;      // [n_trows][kListMax] draft logit of each listed token (rows with a draft row)
 };
 
 struct RowShared {
@@ -1127,6 +1128,18 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             const int list_n = (n_kept <= kListMax && st.nt <= kNB) ? n_kept : -1;
             const uint32_t tk = fkey(thr);
             uint2* out = a.kept + (size_t)row * kListMax;
+            // With a draft row at this position, each listed token also gets
+            // the draft's logit, read now (this row has slack before the
+            // draft rows finish), so the draw needs no gather of its own.
+            const int kpos_row = row % (a.sh.K + 1);
+            const bool with_draft = kpos_row < a.sh.K;
+            const char* dp = with_draft ? row_ptr(a.sh, a.sh.n_trows + (row / (a.sh.K + 1)) * a.sh.K + kpos_row)
+                                        : nullptr;
+            float* outd = a.kept_d + (size_t)row * kListMax;
+            auto emit = [&](int rank, uint32_t idx, uint32_t bits) {
+                out[rank] = make_uint2(idx, bits);
+                if (with_draft) outd[rank] = load_logit(dp, a.sh.ddt, idx);
+            };
             // Tokens come in blocks of 64 groups (64 * per tokens) that each
             // belong to one wave (block b to wave b mod kRW), and a wave's
             // list holds its blocks' entries contiguously in block order.  So
@@ -1180,7 +1193,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                         const uint32_t idx = (uint32_t)own[i];
                         const uint32_t blk = idx >> kBlkShift;
                         const int rank = (int)S.th_hc[blk] + kpos[i] - (int)S.hm[blk];
-                        if (rank < nk) out[rank] = make_uint2(idx, (uint32_t)(own[i] >> 32));
+                        if (rank < nk) emit(rank, idx, (uint32_t)(own[i] >> 32));
                     }
                 }
             } else if (list_n >= 0 && fast) {
@@ -1243,7 +1256,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                     int rank = 0;
 #pragma unroll
                     for (int w = 0; w < kRW; ++w) rank += lo[w];
-                    if (rank < nk) out[rank] = make_uint2(idx, (uint32_t)(me >> 32));
+                    if (rank < nk) emit(rank, idx, (uint32_t)(me >> 32));
                 }
             } else if (list_n >= 0) {
                 constexpr int kLPT = kListMax / kRB;
@@ -1309,7 +1322,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                     const int s0 = (int)S.hm[bkt], len = (int)S.hc[bkt];
                     int rank = 0;
                     for (int q = s0; q < s0 + len; ++q) rank += ((uint32_t)S.u.list[q] < idx) ? 1 : 0;
-                    out[s0 + rank] = make_uint2(idx, (uint32_t)(me >> 32));
+                    emit(s0 + rank, idx, (uint32_t)(me >> 32));
                 }
             }
             if (threadIdx.x == 0) a.kept_n[row] = list_n;

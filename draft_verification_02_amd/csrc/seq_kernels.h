@@ -4,7 +4,7 @@
 //  k_seq_filtered : filtered rows (top-k / top-p).  p_j is nonzero only on the
 //                   stop target row's kept set, stored sorted by index by
 //                   k_row, so the residual max(0, p_j - q_j) is evaluated on
-//                   that list (draft logits gathered by index).  One
+//                   that list (with the draft logits stored beside it).  One
 //                   workgroup per (sequence, possible stop position).
 //  k_draw_sums / k_draw_pick : unfiltered rows.  The residual is spread over
 //                   the whole vocabulary: chunk sums over the stop row pair in
@@ -29,6 +29,7 @@ struct SeqArgs {
     const RowRec* rec;
     const uint2* kept;
     const int* kept_n;
+    const float* kept_d;  // draft logit of each listed token (stop positions j < K)
     double2* chunk_sum;   // [B][n_chunks] (.x residual, .y p)
     int n_chunks;
     int32_t* out_tokens;
@@ -269,9 +270,9 @@ __device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, i
 // Filtered: one workgroup per (sequence, candidate stop position j).  Every
 // workgroup loads, in one round, the accept-test inputs of its sequence, the
 // records of row pair j and the first kSpec entries of target row j's kept
-// list; the workgroup whose j is the stop position then gathers the draft
-// logits of the listed tokens and draws, the others exit.  This puts two
-// dependent memory rounds, not four, between the row kernel and the output.
+// list with the draft logits the row kernel stored beside them; the
+// workgroup whose j is the stop position then draws, the others exit.  So
+// one dependent memory round separates the row kernel from the output.
 // ---------------------------------------------------------------------------
 constexpr int kLPT = 4;                  // kept-list entries per thread
 constexpr int kSpec = kLPT * kSB;        // entries loaded before the stop is known (1024)
@@ -318,6 +319,14 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     uint2 ent[kLPT];
 #pragma unroll
     for (int e = 0; e < kLPT; ++e) ent[e] = L[threadIdx.x * kLPT + e];
+    // the draft logits of the listed tokens, stored beside the list by the
+    // row kernel (positions j < K)
+    float xdl[kLPT];
+    {
+        const float* LD = a.kept_d + (size_t)rt * kListMax;
+#pragma unroll
+        for (int e = 0; e < kLPT; ++e) xdl[e] = LD[threadIdx.x * kLPT + e];
+    }
     const StopRow s = stop_row(a, b, jc);
     // the accepted drafted tokens, one per thread, for the output row
     const int tok = (int)threadIdx.x < jc ? a.sh.tokens[(size_t)b * K + threadIdx.x] : -1;
@@ -335,92 +344,72 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         draw_long_list(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
         return;
     }
-    // The rest is straight-line per draft dtype, so that the gathers of a
-    // thread are in flight together while p is computed.
-    auto finish = [&](auto ddt_tag) {
-        constexpr int DDT = decltype(ddt_tag)::value;
-        // raw draft elements, decoded where used (after p).  Without a draft
-        // row the loads read the target row (at least as many bytes) and are
-        // ignored, so no branch makes the gathers wait early.
-        const char* dp = s.has_draft ? s.dp : s.tp;
-        uint32_t xraw[kLPT];
+    const double inv_zt = 1.0 / s.zt, inv_zd = 1.0 / s.zd;
+    double pr[kLPT], rr[kLPT];
+    double sr = 0.0, sp = 0.0;
+#pragma unroll
+    for (int e = 0; e < kLPT; ++e) {
+        const float xt = __uint_as_float(ent[e].y);
+        pr[e] = (threadIdx.x * kLPT + e < n && xt >= s.thr_t)
+                    ? exp(((double)xt - (double)s.Mt) * a.inv_T) * inv_zt
+                    : 0.0;
+        sp += pr[e];
+    }
+#pragma unroll
+    for (int e = 0; e < kLPT; ++e) {
+        const float xd = s.has_draft ? xdl[e] : -INFINITY;
+        const bool qd = threadIdx.x * kLPT + e < n && xd >= s.thr_d;
+        const double q = qd ? exp(((double)xd - (double)s.Md) * a.inv_T) * inv_zd : 0.0;
+        const double d = pr[e] - q;
+        rr[e] = d > 0.0 ? d : 0.0;
+        sr += rr[e];
+    }
+    double er, ep, tr, tp;
+    seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
+    const bool usep = (jc == K) || !(tr > 0.0);
+    const double S = usep ? tp : tr;
+    const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)jc, PURPOSE_SAMPLE)) * S;
+    const double mine = usep ? sp : sr;
+    const double ex = usep ? ep : er;
+    // the thread whose range holds t: the last one with mass whose range
+    // starts at or before t (prefixes are non-decreasing in thread order);
+    // if rounding put t before all of them, the first one with mass
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
+    const unsigned long long mf = __ballot(mine > 0.0);
+    if (lane == 0) {
+        s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
+        s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
+    }
+    __syncthreads();
+    int tau = -1, first = kSB;
+#pragma unroll
+    for (int w = 0; w < kSB / 64; ++w) {
+        tau = max(tau, s_last[w]);
+        first = min(first, s_first[w]);
+    }
+    if (tau < 0) tau = first;
+    if ((int)threadIdx.x == tau) {
+        double acc = ex;
+        int y = -1, last = -1;
 #pragma unroll
         for (int e = 0; e < kLPT; ++e) {
-            const uint32_t ix = threadIdx.x * kLPT + e < n ? ent[e].x : 0u;
-            xraw[e] = DDT == DT_F32 ? reinterpret_cast<const uint32_t*>(dp)[ix]
-                                    : (uint32_t)reinterpret_cast<const uint16_t*>(dp)[ix];
-        }
-        const double inv_zt = 1.0 / s.zt, inv_zd = 1.0 / s.zd;
-        double pr[kLPT], rr[kLPT];
-        double sr = 0.0, sp = 0.0;
-#pragma unroll
-        for (int e = 0; e < kLPT; ++e) {
-            const float xt = __uint_as_float(ent[e].y);
-            pr[e] = (threadIdx.x * kLPT + e < n && xt >= s.thr_t)
-                        ? exp(((double)xt - (double)s.Mt) * a.inv_T) * inv_zt
-                        : 0.0;
-            sp += pr[e];
-        }
-#pragma unroll
-        for (int e = 0; e < kLPT; ++e) {
-            const float xd = s.has_draft ? __uint_as_float(DDT == DT_F32 ? xraw[e] : xraw[e] << 16) : -INFINITY;
-            const bool qd = threadIdx.x * kLPT + e < n && xd >= s.thr_d;
-            const double q = qd ? exp(((double)xd - (double)s.Md) * a.inv_T) * inv_zd : 0.0;
-            const double d = pr[e] - q;
-            rr[e] = d > 0.0 ? d : 0.0;
-            sr += rr[e];
-        }
-        double er, ep, tr, tp;
-        seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
-        const bool usep = (jc == K) || !(tr > 0.0);
-        const double S = usep ? tp : tr;
-        const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)jc, PURPOSE_SAMPLE)) * S;
-        const double mine = usep ? sp : sr;
-        const double ex = usep ? ep : er;
-        // the thread whose range holds t: the last one with mass whose range
-        // starts at or before t (prefixes are non-decreasing in thread order);
-        // if rounding put t before all of them, the first one with mass
-        const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-        const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
-        const unsigned long long mf = __ballot(mine > 0.0);
-        if (lane == 0) {
-            s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
-            s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
-        }
-        __syncthreads();
-        int tau = -1, first = kSB;
-#pragma unroll
-        for (int w = 0; w < kSB / 64; ++w) {
-            tau = max(tau, s_last[w]);
-            first = min(first, s_first[w]);
-        }
-        if (tau < 0) tau = first;
-        if ((int)threadIdx.x == tau) {
-            double acc = ex;
-            int y = -1, last = -1;
-#pragma unroll
-            for (int e = 0; e < kLPT; ++e) {
-                const int i = threadIdx.x * kLPT + e;
-                const double w = usep ? pr[e] : rr[e];
-                if (y < 0 && i < n && w > 0.0) {
-                    last = (int)ent[e].x;
-                    acc += w;
-                    if (acc > t) y = (int)ent[e].x;
-                }
+            const int i = threadIdx.x * kLPT + e;
+            const double w = usep ? pr[e] : rr[e];
+            if (y < 0 && i < n && w > 0.0) {
+                last = (int)ent[e].x;
+                acc += w;
+                if (acc > t) y = (int)ent[e].x;
             }
-            s_y = y >= 0 ? y : last;
         }
-        __syncthreads();
-        // output row: accepted drafts, the drawn token, then -1
-        int32_t* out = a.out_tokens + (size_t)b * (K + 1);
-        for (int k = threadIdx.x; k <= K; k += kSB)
-            out[k] = k < jc ? (k < kSB ? tok : a.sh.tokens[(size_t)b * K + k]) : (k == jc ? s_y : -1);
-        if (threadIdx.x == 0) a.out_num[b] = jc;
-    };
-    if (s.has_draft && s.ddt == DT_F32)
-        finish(std::integral_constant<int, DT_F32>());
-    else
-        finish(std::integral_constant<int, DT_BF16>());
+        s_y = y >= 0 ? y : last;
+    }
+    __syncthreads();
+    // output row: accepted drafts, the drawn token, then -1
+    int32_t* out = a.out_tokens + (size_t)b * (K + 1);
+    for (int k = threadIdx.x; k <= K; k += kSB)
+        out[k] = k < jc ? (k < kSB ? tok : a.sh.tokens[(size_t)b * K + k]) : (k == jc ? s_y : -1);
+    if (threadIdx.x == 0) a.out_num[b] = jc;
 }
 
 // ---------------------------------------------------------------------------

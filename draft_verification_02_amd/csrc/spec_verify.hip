@@ -16,7 +16,8 @@ namespace {
 using namespace sv;
 
 // Library-owned scratch for one (device, stream): row records, kept lists of
-// filtered target rows, greedy argmax indices and draw chunk sums.  Every
+// filtered target rows (with the draft logit of each listed token), greedy
+// argmax indices and draw chunk sums.  Every
 // kernel writes what it later reads within the same call, so nothing needs
 // clearing between calls.
 struct Workspace {
@@ -25,6 +26,7 @@ struct Workspace {
     RowRec* rec = nullptr;
     uint2* kept = nullptr;
     int* kept_n = nullptr;
+    float* kept_d = nullptr;
     int32_t* gidx = nullptr;
     double2* chunk_sum = nullptr;
 };
@@ -53,6 +55,7 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     const size_t o_rec = off; off = align_up(off + nw.cap_rows * sizeof(RowRec));
     const size_t o_kept = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(uint2));
     const size_t o_kn = off; off = align_up(off + nw.cap_trows * sizeof(int));
+    const size_t o_kd = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(float));
     const size_t o_g = off; off = align_up(off + nw.cap_trows * sizeof(int32_t));
     const size_t o_cs = off; off = align_up(off + nw.cap_chunks * sizeof(double2));
     if (w.base) {
@@ -66,6 +69,7 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     nw.rec = reinterpret_cast<RowRec*>(b + o_rec);
     nw.kept = reinterpret_cast<uint2*>(b + o_kept);
     nw.kept_n = reinterpret_cast<int*>(b + o_kn);
+    nw.kept_d = reinterpret_cast<float*>(b + o_kd);
     nw.gidx = reinterpret_cast<int32_t*>(b + o_g);
     nw.chunk_sum = reinterpret_cast<double2*>(b + o_cs);
     w = nw;
@@ -176,6 +180,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     ra.rec = ws->rec;
     ra.kept = ws->kept;
     ra.kept_n = ws->kept_n;
+    ra.kept_d = ws->kept_d;
 
     void *evb, *eva;
     take_events(&evb, &eva);
@@ -191,6 +196,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     sa.rec = ws->rec;
     sa.kept = ws->kept;
     sa.kept_n = ws->kept_n;
+    sa.kept_d = ws->kept_d;
     sa.chunk_sum = ws->chunk_sum;
     sa.n_chunks = n_chunks;
     sa.out_tokens = out_tokens;

@@ -116,6 +116,21 @@ def test_filters(top_k, top_p):
     check_sampling(w)
 
 
+@pytest.mark.parametrize("top_k,top_p", [(3000, 1.0), (0, 0.99)])
+def test_rows_resolved_by_rereading(top_k, top_p):
+    """Kept sets larger than the capture reservoir: such rows are resolved by
+    re-reading the row (flagged per row); the path must be taken and agree."""
+    _print_case(f"re-read resolution top_k={top_k} top_p={top_p}")
+    w = wl.make(4, 5, 30011, temperature=0.9, top_k=top_k, top_p=top_p, rho=0.8, n_boost=3,
+                seed=top_k + 17, vseed=top_k + 5)
+    rep = check_sampling(w)
+    assert rep is not None
+    _, _, ts, ds = gpu_sampling(w)
+    flags = np.concatenate([ts["flags"].ravel(), ds["flags"].ravel()])
+    assert (flags & binding.ROW_FILTERED).all()
+    assert (flags & binding.ROW_EXACT_PATH).any(), "no row took the re-read path"
+
+
 def test_ties_at_filter_thresholds():
     """Quantised logits: heavy ties at the top-k value and inside nucleus groups."""
     _print_case("ties")

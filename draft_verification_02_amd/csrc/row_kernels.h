@@ -617,8 +617,12 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
 __device__ __forceinline__ u64 grid_weight(float x, float kref, double c, int fx) {
     const double y = fmax(fma((double)x, c, -8.0 * (double)kref), -2000.0);
     const double n = floor(y);
-    const float w = __builtin_amdgcn_exp2f((float)(y - n));  // in [1, 2)
-    return (u64)ldexp((double)w, (int)n + fx);
+    const float w = __builtin_amdgcn_exp2f((float)(y - n));  // in [1, 2]
+    // w = m 2^(e - 23) with a 24-bit m; the weight is m shifted into place
+    const uint32_t b = __float_as_uint(w);
+    const u64 m = (u64)((b & 0x7FFFFFu) | 0x800000u);
+    const int sh = (int)n + fx - 23 + (int)(b >> 23) - 127;
+    return sh >= 0 ? m << min(sh, 40) : (sh > -24 ? m >> -sh : 0ull);
 }
 
 // Resolve top-k / top-p from the candidates.  Entries (up to kOwn per thread:
@@ -774,24 +778,34 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     return true;
 }
 
-// Exact resolution by re-reading the row: radix selection over every logit
-// of the row (counts for top-k, fixed-point masses for top-p).
+// f(index, logit) over every logit of the row, each thread taking groups
+// tid, tid + kRB, ... with kFE groups' loads in flight at once (indices past
+// the row re-read its last group and are not passed on).
+constexpr int kFE = 8;
 template <int DT, class F>
 __device__ __forceinline__ void row_for_each(const char* rowp, int V, F&& f) {
     constexpr int esz = DT == DT_BF16 ? 2 : 4;
     constexpr int per = 16 / esz;
     if ((((uintptr_t)rowp) & 15) == 0) {
         const int ng = V / per;
-        for (int g = threadIdx.x; g < ng; g += kRB) {
-            const u32x4 raw = ld16_nt(rowp + (size_t)g * 16);
-            const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+        for (int g0 = threadIdx.x; g0 < ng; g0 += kRB * kFE) {
+            u32x4 raw[kFE];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                if (DT == DT_BF16) {
-                    f(g * per + 2 * q, bf16_lo(w[q]));
-                    f(g * per + 2 * q + 1, bf16_hi(w[q]));
-                } else {
-                    f(g * per + q, __uint_as_float(w[q]));
+            for (int u = 0; u < kFE; ++u) raw[u] = ld16_nt(rowp + (size_t)min(g0 + u * kRB, ng - 1) * 16);
+#pragma unroll
+            for (int u = 0; u < kFE; ++u) {
+                const int g = g0 + u * kRB;
+                if (g < ng) {
+                    const uint32_t w[4] = {raw[u].x, raw[u].y, raw[u].z, raw[u].w};
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        if (DT == DT_BF16) {
+                            f(g * per + 2 * q, bf16_lo(w[q]));
+                            f(g * per + 2 * q + 1, bf16_hi(w[q]));
+                        } else {
+                            f(g * per + q, __uint_as_float(w[q]));
+                        }
+                    }
                 }
             }
         }
@@ -801,63 +815,171 @@ __device__ __forceinline__ void row_for_each(const char* rowp, int V, F&& f) {
     }
 }
 
+constexpr int kGather = 4096;             // entries of one bin gathered into LDS by the re-read selection
+
+// Exact selection by re-reading the row, for rows whose kept set the
+// candidates cannot decide.  Over the keys >= floor_key: by_count, the
+// largest key K whose count of keys >= K reaches `target` (the top-k value);
+// otherwise the largest K whose fixed-point mass of keys >= K reaches
+// `target` (the top-p crossing group).  Returns K with the count and mass of
+// the keys above it and of its group.  Masses are grid weights (units of
+// 2^(8 kref - fx)), as on the candidate path.
+//
+// Pass 1 bins the row by value: kNB bins from M down over 64 binary orders
+// of magnitude of weight (lower values share the last bin), counts and
+// masses in per-wave LDS histograms (no cross-wave contention) merged in
+// wave order.  Inside the bin where the target is reached, an 8-bit radix
+// over the keys, below the prefix that every key of the bin shares, finds the
+// exact group.  The bin's entries are gathered into LDS in one more pass
+// when they fit (kGather), and counted per digit there; otherwise the row is
+// re-read for every digit, with atomics only for that bin's entries.
 template <int DT>
-__device__ __forceinline__ Sel row_select_exact(RowShared& S, const char* rowp, int V, float M, double inv_T,
-                                                uint32_t floor_key, bool by_count, u64 target, double scale) {
-    const int nlev = DT == DT_BF16 ? 2 : 4;
-    uint32_t prefix = 0u, mask = 0u;
-    u64 A = 0ull;
-    uint32_t C = 0u;
-    for (int lvl = 0; lvl < nlev; ++lvl) {
-        const int shift = 24 - 8 * lvl;
-        for (int i = threadIdx.x; i < 256; i += kRB) {
-            S.hm[i] = 0ull;
-            S.hc[i] = 0u;
+__device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a, const char* rowp, int V, float M, float kref,
+                                 uint32_t floor_key, bool by_count, u64 target) {
+    const int tid = threadIdx.x, wave = tid >> 6;
+    static_assert(sizeof(u64) * kRW * kNB <= sizeof(S.u) && sizeof(uint32_t) * kRW * kNB <= sizeof(S.cand),
+                  "per-wave histograms fit the reservoir space");
+    static_assert(sizeof(u64) * kGather <= sizeof(S.u) && sizeof(uint32_t) * kGather <= sizeof(S.cand),
+                  "a gathered bin fits the reservoir space");
+    u64* pm = reinterpret_cast<u64*>(&S.u);             // [kRW][kNB] masses
+    uint32_t* pc = reinterpret_cast<uint32_t*>(S.cand);  // [kRW][kNB] counts
+    const float span = (float)(64.0 / a.c64);            // logit range of 64 binary orders of weight
+    const float bscale = (float)(kNB - 1) / span;
+    auto vbin = [&](float x) { return (int)fminf((M - x) * bscale, (float)(kNB - 1)); };
+    auto weight = [&](float x) { return grid_weight(x, kref, a.c64, a.fx_shift); };
+
+    __syncthreads();  // the reservoir space is free
+    for (int i = tid; i < kRW * kNB; i += kRB) {
+        pm[i] = 0ull;
+        pc[i] = 0u;
+    }
+    __syncthreads();
+    u64* my_m = pm + wave * kNB;
+    uint32_t* my_c = pc + wave * kNB;
+    row_for_each<DT>(rowp, V, [&](int, float x) {
+        if (fkey(x) >= floor_key) {
+            const int b = vbin(x);
+            atomicAdd(&my_m[b], weight(x));
+            atomicAdd(&my_c[b], 1u);
         }
+    });
+    __syncthreads();
+    for (int b = tid; b < kNB; b += kRB) {
+        u64 m = 0ull;
+        uint32_t c = 0u;
+#pragma unroll
+        for (int w = 0; w < kRW; ++w) {
+            m += pm[w * kNB + b];
+            c += pc[w * kNB + b];
+        }
+        S.hm[b] = m;
+        S.hc[b] = c;
+    }
+    __syncthreads();
+    Sel r;
+    r.ok = 0;
+    r.key = 0u;
+    r.above = r.group = 0ull;
+    r.cnt_above = r.cnt_group = 0u;
+    // every wave finds the bin where the target is reached (same data, same result)
+    int bin;
+    u64 bsel, both;
+    if (by_count)
+        wave_first_reach([&](int i) { return (u64)S.hc[i]; }, [&](int i) { return S.hm[i]; }, target, bin, bsel,
+                         both);
+    else
+        wave_first_reach([&](int i) { return S.hm[i]; }, [&](int i) { return (u64)S.hc[i]; }, target, bin, bsel,
+                         both);
+    if (bin < 0) return r;  // the totals stay below the target
+    u64 A = by_count ? both : bsel;                   // mass above
+    uint32_t C = (uint32_t)(by_count ? bsel : both);  // count above
+    // keys every entry of the bin lies between (its value bounds, widened by
+    // a fraction of a bin against rounding in vbin)
+    const float v_hi = bin == 0 ? INFINITY : M - ((float)bin - 0.0625f) / bscale;
+    const float v_lo = bin == kNB - 1 ? -INFINITY : M - ((float)bin + 1.0625f) / bscale;
+    const uint32_t k_lo = max(fkey(v_lo), floor_key), k_hi = fkey(v_hi);
+    const uint32_t diff = k_lo ^ k_hi;
+    if (diff == 0u) {  // one key only
+        r.ok = 1;
+        r.key = k_lo;
+        r.above = A;
+        r.cnt_above = C;
+        r.group = S.hm[bin];
+        r.cnt_group = S.hc[bin];
+        return r;
+    }
+    const int top_bit = 31 - __clz((int)diff);
+    uint32_t mask = top_bit >= 24 ? 0u : (0xFFFFFFFFu << (((top_bit >> 3) + 1) * 8));
+    uint32_t prefix = k_lo & mask;
+    // A bin that fits is gathered into LDS once (keys and weights), and its
+    // digits are counted there; a larger one is re-read for every digit.
+    const int nb = (int)S.hc[bin];
+    const bool gathered = nb <= kGather;
+    uint32_t* gkey = pc;  // the histograms are merged: their space is free
+    u64* gw = pm;
+    if (gathered) {
+        if (tid == 0) S.nlist = 0;
         __syncthreads();
         row_for_each<DT>(rowp, V, [&](int, float x) {
             const uint32_t k = fkey(x);
-            if (k >= floor_key && (k & mask) == prefix) {
-                const uint32_t d = (k >> shift) & 255u;
-                const u64 w = by_count ? 1ull
-                                       : (u64)(exp(((double)x - (double)M) * inv_T) * scale);
-                atomicAdd(&S.hm[d], w);
-                atomicAdd(&S.hc[d], 1u);
+            if (k >= floor_key && vbin(x) == bin) {
+                const int slot = atomicAdd(&S.nlist, 1);
+                if (slot < kGather) {
+                    gkey[slot] = k;
+                    gw[slot] = weight(x);
+                }
             }
         });
         __syncthreads();
-        if (threadIdx.x < 64) {
-            int bin;
-            u64 above;
-            wave_find_from_top(S.hm, target - A, bin, above);
-            if (threadIdx.x == 0) {
-                Sel r;
-                if (bin < 0) {
-                    r.ok = 0;
-                } else {
-                    uint32_t ca = 0u;
-                    for (int d = 255; d > bin; --d) ca += S.hc[d];
-                    r.ok = 1;
-                    r.key = prefix | ((uint32_t)bin << shift);
-                    r.above = A + above;
-                    r.group = S.hm[bin];
-                    r.cnt_above = C + ca;
-                    r.cnt_group = S.hc[bin];
-                }
-                S.sel = r;
-            }
+    }
+    for (int shift = (top_bit >> 3) * 8; shift >= 0; shift -= 8) {
+        for (int i = tid; i < 256; i += kRB) {
+            S.bw[i] = 0ull;
+            S.bkey[i] = 0u;
         }
         __syncthreads();
-        const Sel r = S.sel;
-        if (!r.ok) return r;
-        prefix = r.key;
-        mask |= 0xFFu << shift;
-        A = r.above;
-        C = r.cnt_above;
+        auto count_digit = [&](uint32_t k, u64 w) {
+            if ((k & mask) == prefix) {
+                const uint32_t d = (k >> shift) & 255u;
+                atomicAdd(&S.bw[d], w);
+                atomicAdd(&S.bkey[d], 1u);
+            }
+        };
+        if (gathered) {
+            for (int e = tid; e < nb; e += kRB) count_digit(gkey[e], gw[e]);
+        } else {
+            row_for_each<DT>(rowp, V, [&](int, float x) {
+                const uint32_t k = fkey(x);
+                if (k >= floor_key && vbin(x) == bin) count_digit(k, weight(x));
+            });
+        }
         __syncthreads();
+        // digits from the top: index i is digit 255 - i
+        int di;
+        u64 dsel, doth;
+        const u64 rest = by_count ? target - C : target - A;
+        if (by_count)
+            wave_first_reach([&](int i) { return i < 256 ? (u64)S.bkey[255 - i] : 0ull; },
+                             [&](int i) { return i < 256 ? S.bw[255 - i] : 0ull; }, rest, di, dsel, doth);
+        else
+            wave_first_reach([&](int i) { return i < 256 ? S.bw[255 - i] : 0ull; },
+                             [&](int i) { return i < 256 ? (u64)S.bkey[255 - i] : 0ull; }, rest, di, dsel, doth);
+        if (di < 0) return r;  // cannot happen with consistent passes; the caller keeps the whole range
+        const uint32_t d = 255u - (uint32_t)di;
+        A += by_count ? doth : dsel;
+        C += (uint32_t)(by_count ? dsel : doth);
+        prefix |= d << shift;
+        mask |= 0xFFu << shift;
+        if (shift == 0) {
+            r.group = S.bw[d];
+            r.cnt_group = S.bkey[d];
+        }
+        __syncthreads();  // every wave has read the digit histogram
     }
-    Sel r = S.sel;
-    if (nlev == 2) r.key = bf16_key_fill(r.key);
+    r.ok = 1;
+    r.key = prefix;
+    r.above = A;
+    r.cnt_above = C;
     return r;
 }
 
@@ -1085,36 +1207,38 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             z_kept = zk_grid * exp2(8.0 * (double)kref - (double)M * a.c64);
         } else {
             flags |= SPEC_ROW_EXACT_PATH;
-            __syncthreads();
-            uint32_t tk = 0u;
+            uint32_t thk = 0u;
             uint32_t cnt = (uint32_t)V;
+            u64 zfx = 0ull;  // kept mass, grid units
+            bool have_z = false;
             if (a.use_k) {
-                const Sel sk = row_select_exact<DT>(S, rowp, V, M, a.inv_T, 0u, true, (u64)a.top_k, scale);
-                tk = sk.key;
-                cnt = sk.cnt_above + sk.cnt_group;
+                const Sel sk = row_select_reread<DT>(S, a, rowp, V, M, kref, 0u, true, (u64)a.top_k);
+                if (sk.ok) {
+                    thk = sk.key;
+                    cnt = sk.cnt_above + sk.cnt_group;
+                    zfx = sk.above + sk.group;
+                    have_z = true;
+                }
             }
-            u64 part = 0ull;
-            row_for_each<DT>(rowp, V, [&](int, float x) {
-                if (fkey(x) >= tk) part += (u64)(exp(((double)x - (double)M) * a.inv_T) * scale);
-            });
-            const u64 tot = rb_sum_u64(part, S.red_u);
-            uint32_t thk = tk;
-            u64 zfx = tot;
             if (a.use_p) {
-                const double zbase = a.use_k ? (double)tot / scale : Z;
-                u64 target = (u64)ceil((double)a.top_p * zbase * scale);
+                // top-p on the (top-k) kept set: the target mass in grid units
+                const double zbase = have_z ? (double)zfx : Zg * scale;
+                u64 target = (u64)ceil((double)a.top_p * zbase);
                 if (target == 0ull) target = 1ull;
-                if (target > tot) target = tot;  // rounding: keep the whole top-k range
-                const Sel sp = row_select_exact<DT>(S, rowp, V, M, a.inv_T, tk, false, target, scale);
+                if (have_z && target > zfx) target = zfx;  // rounding: keep the whole top-k set
+                const Sel sp = row_select_reread<DT>(S, a, rowp, V, M, kref, thk, false, target);
                 if (sp.ok) {
                     thk = sp.key;
                     zfx = sp.above + sp.group;
                     cnt = sp.cnt_above + sp.cnt_group;
+                    have_z = true;
                 }
             }
             thr = key_to_float(thk);
-            z_kept = (double)zfx / scale;
             n_kept = (int)cnt;
+            // kept mass relative to the row maximum (the whole row when no
+            // selection applied)
+            z_kept = have_z ? (double)zfx / scale * exp2(8.0 * (double)kref - (double)M * a.c64) : Z;
         }
         // kept list of a target row, sorted by token index.  Fast path: every
         // wave's candidates are in index order (a wave captures its groups in

@@ -828,7 +828,8 @@ constexpr int kGather = 4096;             // entries of one bin gathered into LD
 // Pass 1 bins the row by value: kNB bins from M down over 64 binary orders
 // of magnitude of weight (lower values share the last bin), counts and
 // masses in per-wave LDS histograms (no cross-wave contention) merged in
-// wave order.  Inside the bin where the target is reached, an 8-bit radix
+// wave order.  Masses are taken relative to each bin's top (see below), so
+// a logit costs one fp32 exp2.  Inside the bin where the target is reached, an 8-bit radix
 // over the keys, below the prefix that every key of the bin shares, finds the
 // exact group.  The bin's entries are gathered into LDS in one more pass
 // when they fit (kGather), and counted per digit there; otherwise the row is
@@ -846,7 +847,19 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
     const float span = (float)(64.0 / a.c64);            // logit range of 64 binary orders of weight
     const float bscale = (float)(kNB - 1) / span;
     auto vbin = [&](float x) { return (int)fminf((M - x) * bscale, (float)(kNB - 1)); };
-    auto weight = [&](float x) { return grid_weight(x, kref, a.c64, a.fx_shift); };
+    // Weights relative to the top of each value bin: w = G_b * 2^((x - x_b) c)
+    // with the factor 2^((x - x_b) c) in [2^-1/8, 1] taken in fp32 (a small
+    // exponent, so about one ulp) and held in 31-bit fixed point; G_b, the
+    // bin's scale into the row's fixed-point units, applies once per bin.
+    const float cf = (float)a.c64;
+    auto xtop = [&](int b) { return M - (float)b / bscale; };
+    auto local_w = [&](float x, int b) -> u64 {
+        const float e = fminf((x - xtop(b)) * cf, 0.f);
+        return (u64)(uint32_t)(__builtin_amdgcn_exp2f(e) * 2147483648.0f);
+    };
+    auto bin_scale = [&](int b) {
+        return exp2((double)xtop(b) * a.c64 - 8.0 * (double)kref + (double)(a.fx_shift - 31));
+    };
 
     __syncthreads();  // the reservoir space is free
     for (int i = tid; i < kRW * kNB; i += kRB) {
@@ -859,7 +872,7 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
     row_for_each<DT>(rowp, V, [&](int, float x) {
         if (fkey(x) >= floor_key) {
             const int b = vbin(x);
-            atomicAdd(&my_m[b], weight(x));
+            atomicAdd(&my_m[b], local_w(x, b));
             atomicAdd(&my_c[b], 1u);
         }
     });
@@ -872,7 +885,7 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
             m += pm[w * kNB + b];
             c += pc[w * kNB + b];
         }
-        S.hm[b] = m;
+        S.hm[b] = (u64)((double)m * bin_scale(b));
         S.hc[b] = c;
     }
     __syncthreads();
@@ -891,8 +904,10 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
         wave_first_reach([&](int i) { return S.hm[i]; }, [&](int i) { return (u64)S.hc[i]; }, target, bin, bsel,
                          both);
     if (bin < 0) return r;  // the totals stay below the target
-    u64 A = by_count ? both : bsel;                   // mass above
+    u64 A = by_count ? both : bsel;                   // mass above the bin
     uint32_t C = (uint32_t)(by_count ? bsel : both);  // count above
+    const double G = bin_scale(bin);
+    u64 A_in = 0ull;  // mass above inside the bin, bin-local units
     // keys every entry of the bin lies between (its value bounds, widened by
     // a fraction of a bin against rounding in vbin)
     const float v_hi = bin == 0 ? INFINITY : M - ((float)bin - 0.0625f) / bscale;
@@ -922,11 +937,18 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
         __syncthreads();
         row_for_each<DT>(rowp, V, [&](int, float x) {
             const uint32_t k = fkey(x);
-            if (k >= floor_key && vbin(x) == bin) {
-                const int slot = atomicAdd(&S.nlist, 1);
-                if (slot < kGather) {
+            const bool hit = k >= floor_key && vbin(x) == bin;
+            const u64 m = __builtin_amdgcn_ballot_w64(hit);
+            if (m) {  // one atomic per wave and call
+                const int leader = __ffsll((long long)m) - 1;
+                int base = 0;
+                if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(&S.nlist, __popcll(m));
+                base = __builtin_amdgcn_readlane(base, leader);
+                const int slot = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                if (hit && slot < kGather) {
                     gkey[slot] = k;
-                    gw[slot] = weight(x);
+                    gw[slot] = local_w(x, bin);
                 }
             }
         });
@@ -950,14 +972,16 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
         } else {
             row_for_each<DT>(rowp, V, [&](int, float x) {
                 const uint32_t k = fkey(x);
-                if (k >= floor_key && vbin(x) == bin) count_digit(k, weight(x));
+                if (k >= floor_key && vbin(x) == bin) count_digit(k, local_w(x, bin));
             });
         }
         __syncthreads();
         // digits from the top: index i is digit 255 - i
         int di;
         u64 dsel, doth;
-        const u64 rest = by_count ? target - C : target - A;
+        // what is still needed, in count or in bin-local mass
+        const u64 rest = by_count ? (u64)(target - C)
+                                  : max(1ull, (u64)ceil((double)(target - A) / G) - A_in);
         if (by_count)
             wave_first_reach([&](int i) { return i < 256 ? (u64)S.bkey[255 - i] : 0ull; },
                              [&](int i) { return i < 256 ? S.bw[255 - i] : 0ull; }, rest, di, dsel, doth);
@@ -966,19 +990,19 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
                              [&](int i) { return i < 256 ? (u64)S.bkey[255 - i] : 0ull; }, rest, di, dsel, doth);
         if (di < 0) return r;  // cannot happen with consistent passes; the caller keeps the whole range
         const uint32_t d = 255u - (uint32_t)di;
-        A += by_count ? doth : dsel;
+        A_in += by_count ? doth : dsel;
         C += (uint32_t)(by_count ? dsel : doth);
         prefix |= d << shift;
         mask |= 0xFFu << shift;
         if (shift == 0) {
-            r.group = S.bw[d];
+            r.group = (u64)((double)S.bw[d] * G);
             r.cnt_group = S.bkey[d];
         }
         __syncthreads();  // every wave has read the digit histogram
     }
     r.ok = 1;
     r.key = prefix;
-    r.above = A;
+    r.above = A + (u64)((double)A_in * G);
     r.cnt_above = C;
     return r;
 }
@@ -1389,9 +1413,18 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                 if (threadIdx.x == 0) S.nlist = 0;
                 __syncthreads();
                 row_for_each<DT>(rowp, V, [&](int i, float x) {
-                    if (x >= thr) {
-                        const int p = atomicAdd(&S.nlist, 1);
-                        if (p < kListMax) S.u.list[p] = ((u64)__float_as_uint(x) << 32) | (uint32_t)i;
+                    // one atomic per wave and call: the first hit lane reserves
+                    // the wave's slots
+                    const bool hit = x >= thr;
+                    const u64 m = __builtin_amdgcn_ballot_w64(hit);
+                    if (m) {
+                        const int leader = __ffsll((long long)m) - 1;
+                        int base = 0;
+                        if ((int)(threadIdx.x & 63) == leader) base = atomicAdd(&S.nlist, __popcll(m));
+                        base = __builtin_amdgcn_readlane(base, leader);
+                        const int p = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                                                           __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+                        if (hit && p < kListMax) S.u.list[p] = ((u64)__float_as_uint(x) << 32) | (uint32_t)i;
                     }
                 });
                 __syncthreads();

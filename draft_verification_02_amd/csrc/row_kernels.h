@@ -316,6 +316,14 @@ struct RowStream {
 constexpr int kNB = 512;                 // value bins used to resolve filters
 constexpr int kBinMax = 512;             // largest bin resolved pairwise
 
+// Streaming statistics of one part of a row (rows split across workgroups).
+struct PartRec {
+    float m, k;  // maximum, power-of-two reference
+    double z;    // sum of 2^(x c - 8 k) over the part
+};
+constexpr int kPartTiles = 4;             // tiles of one part, loaded together
+constexpr int kMaxParts = 16;             // parts of one row at most
+
 struct RowArgs {
     Shape sh;
     float c_hi, c_lo;   // log2(e)/T = c_hi + c_lo to about 2^-48 relative, c_hi < log2(e)/T, c_lo > 0
@@ -330,6 +338,8 @@ struct RowArgs {
     uint2* kept;        // [n_trows][kListMax] (index, logit bits), ascending index
     int* kept_n;        // [n_trows]; -1 when the list was not stored
     float* kept_d;      // [n_trows][kListMax] draft logit of each listed token (rows with a draft row)
+    int parts;          // > 1: unfiltered rows split into this many parts (one workgroup each)
+    PartRec* prec;      // [rows][parts]
 };
 
 struct RowShared {
@@ -1505,8 +1515,96 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     }
 }
 
+// One part of an unfiltered row (few rows: each is split across `parts`
+// workgroups so that the whole GPU streams).  The part's up to kPartTiles
+// tiles are loaded together; its maximum and power-of-two sum go to prec and
+// k_row_merge combines the parts in order.
+template <int DT>
+__device__ __forceinline__ void row_part_plain(const RowArgs& a, RowShared& S, int row, int part) {
+    const char* rowp = row_ptr(a.sh, row);
+    const int V = a.sh.V;
+    const RowStream<DT> st(rowp, V);
+    constexpr int NL = RowStream<DT>::NL;
+    const int tpp = (st.nt + a.parts - 1) / a.parts;
+    const int t0 = part * tpp, n = max(0, min(st.nt, t0 + tpp) - t0);
+    float m_th = -INFINITY, k_th = -INFINITY;
+    double z_th = 0.0;
+    u32x4 raw[kPartTiles][NL];
+#pragma unroll
+    for (int i = 0; i < kPartTiles; ++i)
+        if (i < n) st.issue(t0 + i, raw[i]);
+#pragma unroll
+    for (int i = 0; i < kPartTiles; ++i) {
+        if (i < n) {
+            float v[kREPT];
+            st.unpack(t0 + i, raw[i], v);
+            float tm = v[0];
+#pragma unroll
+            for (int q = 1; q < kREPT; ++q) tm = fmaxf(tm, v[q]);
+            m_th = fmaxf(m_th, tm);
+            const float kt = ceilf(tm * a.c8);
+            if (kt > k_th) {
+                z_th = k_th == -INFINITY ? 0.0 : ldexp(z_th, (int)fmaxf(8.f * (k_th - kt), -4096.f));
+                k_th = kt;
+            }
+            if (k_th != -INFINITY) {
+                const float nmc = -8.f * k_th;
+                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < kREPT; ++q)
+                    acc[q & 3] += __builtin_amdgcn_exp2f(fmaf(v[q], a.c_lo, fmaf(v[q], a.c_hi, nmc)));
+                z_th += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
+            }
+        }
+    }
+    const RowTot tot = rb_row_totals(RowTot{m_th, k_th, z_th, 0ull}, S);
+    if (threadIdx.x == 0) a.prec[(size_t)row * a.parts + part] = PartRec{tot.m, tot.k, tot.z};
+}
+
+// The record of each split unfiltered row from its parts (combined in part
+// order): one thread per row.
+__global__ void __launch_bounds__(256) k_row_merge(RowArgs a) {
+    const int row = blockIdx.x * blockDim.x + threadIdx.x;
+    if (row >= a.sh.n_trows + a.sh.n_drows) return;
+    RowTot t{-INFINITY, -INFINITY, 0.0, 0ull};
+    for (int p = 0; p < a.parts; ++p) {
+        const PartRec q = a.prec[(size_t)row * a.parts + p];
+        t = row_tot_combine(t, RowTot{q.m, q.k, q.z, 0ull});
+    }
+    const float M = t.m;
+    const double Z = t.k != -INFINITY ? t.z * exp2(8.0 * (double)t.k - (double)M * a.c64) : 0.0;
+    const int V = a.sh.V;
+    RowRec r;
+    r.s.max_logit = M;
+    r.z_all = Z;
+    r.pad = 0.0;
+    r.s.thresh = -INFINITY;
+    r.s.n_kept = V;
+    r.s.flags = 0;
+    r.s.z_kept = Z;
+    double prob = __longlong_as_double(0x7FF8000000000000LL);  // NaN: no drafted token
+    if (row_has_token(a.sh, row)) {
+        prob = 0.0;
+        const int d_tok = row_token(a.sh, row);
+        if (d_tok >= 0 && d_tok < V) {
+            const float xd = load_logit(row_ptr(a.sh, row), row_dt(a.sh, row), d_tok);
+            prob = exp(((double)xd - (double)M) * a.inv_T) / Z;
+        }
+    }
+    r.s.prob_at_token = prob;
+    a.rec[row] = r;
+}
+
 __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
     __shared__ RowShared S;
+    if (a.parts > 1) {
+        const int row = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
+        if (row_dt(a.sh, row) == DT_BF16)
+            row_part_plain<DT_BF16>(a, S, row, part);
+        else
+            row_part_plain<DT_F32>(a, S, row, part);
+        return;
+    }
     const int row = blockIdx.x;
     const bool bf = row_dt(a.sh, row) == DT_BF16;
     if (a.use_k) {

@@ -29,6 +29,7 @@ struct Workspace {
     float* kept_d = nullptr;
     int32_t* gidx = nullptr;
     double2* chunk_sum = nullptr;
+    PartRec* prec = nullptr;
 };
 
 std::mutex g_mu;
@@ -58,6 +59,7 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     const size_t o_kd = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(float));
     const size_t o_g = off; off = align_up(off + nw.cap_trows * sizeof(int32_t));
     const size_t o_cs = off; off = align_up(off + nw.cap_chunks * sizeof(double2));
+    const size_t o_pr = off; off = align_up(off + nw.cap_rows * (size_t)kMaxParts * sizeof(PartRec));
     if (w.base) {
         // the old buffer may still be in use by work queued on this stream
         if (hipStreamSynchronize(stream) != hipSuccess) return SPEC_E_LAUNCH;
@@ -72,6 +74,7 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     nw.kept_d = reinterpret_cast<float*>(b + o_kd);
     nw.gidx = reinterpret_cast<int32_t*>(b + o_g);
     nw.chunk_sum = reinterpret_cast<double2*>(b + o_cs);
+    nw.prec = reinterpret_cast<PartRec*>(b + o_pr);
     w = nw;
     *out = &w;
     return SPEC_OK;
@@ -181,13 +184,27 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     ra.kept = ws->kept;
     ra.kept_n = ws->kept_n;
     ra.kept_d = ws->kept_d;
+    // Few unfiltered rows: split each across workgroups (at most kPartTiles
+    // tiles each) so that about 512 workgroups stream, then merge per row.
+    ra.parts = 1;
+    ra.prec = ws->prec;
+    if (!filtered) {
+        const int nt = (int)ceil_div(V, kRTile);
+        const int want = (int)std::min<long long>(kMaxParts, ceil_div(512, rows));
+        const int tpp = (int)ceil_div(nt, std::max(1, want));
+        if (want > 1 && tpp <= kPartTiles) ra.parts = (int)ceil_div(nt, tpp);
+    }
 
     void *evb, *eva;
     take_events(&evb, &eva);
     if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
-    hipLaunchKernelGGL(k_row, dim3(rows), dim3(kRB), 0, stream, ra);
+    hipLaunchKernelGGL(k_row, dim3((unsigned)((long long)rows * ra.parts)), dim3(kRB), 0, stream, ra);
     if ((rc = launch_status())) return rc;
     if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
+    if (ra.parts > 1) {
+        hipLaunchKernelGGL(k_row_merge, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, stream, ra);
+        if ((rc = launch_status())) return rc;
+    }
 
     SeqArgs sa;
     sa.sh = sh;

@@ -338,6 +338,7 @@ struct RowArgs {
     uint2* kept;        // [n_trows][kListMax] (index, logit bits), ascending index
     int* kept_n;        // [n_trows]; -1 when the list was not stored
     float* kept_d;      // [n_trows][kListMax] draft logit of each listed token (rows with a draft row)
+    double* kept_p;     // [n_trows][kListMax] p of each listed token
     int parts;          // > 1: unfiltered rows split into this many parts (one workgroup each)
     PartRec* prec;      // [rows][parts]
 };
@@ -1286,16 +1287,20 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             const int list_n = (n_kept <= kListMax && st.nt <= kNB) ? n_kept : -1;
             const uint32_t tk = fkey(thr);
             uint2* out = a.kept + (size_t)row * kListMax;
-            // With a draft row at this position, each listed token also gets
-            // the draft's logit, read now (this row has slack before the
-            // draft rows finish), so the draw needs no gather of its own.
+            // Each listed token also gets its probability p and, with a draft
+            // row at this position, the draft's logit, read now (this row has
+            // slack before the draft rows finish), so the draw needs neither
+            // an exp for p nor a gather of its own.
             const int kpos_row = row % (a.sh.K + 1);
             const bool with_draft = kpos_row < a.sh.K;
             const char* dp = with_draft ? row_ptr(a.sh, a.sh.n_trows + (row / (a.sh.K + 1)) * a.sh.K + kpos_row)
                                         : nullptr;
             float* outd = a.kept_d + (size_t)row * kListMax;
+            double* outp = a.kept_p + (size_t)row * kListMax;
+            const double inv_zk = 1.0 / z_kept;
             auto emit = [&](int rank, uint32_t idx, uint32_t bits) {
                 out[rank] = make_uint2(idx, bits);
+                outp[rank] = exp(((double)__uint_as_float(bits) - (double)M) * a.inv_T) * inv_zk;
                 if (with_draft) outd[rank] = load_logit(dp, a.sh.ddt, idx);
             };
             // Tokens come in blocks of 64 groups (64 * per tokens) that each

@@ -30,6 +30,7 @@ struct SeqArgs {
     const uint2* kept;
     const int* kept_n;
     const float* kept_d;  // draft logit of each listed token (stop positions j < K)
+    const double* kept_p; // p of each listed token
     double2* chunk_sum;   // [B][n_chunks] (.x residual, .y p)
     int n_chunks;
     int32_t* out_tokens;
@@ -270,7 +271,7 @@ __device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, i
 // Filtered: one workgroup per (sequence, candidate stop position j).  Every
 // workgroup loads, in one round, the accept-test inputs of its sequence, the
 // records of row pair j and the first kSpec entries of target row j's kept
-// list with the draft logits the row kernel stored beside them; the
+// list with the p values and draft logits the row kernel stored beside them; the
 // workgroup whose j is the stop position then draws, the others exit.  So
 // one dependent memory round separates the row kernel from the output.
 // ---------------------------------------------------------------------------
@@ -319,13 +320,18 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     uint2 ent[kLPT];
 #pragma unroll
     for (int e = 0; e < kLPT; ++e) ent[e] = L[threadIdx.x * kLPT + e];
-    // the draft logits of the listed tokens, stored beside the list by the
-    // row kernel (positions j < K)
+    // p and the draft logits of the listed tokens, stored beside the list by
+    // the row kernel (draft logits for positions j < K)
     float xdl[kLPT];
+    double pl[kLPT];
     {
         const float* LD = a.kept_d + (size_t)rt * kListMax;
+        const double* LP = a.kept_p + (size_t)rt * kListMax;
 #pragma unroll
-        for (int e = 0; e < kLPT; ++e) xdl[e] = LD[threadIdx.x * kLPT + e];
+        for (int e = 0; e < kLPT; ++e) {
+            xdl[e] = LD[threadIdx.x * kLPT + e];
+            pl[e] = LP[threadIdx.x * kLPT + e];
+        }
     }
     const StopRow s = stop_row(a, b, jc);
     // the accepted drafted tokens, one per thread, for the output row
@@ -344,15 +350,12 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         draw_long_list(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
         return;
     }
-    const double inv_zt = 1.0 / s.zt, inv_zd = 1.0 / s.zd;
+    const double inv_zd = 1.0 / s.zd;
     double pr[kLPT], rr[kLPT];
     double sr = 0.0, sp = 0.0;
 #pragma unroll
     for (int e = 0; e < kLPT; ++e) {
-        const float xt = __uint_as_float(ent[e].y);
-        pr[e] = (threadIdx.x * kLPT + e < n && xt >= s.thr_t)
-                    ? exp(((double)xt - (double)s.Mt) * a.inv_T) * inv_zt
-                    : 0.0;
+        pr[e] = threadIdx.x * kLPT + e < n ? pl[e] : 0.0;
         sp += pr[e];
     }
 #pragma unroll

@@ -16,7 +16,7 @@ namespace {
 using namespace sv;
 
 // Library-owned scratch for one (device, stream): row records, kept lists of
-// filtered target rows (with the draft logit of each listed token), greedy
+// filtered target rows (with p and the draft logit of each listed token), greedy
 // argmax indices and draw chunk sums.  Every
 // kernel writes what it later reads within the same call, so nothing needs
 // clearing between calls.
@@ -27,6 +27,7 @@ struct Workspace {
     uint2* kept = nullptr;
     int* kept_n = nullptr;
     float* kept_d = nullptr;
+    double* kept_p = nullptr;
     int32_t* gidx = nullptr;
     double2* chunk_sum = nullptr;
     PartRec* prec = nullptr;
@@ -57,6 +58,7 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     const size_t o_kept = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(uint2));
     const size_t o_kn = off; off = align_up(off + nw.cap_trows * sizeof(int));
     const size_t o_kd = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(float));
+    const size_t o_kp = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(double));
     const size_t o_g = off; off = align_up(off + nw.cap_trows * sizeof(int32_t));
     const size_t o_cs = off; off = align_up(off + nw.cap_chunks * sizeof(double2));
     const size_t o_pr = off; off = align_up(off + nw.cap_rows * (size_t)kMaxParts * sizeof(PartRec));
@@ -72,6 +74,7 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     nw.kept = reinterpret_cast<uint2*>(b + o_kept);
     nw.kept_n = reinterpret_cast<int*>(b + o_kn);
     nw.kept_d = reinterpret_cast<float*>(b + o_kd);
+    nw.kept_p = reinterpret_cast<double*>(b + o_kp);
     nw.gidx = reinterpret_cast<int32_t*>(b + o_g);
     nw.chunk_sum = reinterpret_cast<double2*>(b + o_cs);
     nw.prec = reinterpret_cast<PartRec*>(b + o_pr);
@@ -184,6 +187,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     ra.kept = ws->kept;
     ra.kept_n = ws->kept_n;
     ra.kept_d = ws->kept_d;
+    ra.kept_p = ws->kept_p;
     // Few unfiltered rows: split each across workgroups (at most kPartTiles
     // tiles each) so that about 512 workgroups stream, then merge per row.
     ra.parts = 1;
@@ -214,6 +218,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     sa.kept = ws->kept;
     sa.kept_n = ws->kept_n;
     sa.kept_d = ws->kept_d;
+    sa.kept_p = ws->kept_p;
     sa.chunk_sum = ws->chunk_sum;
     sa.n_chunks = n_chunks;
     sa.out_tokens = out_tokens;

@@ -1,6 +1,7 @@
 // spec_verify.hip — C-ABI entry points of the verification library: argument
 // checks, per-(device, stream) workspace, kernel launches.
 #include <hip/hip_runtime.h>
+#include <hip/hip_ext.h>
 
 #include <cmath>
 #include <cstring>
@@ -201,10 +202,11 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
 
     void *evb, *eva;
     take_events(&evb, &eva);
-    if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
-    hipLaunchKernelGGL(k_row, dim3((unsigned)((long long)rows * ra.parts)), dim3(kRB), 0, stream, ra);
+    // with a measurement pair, the events are attached to the dispatch itself
+    // (start and end of the kernel, no packets of their own around it)
+    hipExtLaunchKernelGGL(k_row, dim3((unsigned)((long long)rows * ra.parts)), dim3(kRB), 0, stream,
+                          static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, ra);
     if ((rc = launch_status())) return rc;
-    if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
     if (ra.parts > 1) {
         hipLaunchKernelGGL(k_row_merge, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, stream, ra);
         if ((rc = launch_status())) return rc;

@@ -363,7 +363,10 @@ struct RowShared {
     u64 red_u[kRW];
     int red_i[kRW];
     uint32_t red_k[kRW];
-    float red_kf[kRW];
+    double tot_z[kRW];        // the row totals, per wave (one exchange per workgroup)
+    u64 tot_c[kRW];
+    float tot_m[kRW];
+    float tot_k[kRW];
     int nbin;
     int nbin2[2];             // gather counters of the two bin resolutions
     int nlist;
@@ -503,53 +506,62 @@ __device__ __forceinline__ void capture_units(RowShared& S, const u32x4 (&unit)[
 // logit >= tau of every captured group, as (logit bits << 32) | index,
 // appended in segment order (unit lane + 64 i: i, then lane, which is
 // ascending token index) to the wave's own region S.cand[wave * kCW, ...)
-// after its first `base` entries.  One unit per lane at a time, so that it
-// needs few registers.  Candidates past kCW, and the values that are no
-// candidates, go to the lane's scratch slot, so nothing branches.  Returns
-// the wave's candidate count (uniform, base included) with bit 32 set when
-// the segment or the region overflowed.
+// after its first `base` entries.  Every lane reads all kUPL of its unit
+// slots at once (slots past the fill hold stale bytes and count no hits), so
+// the reads and the kUPL hit scans overlap instead of running one after the
+// other.  Candidates past kCW, and the values that are no candidates, go to
+// the lane's scratch slot, so nothing branches per lane.  Returns the wave's
+// candidate count (uniform, base included) with bit 32 set when the segment
+// or the region overflowed.
 template <int DT>
 __device__ __forceinline__ u64 wave_expand(RowShared& S, int V, float tau, int fill, int ovf, int base) {
     constexpr int per = RowStream<DT>::per;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     u64* region = S.cand + wave * kCW;
+    u32x4 ur[kUPL];
+    uint32_t ug[kUPL];
+#pragma unroll
+    for (int i = 0; i < kUPL; ++i) {
+        ur[i] = S.u.st.raw[wave * kSegU + lane + 64 * i];
+        ug[i] = S.u.st.grp[wave * kSegU + lane + 64 * i];
+    }
+    int lim[kUPL], c[kUPL], incl[kUPL];
+#pragma unroll
+    for (int i = 0; i < kUPL; ++i) {
+        lim[i] = lane + 64 * i < fill ? V - (int)ug[i] * per : 0;  // slots of the unit inside the row
+        c[i] = 0;
+#pragma unroll
+        for (int q = 0; q < per; ++q) c[i] += (q < lim[i] && RowStream<DT>::unit_value(ur[i], q) >= tau) ? 1 : 0;
+    }
+#pragma unroll
+    for (int i = 0; i < kUPL; ++i) incl[i] = wave_incl_scan(c[i]);
     int n = base;
 #pragma unroll
     for (int i = 0; i < kUPL; ++i) {
-        if (64 * i < fill) {  // uniform: some lane of the wave holds unit i
-            const int k = lane + 64 * i;
-            u32x4 ur = u32x4{0u, 0u, 0u, 0u};
-            uint32_t ug = 0u;
-            int lim = 0;
-            if (k < fill) {
-                ur = S.u.st.raw[wave * kSegU + k];
-                ug = S.u.st.grp[wave * kSegU + k];
-                lim = V - (int)ug * per;  // slots of the unit inside the row
-            }
-            int c = 0;
-#pragma unroll
-            for (int q = 0; q < per; ++q) c += (q < lim && RowStream<DT>::unit_value(ur, q) >= tau) ? 1 : 0;
-            const int incl = wave_incl_scan(c);
-            int p = n + incl - c;
-            n += lane_read(incl, 63);
+        const int ti = lane_read(incl[i], 63);
+        if (ti > 0) {  // uniform
+            int p = n + incl[i] - c[i];
 #pragma unroll
             for (int q = 0; q < per; ++q) {
-                const float x = RowStream<DT>::unit_value(ur, q);
-                const bool hit = q < lim && x >= tau;
+                const float x = RowStream<DT>::unit_value(ur[i], q);
+                const bool hit = q < lim[i] && x >= tau;
                 u64* slot = (hit && p < kCW) ? region + p : S.cand + kCap + lane;
-                *slot = ((u64)__float_as_uint(x) << 32) | (ug * per + q);
+                *slot = ((u64)__float_as_uint(x) << 32) | (ug[i] * per + q);
                 p += hit ? 1 : 0;
             }
         }
+        n += ti;
     }
     return (u64)min(n, kCW) | ((u64)((n > kCW ? 1 : 0) | ovf) << 32);
 }
 
-// A row's totals, combined over the block in one exchange: the largest
-// logit, the per-thread sums taken to the largest grid reference k (exact
-// power-of-two rescales) and added, and a 64-bit count.  Every combine step
-// is commutative, so the butterfly leaves the same value in every lane and
-// the result does not depend on timing.
+// A row's totals: the largest logit, the per-thread sums taken to the
+// largest grid reference k (exact power-of-two rescales) and added, and the
+// sum of one 64-bit count per wave (lane 0's).  Inside a wave: the maxima
+// first, then every sum rescaled to the wave's k and added in a fixed
+// pattern; across waves the same in wave order, so the result does not
+// depend on timing.  One barrier, on slots of its own: at most one call per
+// workgroup.
 struct RowTot {
     float m, k;
     double z;
@@ -565,30 +577,33 @@ __device__ __forceinline__ RowTot row_tot_combine(const RowTot& a, const RowTot&
     r.c = a.c + b.c;
     return r;
 }
+__device__ __forceinline__ double z_to_ref(double z, float k, float kr) {
+    return k == -INFINITY ? 0.0 : ldexp(z, (int)fmaxf(8.f * (k - kr), -4096.f));
+}
 __device__ __forceinline__ RowTot rb_row_totals(RowTot t, RowShared& S) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    auto step = [&](RowTot o) { t = row_tot_combine(t, o); };
-    step(RowTot{dpp_move<kDppQuadXor1>(t.m), dpp_move<kDppQuadXor1>(t.k), dpp_move<kDppQuadXor1>(t.z),
-                dpp_move<kDppQuadXor1>(t.c)});
-    step(RowTot{dpp_move<kDppQuadXor2>(t.m), dpp_move<kDppQuadXor2>(t.k), dpp_move<kDppQuadXor2>(t.z),
-                dpp_move<kDppQuadXor2>(t.c)});
-    step(RowTot{dpp_move<kDppRowHalfMirror>(t.m), dpp_move<kDppRowHalfMirror>(t.k),
-                dpp_move<kDppRowHalfMirror>(t.z), dpp_move<kDppRowHalfMirror>(t.c)});
-    step(RowTot{dpp_move<kDppRowMirror>(t.m), dpp_move<kDppRowMirror>(t.k), dpp_move<kDppRowMirror>(t.z),
-                dpp_move<kDppRowMirror>(t.c)});
-    auto row = [&](int l) { return RowTot{lane_read(t.m, l), lane_read(t.k, l), lane_read(t.z, l), lane_read(t.c, l)}; };
-    t = row_tot_combine(row_tot_combine(row(0), row(16)), row_tot_combine(row(32), row(48)));
-    __syncthreads();
+    const float wm = wave_max(t.m);
+    const float wk = wave_max(t.k);
+    const double wz = wave_sum(z_to_ref(t.z, t.k, wk));
     if (lane == 0) {
-        S.red_f[wave] = t.m;
-        S.red_kf[wave] = t.k;
-        S.red_d[wave] = t.z;
-        S.red_u[wave] = t.c;
+        S.tot_m[wave] = wm;
+        S.tot_k[wave] = wk;
+        S.tot_z[wave] = wz;
+        S.tot_c[wave] = t.c;
     }
     __syncthreads();
-    RowTot r{S.red_f[0], S.red_kf[0], S.red_d[0], S.red_u[0]};
+    RowTot r{S.tot_m[0], S.tot_k[0], 0.0, S.tot_c[0]};
 #pragma unroll
-    for (int w = 1; w < kRW; ++w) r = row_tot_combine(r, RowTot{S.red_f[w], S.red_kf[w], S.red_d[w], S.red_u[w]});
+    for (int w = 1; w < kRW; ++w) {
+        r.m = fmaxf(r.m, S.tot_m[w]);
+        r.k = fmaxf(r.k, S.tot_k[w]);
+        r.c += S.tot_c[w];
+    }
+    double zs[kRW];
+#pragma unroll
+    for (int w = 0; w < kRW; ++w) zs[w] = z_to_ref(S.tot_z[w], S.tot_k[w], r.k);
+    static_assert(kRW == 8, "the cross-wave sum is written for eight waves");
+    r.z = ((zs[0] + zs[1]) + (zs[2] + zs[3])) + ((zs[4] + zs[5]) + (zs[6] + zs[7]));
     return r;
 }
 
@@ -1206,9 +1221,9 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         expand_now();
         n_own = min(kOwn, max(0, (n_w - (int)(threadIdx.x & 63) + 63) / 64));
         // one contribution per wave: count | overflow << 32
-        cflags = (threadIdx.x & 63) == 0 ? ((u64)n_w | ((u64)(ovf ? 1 : 0) << 32)) : 0ull;
+        cflags = (u64)n_w | ((u64)(ovf ? 1 : 0) << 32);
     }
-    // the barriers of the block totals also end every wave's use of its segment
+    // the barrier of the block totals also ends every wave's use of its segment
     const RowTot tot =
         rb_row_totals(RowTot{MODE == MODE_TOPK ? m_run : m_th, kSum ? k_th : -INFINITY, z_th, cflags}, S);
     const float M = tot.m;

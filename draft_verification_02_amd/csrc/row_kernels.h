@@ -36,7 +36,6 @@ constexpr int kREPT = 16;                // logits per thread per tile
 constexpr int kRTile = kRB * kREPT;      // 8192 logits per tile
 constexpr int kSegU = 256;               // captured 16-byte units per wave segment
 constexpr int kUnits = kSegU * kRW;      // 2048 units per workgroup
-constexpr int kUPL = kSegU / 64;         // units per lane when a wave expands its segment
 constexpr int kCW = 320;                 // candidates (logit, index) per wave after expansion
 constexpr int kCap = kCW * kRW;          // candidates per workgroup (2560)
 constexpr int kOwn = (kCW + 63) / 64;    // candidates per thread during resolution (5)
@@ -371,6 +370,12 @@ struct RowShared {
     int nbin2[2];             // gather counters of the two bin resolutions
     int nlist;
     int ibin;
+    u64 bc_u[2];              // results handed from wave 0 to the others
+    u64 bc_m;
+    double side_zs;           // wave 1's side results of the resolution
+    double side_pt;
+    uint32_t bc_k[2];
+    int bc_i;
     u64 ubefore;
     uint32_t cbefore;
 };
@@ -502,55 +507,37 @@ __device__ __forceinline__ void capture_units(RowShared& S, const u32x4 (&unit)[
     ovf = __builtin_amdgcn_readfirstlane(ok ? ovf : 1);
 }
 
-// Expands the units [0, fill) of this wave's segment into candidates, every
-// logit >= tau of every captured group, as (logit bits << 32) | index,
-// appended in segment order (unit lane + 64 i: i, then lane, which is
+// Expands the units [from, min(from + 64, fill)) of this wave's segment into
+// candidates, every logit >= tau of every captured group, as (logit bits <<
+// 32) | index, appended in segment order (one unit per lane, lane order is
 // ascending token index) to the wave's own region S.cand[wave * kCW, ...)
-// after its first `base` entries.  Every lane reads all kUPL of its unit
-// slots at once (slots past the fill hold stale bytes and count no hits), so
-// the reads and the kUPL hit scans overlap instead of running one after the
-// other.  Candidates past kCW, and the values that are no candidates, go to
-// the lane's scratch slot, so nothing branches per lane.  Returns the wave's
-// candidate count (uniform, base included) with bit 32 set when the segment
-// or the region overflowed.
+// after its first `base` entries.  Candidates past kCW, and the values that
+// are no candidates, go to the lane's scratch slot, so nothing branches per
+// lane.  Returns the wave's candidate count (uniform, base included) with bit
+// 32 set when the segment or the region overflowed.
 template <int DT>
-__device__ __forceinline__ u64 wave_expand(RowShared& S, int V, float tau, int fill, int ovf, int base) {
+__device__ __forceinline__ u64 wave_expand(RowShared& S, int V, float tau, int from, int fill, int ovf, int base) {
     constexpr int per = RowStream<DT>::per;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     u64* region = S.cand + wave * kCW;
-    u32x4 ur[kUPL];
-    uint32_t ug[kUPL];
+    // a slot past the fill holds stale bytes and counts no hits
+    const int k = wave * kSegU + min(from + lane, kSegU - 1);
+    const u32x4 ur = S.u.st.raw[k];
+    const uint32_t ug = S.u.st.grp[k];
+    const int lim = from + lane < fill ? V - (int)ug * per : 0;  // slots of the unit inside the row
+    int c = 0;
 #pragma unroll
-    for (int i = 0; i < kUPL; ++i) {
-        ur[i] = S.u.st.raw[wave * kSegU + lane + 64 * i];
-        ug[i] = S.u.st.grp[wave * kSegU + lane + 64 * i];
-    }
-    int lim[kUPL], c[kUPL], incl[kUPL];
+    for (int q = 0; q < per; ++q) c += (q < lim && RowStream<DT>::unit_value(ur, q) >= tau) ? 1 : 0;
+    const int incl = wave_incl_scan(c);
+    const int n = base + lane_read(incl, 63);
+    int p = base + incl - c;
 #pragma unroll
-    for (int i = 0; i < kUPL; ++i) {
-        lim[i] = lane + 64 * i < fill ? V - (int)ug[i] * per : 0;  // slots of the unit inside the row
-        c[i] = 0;
-#pragma unroll
-        for (int q = 0; q < per; ++q) c[i] += (q < lim[i] && RowStream<DT>::unit_value(ur[i], q) >= tau) ? 1 : 0;
-    }
-#pragma unroll
-    for (int i = 0; i < kUPL; ++i) incl[i] = wave_incl_scan(c[i]);
-    int n = base;
-#pragma unroll
-    for (int i = 0; i < kUPL; ++i) {
-        const int ti = lane_read(incl[i], 63);
-        if (ti > 0) {  // uniform
-            int p = n + incl[i] - c[i];
-#pragma unroll
-            for (int q = 0; q < per; ++q) {
-                const float x = RowStream<DT>::unit_value(ur[i], q);
-                const bool hit = q < lim[i] && x >= tau;
-                u64* slot = (hit && p < kCW) ? region + p : S.cand + kCap + lane;
-                *slot = ((u64)__float_as_uint(x) << 32) | (ug[i] * per + q);
-                p += hit ? 1 : 0;
-            }
-        }
-        n += ti;
+    for (int q = 0; q < per; ++q) {
+        const float x = RowStream<DT>::unit_value(ur, q);
+        const bool hit = q < lim && x >= tau;
+        u64* slot = (hit && p < kCW) ? region + p : S.cand + kCap + lane;
+        *slot = ((u64)__float_as_uint(x) << 32) | (ug * per + q);
+        p += hit ? 1 : 0;
     }
     return (u64)min(n, kCW) | ((u64)((n > kCW ? 1 : 0) | ovf) << 32);
 }
@@ -655,54 +642,95 @@ __device__ __forceinline__ u64 grid_weight(float x, float kref, double c, int fx
 // its wave's candidates lane + 64 i) hold every logit >= the capture threshold.
 // Masses are in units of 2^(8 kref) / scale (Zg: the row sum in units of
 // 2^(8 kref)); z_kept is returned in units of 2^(8 kref).  Returns false when the candidates
-// cannot decide (the caller then re-reads the row).
+// cannot decide (the caller then re-reads the row).  `side` runs once on
+// wave 1 while wave 0 scans the bins, ahead of a barrier.
 //
 // The candidates are binned by value (kNB bins over [lo, M]) with their
-// count and fixed-point mass.  Every wave scans the bins itself, so the
-// crossing bin needs no broadcast; inside that bin the entries are gathered
-// and every entry learns the count and mass of the bin's entries with a
-// strictly larger key (within one wave when the bin holds at most 64).
-// The bins and the gather counters were cleared when the row started.
+// count and fixed-point mass.  Wave 0 scans the bins for the crossing bin
+// and hands it to the others through LDS (the scan is VALU work that eight
+// waves, two to a SIMD, would repeat for nothing); inside that bin the
+// entries are gathered and every entry learns the count and mass of the
+// bin's entries with a strictly larger key (wave 0 alone when the bin holds
+// at most 64).  The bins and the gather counters were cleared when the row
+// started.
+template <int DT, class Side>
 __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S, float M, float kref, double Zg,
                                                   int n_own, float tau, double scale, uint32_t& thr_key,
-                                                  double& z_kept, int& n_kept) {
+                                                  double& z_kept, int& n_kept, Side&& side) {
     const int tid = threadIdx.x, lane = tid & 63;
     const u64* mine = S.cand + (tid >> 6) * kCW + lane;  // this thread's candidates: mine[64 i], i < n_own
     uint32_t key[kOwn];
     u64 wt[kOwn];
     int bin[kOwn];
     float xmin = INFINITY;
+    // every slot is read (those past n_own hold stale entries of the region
+    // and are not used), so the reads need no branches and go out together
+    u64 ent[kOwn];
+#pragma unroll
+    for (int i = 0; i < kOwn; ++i) ent[i] = mine[64 * i];
+    // Straight-line over all slots (unused ones on a stand-in value), so the
+    // slots' weight computations overlap.
 #pragma unroll
     for (int i = 0; i < kOwn; ++i) {
-        key[i] = 0u;
-        wt[i] = 0ull;
-        if (i < n_own) {
-            const float x = __uint_as_float((uint32_t)(mine[64 * i] >> 32));
-            key[i] = fkey(x);
-            wt[i] = grid_weight(x, kref, a.c64, a.fx_shift);
-            xmin = fminf(xmin, x);
-        }
+        const bool use = i < n_own;
+        const float x = use ? __uint_as_float((uint32_t)(ent[i] >> 32)) : M;
+        key[i] = use ? fkey(x) : 0u;
+        wt[i] = use ? grid_weight(x, kref, a.c64, a.fx_shift) : 0ull;
+        xmin = use ? fminf(xmin, x) : xmin;
     }
     // every candidate is >= tau; a row captured whole has tau = -inf
     const float lo = tau != -INFINITY ? tau : rb_min(xmin, S.red_f);
     const float span = M - lo;
     const float bscale = span > 0.f ? (float)(kNB - 1) / span : 0.f;
 #pragma unroll
+    for (int i = 0; i < kOwn; ++i)
+        bin[i] = i < n_own ? min(kNB - 1, (int)((M - key_to_float(key[i])) * bscale)) : kNB;
+#pragma unroll
     for (int i = 0; i < kOwn; ++i) {
-        bin[i] = kNB;
         if (i < n_own) {
-            bin[i] = min(kNB - 1, (int)((M - key_to_float(key[i])) * bscale));
             atomicAdd(&S.hc[bin[i]], 1u);
             atomicAdd(&S.hm[bin[i]], wt[i]);
         }
     }
     __syncthreads();
 
-    // Exact decision inside bin b (entries with key >= floor_key): kept
-    // <=> base + (count or mass of the bin's entries with a larger key) <
-    // limit.  Returns the smallest kept key, the kept count and mass.
-    auto resolve_bin = [&](int b, int call, uint32_t floor_key, u64 base, bool by_count, u64 limit,
-                           uint32_t& kmin, uint32_t& kcnt, u64& kmass) -> bool {
+    // A bin of a bf16 row whose value range (widened by a quarter bin, far
+    // beyond the rounding of the bin arithmetic) holds one bf16 value at or
+    // above floor_key holds one key: its entries all tie.  bf16 keys are
+    // t << 16 | (t >= 0x8000 ? 0 : 0xFFFF), increasing in t.
+    auto single_key = [&](int b, uint32_t floor_key, uint32_t& kk) -> bool {
+        if (DT != DT_BF16 || b >= kNB - 1 || !(bscale > 0.f)) return false;
+        const float w = 1.f / bscale;
+        if (!(w > 0x1p-16f * fabsf(M))) return false;
+        auto k16 = [](uint32_t t) { return (t << 16) | (t >= 0x8000u ? 0u : 0xFFFFu); };
+        const uint32_t klo = max(fkey(M - ((float)b + 1.25f) * w), floor_key);
+        const uint32_t khi = b == 0 ? 0xFFFFFFFFu : fkey(M - ((float)b - 0.25f) * w);
+        uint32_t tl = klo >> 16, th = khi >> 16;
+        if (k16(tl) < klo) ++tl;
+        if (k16(th) > khi) {
+            if (th == 0u) return false;
+            --th;
+        }
+        if (tl != th) return false;
+        kk = k16(tl);
+        return true;
+    };
+    // Exact decision inside bin b (entries with key >= floor_key, bcnt of
+    // them with mass bmass): kept <=> base + (count or mass of the bin's
+    // entries with a larger key) < limit.  The bin is the first to reach the
+    // limit, so base < limit: tied entries are all kept.  Returns the
+    // smallest kept key, the kept count and mass.
+    auto resolve_bin = [&](int b, int call, uint32_t floor_key, u64 base, bool by_count, u64 limit, uint32_t bcnt,
+                           u64 bmass, uint32_t& kmin, uint32_t& kcnt, u64& kmass) -> bool {
+        {
+            uint32_t kk;
+            if (single_key(b, floor_key, kk)) {
+                kmin = kk;
+                kcnt = bcnt;
+                kmass = bmass;
+                return true;
+            }
+        }
         // gather (contention only among the bin's own entries)
         u64* bw = call == 0 ? S.bw : S.bw + kBinMax / 2;
         uint32_t* bk = call == 0 ? S.bkey : S.bkey + kBinMax / 2;
@@ -721,21 +749,35 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         const int nb = S.nbin2[call];
         if (nb > cap) return false;
         if (nb <= 64) {
-            // one entry per lane; every wave computes the same result
-            const uint32_t k = lane < nb ? bk[lane] : 0u;
-            const u64 w = lane < nb ? bw[lane] : 0ull;
-            uint32_t cgt = 0u;
-            u64 mgt = 0ull;
-            for (int jj = 0; jj < nb; ++jj) {
-                const uint32_t kj = lane_read(k, jj);
-                const u64 wj = lane_read(w, jj);
-                cgt += kj > k ? 1u : 0u;
-                mgt += kj > k ? wj : 0ull;
+            // one entry per lane of wave 0, which hands the result on
+            if (tid < 64) {
+                const uint32_t k = lane < nb ? bk[lane] : 0u;
+                const u64 w = lane < nb ? bw[lane] : 0ull;
+                uint32_t cgt = 0u;
+                u64 mgt = 0ull;
+                for (int jj = 0; jj < nb; ++jj) {
+                    const uint32_t kj = lane_read(k, jj);
+                    const u64 wj = lane_read(w, jj);
+                    cgt += kj > k ? 1u : 0u;
+                    mgt += kj > k ? wj : 0ull;
+                }
+                const bool kept = lane < nb && (by_count ? base + cgt < limit : base + mgt < limit);
+                const uint32_t c = (uint32_t)__popcll(__ballot(kept));
+                const u64 m = wave_allreduce(kept ? w : 0ull, [](u64 x, u64 y) { return x + y; });
+                const uint32_t mn =
+                    wave_allreduce(kept ? k : 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+                if (tid == 0) {
+                    S.bc_m = m;
+                    S.bc_k[0] = c;
+                    S.bc_k[1] = mn;
+                }
             }
-            const bool kept = lane < nb && (by_count ? base + cgt < limit : base + mgt < limit);
-            kcnt = (uint32_t)__popcll(__ballot(kept));
-            kmass = wave_allreduce(kept ? w : 0ull, [](u64 x, u64 y) { return x + y; });
-            kmin = wave_allreduce(kept ? k : 0xFFFFFFFFu, [](uint32_t x, uint32_t y) { return x < y ? x : y; });
+            __syncthreads();
+            // (the next write to these slots follows the barriers of the next
+            // crossing-bin search)
+            kmass = S.bc_m;
+            kcnt = S.bc_k[0];
+            kmin = S.bc_k[1];
             return true;
         }
         uint32_t my_c = 0u;
@@ -771,11 +813,32 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     uint32_t tau_k = 0u, in_k_cnt = 0u;
     u64 in_k_mass = 0ull;
     u64 cb_k = 0ull, mb_k = 0ull;
+    // wave 0 finds the crossing bin; the others take it from LDS (wave 1
+    // runs `side` meanwhile, once)
+    bool side_done = false;
+    auto find_bcast = [&](auto&& va, auto&& vb, u64 target, int& b, u64& before_a, u64& before_b) {
+        if (!side_done && (tid >> 6) == 1) side();
+        side_done = true;
+        if (tid < 64) {
+            wave_first_reach(va, vb, target, b, before_a, before_b);
+            if (tid == 0) {
+                S.bc_i = b;
+                S.bc_u[0] = before_a;
+                S.bc_u[1] = before_b;
+            }
+        }
+        __syncthreads();
+        // (the next write to these slots follows a barrier of resolve_bin)
+        b = S.bc_i;
+        before_a = S.bc_u[0];
+        before_b = S.bc_u[1];
+    };
     if (a.use_k) {
-        wave_first_reach([&](int i) { return (u64)S.hc[i]; }, [&](int i) { return S.hm[i]; },
-                         (u64)a.top_k, bk, cb_k, mb_k);
+        find_bcast([&](int i) { return (u64)S.hc[i]; }, [&](int i) { return S.hm[i]; }, (u64)a.top_k, bk, cb_k,
+                   mb_k);
         if (bk < 0) return false;  // fewer than top_k entries captured
-        if (!resolve_bin(bk, 0, 0u, cb_k, true, (u64)a.top_k, tau_k, in_k_cnt, in_k_mass)) return false;
+        if (!resolve_bin(bk, 0, 0u, cb_k, true, (u64)a.top_k, S.hc[bk], S.hm[bk], tau_k, in_k_cnt, in_k_mass))
+            return false;
     }
     const u64 zk = a.use_k ? mb_k + in_k_mass : 0ull;
     if (!a.use_p) {
@@ -791,13 +854,15 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     if (a.use_k && target > zk) target = zk;  // rounding: keep the whole top-k set
     int bp;
     u64 mb_p, cb_p;
-    wave_first_reach([&](int i) -> u64 { return i < bk ? S.hm[i] : (i == bk ? in_k_mass : 0ull); },
-                     [&](int i) -> u64 { return i < bk ? S.hc[i] : (i == bk ? in_k_cnt : 0u); },
-                     target, bp, mb_p, cb_p);
+    find_bcast([&](int i) -> u64 { return i < bk ? S.hm[i] : (i == bk ? in_k_mass : 0ull); },
+               [&](int i) -> u64 { return i < bk ? S.hc[i] : (i == bk ? in_k_cnt : 0u); }, target, bp, mb_p,
+               cb_p);
     if (bp < 0) return false;  // the crossing lies below the candidates
     uint32_t kmin, kcnt;
     u64 kmass;
-    if (!resolve_bin(bp, 1, bp == bk ? tau_k : 0u, mb_p, false, target, kmin, kcnt, kmass)) return false;
+    if (!resolve_bin(bp, 1, bp == bk ? tau_k : 0u, mb_p, false, target, bp == bk ? in_k_cnt : S.hc[bp],
+                     bp == bk ? in_k_mass : S.hm[bp], kmin, kcnt, kmass))
+        return false;
     thr_key = kmin;
     n_kept = (int)(cb_p + kcnt);
     z_kept = (double)(mb_p + kmass) / scale;
@@ -1054,9 +1119,11 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     // are already finishing their row (priority drops again below).
     __builtin_amdgcn_s_setprio(1);
     // the drafted token's logit, fetched while the row streams
+    // (thread 0 writes the record; thread 64 takes the token's weight off
+    // the path of wave 0 during the resolution)
     int d_tok = -1;
     float xd = -INFINITY;
-    if (threadIdx.x == 0 && row_has_token(a.sh, row)) {
+    if ((threadIdx.x == 0 || threadIdx.x == 64) && row_has_token(a.sh, row)) {
         d_tok = row_token(a.sh, row);
         if (d_tok >= 0 && d_tok < V) xd = load_logit(rowp, DT, d_tok);
     }
@@ -1135,15 +1202,26 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             tau = fmaxf(tau, first_threshold(S, m_run, max(1, min(a.top_k, kRB))));
         }
     };
-    // Expands the captured units so far into the wave's candidates and
-    // empties the segment.
-    int n_w = 0;  // this wave's candidates (uniform per wave)
-    auto expand_now = [&]() {
-        if (kFilt) {
-            const u64 w = wave_expand<DT>(S, V, tau, fill, ovf, n_w);
+    // The captured units are expanded into the wave's candidates 64 at a
+    // time while the row streams, so that a wave has few of them left to
+    // expand when its stream ends.
+    int n_w = 0;   // this wave's candidates (uniform per wave)
+    int done = 0;  // units of the segment expanded so far (uniform per wave)
+    auto expand_batch = [&]() {
+        if (kFilt && fill - done >= 64) {
+            const u64 w = wave_expand<DT>(S, V, tau, done, fill, ovf, n_w);
             n_w = (int)(uint32_t)w;
             ovf = (int)(w >> 32);
-            fill = 0;
+            done += 64;
+        }
+    };
+    auto expand_rest = [&]() {
+        if (kFilt) {
+            for (; done < fill; done += 64) {
+                const u64 w = wave_expand<DT>(S, V, tau, done, fill, ovf, n_w);
+                n_w = (int)(uint32_t)w;
+                ovf = (int)(w >> 32);
+            }
         }
     };
     auto full_tile = [&](int t, const u32x4 (&raw)[NL]) {
@@ -1151,6 +1229,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         RowStream<DT>::unpack_full(raw, v);
         core(v, raw, t * (kRB * NL) + (int)threadIdx.x, kRB, t == 0);
         refresh(t);
+        expand_batch();
     };
     auto any_tile = [&](int t, const u32x4 (&raw)[NL]) {
         float v[kREPT];
@@ -1218,7 +1297,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     int n_own = 0;
     u64 cflags = 0ull;
     if (kFilt) {
-        expand_now();
+        expand_rest();
         n_own = min(kOwn, max(0, (n_w - (int)(threadIdx.x & 63) + 63) / 64));
         // one contribution per wave: count | overflow << 32
         cflags = (u64)n_w | ((u64)(ovf ? 1 : 0) << 32);
@@ -1227,36 +1306,53 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     const RowTot tot =
         rb_row_totals(RowTot{MODE == MODE_TOPK ? m_run : m_th, kSum ? k_th : -INFINITY, z_th, cflags}, S);
     const float M = tot.m;
-    // the row sum relative to the row maximum: z * 2^(8 k - M log2(e) / T)
-    const double Z = (kSum && tot.k != -INFINITY) ? tot.z * exp2(8.0 * (double)tot.k - (double)M * a.c64) : 0.0;
     const int n_res = (tot.c >> 32) ? kCap + 1 : (int)(uint32_t)tot.c;
 
     float thr = -INFINITY;
-    double z_kept = Z;
     int n_kept = V;
     int flags = 0;
+    double Z = 0.0;       // the row sum relative to the row maximum
+    double z_kept = 0.0;  // the kept mass relative to the row maximum
+    double ptok = 0.0;    // thread 0: the drafted token's probability, when it is kept
 
-    // exp of the drafted token's logit against the row maximum, ahead of the
-    // resolution's barriers (thread 0 writes the record)
-    double e_tok = 0.0;
-    if (threadIdx.x == 0 && d_tok >= 0 && d_tok < V) e_tok = exp(((double)xd - (double)M) * a.inv_T);
-
-    if (kFilt) {
+    if (!kFilt) {
+        // z * 2^(8 k - M log2(e) / T)
+        Z = (kSum && tot.k != -INFINITY) ? tot.z * exp2(8.0 * (double)tot.k - (double)M * a.c64) : 0.0;
+        z_kept = Z;
+        if (threadIdx.x == 0 && d_tok >= 0 && d_tok < V) ptok = exp(((double)xd - (double)M) * a.inv_T) / Z;
+    } else {
         flags = SPEC_ROW_FILTERED;
         const double scale = ldexp(1.0, a.fx_shift);
         uint32_t thr_key = 0u;
         // power-of-two reference of the row: the streaming sums use the same
         // (a thread's reference is ceil(its max * c / 8))
         const float kref = M != -INFINITY ? ceilf(M * a.c8) : 0.f;
+        // the row sum in grid units (2^(8 kref)); one grid unit is
+        // 2^(8 kref - M log2(e) / T) against the row maximum
         const double Zg = (kSum && tot.k != -INFINITY) ? ldexp(tot.z, (int)(8.f * (tot.k - kref))) : 0.0;
+        // Wave 1 takes the grid unit and the drafted token's weight in grid
+        // units (two fp64 exp2) while wave 0 searches the bins.
+        auto side = [&]() {
+            const double zs = exp2(8.0 * (double)kref - (double)M * a.c64);
+            const double pt = exp2((double)xd * a.c64 - 8.0 * (double)kref);
+            if (threadIdx.x == 64) {
+                S.side_zs = zs;
+                S.side_pt = pt;
+            }
+        };
         double zk_grid = 0.0;
         bool fast = n_res <= kCap &&
-                    resolve_reservoir(a, S, M, kref, Zg, n_own, tau0, scale, thr_key, zk_grid, n_kept);
+                    resolve_reservoir<DT>(a, S, M, kref, Zg, n_own, tau0, scale, thr_key, zk_grid, n_kept, side);
         if (fast) {
             thr = key_to_float(thr_key);
-            z_kept = zk_grid * exp2(8.0 * (double)kref - (double)M * a.c64);
+            const double zs = S.side_zs;
+            z_kept = zk_grid * zs;
+            Z = Zg * zs;
+            if (threadIdx.x == 0) ptok = S.side_pt / zk_grid;
         } else {
             flags |= SPEC_ROW_EXACT_PATH;
+            const double zs = exp2(8.0 * (double)kref - (double)M * a.c64);
+            Z = Zg * zs;
             uint32_t thk = 0u;
             uint32_t cnt = (uint32_t)V;
             u64 zfx = 0ull;  // kept mass, grid units
@@ -1288,7 +1384,9 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             n_kept = (int)cnt;
             // kept mass relative to the row maximum (the whole row when no
             // selection applied)
-            z_kept = have_z ? (double)zfx / scale * exp2(8.0 * (double)kref - (double)M * a.c64) : Z;
+            z_kept = have_z ? (double)zfx / scale * zs : Z;
+            if (threadIdx.x == 0 && d_tok >= 0 && d_tok < V)
+                ptok = exp(((double)xd - (double)M) * a.inv_T) / z_kept;
         }
         // kept list of a target row, sorted by token index.  Fast path: every
         // wave's candidates are in index order (a wave captures its groups in
@@ -1528,7 +1626,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         double prob = __longlong_as_double(0x7FF8000000000000LL);  // NaN: no drafted token
         if (row_has_token(a.sh, row)) {
             prob = 0.0;
-            if (d_tok >= 0 && d_tok < V && xd >= thr) prob = e_tok / z_kept;
+            if (d_tok >= 0 && d_tok < V && xd >= thr) prob = ptok;
         }
         r.s.prob_at_token = prob;
         a.rec[row] = r;

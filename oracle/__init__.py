@@ -89,6 +89,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_verify.argtypes = [vp, i32, vp, i32, vp, i32, i32, i32, f64, i32, f64,
                                     u64, i32, vp, vp, vp, vp, vp, vp]
         L.oracle_verify.restype = i32
+        L.oracle_verify_point.argtypes = [vp, i32, vp, i32, i32, i32, f64, i32, f64, u64, i32,
+                                          vp, vp, vp, vp, vp]
+        L.oracle_verify_point.restype = i32
         L.oracle_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
         L.oracle_verify_greedy.restype = i32
         _lib = L
@@ -168,6 +171,34 @@ def verify(target, draft, tokens, temperature, top_k=0, top_p=1.0, seed=0, seq_b
     res = {"tokens": out_tok, "num_accepted": out_n}
     if am is not None:
         res.update(accept_margin=am, sample_margin=sm, target_info=ti, draft_info=di)
+    return res
+
+
+def verify_point(target, tokens, temperature, top_k=0, top_p=1.0, seed=0, seq_base=0,
+                 diagnostics=True):
+    """Verification against point-mass drafts (no draft logits): target
+    [B, K+1, V], tokens [B, K].  Same result dict as ``verify`` (without
+    ``draft_info``)."""
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, K)
+    out_tok = np.empty((B, K + 1), dtype=np.int32)
+    out_n = np.empty(B, dtype=np.int32)
+    am = sm = ti = None
+    if diagnostics and temperature > 0:
+        am = np.full((B, K), np.nan)
+        sm = np.zeros(B)
+        ti = np.zeros((B, K + 1), dtype=ROW_INFO_DTYPE)
+    rc = lib().oracle_verify_point(_ptr(target), dtype_code(target), _ptr(tokens), B, K, V,
+                                   float(temperature), int(top_k), float(top_p),
+                                   int(seed) & 0xFFFFFFFFFFFFFFFF, int(seq_base), _ptr(out_tok),
+                                   _ptr(out_n), _ptr(am), _ptr(sm), _ptr(ti))
+    if rc:
+        raise ValueError(f"oracle_verify_point failed ({rc})")
+    res = {"tokens": out_tok, "num_accepted": out_n}
+    if am is not None:
+        res.update(accept_margin=am, sample_margin=sm, target_info=ti)
     return res
 
 

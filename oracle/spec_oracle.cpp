@@ -407,4 +407,115 @@ int oracle_verify(const void* target, int target_dtype, const void* draft,
     return 0;
 }
 
+/*
+ * Point-mass drafts.  A drafter that proposes d_k with certainty has
+ * q_k = delta(d_k); top-k and top-p leave a point mass unchanged.  The
+ * rejection test ("Why the output is identical" on the same page; FlashMap
+ * page section 4) with q_k(d_k) = 1 accepts d_k with probability
+ * min(1, p_k(d_k)), i.e. when u * 1 < p_k(d_k).  After the first rejection
+ * at j < K the stop token comes from max(0, p_j - delta(d_j)) normalised:
+ * p_j with d_j taken out.  After K acceptances the bonus token comes from
+ * p_K.  Uniforms, inverse CDF and the S = 0 reading are those of
+ * oracle_verify.
+ */
+int oracle_verify_point(const void* target, int target_dtype,
+                        const int32_t* draft_tokens, int B, int K, int V,
+                        double temperature, int top_k, double top_p,
+                        uint64_t seed, int seq_base, int32_t* out_tokens,
+                        int32_t* out_num_accepted, double* accept_margin,
+                        double* sample_margin, oracle_row_info* target_info) {
+    if (B < 0 || K < 0 || V < 1 || seq_base < 0) return 1;
+    if (!dtype_ok(target_dtype)) return 1;
+    if (!(temperature >= 0.0) || !std::isfinite(temperature)) return 1;
+    if (!(top_p > 0.0 && top_p <= 1.0)) return 1;
+    if (temperature == 0.0)
+        return oracle_verify_greedy(target, target_dtype, draft_tokens, B, K, V,
+                                    out_tokens, out_num_accepted);
+    if (B == 0) return 0;
+    if (!target || !out_tokens || !out_num_accepted) return 1;
+    if (K > 0 && !draft_tokens) return 1;
+    const size_t tsz = dtype_size(target_dtype);
+
+    for (int b = 0; b < B; ++b) {
+        const uint32_t gb = static_cast<uint32_t>(seq_base + b);
+        const int32_t* d = draft_tokens + static_cast<size_t>(b) * K;
+
+        std::vector<Row> P(K + 1);
+        for (int k = 0; k <= K; ++k) {
+            const void* row = static_cast<const char*>(target) +
+                              (static_cast<size_t>(b) * (K + 1) + k) * V * tsz;
+            if (process_row(row, target_dtype, V, temperature, top_k, top_p, P[k]))
+                return 2;
+        }
+
+        /* q_k(x) is 1 at x = d_k and 0 elsewhere; a token outside [0, V)
+         * has p = 0 and is rejected. */
+        auto q_of = [&](int k, int x) { return x == d[k] ? 1.0 : 0.0; };
+
+        int j = K;
+        for (int k = 0; k < K; ++k) {
+            const int x = d[k];
+            const double p = (x >= 0 && x < V) ? P[k].prob[x] : 0.0;
+            if (x >= 0 && x < V) P[k].info.prob_at_token = p;
+            const double q = 1.0;
+            const double u = oracle_u24(seed, gb, static_cast<uint32_t>(k),
+                                        ORACLE_PURPOSE_ACCEPT);
+            if (accept_margin)
+                accept_margin[static_cast<size_t>(b) * K + k] = std::fabs(u * q - p) / q;
+            if (!(u * q < p)) {
+                j = k;
+                break;
+            }
+        }
+        if (accept_margin)
+            for (int k = j + 1; k < K; ++k)
+                accept_margin[static_cast<size_t>(b) * K + k] = kNaN;
+
+        std::vector<double> r(V);
+        double S = 0.0;
+        if (j < K) {
+            for (int i = 0; i < V; ++i) {
+                const double diff = P[j].prob[i] - q_of(j, i);
+                r[i] = diff > 0.0 ? diff : 0.0;
+            }
+            for (int i = 0; i < V; ++i) S += r[i];
+        }
+        if (j == K || S == 0.0) {
+            for (int i = 0; i < V; ++i) r[i] = P[j].prob[i];
+            S = 0.0;
+            for (int i = 0; i < V; ++i) S += r[i];
+        }
+        const double t = oracle_u53(seed, gb, static_cast<uint32_t>(j),
+                                    ORACLE_PURPOSE_SAMPLE) * S;
+        int y = -1, last_pos = -1;
+        double cum = 0.0, margin = 0.0;
+        for (int i = 0; i < V; ++i) {
+            if (!(r[i] > 0.0)) continue;
+            last_pos = i;
+            const double prev = cum;
+            cum += r[i];
+            if (y < 0 && cum > t) {
+                y = i;
+                margin = std::min(t - prev, cum - t) / S;
+            }
+        }
+        if (y < 0) {
+            y = last_pos;
+            margin = 0.0;
+        }
+        if (sample_margin) sample_margin[b] = margin;
+
+        int32_t* out = out_tokens + static_cast<size_t>(b) * (K + 1);
+        for (int k = 0; k < j; ++k) out[k] = d[k];
+        out[j] = y;
+        for (int k = j + 1; k <= K; ++k) out[k] = -1;
+        out_num_accepted[b] = j;
+
+        if (target_info)
+            for (int k = 0; k <= K; ++k)
+                target_info[static_cast<size_t>(b) * (K + 1) + k] = P[k].info;
+    }
+    return 0;
+}
+
 }  // extern "C"

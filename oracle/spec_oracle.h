@@ -98,6 +98,20 @@ int oracle_verify(const void* target, int target_dtype, const void* draft,
                   double* sample_margin, oracle_row_info* target_info,
                   oracle_row_info* draft_info);
 
+/* Verification against a deterministic drafter (lookup table, n-gram or
+ * prompt-lookup proposals: "Speculative decoding and multi-token prediction:
+ * how LLMs generate faster", sections "Draft and verify" and "Where drafts
+ * come from").  The drafter proposes d_k with certainty, so its distribution
+ * is the point mass at d_k and no draft logits exist.  Same arguments and
+ * outputs as oracle_verify without the draft rows; accept_margin holds
+ * |u - p| (q = 1).  temperature == 0 gives greedy semantics. */
+int oracle_verify_point(const void* target, int target_dtype,
+                        const int32_t* draft_tokens, int B, int K, int V,
+                        double temperature, int top_k, double top_p,
+                        uint64_t seed, int seq_base, int32_t* out_tokens,
+                        int32_t* out_num_accepted, double* accept_margin,
+                        double* sample_margin, oracle_row_info* target_info);
+
 /* Greedy verification: g_k = argmax of target row k (lowest index among
  * equal maxima), accept while d_k == g_k, then emit g_j. */
 int oracle_verify_greedy(const void* target, int target_dtype,

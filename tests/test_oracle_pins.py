@@ -419,3 +419,127 @@ def test_invalid_arguments_rejected():
                dict(temperature=1.0, top_p=0.0), dict(temperature=1.0, top_p=1.5)):
         with pytest.raises(ValueError):
             oracle.verify(t, d, tok, kw.pop("temperature"), **kw)
+
+
+# --------------------------------------------------------------------------
+# Point-mass drafts (lookup / n-gram / prompt-lookup proposers)
+# --------------------------------------------------------------------------
+
+def _one_hot_logits(tokens, V):
+    """Draft logits whose processed distribution is exactly the point mass at
+    each drafted token (0 there, -inf elsewhere)."""
+    B, K = tokens.shape
+    d = np.full((B, K, V), NEG_INF, np.float32)
+    b, k = np.meshgrid(np.arange(B), np.arange(K), indexing="ij")
+    d[b, k, tokens] = 0.0
+    return d
+
+
+@pytest.mark.parametrize("T,top_k,top_p,bf16", [(1.0, 0, 1.0, False), (0.7, 0, 0.9, True),
+                                                (1.0, 5, 0.95, True), (1.6, 3, 1.0, False)])
+def test_point_drafts_equal_general_rule_with_one_hot_draft(T, top_k, top_p, bf16):
+    """A deterministic drafter's distribution is the point mass at its
+    proposal; top-k / top-p leave it unchanged.  The point-mass verifier must
+    then reproduce the general verifier fed one-hot draft rows token for
+    token (same accept tests with q = 1, same residual p - delta, same
+    draws), including the margins."""
+    rng = np.random.default_rng(11 + top_k)
+    B, K, V = 400, 5, 40
+    t = (rng.standard_normal((B, K + 1, V)) * 2).astype(np.float32)
+    if bf16:
+        t = wl.f32_to_bf16_bits(t)
+    # proposals: the argmax of a noisy copy of the target (a plausible
+    # deterministic drafter), so both accepts and rejects occur
+    tf = wl.as_f32(t)
+    toks = np.argmax(tf[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32) * 2, axis=2).astype(np.int32)
+    rp = oracle.verify_point(t, toks, T, top_k, top_p, seed=321, seq_base=7)
+    rg = oracle.verify(t, _one_hot_logits(toks, V), toks, T, top_k, top_p, seed=321, seq_base=7)
+    assert (rp["tokens"] == rg["tokens"]).all()
+    assert (rp["num_accepted"] == rg["num_accepted"]).all()
+    assert 0 < rp["num_accepted"].mean() < K
+    np.testing.assert_array_equal(rp["accept_margin"], rg["accept_margin"])
+    np.testing.assert_array_equal(rp["sample_margin"], rg["sample_margin"])
+
+
+def test_point_drafts_output_distribution_equals_target():
+    """V = 8, K = 3, fixed proposals x_k: the token emitted at every position
+    (among sequences that reach it) is distributed as p_k, the acceptance
+    rate at k is p_k(x_k), and a correction after a rejection at k follows
+    p_k with x_k removed, normalised (threatfrontier, "Why the output is
+    identical" and "Where drafts come from"; FlashMap page section 4)."""
+    rng = np.random.default_rng(17)
+    V, K, B = 8, 3, 1 << 18
+    T, top_k, top_p = 0.9, 0, 0.95
+    t_log = (rng.standard_normal((K + 1, V)) * 1.5).astype(np.float32)
+    P = np.stack([brute_force_processed(t_log[k], T, top_k, top_p) for k in range(K + 1)])
+    x = np.array([int(np.argsort(P[k])[-2]) for k in range(K)], np.int32)  # second most likely
+    toks = np.ascontiguousarray(np.broadcast_to(x, (B, K)))
+    target = np.ascontiguousarray(np.broadcast_to(t_log, (B, K + 1, V)))
+    r = oracle.verify_point(target, toks, T, top_k, top_p, seed=5, diagnostics=False)
+    n_acc, out = r["num_accepted"], r["tokens"]
+    assert ((out >= 0).sum(axis=1) == n_acc + 1).all()
+    for k in range(K + 1):
+        reach = n_acc >= k
+        assert chi2_pvalue(out[reach, k], P[k]) > 1e-6, k
+        if k < K:
+            alpha = P[k][x[k]]
+            n = reach.sum()
+            acc = (n_acc[reach] > k).mean()
+            assert abs(acc - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / n), k
+            rej = n_acc == k
+            resid = P[k].copy()
+            resid[x[k]] = 0.0
+            assert chi2_pvalue(out[rej, k], resid / resid.sum()) > 1e-6, k
+            assert (out[n_acc > k, k] == x[k]).all()
+
+
+@pytest.mark.parametrize("k,a,printed", _load_golden_E())
+def test_point_drafts_expected_tokens_per_pass(k, a, printed):
+    """p_k = (a, 1-a) on tokens (0, 1) and the drafter always proposes token
+    0: acceptance is i.i.d. with rate a and E[tokens per pass] is the page's
+    printed (1 - a^(k+1)) / (1 - a) (threatfrontier, "Acceptance rate is
+    the whole economics"); every correction is token 1."""
+    V, B = 8, 1 << 18
+    t_row = np.full(V, NEG_INF, np.float32)
+    t_row[0] = np.log(a)
+    t_row[1] = np.log(1 - a)
+    target = np.ascontiguousarray(np.broadcast_to(t_row, (B, k + 1, V)))
+    r = oracle.verify_point(target, np.zeros((B, k), np.int32), 1.0, seed=4048 + int(a * 10),
+                            diagnostics=False)
+    n = r["num_accepted"]
+    pa = softmax64(t_row)[0]
+    pmf = np.array([pa**i * (1 - pa) for i in range(k)] + [pa**k])
+    mean = (np.arange(k + 1) * pmf).sum() + 1
+    var = (np.arange(k + 1) ** 2 * pmf).sum() - (mean - 1) ** 2
+    assert round((1 - a ** (k + 1)) / (1 - a), 2) == printed
+    assert abs((n + 1).mean() - mean) < 5 * np.sqrt(var / B)
+    assert chi2_pvalue(n, pmf) > 1e-6
+    rows = np.arange(B)
+    assert (r["tokens"][rows[n < k], n[n < k]] == 1).all()
+
+
+def test_point_drafts_edge_cases():
+    """Out-of-range proposals are rejected (p = 0) and the stop token is a
+    plain draw from p_0; a proposal carrying all of p's mass is always
+    accepted; temperature 0 is greedy."""
+    rng = np.random.default_rng(23)
+    B, K, V = 64, 3, 12
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32)
+    toks = np.full((B, K), -1, np.int32)
+    toks[32:] = V
+    r = oracle.verify_point(t, toks, 1.0, seed=2)
+    assert (r["num_accepted"] == 0).all()
+    rb = oracle.verify(t[:, :1].copy(), None, np.zeros((B, 0), np.int32), 1.0, seed=2)
+    # with no token removed, the correction at 0 is the bonus-style draw from
+    # p_0 with the same uniform (position 0, sample purpose)
+    assert (r["tokens"][:, 0] == rb["tokens"][:, 0]).all()
+    t1 = np.full((B, K + 1, V), NEG_INF, np.float32)
+    t1[:, :, 3] = 0.0
+    r = oracle.verify_point(t1, np.full((B, K), 3, np.int32), 1.2, seed=9)
+    assert (r["num_accepted"] == K).all() and (r["tokens"] == 3).all()
+    toks = np.argmax(t[:, :K], axis=2).astype(np.int32)
+    toks[::3, 1] = (toks[::3, 1] + 1) % V
+    g = oracle.verify_point(t, toks, 0.0)
+    ref = oracle.verify_greedy(t, toks)
+    assert (g["tokens"] == ref["tokens"]).all() and (g["num_accepted"] == ref["num_accepted"]).all()
+    assert (g["num_accepted"][::3] == 1).all() and (g["num_accepted"][1::3] == K).all()

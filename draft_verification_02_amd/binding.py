@@ -26,8 +26,8 @@ ROW_STATS_FIELDS = [("max_logit", "<f4"), ("thresh", "<f4"), ("n_kept", "<i4"),
                     ("flags", "<i4"), ("z_kept", "<f8"), ("prob_at_token", "<f8")]
 ROW_STATS_BYTES = 32
 
-EXPORTS = ["spec_verify", "spec_verify_greedy", "spec_verify_stats", "spec_rng_uniforms",
-           "spec_profile_events", "spec_status_string", "spec_release_workspace"]
+EXPORTS = ["spec_verify", "spec_verify_point", "spec_verify_greedy", "spec_verify_stats",
+           "spec_rng_uniforms", "spec_profile_events", "spec_status_string", "spec_release_workspace"]
 
 _lib = None
 
@@ -50,6 +50,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
                                ctypes.c_void_p)
     L.spec_verify.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32, i32]
     L.spec_verify.restype = i32
+    L.spec_verify_point.argtypes = [vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32]
+    L.spec_verify_point.restype = i32
     L.spec_verify_greedy.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32]
     L.spec_verify_greedy.restype = i32
     L.spec_verify_stats.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp,
@@ -137,6 +139,21 @@ def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
                             int(top_k), float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
                             _ptr(out_tokens), _ptr(out_num), _stream_handle(stream),
                             _dtype_code(target), ddt)
+    _check(rc)
+    return out_tokens, out_num
+
+
+def spec_verify_point(target: torch.Tensor, tokens: torch.Tensor | None, temperature: float,
+                      top_k: int = 0, top_p: float = 1.0, seed: int = 0, out_tokens=None,
+                      out_num_accepted=None, stream=None):
+    """Verify point-mass drafts (no draft logits): target [B, K+1, V],
+    tokens [B, K] int32.  Returns (out_tokens [B, K+1], out_num_accepted [B])."""
+    B, K, V = _shapes(target, None, tokens, need_draft=False)
+    out_tokens, out_num = _outputs(B, K, target.device, out_tokens, out_num_accepted)
+    rc = load().spec_verify_point(_ptr(target), _ptr(tokens) if K > 0 else None, B, K, V,
+                                  float(temperature), int(top_k), float(top_p),
+                                  int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out_tokens), _ptr(out_num),
+                                  _stream_handle(stream), _dtype_code(target))
     _check(rc)
     return out_tokens, out_num
 

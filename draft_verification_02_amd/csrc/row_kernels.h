@@ -1405,7 +1405,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             // slack before the draft rows finish), so the draw needs neither
             // an exp for p nor a gather of its own.
             const int kpos_row = row % (a.sh.K + 1);
-            const bool with_draft = kpos_row < a.sh.K;
+            const bool with_draft = kpos_row < a.sh.K && a.sh.n_drows > 0;
             const char* dp = with_draft ? row_ptr(a.sh, a.sh.n_trows + (row / (a.sh.K + 1)) * a.sh.K + kpos_row)
                                         : nullptr;
             float* outd = a.kept_d + (size_t)row * kListMax;

@@ -35,6 +35,7 @@ struct SeqArgs {
     int n_chunks;
     int32_t* out_tokens;
     int32_t* out_num;
+    int point;            // drafts are point masses at the drafted tokens (no draft rows)
 };
 
 // Stop position of sequence b: first k with !(u_k * q_k(d_k) < p_k(d_k)),
@@ -47,7 +48,8 @@ __device__ __forceinline__ int first_rejection(const SeqArgs& a, int b) {
         bool reject = false;
         if (k < K) {
             const double p = a.rec[(size_t)b * (K + 1) + k].s.prob_at_token;
-            const double q = a.rec[a.sh.n_trows + (size_t)b * K + k].s.prob_at_token;
+            // a point-mass draft gives its own token probability 1
+            const double q = a.point ? 1.0 : a.rec[a.sh.n_trows + (size_t)b * K + k].s.prob_at_token;
             const double u = uniform24(draw_block(a.seed, (uint32_t)b, (uint32_t)k, PURPOSE_ACCEPT));
             reject = !(u * q < p);
         }
@@ -57,7 +59,8 @@ __device__ __forceinline__ int first_rejection(const SeqArgs& a, int b) {
     return K;
 }
 
-// The stop row pair of a sequence: target row j, draft row j when j < K.
+// The stop row pair of a sequence: target row j, draft row j when j < K
+// (or, for point-mass drafts, the drafted token dtok, where q = 1).
 struct StopRow {
     const char* tp;
     const char* dp;
@@ -65,6 +68,7 @@ struct StopRow {
     float Mt, Md, thr_t, thr_d;
     double zt, zd;
     bool has_draft;
+    int dtok;  // -1 unless the draft is a point mass at dtok
 };
 
 __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
@@ -77,7 +81,8 @@ __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
     s.Mt = Rt.s.max_logit;
     s.thr_t = Rt.s.thresh;
     s.zt = Rt.s.z_kept;
-    s.has_draft = j < K;
+    s.has_draft = j < K && !a.point;
+    s.dtok = j < K && a.point ? a.sh.tokens[(size_t)b * K + j] : -1;
     if (s.has_draft) {
         const int rd = a.sh.n_trows + b * K + j;
         const RowRec& Rd = a.rec[rd];
@@ -101,7 +106,7 @@ __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
 __device__ __forceinline__ void stop_terms_x(const StopRow& s, double inv_T, int i, float xt,
                                              double& p, double& r) {
     p = xt >= s.thr_t ? exp(((double)xt - (double)s.Mt) * inv_T) / s.zt : 0.0;
-    double q = 0.0;
+    double q = i == s.dtok ? 1.0 : 0.0;
     if (s.has_draft) {
         const float xd = load_logit(s.dp, s.ddt, i);
         q = xd >= s.thr_d ? exp(((double)xd - (double)s.Md) * inv_T) / s.zd : 0.0;
@@ -361,8 +366,10 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
 #pragma unroll
     for (int e = 0; e < kLPT; ++e) {
         const float xd = s.has_draft ? xdl[e] : -INFINITY;
-        const bool qd = threadIdx.x * kLPT + e < n && xd >= s.thr_d;
-        const double q = qd ? exp(((double)xd - (double)s.Md) * a.inv_T) * inv_zd : 0.0;
+        const bool in = threadIdx.x * kLPT + e < n;
+        const bool qd = in && xd >= s.thr_d;
+        const double q = qd ? exp(((double)xd - (double)s.Md) * a.inv_T) * inv_zd
+                            : (in && (int)ent[e].x == s.dtok ? 1.0 : 0.0);
         const double d = pr[e] - q;
         rr[e] = d > 0.0 ? d : 0.0;
         sr += rr[e];
@@ -447,7 +454,8 @@ __device__ __forceinline__ void run_terms(const StopRow& s, double inv_T, int lo
 #pragma unroll
     for (int e = 0; e < kCPT; ++e) {
         p[e] = xt[e] >= s.thr_t ? exp(((double)xt[e] - (double)s.Mt) * inv_T) * inv_zt : 0.0;
-        const double q = (s.has_draft && xd[e] >= s.thr_d) ? exp(((double)xd[e] - (double)s.Md) * inv_T) * inv_zd : 0.0;
+        const double q = (s.has_draft && xd[e] >= s.thr_d) ? exp(((double)xd[e] - (double)s.Md) * inv_T) * inv_zd
+                                                           : (lo + e == s.dtok ? 1.0 : 0.0);
         const double d = p[e] - q;
         r[e] = d > 0.0 ? d : 0.0;
     }

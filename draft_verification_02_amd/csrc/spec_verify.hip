@@ -138,10 +138,10 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
 int run_sampling(const void* target, const void* draft, const int32_t* tokens, int B, int K, int V,
                  float temperature, int top_k, float top_p, uint64_t seed, int32_t* out_tokens,
                  int32_t* out_num, hipStream_t stream, int tdt, int ddt, spec_row_stats_t* tstats,
-                 spec_row_stats_t* dstats) {
+                 spec_row_stats_t* dstats, bool point) {
     int tsz, dsz = 4;
     if (!dtype_size(tdt, &tsz)) return SPEC_E_UNSUPPORTED;
-    if (K > 0 && !dtype_size(ddt, &dsz)) return SPEC_E_UNSUPPORTED;
+    if (K > 0 && !point && !dtype_size(ddt, &dsz)) return SPEC_E_UNSUPPORTED;
     int rc = check_sizes(B, K, V);
     if (rc) return rc;
     if (!(top_p > 0.0f && top_p <= 1.0f)) return SPEC_E_INVALID;
@@ -150,10 +150,12 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     if (!std::isfinite(c) || !(c < 3.0e38)) return SPEC_E_INVALID;
     if (B == 0) return SPEC_OK;
     if (!target || !out_tokens || !out_num) return SPEC_E_INVALID;
-    if (K > 0 && (!draft || !tokens)) return SPEC_E_INVALID;
+    if (K > 0 && ((!point && !draft) || !tokens)) return SPEC_E_INVALID;
+    if (point) draft = nullptr;
 
+    // point-mass drafts have no draft rows
     const int n_trows = B * (K + 1);
-    const int n_drows = B * K;
+    const int n_drows = point ? 0 : B * K;
     const int rows = n_trows + n_drows;
     const bool use_k = top_k > 0 && top_k < V;
     const bool use_p = top_p < 1.0f;
@@ -225,6 +227,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     sa.n_chunks = n_chunks;
     sa.out_tokens = out_tokens;
     sa.out_num = out_num;
+    sa.point = point ? 1 : 0;
     if (filtered) {
         hipLaunchKernelGGL(k_seq_filtered, dim3((unsigned)((long long)B * (K + 1))), dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
@@ -258,7 +261,21 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
                           target_dtype);
     return run_sampling(target_logits, draft_logits, draft_tokens, B, K, V, temperature, top_k, top_p,
                         seed, out_tokens, out_num_accepted, s, target_dtype, draft_dtype, nullptr,
-                        nullptr);
+                        nullptr, false);
+}
+
+int spec_verify_point(const void* target_logits, const int32_t* draft_tokens, int B, int K, int V,
+                      float temperature, int top_k, float top_p, uint64_t seed, int32_t* out_tokens,
+                      int32_t* out_num_accepted, void* stream, int target_dtype) {
+    if (!std::isfinite(temperature) || temperature < 0.0f) return SPEC_E_INVALID;
+    if (!(top_p > 0.0f && top_p <= 1.0f)) return SPEC_E_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (temperature == 0.0f)
+        return run_greedy(target_logits, draft_tokens, B, K, V, out_tokens, out_num_accepted, s,
+                          target_dtype);
+    return run_sampling(target_logits, nullptr, draft_tokens, B, K, V, temperature, top_k, top_p, seed,
+                        out_tokens, out_num_accepted, s, target_dtype, SPEC_DTYPE_F32, nullptr, nullptr,
+                        true);
 }
 
 int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int K, int V,
@@ -276,7 +293,7 @@ int spec_verify_stats(const void* target_logits, const void* draft_logits,
     if (!std::isfinite(temperature) || !(temperature > 0.0f)) return SPEC_E_INVALID;
     return run_sampling(target_logits, draft_logits, draft_tokens, B, K, V, temperature, top_k, top_p,
                         seed, out_tokens, out_num_accepted, static_cast<hipStream_t>(stream),
-                        target_dtype, draft_dtype, target_stats, draft_stats);
+                        target_dtype, draft_dtype, target_stats, draft_stats, false);
 }
 
 int spec_rng_uniforms(uint64_t seed, int B, int K, double* u_accept, double* u_sample,

@@ -127,6 +127,27 @@ int spec_verify(const void* target_logits, const void* draft_logits,
                 int target_dtype, int draft_dtype);
 
 /*
+ * Verification against point-mass drafts: a drafter that proposes each token
+ * with certainty (a lookup table, n-gram or prompt-lookup proposer, or greedy
+ * draft heads; "Speculative decoding and multi-token prediction: how LLMs
+ * generate faster", sections "Draft and verify" and "Where drafts come
+ * from") has q_k = delta(d_k), so no draft logits are read.  The test of
+ * "Why the output is identical" (same page) then accepts d_k when
+ * u_k < p_k(d_k); after the first rejection j the stop token is drawn from
+ * p_j with d_j removed and renormalised; after K acceptances the bonus token
+ * from p_K.  Temperature, top-k and top-p process the target rows as in
+ * spec_verify (a point mass is unchanged by them).  Same arguments,
+ * conventions, random stream and errors as spec_verify without draft_logits
+ * and draft_dtype; temperature == 0 gives greedy semantics.  Reads only the
+ * target logits: B*(K+1)*V*sizeof(target) bytes.
+ */
+int spec_verify_point(const void* target_logits, const int32_t* draft_tokens,
+                      int B, int K, int V, float temperature, int top_k,
+                      float top_p, uint64_t seed, int32_t* out_tokens,
+                      int32_t* out_num_accepted, void* stream,
+                      int target_dtype);
+
+/*
  * Greedy verification: g_k = argmax of target row k (lowest index among equal
  * maxima), accept while d_k == g_k, emit g_j at the first mismatch j (or the
  * bonus argmax g_K).  Reads target logits only.  Same conventions as

@@ -173,3 +173,50 @@ def check_greedy(w: wl.Workload, via_verify=False):
     ref = oracle.verify_greedy(w.target, w.tokens)
     np.testing.assert_array_equal(num.cpu().numpy(), ref["num_accepted"])
     np.testing.assert_array_equal(tok.cpu().numpy(), ref["tokens"])
+
+
+def point_tokens(w: wl.Workload) -> np.ndarray:
+    """Proposals of a deterministic drafter for workload w: the argmax of each
+    draft row (a greedy draft head); the draft logits themselves are not
+    passed to the verifier."""
+    return np.argmax(wl.as_f32(w.draft), axis=2).astype(np.int32)
+
+
+def check_point(w: wl.Workload, tokens: np.ndarray, seqs=None, report=None) -> Report:
+    """spec_verify_point on the GPU against oracle.verify_point: token ids
+    exact, except where the first differing decision is ambiguous (accept
+    |u - p| <= 1e-5, a nucleus boundary within 1e-6 of top_p, a draw within
+    1e-12 * S of a boundary); such mismatches at most 1e-6 of the decisions."""
+    rep = report or Report()
+    t = to_device(w.target)
+    k = torch.from_numpy(np.ascontiguousarray(tokens, dtype=np.int32)).to("cuda")
+    g_tok, g_num = binding.spec_verify_point(t, k, w.temperature, w.top_k, w.top_p, w.seed)
+    torch.cuda.synchronize()
+    g_tok, g_num = g_tok.cpu().numpy(), g_num.cpu().numpy()
+    if seqs is None:
+        seqs = range(w.B)
+    K = w.K
+    for b in seqs:
+        r = oracle.verify_point(w.target[b:b + 1], tokens[b:b + 1], f32(w.temperature), w.top_k,
+                                f32(w.top_p), w.seed, seq_base=int(b))
+        ti = r["target_info"][0]
+        j_o, j_g = int(r["num_accepted"][0]), int(g_num[b])
+        rep.decisions += j_o + (1 if j_o < K else 0) + 1
+        amb_t = ti["nucleus_margin"] <= NUCLEUS_BAND
+        if j_g == j_o and np.array_equal(g_tok[b], r["tokens"][0]):
+            continue
+        m = min(j_g, j_o)
+        if j_g != j_o:
+            am = r["accept_margin"][0, m]
+            ok = am <= ACCEPT_BAND or amb_t[m]
+            why = f"accept at position {m}: margin {am:.3g}"
+        else:
+            sm = r["sample_margin"][0]
+            ok = sm <= SAMPLE_BAND or amb_t[m]
+            why = f"draw at position {m}: margin {sm:.3g}"
+        assert ok, (f"sequence {b}: GPU {g_tok[b].tolist()} (j={j_g}) vs oracle "
+                    f"{r['tokens'][0].tolist()} (j={j_o}); {why} is outside every band")
+        rep.mismatch_tolerated += 1
+        rep.details.append((b, why))
+    assert rep.mismatch_tolerated <= 1e-6 * rep.decisions, rep
+    return rep

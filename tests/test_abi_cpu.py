@@ -67,6 +67,21 @@ def test_invalid_arguments_rejected_on_host(lib, kw, code):
     assert _call(lib, **kw) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1.0), 1), (dict(T=float("nan")), 1), (dict(top_p=0.0), 1), (dict(top_p=2.0), 1),
+    (dict(B=-1), 1), (dict(K=-1), 1), (dict(V=0), 1), (dict(tdt=5), 2),
+    (dict(target=None), 1), (dict(out=None), 1), (dict(tokens=None), 1),
+])
+def test_point_entry_rejects_invalid_arguments_on_host(lib, kw, code):
+    a = dict(target=ctypes.c_void_p(16), tokens=ctypes.c_void_p(16), B=1, K=1, V=4, T=1.0,
+             top_k=0, top_p=1.0, seed=0, out=ctypes.c_void_p(16), num=ctypes.c_void_p(16),
+             stream=None, tdt=0)
+    a.update(kw)
+    assert lib.spec_verify_point(a["target"], a["tokens"], a["B"], a["K"], a["V"], a["T"],
+                                 a["top_k"], a["top_p"], a["seed"], a["out"], a["num"],
+                                 a["stream"], a["tdt"]) == code
+
+
 def test_empty_batch_returns_ok_without_device_work(lib):
     assert _call(lib, B=0, target=None, draft=None, tokens=None, out=None, num=None) == 0
     assert lib.spec_verify_greedy(None, None, 0, 3, 10, None, None, None, 1) == 0

@@ -236,3 +236,85 @@ def test_stats_entry_matches_plain_entry():
     b = gpu_sampling(w, stats=False)
     np.testing.assert_array_equal(a[0], b[0])
     np.testing.assert_array_equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Point-mass drafts (no draft logits)
+# ---------------------------------------------------------------------------
+
+def test_point_c3_shape_full_size_sampled():
+    """c3's target rows, drafts proposed by the draft rows' argmax."""
+    from parity import check_point, point_tokens
+    _print_case("point c3 full, 8 sequences checked")
+    w = wl.config(3)
+    print(check_point(w, point_tokens(w), seqs=[0, 3, 9, 14, 20, 23, 28, 31]))
+
+
+@pytest.mark.parametrize("cfg,kw", [(3, dict(B=8, V=40000)), (2, dict(B=4, V=20000)),
+                                    (5, dict(B=6, V=30011)), (1, {})])
+def test_point_small_all_sequences(cfg, kw):
+    from parity import Report, check_point, point_tokens
+    _print_case(f"point cfg{cfg} {kw}")
+    rep = Report()
+    for rnd in range(4):
+        w = wl.config(cfg, rnd, **kw)
+        check_point(w, point_tokens(w), report=rep)
+        # proposals that are the sampled draft tokens (in range, any value)
+        check_point(w, w.tokens, report=rep)
+    print(rep)
+
+
+def test_point_c5_full_size_sampled():
+    from parity import check_point, point_tokens
+    _print_case("point c5 full, 16 sequences checked")
+    w = wl.config(5)
+    print(check_point(w, point_tokens(w), seqs=list(range(0, 256, 16))))
+
+
+@pytest.mark.parametrize("V", [1, 7, 8193])
+@pytest.mark.parametrize("tdt", [wl.F32, wl.BF16])
+def test_point_ragged_vocab_and_dtypes(V, tdt):
+    from parity import check_point
+    _print_case(f"point ragged V={V} tdt={tdt}")
+    w = wl.make(3, 4, V, target_dtype=tdt, draft_dtype=wl.F32, temperature=1.0, rho=0.9,
+                seed=V * 3 + tdt, vseed=V + 7)
+    check_point(w, w.tokens)
+
+
+def test_point_edge_cases():
+    """Out-of-range proposals (always rejected, plain draw from p_0), K = 0,
+    a proposal holding all the mass (always accepted), temperature 0
+    (greedy), and the point entry against the general entry fed one-hot
+    draft rows."""
+    from parity import check_point, to_device
+    _print_case("point edge cases")
+    w = wl.make(6, 3, 5000, temperature=0.8, top_p=0.9, rho=0.9, seed=5, vseed=6)
+    toks = w.tokens.copy()
+    toks[:3] = -1
+    toks[3:, 1] = 5000
+    check_point(w, toks)
+    w0 = wl.make(5, 0, 777, temperature=1.0, seed=8, vseed=9)
+    check_point(w0, np.zeros((5, 0), np.int32))
+    t1 = np.full((4, 3, 300), -np.inf, np.float32)
+    t1[:, :, 17] = 1.0
+    k1 = np.full((4, 2), 17, np.int32)
+    tok, num = binding.spec_verify_point(to_device(t1), torch.from_numpy(k1).cuda(), 1.3)
+    torch.cuda.synchronize()
+    assert (num.cpu().numpy() == 2).all() and (tok.cpu().numpy() == 17).all()
+    wg = wl.config(4, B=8, V=20000)
+    tg, kg = to_device(wg.target), torch.from_numpy(wg.tokens).cuda()
+    a = binding.spec_verify_point(tg, kg, 0.0)
+    b = binding.spec_verify_greedy(tg, kg)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    # one-hot draft rows through the general entry give the same tokens
+    V = 4099
+    w1 = wl.make(8, 4, V, temperature=0.9, top_k=40, top_p=0.95, rho=0.8, seed=21, vseed=22)
+    oh = np.full((8, 4, V), -np.inf, np.float32)
+    bb, kk = np.meshgrid(np.arange(8), np.arange(4), indexing="ij")
+    oh[bb, kk, w1.tokens] = 0.0
+    tgt, kt = to_device(w1.target), torch.from_numpy(w1.tokens).cuda()
+    pa = binding.spec_verify_point(tgt, kt, w1.temperature, w1.top_k, w1.top_p, w1.seed)
+    ga = binding.spec_verify(tgt, to_device(oh), kt, w1.temperature, w1.top_k, w1.top_p, w1.seed)
+    torch.cuda.synchronize()
+    assert torch.equal(pa[0], ga[0]) and torch.equal(pa[1], ga[1])

@@ -9,6 +9,10 @@ serve a step from the previous one.
 Prints one JSON line with the headline metric (verified draft positions/s),
 the roofline of the dominant (streaming) kernel measured with HIP events on
 the call's stream, and the CPU oracle timed on the host as a baseline.
+
+--mode point measures spec_verify_point instead: the same target rows, with
+the drafts given as point masses (each draft row's argmax, the proposals of a
+greedy draft head) and no draft logits read.
 """
 from __future__ import annotations
 
@@ -26,6 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936, 1 GPU"
+METRIC_POINT = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936, 1 GPU, "
+                "point-mass drafts (spec_verify_point)")
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -69,12 +75,17 @@ def traffic_from_profiles(config_name: str, src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, max_seqs: int):
+def cpu_baseline(w, max_seqs: int, point_tokens=None):
     import oracle  # CPU baseline leg only
 
     seqs = list(range(min(w.B, max_seqs)))
     t0 = time.perf_counter()
     for b in seqs:
+        if point_tokens is not None:
+            oracle.verify_point(w.target[b:b + 1], point_tokens[b:b + 1],
+                                float(np.float32(w.temperature)), w.top_k,
+                                float(np.float32(w.top_p)), w.seed, seq_base=b, diagnostics=False)
+            continue
         oracle.verify(w.target[b:b + 1], w.draft[b:b + 1], w.tokens[b:b + 1],
                       float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p)),
                       w.seed, seq_base=b, diagnostics=False)
@@ -93,6 +104,9 @@ def main():
     ap.add_argument("--no-settle", dest="settle", action="store_false",
                     help="skip the untimed settle phase after the warmup steps")
     ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--mode", choices=["general", "point"], default="general",
+                    help="general: spec_verify with draft logits (the headline); point: "
+                         "spec_verify_point with point-mass drafts")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
     ap.add_argument("--cpu-seqs", type=int, default=32)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -123,7 +137,10 @@ def main():
     if w.greedy:
         raise SystemExit("the headline workload is a sampling workload")
     dev = torch.device("cuda:0")
-    ideal = w.ideal_bytes()
+    point = args.mode == "point"
+    # point-mass drafts: the draft rows' argmax, a greedy draft head's proposals
+    ptoks = np.argmax(wl.as_f32(w.draft), axis=2).astype(np.int32) if point else None
+    ideal = w.target.nbytes if point else w.ideal_bytes()
     n_sets = args.sets or max(4, int(np.ceil(2.5 * MALL_BYTES / ideal)))
 
     def up(a):
@@ -131,13 +148,18 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    sets = [(up(w.target), up(w.draft), up(w.tokens)) for _ in range(n_sets)]
+    sets = [(up(w.target), None if point else up(w.draft), up(ptoks if point else w.tokens))
+            for _ in range(n_sets)]
     out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
     out_n = torch.empty((w.B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
         t, d, k = sets[i % n_sets]
+        if point:
+            binding.spec_verify_point(t, k, w.temperature, w.top_k, w.top_p, w.seed, out_t, out_n,
+                                      stream=stream)
+            return
         binding.spec_verify(t, d, k, w.temperature, w.top_k, w.top_p, w.seed, out_t, out_n,
                             stream=stream)
 
@@ -194,11 +216,11 @@ def main():
 
     src_hash = kernel_source_hash()
     achieved = ideal / (k_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(w.name, src_hash)
+    traffic = None if point else traffic_from_profiles(w.name, src_hash)
     positions = w.B * w.K
     value = positions / (ms * 1e-3)
     line = {
-        "metric": METRIC,
+        "metric": METRIC_POINT if point else METRIC,
         "value": round(value, 1),
         "unit": "verified draft positions/s",
         "n_gpus": 1,
@@ -211,8 +233,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f32+f64",
         "data": "synthetic",
-        "config": {"workload": w.name, "B": w.B, "K": w.K, "V": w.V, "target": "bf16",
-                   "draft": "f32", "temperature": w.temperature, "top_k": w.top_k,
+        "config": {"workload": w.name + ("-point" if point else ""), "B": w.B, "K": w.K, "V": w.V,
+                   "target": "bf16", "draft": "point mass" if point else "f32",
+                   "temperature": w.temperature, "top_k": w.top_k,
                    "top_p": w.top_p, "input_sets_rotated": n_sets, "ideal_bytes": ideal},
         "hbm_gbs_step": round(ideal / (ms * 1e-3) / 1e9, 1),
         "pct_peak_step": round(100 * ideal / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
@@ -223,7 +246,7 @@ def main():
         "wall_s_timed": round(t_wall, 4),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, ptoks)
     print(json.dumps(line), flush=True)
 
 

@@ -202,6 +202,46 @@ def verify_point(target, tokens, temperature, top_k=0, top_p=1.0, seed=0, seq_ba
     return res
 
 
+def verify_ragged(target, draft, tokens, draft_lens, temperature, top_k=0, top_p=1.0, seed=0,
+                  point=False):
+    """Per-sequence draft lengths: sequence b verifies only its first
+    draft_lens[b] drafted tokens (0 <= draft_lens[b] <= K), against target rows
+    0..draft_lens[b] (the bonus token comes from row draft_lens[b]); the rows past
+    them are not part of the problem.  Each sequence is the plain verification
+    of its own prefix of the padded [B, K+1, V] / [B, K, V] / [B, K] inputs,
+    with its own global sequence index in the random stream.  Outputs are
+    padded with -1 to K+1.  Also returns the per-position acceptance
+    counters: tested[k] = sequences whose accept test at position k ran,
+    accepted[k] = sequences that accepted position k."""
+    target = np.ascontiguousarray(target)
+    B, K1, V = target.shape
+    K = K1 - 1
+    lens = np.asarray(draft_lens, dtype=np.int64).reshape(B)
+    if (lens < 0).any() or (lens > K).any():
+        raise ValueError("draft_lens out of [0, K]")
+    out_tok = np.full((B, K + 1), -1, dtype=np.int32)
+    out_n = np.zeros(B, dtype=np.int32)
+    tested = np.zeros(K, dtype=np.int64)
+    accepted = np.zeros(K, dtype=np.int64)
+    for b in range(B):
+        kb = int(lens[b])
+        t = target[b:b + 1, :kb + 1]
+        tk = np.ascontiguousarray(tokens[b:b + 1, :kb])
+        if point:
+            r = verify_point(t, tk, temperature, top_k, top_p, seed, seq_base=b, diagnostics=False)
+        elif temperature == 0:
+            r = verify_greedy(t, tk)
+        else:
+            d = None if kb == 0 else draft[b:b + 1, :kb]
+            r = verify(t, d, tk, temperature, top_k, top_p, seed, seq_base=b, diagnostics=False)
+        n = int(r["num_accepted"][0])
+        out_tok[b, :kb + 1] = r["tokens"][0]
+        out_n[b] = n
+        tested[:min(n + 1, kb)] += 1
+        accepted[:n] += 1
+    return {"tokens": out_tok, "num_accepted": out_n, "tested": tested, "accepted": accepted}
+
+
 def verify_greedy(target, tokens):
     target = np.ascontiguousarray(target)
     B, K1, V = target.shape

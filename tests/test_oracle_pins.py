@@ -543,3 +543,59 @@ def test_point_drafts_edge_cases():
     ref = oracle.verify_greedy(t, toks)
     assert (g["tokens"] == ref["tokens"]).all() and (g["num_accepted"] == ref["num_accepted"]).all()
     assert (g["num_accepted"][::3] == 1).all() and (g["num_accepted"][1::3] == K).all()
+
+
+# --------------------------------------------------------------------------
+# Per-sequence draft lengths (ragged K) and acceptance counters
+# --------------------------------------------------------------------------
+
+def test_ragged_full_lengths_equal_plain_verification():
+    rng = np.random.default_rng(31)
+    B, K, V = 40, 5, 60
+    t = rng.standard_normal((B, K + 1, V)).astype(np.float32) * 2
+    d = (0.7 * t[:, :K] + rng.standard_normal((B, K, V)).astype(np.float32)).astype(np.float32)
+    toks = rng.integers(0, V, (B, K)).astype(np.int32)
+    r = oracle.verify_ragged(t, d, toks, np.full(B, K), 0.9, 0, 0.95, seed=8)
+    ref = oracle.verify(t, d, toks, 0.9, 0, 0.95, seed=8, diagnostics=False)
+    assert (r["tokens"] == ref["tokens"]).all() and (r["num_accepted"] == ref["num_accepted"]).all()
+    # length 0: the bonus draw from p_0 alone
+    r0 = oracle.verify_ragged(t, d, toks, np.zeros(B, int), 0.9, 0, 0.95, seed=8)
+    ref0 = oracle.verify(t[:, :1].copy(), None, np.zeros((B, 0), np.int32), 0.9, 0, 0.95, seed=8,
+                         diagnostics=False)
+    assert (r0["tokens"][:, 0] == ref0["tokens"][:, 0]).all() and (r0["tokens"][:, 1:] == -1).all()
+    assert (r0["tested"] == 0).all() and (r0["num_accepted"] == 0).all()
+
+
+def test_ragged_lengths_tokens_per_pass_and_counters():
+    """Identical p, q at every position (i.i.d. acceptance alpha = sum
+    min(p, q)): among sequences with draft length L the mean tokens per pass
+    is 1 + alpha + ... + alpha^L (threatfrontier, "Acceptance rate is the
+    whole economics"), and the per-position counters give
+    accepted[k] / tested[k] = alpha at every position (FlashMap section 4:
+    each test accepts with probability sum min(p, q) given it runs)."""
+    rng = np.random.default_rng(37)
+    V, K, B = 8, 4, 1 << 17
+    p_log = (rng.standard_normal(V) * 1.2).astype(np.float32)
+    q_log = (0.5 * p_log + rng.standard_normal(V)).astype(np.float32)
+    P, Q = softmax64(p_log), softmax64(q_log)
+    alpha = np.minimum(P, Q).sum()
+    target = np.ascontiguousarray(np.broadcast_to(p_log, (B, K + 1, V)))
+    draft = np.ascontiguousarray(np.broadcast_to(q_log, (B, K, V)))
+    toks = np.empty((B, K), np.int32)
+    for k in range(K):
+        toks[:, k] = rng.choice(V, size=B, p=Q)
+    lens = rng.integers(0, K + 1, B)
+    r = oracle.verify_ragged(target, draft, toks, lens, 1.0, seed=1234)
+    n = r["num_accepted"]
+    assert (n <= lens).all()
+    assert ((r["tokens"] >= 0).sum(axis=1) == n + 1).all()
+    for L in range(K + 1):
+        m = lens == L
+        e = sum(alpha ** i for i in range(L + 1))
+        pmf = np.array([alpha ** i * (1 - alpha) for i in range(L)] + [alpha ** L])
+        sd = np.sqrt(((np.arange(L + 1) + 1) ** 2 * pmf).sum() - e ** 2)
+        assert abs((n[m] + 1).mean() - e) < 5 * sd / np.sqrt(m.sum()) + 1e-12, L
+    for k in range(K):
+        tk, ak = r["tested"][k], r["accepted"][k]
+        assert tk == ((lens > k) & (n >= k)).sum() and ak == (n > k).sum()
+        assert abs(ak / tk - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / tk), k

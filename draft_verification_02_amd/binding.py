@@ -26,7 +26,7 @@ ROW_STATS_FIELDS = [("max_logit", "<f4"), ("thresh", "<f4"), ("n_kept", "<i4"),
                     ("flags", "<i4"), ("z_kept", "<f8"), ("prob_at_token", "<f8")]
 ROW_STATS_BYTES = 32
 
-EXPORTS = ["spec_verify", "spec_verify_point", "spec_verify_greedy", "spec_verify_stats",
+EXPORTS = ["spec_verify", "spec_verify_ragged", "spec_verify_point", "spec_verify_greedy", "spec_verify_stats",
            "spec_rng_uniforms", "spec_profile_events", "spec_status_string", "spec_release_workspace"]
 
 _lib = None
@@ -50,6 +50,9 @@ def load(path: str = LIB) -> ctypes.CDLL:
                                ctypes.c_void_p)
     L.spec_verify.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32, i32]
     L.spec_verify.restype = i32
+    L.spec_verify_ragged.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, vp,
+                                     vp, i32, i32]
+    L.spec_verify_ragged.restype = i32
     L.spec_verify_point.argtypes = [vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32]
     L.spec_verify_point.restype = i32
     L.spec_verify_greedy.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32]
@@ -141,6 +144,33 @@ def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
                             _dtype_code(target), ddt)
     _check(rc)
     return out_tokens, out_num
+
+
+def spec_verify_ragged(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor | None,
+                       lens: torch.Tensor, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                       seed: int = 0, counters: bool = True, out_tokens=None, out_num_accepted=None,
+                       stream=None):
+    """Per-sequence draft lengths lens [B] int32 (device).  Returns
+    (out_tokens [B, K+1], out_num_accepted [B], tested [K], accepted [K]);
+    the counters are None when ``counters`` is False."""
+    B, K, V = _shapes(target, draft, tokens, need_draft=temperature > 0)
+    assert lens.dtype == torch.int32 and tuple(lens.shape) == (B,)
+    _dev(lens, "draft_lens")
+    out_tokens, out_num = _outputs(B, K, target.device, out_tokens, out_num_accepted)
+    tested = accepted = None
+    if counters:
+        tested = torch.empty((K,), dtype=torch.int32, device=target.device)
+        accepted = torch.empty((K,), dtype=torch.int32, device=target.device)
+    use_draft = draft is not None and K > 0 and temperature > 0
+    ddt = _dtype_code(draft) if use_draft else SPEC_DTYPE_F32
+    rc = load().spec_verify_ragged(_ptr(target), _ptr(draft) if use_draft else None,
+                                   _ptr(tokens) if K > 0 else None, _ptr(lens), B, K, V,
+                                   float(temperature), int(top_k), float(top_p),
+                                   int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out_tokens), _ptr(out_num),
+                                   _ptr(tested), _ptr(accepted), _stream_handle(stream),
+                                   _dtype_code(target), ddt)
+    _check(rc)
+    return out_tokens, out_num, tested, accepted
 
 
 def spec_verify_point(target: torch.Tensor, tokens: torch.Tensor | None, temperature: float,

@@ -62,6 +62,7 @@ struct Shape {
     int tdt, ddt;
     int tsz, dsz;
     int n_trows, n_drows;
+    const int32_t* lens;  // per-sequence draft lengths in [0, K] (clamped), or null: all K
 };
 
 __device__ __forceinline__ const char* row_ptr(const Shape& sh, int row) {
@@ -71,8 +72,20 @@ __device__ __forceinline__ const char* row_ptr(const Shape& sh, int row) {
 __device__ __forceinline__ int row_dt(const Shape& sh, int row) {
     return row < sh.n_trows ? sh.tdt : sh.ddt;
 }
+// Draft length of sequence b: its first K_b drafts are verified against
+// target rows 0..K_b (the bonus comes from row K_b); rows past them are not
+// read.
+__device__ __forceinline__ int seq_len(const Shape& sh, int b) {
+    return sh.lens ? min(max(sh.lens[b], 0), sh.K) : sh.K;
+}
+__device__ __forceinline__ bool row_live(const Shape& sh, int row) {
+    if (!sh.lens) return true;
+    if (row < sh.n_trows) return row % (sh.K + 1) <= seq_len(sh, row / (sh.K + 1));
+    const int r = row - sh.n_trows;
+    return r % sh.K < seq_len(sh, r / sh.K);
+}
 __device__ __forceinline__ bool row_has_token(const Shape& sh, int row) {
-    return row >= sh.n_trows || (row % (sh.K + 1)) < sh.K;
+    return row >= sh.n_trows || (row % (sh.K + 1)) < seq_len(sh, row / (sh.K + 1));
 }
 __device__ __forceinline__ int row_token(const Shape& sh, int row) {
     if (row < sh.n_trows) {
@@ -1241,51 +1254,46 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         refresh(t);
     };
     {
-        // Steady state: four full tiles of loads in flight in rotating
+        // Steady state: NS = 4 full tiles of loads in flight in rotating
         // registers, straight-line code so that each tile waits only for its
-        // own loads.  Rows with fewer than five full tiles go tile by tile.
-        u32x4 rA[NL], rB[NL], rC[NL], rD[NL];
+        // own loads (eight for bf16 rows, the same registers, was slower).
+        // Rows with fewer than five full tiles go tile by tile.
         const int nf = st.nfull;
         int t = 0;
-        if (nf >= 5) {
-            st.issue_full(0, rA);
-            st.issue_full(1, rB);
-            st.issue_full(2, rC);
-            st.issue_full(3, rD);
-            full_tile(0, rA);
-            st.issue_full(4, rA);
+        auto rotate = [&](auto ns) {
+            constexpr int NS = decltype(ns)::value;
+            u32x4 rs[NS][NL];
+#pragma unroll
+            for (int q = 0; q < NS; ++q) st.issue_full(q, rs[q]);
+            full_tile(0, rs[0]);
+            st.issue_full(NS, rs[0]);
             t = 1;
             // Every scalar load is complete here (lgkmcnt(0), other counters
             // left alone): without it the compiler waits on lgkmcnt inside the
             // loop, and with capture stores in flight that wait is for the LDS.
             __builtin_amdgcn_s_waitcnt(0xC07F);
-            for (; t + 7 < nf; t += 4) {
-                full_tile(t, rB);
-                st.issue_full(t + 4, rB);
-                full_tile(t + 1, rC);
-                st.issue_full(t + 5, rC);
-                full_tile(t + 2, rD);
-                st.issue_full(t + 6, rD);
-                full_tile(t + 3, rA);
-                st.issue_full(t + 7, rA);
+            for (; t + 2 * NS - 1 < nf; t += NS) {
+#pragma unroll
+                for (int q = 0; q < NS; ++q) {
+                    full_tile(t + q, rs[(1 + q) % NS]);
+                    st.issue_full(t + q + NS, rs[(1 + q) % NS]);
+                }
             }
-            // drain: the rest of the row (at most four more tiles, the last
+            // drain: the rest of the row (at most NS more tiles, the last
             // possibly partial) rides the same rotation with clamped loads
-            full_tile(t, rB);
-            st.issue_clamped(t + 4, rB);
-            full_tile(t + 1, rC);
-            st.issue_clamped(t + 5, rC);
-            full_tile(t + 2, rD);
-            st.issue_clamped(t + 6, rD);
-            full_tile(t + 3, rA);
-            st.issue_clamped(t + 7, rA);
-            t += 4;
-            if (t < st.nt) any_tile(t, rB);
-            if (t + 1 < st.nt) any_tile(t + 1, rC);
-            if (t + 2 < st.nt) any_tile(t + 2, rD);
-            if (t + 3 < st.nt) any_tile(t + 3, rA);
+#pragma unroll
+            for (int q = 0; q < NS; ++q) {
+                full_tile(t + q, rs[(1 + q) % NS]);
+                st.issue_clamped(t + q + NS, rs[(1 + q) % NS]);
+            }
+            t += NS;
+#pragma unroll
+            for (int q = 0; q < NS; ++q)
+                if (t + q < st.nt) any_tile(t + q, rs[(1 + q) % NS]);
             t = st.nt;
-        }
+        };
+        if (nf >= 5) rotate(std::integral_constant<int, 4>());
+        u32x4 rA[NL];
         for (; t < st.nt; ++t) {
             st.issue(t, rA);
             any_tile(t, rA);
@@ -1405,7 +1413,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             // slack before the draft rows finish), so the draw needs neither
             // an exp for p nor a gather of its own.
             const int kpos_row = row % (a.sh.K + 1);
-            const bool with_draft = kpos_row < a.sh.K && a.sh.n_drows > 0;
+            const bool with_draft = a.sh.n_drows > 0 && kpos_row < seq_len(a.sh, row / (a.sh.K + 1));
             const char* dp = with_draft ? row_ptr(a.sh, a.sh.n_trows + (row / (a.sh.K + 1)) * a.sh.K + kpos_row)
                                         : nullptr;
             float* outd = a.kept_d + (size_t)row * kListMax;
@@ -1683,7 +1691,7 @@ __device__ __forceinline__ void row_part_plain(const RowArgs& a, RowShared& S, i
 // order): one thread per row.
 __global__ void __launch_bounds__(256) k_row_merge(RowArgs a) {
     const int row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= a.sh.n_trows + a.sh.n_drows) return;
+    if (row >= a.sh.n_trows + a.sh.n_drows || !row_live(a.sh, row)) return;
     RowTot t{-INFINITY, -INFINITY, 0.0, 0ull};
     for (int p = 0; p < a.parts; ++p) {
         const PartRec q = a.prec[(size_t)row * a.parts + p];
@@ -1717,6 +1725,7 @@ __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
     __shared__ RowShared S;
     if (a.parts > 1) {
         const int row = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
+        if (!row_live(a.sh, row)) return;
         if (row_dt(a.sh, row) == DT_BF16)
             row_part_plain<DT_BF16>(a, S, row, part);
         else
@@ -1724,6 +1733,7 @@ __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
         return;
     }
     const int row = blockIdx.x;
+    if (!row_live(a.sh, row)) return;  // past its sequence's draft length
     const bool bf = row_dt(a.sh, row) == DT_BF16;
     if (a.use_k) {
         if (bf)
@@ -1783,6 +1793,7 @@ __device__ __forceinline__ void argmax_body(const Shape& sh, int row, int32_t* g
 __global__ void __launch_bounds__(kRB) k_row_argmax(Shape sh, int32_t* gidx) {
     __shared__ u64 s_red[kRW];
     const int row = blockIdx.x;
+    if (!row_live(sh, row)) return;
     if (sh.tdt == DT_BF16)
         argmax_body<DT_BF16>(sh, row, gidx, s_red);
     else

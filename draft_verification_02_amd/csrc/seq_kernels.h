@@ -43,10 +43,11 @@ struct SeqArgs {
 __device__ __forceinline__ int first_rejection(const SeqArgs& a, int b) {
     const int lane = threadIdx.x & 63;
     const int K = a.sh.K;
-    for (int k0 = 0; k0 < K; k0 += 64) {
+    const int Kb = seq_len(a.sh, b);
+    for (int k0 = 0; k0 < Kb; k0 += 64) {
         const int k = k0 + lane;
         bool reject = false;
-        if (k < K) {
+        if (k < Kb) {
             const double p = a.rec[(size_t)b * (K + 1) + k].s.prob_at_token;
             // a point-mass draft gives its own token probability 1
             const double q = a.point ? 1.0 : a.rec[a.sh.n_trows + (size_t)b * K + k].s.prob_at_token;
@@ -56,10 +57,10 @@ __device__ __forceinline__ int first_rejection(const SeqArgs& a, int b) {
         const unsigned long long m = __ballot(reject);
         if (m) return k0 + __ffsll((long long)m) - 1;
     }
-    return K;
+    return Kb;
 }
 
-// The stop row pair of a sequence: target row j, draft row j when j < K
+// The stop row pair of a sequence: target row j, draft row j when j < K_b
 // (or, for point-mass drafts, the drafted token dtok, where q = 1).
 struct StopRow {
     const char* tp;
@@ -68,7 +69,8 @@ struct StopRow {
     float Mt, Md, thr_t, thr_d;
     double zt, zd;
     bool has_draft;
-    int dtok;  // -1 unless the draft is a point mass at dtok
+    bool bonus;  // j is the sequence's draft length: the bonus row, drawn from p_j
+    int dtok;    // -1 unless the draft is a point mass at dtok
 };
 
 __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
@@ -81,8 +83,10 @@ __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
     s.Mt = Rt.s.max_logit;
     s.thr_t = Rt.s.thresh;
     s.zt = Rt.s.z_kept;
-    s.has_draft = j < K && !a.point;
-    s.dtok = j < K && a.point ? a.sh.tokens[(size_t)b * K + j] : -1;
+    const int Kb = seq_len(a.sh, b);
+    s.bonus = j >= Kb;
+    s.has_draft = j < Kb && !a.point;
+    s.dtok = j < Kb && a.point ? a.sh.tokens[(size_t)b * K + j] : -1;
     if (s.has_draft) {
         const int rd = a.sh.n_trows + b * K + j;
         const RowRec& Rd = a.rec[rd];
@@ -195,7 +199,7 @@ __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, do
     double er, tr, ep, tp;
     seq_excl_scan(sr, s_val, s_excl, s_total, er, tr);
     seq_excl_scan(sp, s_val, s_excl, s_total, ep, tp);
-    const bool usep = (j == a.sh.K) || !(tr > 0.0);
+    const bool usep = s.bonus || !(tr > 0.0);
     const double S = usep ? tp : tr;
     const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
     const double mine = usep ? sp : sr;
@@ -250,7 +254,7 @@ __device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, i
     double er, tr, ep, tp;
     seq_excl_scan(sr, s_val, s_excl, s_total, er, tr);
     seq_excl_scan(sp, s_val, s_excl, s_total, ep, tp);
-    const bool usep = (j == a.sh.K) || !(tr > 0.0);
+    const bool usep = s.bonus || !(tr > 0.0);
     const double S = usep ? tp : tr;
     const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
     const double mine = usep ? sp : sr;
@@ -376,7 +380,7 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     }
     double er, ep, tr, tp;
     seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
-    const bool usep = (jc == K) || !(tr > 0.0);
+    const bool usep = s.bonus || !(tr > 0.0);
     const double S = usep ? tp : tr;
     const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)jc, PURPOSE_SAMPLE)) * S;
     const double mine = usep ? sp : sr;
@@ -532,7 +536,7 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
     double er, ep, tr, tp;
     seq_excl_scan2(mr, mp, s_wa, s_wb, er, ep, tr, tp);  // (its barrier also publishes s_j)
     const int j = s_j;
-    const bool usep = (j == K) || !(tr > 0.0);
+    const bool usep = j >= seq_len(a.sh, b) || !(tr > 0.0);
     const double S = usep ? tp : tr;
     const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -622,10 +626,11 @@ __global__ void k_greedy_prefix(Shape sh, const int32_t* gidx, int32_t* out_toke
     const int b = blockIdx.x * blockDim.x + threadIdx.x;
     if (b >= sh.B) return;
     const int K = sh.K;
+    const int Kb = seq_len(sh, b);
     const int32_t* g = gidx + (size_t)b * (K + 1);
     const int32_t* d = sh.tokens + (size_t)b * K;
-    int j = K;
-    for (int k = 0; k < K; ++k)
+    int j = Kb;
+    for (int k = 0; k < Kb; ++k)
         if (d[k] != g[k]) {
             j = k;
             break;
@@ -635,6 +640,34 @@ __global__ void k_greedy_prefix(Shape sh, const int32_t* gidx, int32_t* out_toke
     out[j] = g[j];
     for (int k = j + 1; k <= K; ++k) out[k] = -1;
     out_num[b] = j;
+}
+
+// Per-position acceptance counters from the per-sequence results (one
+// workgroup): tested[k] = sequences whose accept test at position k ran
+// (k < K_b and num_accepted >= k), accepted[k] = sequences that accepted
+// position k (num_accepted > k).  Integer counts in LDS, so the result does
+// not depend on timing.
+constexpr int kTelemMaxK = 1024;
+__global__ void __launch_bounds__(kSB) k_accept_counts(Shape sh, const int32_t* out_num, int32_t* tested,
+                                                       int32_t* accepted) {
+    __shared__ int s_t[kTelemMaxK], s_a[kTelemMaxK];
+    const int K = sh.K;
+    for (int k = threadIdx.x; k < K; k += kSB) {
+        s_t[k] = 0;
+        s_a[k] = 0;
+    }
+    __syncthreads();
+    for (int b = threadIdx.x; b < sh.B; b += kSB) {
+        const int n = out_num[b];
+        const int nt = min(n + 1, seq_len(sh, b));
+        for (int k = 0; k < nt; ++k) atomicAdd(&s_t[k], 1);
+        for (int k = 0; k < n; ++k) atomicAdd(&s_a[k], 1);
+    }
+    __syncthreads();
+    for (int k = threadIdx.x; k < K; k += kSB) {
+        if (tested) tested[k] = s_t[k];
+        if (accepted) accepted[k] = s_a[k];
+    }
 }
 
 // Copy row records to the caller's stats arrays.

@@ -111,8 +111,17 @@ void take_events(void** evb, void** eva) {
     g_ev_before = g_ev_after = nullptr;
 }
 
+int run_counts(const Shape& sh, const int32_t* out_num, int32_t* tested, int32_t* accepted,
+               hipStream_t stream) {
+    if (!tested && !accepted) return SPEC_OK;
+    if (sh.K == 0) return SPEC_OK;
+    hipLaunchKernelGGL(k_accept_counts, dim3(1), dim3(kSB), 0, stream, sh, out_num, tested, accepted);
+    return launch_status();
+}
+
 int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, int32_t* out_tokens,
-               int32_t* out_num, hipStream_t stream, int tdt) {
+               int32_t* out_num, hipStream_t stream, int tdt, const int32_t* lens = nullptr,
+               int32_t* tested = nullptr, int32_t* accepted = nullptr) {
     int tsz;
     if (!dtype_size(tdt, &tsz)) return SPEC_E_UNSUPPORTED;
     int rc = check_sizes(B, K, V);
@@ -123,7 +132,7 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     Workspace* ws;
     rc = get_workspace(stream, 0, n_trows, 0, &ws);
     if (rc) return rc;
-    const Shape sh{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0, n_trows, 0};
+    const Shape sh{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0, n_trows, 0, lens};
     void *evb, *eva;
     take_events(&evb, &eva);
     if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
@@ -132,13 +141,15 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
     hipLaunchKernelGGL(k_greedy_prefix, dim3((unsigned)ceil_div(B, 256)), dim3(256), 0, stream, sh,
                        (const int32_t*)ws->gidx, out_tokens, out_num);
-    return launch_status();
+    if ((rc = launch_status())) return rc;
+    return run_counts(sh, out_num, tested, accepted, stream);
 }
 
 int run_sampling(const void* target, const void* draft, const int32_t* tokens, int B, int K, int V,
                  float temperature, int top_k, float top_p, uint64_t seed, int32_t* out_tokens,
                  int32_t* out_num, hipStream_t stream, int tdt, int ddt, spec_row_stats_t* tstats,
-                 spec_row_stats_t* dstats, bool point) {
+                 spec_row_stats_t* dstats, bool point, const int32_t* lens = nullptr,
+                 int32_t* tested = nullptr, int32_t* accepted = nullptr) {
     int tsz, dsz = 4;
     if (!dtype_size(tdt, &tsz)) return SPEC_E_UNSUPPORTED;
     if (K > 0 && !point && !dtype_size(ddt, &dsz)) return SPEC_E_UNSUPPORTED;
@@ -166,7 +177,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     if (rc) return rc;
 
     const Shape sh{static_cast<const char*>(target), static_cast<const char*>(draft), tokens, B, K, V,
-                   tdt, ddt, tsz, dsz, n_trows, n_drows};
+                   tdt, ddt, tsz, dsz, n_trows, n_drows, lens};
     RowArgs ra;
     ra.sh = sh;
     // c = c_hi + c_lo with c_hi the largest float below c, so that c_lo > 0:
@@ -242,7 +253,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
                            (const RowRec*)ws->rec, n_trows, n_drows, tstats, dstats);
         if ((rc = launch_status())) return rc;
     }
-    return SPEC_OK;
+    return run_counts(sh, out_num, tested, accepted, stream);
 }
 
 }  // namespace
@@ -276,6 +287,24 @@ int spec_verify_point(const void* target_logits, const int32_t* draft_tokens, in
     return run_sampling(target_logits, nullptr, draft_tokens, B, K, V, temperature, top_k, top_p, seed,
                         out_tokens, out_num_accepted, s, target_dtype, SPEC_DTYPE_F32, nullptr, nullptr,
                         true);
+}
+
+int spec_verify_ragged(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens,
+                       const int32_t* draft_lens, int B, int K, int V, float temperature, int top_k,
+                       float top_p, uint64_t seed, int32_t* out_tokens, int32_t* out_num_accepted,
+                       int32_t* pos_tested, int32_t* pos_accepted, void* stream, int target_dtype,
+                       int draft_dtype) {
+    if (!std::isfinite(temperature) || temperature < 0.0f) return SPEC_E_INVALID;
+    if (!(top_p > 0.0f && top_p <= 1.0f)) return SPEC_E_INVALID;
+    if (B > 0 && !draft_lens) return SPEC_E_INVALID;
+    if ((pos_tested || pos_accepted) && K > kTelemMaxK) return SPEC_E_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (temperature == 0.0f)
+        return run_greedy(target_logits, draft_tokens, B, K, V, out_tokens, out_num_accepted, s,
+                          target_dtype, draft_lens, pos_tested, pos_accepted);
+    return run_sampling(target_logits, draft_logits, draft_tokens, B, K, V, temperature, top_k, top_p,
+                        seed, out_tokens, out_num_accepted, s, target_dtype, draft_dtype, nullptr,
+                        nullptr, false, draft_lens, pos_tested, pos_accepted);
 }
 
 int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int K, int V,

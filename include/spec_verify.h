@@ -127,6 +127,34 @@ int spec_verify(const void* target_logits, const void* draft_logits,
                 int target_dtype, int draft_dtype);
 
 /*
+ * Per-sequence draft lengths (the serving engines' per-request number of
+ * speculative tokens: "DFlash" page, section 2, on block size and
+ * num_speculative_tokens) with per-position acceptance counters (the
+ * measured acceptance by position in "FlashMap" section 6; threatfrontier,
+ * "Practical guidance": measure the acceptance rate first).
+ *   draft_lens     [B] int32 device array: sequence b verifies only its first
+ *                  K_b = draft_lens[b] drafts (values are clamped to [0, K])
+ *                  against target rows 0..K_b; the bonus token comes from row
+ *                  K_b.  Rows past K_b are not read (the padded [B][K+1][V] /
+ *                  [B][K][V] / [B][K] layout of spec_verify is kept).
+ *   out_tokens     [B][K+1]: accepted drafts, the emitted token, then -1.
+ *   pos_tested     [K] int32 or NULL: sequences whose accept test at position
+ *                  k ran (k < K_b and num_accepted >= k).
+ *   pos_accepted   [K] int32 or NULL: sequences that accepted position k.
+ * Everything else as spec_verify (temperature == 0: greedy, accepting while
+ * d_k equals the target argmax for k < K_b).  draft_lens must be non-NULL
+ * when B > 0; the counters need K <= 1024.  The counters are written by one
+ * extra small kernel.
+ */
+int spec_verify_ragged(const void* target_logits, const void* draft_logits,
+                       const int32_t* draft_tokens, const int32_t* draft_lens,
+                       int B, int K, int V, float temperature, int top_k,
+                       float top_p, uint64_t seed, int32_t* out_tokens,
+                       int32_t* out_num_accepted, int32_t* pos_tested,
+                       int32_t* pos_accepted, void* stream, int target_dtype,
+                       int draft_dtype);
+
+/*
  * Verification against point-mass drafts: a drafter that proposes each token
  * with certainty (a lookup table, n-gram or prompt-lookup proposer, or greedy
  * draft heads; "Speculative decoding and multi-token prediction: how LLMs

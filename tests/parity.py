@@ -220,3 +220,61 @@ def check_point(w: wl.Workload, tokens: np.ndarray, seqs=None, report=None) -> R
         rep.details.append((b, why))
     assert rep.mismatch_tolerated <= 1e-6 * rep.decisions, rep
     return rep
+
+
+def counters_of(num: np.ndarray, lens: np.ndarray, K: int):
+    """Per-position acceptance counters by their definition."""
+    tested = np.zeros(K, np.int64)
+    accepted = np.zeros(K, np.int64)
+    for n, L in zip(num.tolist(), lens.tolist()):
+        L = min(max(L, 0), K)
+        tested[:min(n + 1, L)] += 1
+        accepted[:n] += 1
+    return tested, accepted
+
+
+def check_ragged(w: wl.Workload, lens: np.ndarray, seqs=None, report=None) -> Report:
+    """spec_verify_ragged on the GPU against the oracle run on each sequence's
+    own prefix (first lens[b] drafts, target rows 0..lens[b]); the same
+    ambiguity bands as check_sampling; the counters against their definition
+    on the GPU's own per-sequence results."""
+    rep = report or Report()
+    t, d, k = upload(w)
+    L = torch.from_numpy(np.ascontiguousarray(lens, dtype=np.int32)).to("cuda")
+    g_tok, g_num, g_t, g_a = binding.spec_verify_ragged(t, d, k, L, w.temperature, w.top_k, w.top_p,
+                                                        w.seed)
+    torch.cuda.synchronize()
+    g_tok, g_num = g_tok.cpu().numpy(), g_num.cpu().numpy()
+    K = w.K
+    if K > 0:
+        et, ea = counters_of(g_num, lens, K)
+        np.testing.assert_array_equal(g_t.cpu().numpy(), et)
+        np.testing.assert_array_equal(g_a.cpu().numpy(), ea)
+    if seqs is None:
+        seqs = range(w.B)
+    for b in seqs:
+        kb = int(min(max(lens[b], 0), K))
+        assert (g_tok[b, kb + 1:] == -1).all(), b
+        tk = np.ascontiguousarray(w.tokens[b:b + 1, :kb])
+        if w.temperature == 0:
+            r = oracle.verify_greedy(w.target[b:b + 1, :kb + 1], tk)
+            assert int(g_num[b]) == int(r["num_accepted"][0]) and np.array_equal(g_tok[b, :kb + 1], r["tokens"][0]), b
+            continue
+        dd = None if kb == 0 else np.ascontiguousarray(w.draft[b:b + 1, :kb])
+        r = oracle.verify(np.ascontiguousarray(w.target[b:b + 1, :kb + 1]), dd, tk, f32(w.temperature),
+                          w.top_k, f32(w.top_p), w.seed, seq_base=int(b))
+        j_o, j_g = int(r["num_accepted"][0]), int(g_num[b])
+        rep.decisions += j_o + (1 if j_o < kb else 0) + 1
+        if j_g == j_o and np.array_equal(g_tok[b, :kb + 1], r["tokens"][0]):
+            continue
+        amb_t = r["target_info"][0]["nucleus_margin"] <= NUCLEUS_BAND
+        amb_d = r["draft_info"][0]["nucleus_margin"] <= NUCLEUS_BAND if kb > 0 else np.zeros(0, bool)
+        m = min(j_g, j_o)
+        if j_g != j_o:
+            ok = r["accept_margin"][0, m] <= ACCEPT_BAND or amb_t[m] or (m < kb and amb_d[m])
+        else:
+            ok = r["sample_margin"][0] <= SAMPLE_BAND or amb_t[m] or (m < kb and amb_d[m])
+        assert ok, (b, g_tok[b].tolist(), r["tokens"][0].tolist())
+        rep.mismatch_tolerated += 1
+    assert rep.mismatch_tolerated <= 1e-6 * max(1, rep.decisions), rep
+    return rep

@@ -82,6 +82,17 @@ def test_point_entry_rejects_invalid_arguments_on_host(lib, kw, code):
                                  a["stream"], a["tdt"]) == code
 
 
+def test_ragged_entry_rejects_invalid_arguments_on_host(lib):
+    p = ctypes.c_void_p(16)
+    def call(lens=p, K=1, T=1.0, top_p=1.0, tested=None, B=1):
+        return lib.spec_verify_ragged(p, p, p, lens, B, K, 4, T, 0, top_p, 0, p, p, tested, None,
+                                      None, 0, 0)
+    assert call(lens=None) == 1
+    assert call(T=-1.0) == 1 and call(top_p=0.0) == 1
+    assert call(K=1025, tested=p) == 1
+    assert call(B=0, lens=None) == 0
+
+
 def test_empty_batch_returns_ok_without_device_work(lib):
     assert _call(lib, B=0, target=None, draft=None, tokens=None, out=None, num=None) == 0
     assert lib.spec_verify_greedy(None, None, 0, 3, 10, None, None, None, 1) == 0

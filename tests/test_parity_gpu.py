@@ -318,3 +318,47 @@ def test_point_edge_cases():
     ga = binding.spec_verify(tgt, to_device(oh), kt, w1.temperature, w1.top_k, w1.top_p, w1.seed)
     torch.cuda.synchronize()
     assert torch.equal(pa[0], ga[0]) and torch.equal(pa[1], ga[1])
+
+
+# ---------------------------------------------------------------------------
+# Per-sequence draft lengths and acceptance counters
+# ---------------------------------------------------------------------------
+
+def _lens(B, K, seed):
+    return np.random.default_rng(seed).integers(0, K + 1, B).astype(np.int32)
+
+
+def test_ragged_c3_full_size_sampled():
+    from parity import check_ragged
+    _print_case("ragged c3 full, 8 sequences checked")
+    w = wl.config(3)
+    print(check_ragged(w, _lens(w.B, w.K, 1), seqs=[0, 2, 7, 12, 19, 25, 30, 31]))
+
+
+@pytest.mark.parametrize("cfg,kw", [(3, dict(B=8, V=40000)), (2, dict(B=4, V=20000)),
+                                    (5, dict(B=6, V=30011)), (1, {}), (4, dict(B=16, V=20000))])
+def test_ragged_small_all_sequences(cfg, kw):
+    from parity import Report, check_ragged
+    _print_case(f"ragged cfg{cfg} {kw}")
+    rep = Report()
+    for rnd in range(3):
+        w = wl.config(cfg, rnd, **kw)
+        check_ragged(w, _lens(w.B, w.K, 10 * cfg + rnd), report=rep)
+    print(rep)
+
+
+def test_ragged_lengths_extremes_and_full_equals_plain():
+    """All lengths 0 (bonus only), all K (bitwise equal to spec_verify),
+    out-of-range lengths (clamped)."""
+    from parity import check_ragged, upload
+    _print_case("ragged extremes")
+    w = wl.make(6, 5, 9000, temperature=0.8, top_p=0.9, rho=0.9, seed=41, vseed=42)
+    check_ragged(w, np.zeros(6, np.int32))
+    check_ragged(w, np.full(6, 5, np.int32))
+    check_ragged(w, np.array([-3, 0, 2, 5, 9, 100], np.int32))
+    t, d, k = upload(w)
+    a = binding.spec_verify_ragged(t, d, k, torch.full((6,), 5, dtype=torch.int32, device="cuda"),
+                                   w.temperature, w.top_k, w.top_p, w.seed)
+    b = binding.spec_verify(t, d, k, w.temperature, w.top_k, w.top_p, w.seed)
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])

@@ -13,6 +13,10 @@ the call's stream, and the CPU oracle timed on the host as a baseline.
 --mode point measures spec_verify_point instead: the same target rows, with
 the drafts given as point masses (each draft row's argmax, the proposals of a
 greedy draft head) and no draft logits read.
+
+--mode ragged measures spec_verify_ragged with per-sequence draft lengths
+drawn uniformly from 0..K (seeded) and the per-position acceptance counters
+on; the bytes counted are those of the rows inside each sequence's length.
 """
 from __future__ import annotations
 
@@ -30,6 +34,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936, 1 GPU"
+METRIC_RAGGED = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K<=7 V=151936, 1 GPU, "
+                 "per-sequence draft lengths U{0..7} (spec_verify_ragged)")
 METRIC_POINT = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936, 1 GPU, "
                 "point-mass drafts (spec_verify_point)")
 PEAK_HBM_GBS = 8000.0
@@ -75,11 +81,21 @@ def traffic_from_profiles(config_name: str, src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, max_seqs: int, point_tokens=None):
+def cpu_baseline(w, max_seqs: int, point_tokens=None, lens=None):
     import oracle  # CPU baseline leg only
 
     seqs = list(range(min(w.B, max_seqs)))
     t0 = time.perf_counter()
+    if lens is not None:
+        sub = slice(0, len(seqs))
+        oracle.verify_ragged(w.target[sub], w.draft[sub], w.tokens[sub], lens[sub],
+                             float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p)),
+                             w.seed)
+        dt = time.perf_counter() - t0
+        return {"value": round(int(lens[sub].sum()) / dt, 3), "unit": "verified draft positions/s",
+                "cores": 1, "kind": "oracle",
+                "sample": f"{len(seqs)} of {w.B} sequences of the same workload, single-threaded "
+                          f"fp64 C++ oracle, {dt:.2f} s"}
     for b in seqs:
         if point_tokens is not None:
             oracle.verify_point(w.target[b:b + 1], point_tokens[b:b + 1],
@@ -104,7 +120,7 @@ def main():
     ap.add_argument("--no-settle", dest="settle", action="store_false",
                     help="skip the untimed settle phase after the warmup steps")
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--mode", choices=["general", "point"], default="general",
+    ap.add_argument("--mode", choices=["general", "point", "ragged"], default="general",
                     help="general: spec_verify with draft logits (the headline); point: "
                          "spec_verify_point with point-mass drafts")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
@@ -138,9 +154,16 @@ def main():
         raise SystemExit("the headline workload is a sampling workload")
     dev = torch.device("cuda:0")
     point = args.mode == "point"
+    ragged = args.mode == "ragged"
     # point-mass drafts: the draft rows' argmax, a greedy draft head's proposals
     ptoks = np.argmax(wl.as_f32(w.draft), axis=2).astype(np.int32) if point else None
     ideal = w.target.nbytes if point else w.ideal_bytes()
+    lens_np = None
+    if ragged:
+        lens_np = np.random.default_rng(w.seed & 0xFFFFFFFF).integers(0, w.K + 1, w.B).astype(np.int32)
+        row_t = w.target[0, 0].nbytes
+        row_d = w.draft[0, 0].nbytes
+        ideal = int(((lens_np + 1) * row_t + lens_np * row_d).sum())
     n_sets = args.sets or max(4, int(np.ceil(2.5 * MALL_BYTES / ideal)))
 
     def up(a):
@@ -150,6 +173,7 @@ def main():
 
     sets = [(up(w.target), None if point else up(w.draft), up(ptoks if point else w.tokens))
             for _ in range(n_sets)]
+    lens_t = up(lens_np) if ragged else None
     out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
     out_n = torch.empty((w.B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
@@ -159,6 +183,11 @@ def main():
         if point:
             binding.spec_verify_point(t, k, w.temperature, w.top_k, w.top_p, w.seed, out_t, out_n,
                                       stream=stream)
+            return
+        if ragged:
+            binding.spec_verify_ragged(t, d, k, lens_t, w.temperature, w.top_k, w.top_p, w.seed,
+                                       counters=True, out_tokens=out_t, out_num_accepted=out_n,
+                                       stream=stream)
             return
         binding.spec_verify(t, d, k, w.temperature, w.top_k, w.top_p, w.seed, out_t, out_n,
                             stream=stream)
@@ -216,11 +245,11 @@ def main():
 
     src_hash = kernel_source_hash()
     achieved = ideal / (k_ms * 1e-3) / 1e9
-    traffic = None if point else traffic_from_profiles(w.name, src_hash)
-    positions = w.B * w.K
+    traffic = None if (point or ragged) else traffic_from_profiles(w.name, src_hash)
+    positions = int(lens_np.sum()) if ragged else w.B * w.K
     value = positions / (ms * 1e-3)
     line = {
-        "metric": METRIC_POINT if point else METRIC,
+        "metric": METRIC_POINT if point else (METRIC_RAGGED if ragged else METRIC),
         "value": round(value, 1),
         "unit": "verified draft positions/s",
         "n_gpus": 1,
@@ -233,7 +262,8 @@ def main():
         "vs_baseline": None,
         "dtype": "f32+f64",
         "data": "synthetic",
-        "config": {"workload": w.name + ("-point" if point else ""), "B": w.B, "K": w.K, "V": w.V,
+        "config": {"workload": w.name + ("-point" if point else ("-ragged" if ragged else "")),
+                   "B": w.B, "K": w.K, "V": w.V,
                    "target": "bf16", "draft": "point mass" if point else "f32",
                    "temperature": w.temperature, "top_k": w.top_k,
                    "top_p": w.top_p, "input_sets_rotated": n_sets, "ideal_bytes": ideal},
@@ -245,8 +275,10 @@ def main():
                      "kernel_source_hash": src_hash},
         "wall_s_timed": round(t_wall, 4),
     }
+    if ragged:
+        line["config"]["draft_lens_total"] = positions
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, ptoks)
+        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, ptoks, lens_np)
     print(json.dumps(line), flush=True)
 
 

@@ -1116,8 +1116,12 @@ __device__ __forceinline__ Sel row_select_reread(RowShared& S, const RowArgs& a,
 // 8 k is the smallest multiple of 8 at or above the thread's largest
 // x * log2(e) / T so far: every term is at most 1, a change of reference is
 // an exact power-of-two rescale (ldexp), and -8 k is an exact float.  The
-// exponent is two FMAs, x * c_lo + (x * c_hi - 8 k), so the rounding of
-// log2(e)/T to a float adds no systematic error.
+// exponent is one FMA, x * c_hi - 8 k, with c_hi = c - c_lo the largest
+// float below c = log2(e) / T: the sum is of 2^(x c_hi - 8 k).  Against the
+// row maximum M that is Z = sum 2^((x - M) c_hi), within c_lo ln2 E[M - x]
+// (under the softmax weights, a few binary orders times c 2^-23) of the sum
+// with c itself; sums in units of 2^(8 kref) of the exact c take the factor
+// 2^(M c_lo).
 template <int DT, int MODE>
 __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row) {
     const char* rowp = row_ptr(a.sh, row);
@@ -1186,11 +1190,13 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
             }
             if (k_th != -INFINITY) {
                 const float nmc = -8.f * k_th;
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                // four partial sums, each started by its first term
+                float acc[4];
 #pragma unroll
                 for (int s = 0; s < kREPT; ++s) {
-                    const float e = fmaf(v[s], a.c_lo, fmaf(v[s], a.c_hi, nmc));
-                    acc[s & 3] += __builtin_amdgcn_exp2f(e);
+                    const float e = fmaf(v[s], a.c_hi, nmc);
+                    const float term = __builtin_amdgcn_exp2f(e);
+                    acc[s & 3] = s < 4 ? term : acc[s & 3] + term;
                 }
                 z_th += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
             }
@@ -1324,8 +1330,8 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     double ptok = 0.0;    // thread 0: the drafted token's probability, when it is kept
 
     if (!kFilt) {
-        // z * 2^(8 k - M log2(e) / T)
-        Z = (kSum && tot.k != -INFINITY) ? tot.z * exp2(8.0 * (double)tot.k - (double)M * a.c64) : 0.0;
+        // z * 2^(8 k - M c_hi)
+        Z = (kSum && tot.k != -INFINITY) ? tot.z * exp2(8.0 * (double)tot.k - (double)M * (double)a.c_hi) : 0.0;
         z_kept = Z;
         if (threadIdx.x == 0 && d_tok >= 0 && d_tok < V) ptok = exp(((double)xd - (double)M) * a.inv_T) / Z;
     } else {
@@ -1335,9 +1341,13 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         // power-of-two reference of the row: the streaming sums use the same
         // (a thread's reference is ceil(its max * c / 8))
         const float kref = M != -INFINITY ? ceilf(M * a.c8) : 0.f;
-        // the row sum in grid units (2^(8 kref)); one grid unit is
-        // 2^(8 kref - M log2(e) / T) against the row maximum
-        const double Zg = (kSum && tot.k != -INFINITY) ? ldexp(tot.z, (int)(8.f * (tot.k - kref))) : 0.0;
+        // the row sum in grid units (2^(8 kref) of the exact c; one grid unit
+        // is 2^(8 kref - M c) against the row maximum): the streamed sum of
+        // 2^(x c_hi - 8 kref) times 2^(M c_lo) (a series, |M c_lo| being tiny)
+        const double ml = (double)M * (double)a.c_lo * 0.6931471805599453;
+        const double Zg = (kSum && tot.k != -INFINITY)
+                              ? ldexp(tot.z, (int)(8.f * (tot.k - kref))) * (1.0 + ml * (1.0 + ml * (0.5 + ml / 6.0)))
+                              : 0.0;
         // Wave 1 takes the grid unit and the drafted token's weight in grid
         // units (two fp64 exp2) while wave 0 searches the bins.
         auto side = [&]() {
@@ -1675,10 +1685,12 @@ __device__ __forceinline__ void row_part_plain(const RowArgs& a, RowShared& S, i
             }
             if (k_th != -INFINITY) {
                 const float nmc = -8.f * k_th;
-                float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                float acc[4];
 #pragma unroll
-                for (int q = 0; q < kREPT; ++q)
-                    acc[q & 3] += __builtin_amdgcn_exp2f(fmaf(v[q], a.c_lo, fmaf(v[q], a.c_hi, nmc)));
+                for (int q = 0; q < kREPT; ++q) {
+                    const float term = __builtin_amdgcn_exp2f(fmaf(v[q], a.c_hi, nmc));
+                    acc[q & 3] = q < 4 ? term : acc[q & 3] + term;
+                }
                 z_th += (double)((acc[0] + acc[1]) + (acc[2] + acc[3]));
             }
         }
@@ -1698,7 +1710,7 @@ __global__ void __launch_bounds__(256) k_row_merge(RowArgs a) {
         t = row_tot_combine(t, RowTot{q.m, q.k, q.z, 0ull});
     }
     const float M = t.m;
-    const double Z = t.k != -INFINITY ? t.z * exp2(8.0 * (double)t.k - (double)M * a.c64) : 0.0;
+    const double Z = t.k != -INFINITY ? t.z * exp2(8.0 * (double)t.k - (double)M * (double)a.c_hi) : 0.0;
     const int V = a.sh.V;
     RowRec r;
     r.s.max_logit = M;

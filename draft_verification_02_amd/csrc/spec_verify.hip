@@ -180,9 +180,9 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
                    tdt, ddt, tsz, dsz, n_trows, n_drows, lens};
     RowArgs ra;
     ra.sh = sh;
-    // c = c_hi + c_lo with c_hi the largest float below c, so that c_lo > 0:
-    // for x = -inf both products are -inf and their sum stays -inf (a c_lo of
-    // the other sign, or zero, would give NaN).
+    // c = c_hi + c_lo with c_hi the largest float below c (so c_hi > 0 and
+    // x = -inf gives -inf, never NaN); streamed sums use c_hi, and c_lo
+    // corrects them where the exact c's units are needed.
     float c_hi = (float)c;
     if ((double)c_hi >= c) c_hi = std::nextafter(c_hi, 0.0f);
     ra.c_hi = c_hi;

@@ -181,6 +181,21 @@ def test_temperatures(T):
     check_sampling(w)
 
 
+@pytest.mark.parametrize("offset", [-3000.0, 500.0, 20000.0])
+@pytest.mark.parametrize("top_p", [0.9, 1.0])
+def test_large_logit_offsets(offset, top_p):
+    """Logits shifted far from zero (f32 rows): the streamed sums use the
+    float just below log2(e)/T and take a 2^(M c_lo) factor into the exact
+    units, which grows with |M|; the nucleus target and p(d_k) must still
+    match the oracle."""
+    _print_case(f"offset {offset} top_p {top_p}")
+    w = wl.make(3, 4, 20011, target_dtype=wl.F32, temperature=0.6, top_p=top_p, rho=0.85,
+                seed=int(abs(offset)) + 3, vseed=11)
+    w.target = (w.target + np.float32(offset)).astype(np.float32)
+    w.draft = (w.draft + np.float32(offset)).astype(np.float32)
+    check_sampling(w)
+
+
 def test_greedy_edge_cases():
     _print_case("greedy edges")
     rng = np.random.default_rng(12)

@@ -9,16 +9,19 @@
 //                                         candidates, so no sum over the row.
 //              Capture: every 16-byte load (8 bf16 or 4 fp32 logits) whose
 //              maximum reaches a threshold set from the row's first tile is
-//              appended, raw, to its wave's LDS segment.  After the stream
-//              the segments are expanded into (logit, index) candidates, the
-//              kept set is resolved exactly from them and, if they cannot
-//              decide (overflow, too few), by re-reading the row.  Writes the
-//              row record (M, Z, threshold, p(d_k) or q(d_k)) and, for target
-//              rows, the kept tokens sorted by index.
+//              appended, raw, to its wave's LDS segment, and expanded 64
+//              units at a time into (logit, index) candidates while the row
+//              streams.  After the stream the kept set is resolved exactly
+//              from the candidates and, if they cannot decide (overflow, too
+//              few), by re-reading the row.  Writes the row record (M, Z,
+//              threshold, p(d_k) or q(d_k)) and, for target rows, the kept
+//              tokens sorted by index.
+//  k_row_merge  : the record of an unfiltered row split over workgroups.
 //  k_row_argmax : greedy mode, lowest-index argmax of a target row.
 //
 // Row numbering: rows [0, B*(K+1)) are target rows b*(K+1)+k, rows
-// [B*(K+1), B*(2K+1)) are draft rows b*K+k.
+// [B*(K+1), B*(2K+1)) are draft rows b*K+k (none for point-mass drafts).
+// With per-sequence draft lengths, rows past a sequence's length exit at once.
 #pragma once
 
 #include <type_traits>

@@ -66,7 +66,19 @@ struct Shape {
     int tsz, dsz;
     int n_trows, n_drows;
     const int32_t* lens;  // per-sequence draft lengths in [0, K] (clamped), or null: all K
+    int32_t* tested;      // [K] per-position acceptance counters, each may be null (zeroed by
+    int32_t* accepted;    //   the row kernel's first workgroup, counted by the output writers)
 };
+
+// The first row workgroup of a call clears the acceptance counters; the
+// kernels that write a sequence's outputs run after it on the stream.
+__device__ __forceinline__ void clear_counters(const Shape& sh) {
+    if (blockIdx.x != 0) return;
+    for (int k = threadIdx.x; k < sh.K; k += blockDim.x) {
+        if (sh.tested) sh.tested[k] = 0;
+        if (sh.accepted) sh.accepted[k] = 0;
+    }
+}
 
 __device__ __forceinline__ const char* row_ptr(const Shape& sh, int row) {
     if (row < sh.n_trows) return sh.target + (size_t)row * sh.V * sh.tsz;
@@ -1738,6 +1750,7 @@ __global__ void __launch_bounds__(256) k_row_merge(RowArgs a) {
 
 __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
     __shared__ RowShared S;
+    clear_counters(a.sh);
     if (a.parts > 1) {
         const int row = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
         if (!row_live(a.sh, row)) return;
@@ -1808,6 +1821,7 @@ __device__ __forceinline__ void argmax_body(const Shape& sh, int row, int32_t* g
 __global__ void __launch_bounds__(kRB) k_row_argmax(Shape sh, int32_t* gidx) {
     __shared__ u64 s_red[kRW];
     const int row = blockIdx.x;
+    clear_counters(sh);
     if (!row_live(sh, row)) return;
     if (sh.tdt == DT_BF16)
         argmax_body<DT_BF16>(sh, row, gidx, s_red);

@@ -172,6 +172,18 @@ __device__ __forceinline__ int pick_thread(double mine, double run_excl, double 
     return tau;
 }
 
+// Per-position acceptance counters of sequence b (num_accepted j): its test
+// at position k ran for k <= j, k < K_b, and accepted for k < j.  Integer
+// atomics, so the totals do not depend on order.
+__device__ __forceinline__ void count_accepts(const Shape& sh, int b, int j) {
+    if (sh.tested) {
+        const int nt = min(j + 1, seq_len(sh, b));
+        for (int k = 0; k < nt; ++k) atomicAdd(&sh.tested[k], 1);
+    }
+    if (sh.accepted)
+        for (int k = 0; k < j; ++k) atomicAdd(&sh.accepted[k], 1);
+}
+
 __device__ __forceinline__ void write_outputs(const SeqArgs& a, int b, int j, int y) {
     const int K = a.sh.K;
     int32_t* out = a.out_tokens + (size_t)b * (K + 1);
@@ -179,6 +191,7 @@ __device__ __forceinline__ void write_outputs(const SeqArgs& a, int b, int j, in
     out[j] = y;
     for (int k = j + 1; k <= K; ++k) out[k] = -1;
     a.out_num[b] = j;
+    count_accepts(a.sh, b, j);
 }
 
 // Draw over the whole stop row pair with one workgroup (thread-contiguous
@@ -423,7 +436,10 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     int32_t* out = a.out_tokens + (size_t)b * (K + 1);
     for (int k = threadIdx.x; k <= K; k += kSB)
         out[k] = k < jc ? (k < kSB ? tok : a.sh.tokens[(size_t)b * K + k]) : (k == jc ? s_y : -1);
-    if (threadIdx.x == 0) a.out_num[b] = jc;
+    if (threadIdx.x == 0) {
+        a.out_num[b] = jc;
+        count_accepts(a.sh, b, jc);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -640,34 +656,7 @@ __global__ void k_greedy_prefix(Shape sh, const int32_t* gidx, int32_t* out_toke
     out[j] = g[j];
     for (int k = j + 1; k <= K; ++k) out[k] = -1;
     out_num[b] = j;
-}
-
-// Per-position acceptance counters from the per-sequence results (one
-// workgroup): tested[k] = sequences whose accept test at position k ran
-// (k < K_b and num_accepted >= k), accepted[k] = sequences that accepted
-// position k (num_accepted > k).  Integer counts in LDS, so the result does
-// not depend on timing.
-constexpr int kTelemMaxK = 1024;
-__global__ void __launch_bounds__(kSB) k_accept_counts(Shape sh, const int32_t* out_num, int32_t* tested,
-                                                       int32_t* accepted) {
-    __shared__ int s_t[kTelemMaxK], s_a[kTelemMaxK];
-    const int K = sh.K;
-    for (int k = threadIdx.x; k < K; k += kSB) {
-        s_t[k] = 0;
-        s_a[k] = 0;
-    }
-    __syncthreads();
-    for (int b = threadIdx.x; b < sh.B; b += kSB) {
-        const int n = out_num[b];
-        const int nt = min(n + 1, seq_len(sh, b));
-        for (int k = 0; k < nt; ++k) atomicAdd(&s_t[k], 1);
-        for (int k = 0; k < n; ++k) atomicAdd(&s_a[k], 1);
-    }
-    __syncthreads();
-    for (int k = threadIdx.x; k < K; k += kSB) {
-        if (tested) tested[k] = s_t[k];
-        if (accepted) accepted[k] = s_a[k];
-    }
+    count_accepts(sh, b, j);
 }
 
 // Copy row records to the caller's stats arrays.

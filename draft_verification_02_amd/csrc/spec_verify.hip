@@ -111,14 +111,6 @@ void take_events(void** evb, void** eva) {
     g_ev_before = g_ev_after = nullptr;
 }
 
-int run_counts(const Shape& sh, const int32_t* out_num, int32_t* tested, int32_t* accepted,
-               hipStream_t stream) {
-    if (!tested && !accepted) return SPEC_OK;
-    if (sh.K == 0) return SPEC_OK;
-    hipLaunchKernelGGL(k_accept_counts, dim3(1), dim3(kSB), 0, stream, sh, out_num, tested, accepted);
-    return launch_status();
-}
-
 int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, int32_t* out_tokens,
                int32_t* out_num, hipStream_t stream, int tdt, const int32_t* lens = nullptr,
                int32_t* tested = nullptr, int32_t* accepted = nullptr) {
@@ -132,7 +124,8 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     Workspace* ws;
     rc = get_workspace(stream, 0, n_trows, 0, &ws);
     if (rc) return rc;
-    const Shape sh{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0, n_trows, 0, lens};
+    const Shape sh{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0, n_trows, 0, lens,
+                   tested, accepted};
     void *evb, *eva;
     take_events(&evb, &eva);
     if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
@@ -141,8 +134,7 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
     hipLaunchKernelGGL(k_greedy_prefix, dim3((unsigned)ceil_div(B, 256)), dim3(256), 0, stream, sh,
                        (const int32_t*)ws->gidx, out_tokens, out_num);
-    if ((rc = launch_status())) return rc;
-    return run_counts(sh, out_num, tested, accepted, stream);
+    return launch_status();
 }
 
 int run_sampling(const void* target, const void* draft, const int32_t* tokens, int B, int K, int V,
@@ -177,7 +169,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     if (rc) return rc;
 
     const Shape sh{static_cast<const char*>(target), static_cast<const char*>(draft), tokens, B, K, V,
-                   tdt, ddt, tsz, dsz, n_trows, n_drows, lens};
+                   tdt, ddt, tsz, dsz, n_trows, n_drows, lens, tested, accepted};
     RowArgs ra;
     ra.sh = sh;
     // c = c_hi + c_lo with c_hi the largest float below c (so c_hi > 0 and
@@ -253,7 +245,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
                            (const RowRec*)ws->rec, n_trows, n_drows, tstats, dstats);
         if ((rc = launch_status())) return rc;
     }
-    return run_counts(sh, out_num, tested, accepted, stream);
+    return SPEC_OK;
 }
 
 }  // namespace
@@ -297,7 +289,6 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, cons
     if (!std::isfinite(temperature) || temperature < 0.0f) return SPEC_E_INVALID;
     if (!(top_p > 0.0f && top_p <= 1.0f)) return SPEC_E_INVALID;
     if (B > 0 && !draft_lens) return SPEC_E_INVALID;
-    if ((pos_tested || pos_accepted) && K > kTelemMaxK) return SPEC_E_INVALID;
     hipStream_t s = static_cast<hipStream_t>(stream);
     if (temperature == 0.0f)
         return run_greedy(target_logits, draft_tokens, B, K, V, out_tokens, out_num_accepted, s,

@@ -143,8 +143,9 @@ int spec_verify(const void* target_logits, const void* draft_logits,
  *   pos_accepted   [K] int32 or NULL: sequences that accepted position k.
  * Everything else as spec_verify (temperature == 0: greedy, accepting while
  * d_k equals the target argmax for k < K_b).  draft_lens must be non-NULL
- * when B > 0; the counters need K <= 1024.  The counters are written by one
- * extra small kernel.
+ * when B > 0.  The counters are cleared by the call's first kernel and
+ * counted with integer atomics by the kernels that write each sequence's
+ * outputs, so they are exact and do not depend on order.
  */
 int spec_verify_ragged(const void* target_logits, const void* draft_logits,
                        const int32_t* draft_tokens, const int32_t* draft_lens,

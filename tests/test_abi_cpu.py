@@ -89,7 +89,6 @@ def test_ragged_entry_rejects_invalid_arguments_on_host(lib):
                                       None, 0, 0)
     assert call(lens=None) == 1
     assert call(T=-1.0) == 1 and call(top_p=0.0) == 1
-    assert call(K=1025, tested=p) == 1
     assert call(B=0, lens=None) == 0
 
 

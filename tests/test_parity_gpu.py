@@ -377,3 +377,30 @@ def test_ragged_lengths_extremes_and_full_equals_plain():
     b = binding.spec_verify(t, d, k, w.temperature, w.top_k, w.top_p, w.seed)
     torch.cuda.synchronize()
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+# ---------------------------------------------------------------------------
+# Long kept-list paths, large K and B
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("tdt,V", [(wl.F32, 151936), (wl.BF16, 300007)])
+def test_kept_lists_of_rows_with_many_token_blocks(tdt, V):
+    """Rows with more than 512 blocks of 64 loads (f32 rows at V = 151936,
+    bf16 rows past 262144): the kept list is ranked by the side-by-side
+    binary searches instead of block counts."""
+    _print_case(f"many blocks tdt={tdt} V={V}")
+    w = wl.make(3, 3, V, target_dtype=tdt, draft_dtype=wl.F32, temperature=0.7, top_p=0.9,
+                rho=0.8, seed=V + tdt, vseed=V + 1)
+    print(check_sampling(w))
+    from parity import check_point
+    check_point(w, w.tokens)
+
+
+def test_long_drafts_and_wide_batches():
+    """K = 63 (the accept scan spans a full wave) and B = 512 sequences."""
+    _print_case("K=63 and B=512")
+    w = wl.make(2, 63, 4099, temperature=1.0, top_p=0.95, rho=0.97, seed=63, vseed=64)
+    print(check_sampling(w))
+    w = wl.make(512, 2, 1000, target_dtype=wl.F32, temperature=0.9, top_k=20, rho=0.8,
+                seed=512, vseed=513)
+    print(check_sampling(w, check_stats=False))

@@ -92,6 +92,9 @@ def lib() -> ctypes.CDLL:
         L.oracle_verify_point.argtypes = [vp, i32, vp, i32, i32, i32, f64, i32, f64, u64, i32,
                                           vp, vp, vp, vp, vp]
         L.oracle_verify_point.restype = i32
+        L.oracle_verify_tree.argtypes = [vp, i32, vp, vp, i32, i32, i32, f64, i32, f64, u64, i32,
+                                         vp, vp, vp, vp, vp, vp]
+        L.oracle_verify_tree.restype = i32
         L.oracle_verify_greedy.argtypes = [vp, i32, vp, i32, i32, i32, vp, vp]
         L.oracle_verify_greedy.restype = i32
         _lib = L
@@ -197,6 +200,38 @@ def verify_point(target, tokens, temperature, top_k=0, top_p=1.0, seed=0, seq_ba
     if rc:
         raise ValueError(f"oracle_verify_point failed ({rc})")
     res = {"tokens": out_tok, "num_accepted": out_n}
+    if am is not None:
+        res.update(accept_margin=am, sample_margin=sm, target_info=ti)
+    return res
+
+
+def verify_tree(target, tokens, parents, temperature, top_k=0, top_p=1.0, seed=0, seq_base=0,
+                diagnostics=True):
+    """Token-tree verification: target [B, N+1, V] (row 0 the root, row i+1
+    after node i), tokens [B, N], parents [B, N] (-1 = root, else an index
+    below the node's own).  Returns ``tokens`` [B, N+1], ``num_accepted`` [B],
+    ``path`` [B, N] and, with ``diagnostics`` at temperature > 0,
+    ``accept_margin`` [B, N], ``sample_margin`` [B], ``target_info`` [B, N+1]."""
+    target = np.ascontiguousarray(target)
+    B, N1, V = target.shape
+    N = N1 - 1
+    tokens = np.ascontiguousarray(tokens, dtype=np.int32).reshape(B, N)
+    parents = np.ascontiguousarray(parents, dtype=np.int32).reshape(B, N)
+    out_tok = np.empty((B, N + 1), dtype=np.int32)
+    out_n = np.empty(B, dtype=np.int32)
+    path = np.empty((B, N), dtype=np.int32)
+    am = sm = ti = None
+    if diagnostics and temperature > 0:
+        am = np.full((B, N), np.nan)
+        sm = np.zeros(B)
+        ti = np.zeros((B, N + 1), dtype=ROW_INFO_DTYPE)
+    rc = lib().oracle_verify_tree(_ptr(target), dtype_code(target), _ptr(tokens), _ptr(parents), B, N,
+                                  V, float(temperature), int(top_k), float(top_p),
+                                  int(seed) & 0xFFFFFFFFFFFFFFFF, int(seq_base), _ptr(out_tok),
+                                  _ptr(out_n), _ptr(path), _ptr(am), _ptr(sm), _ptr(ti))
+    if rc:
+        raise ValueError(f"oracle_verify_tree failed ({rc})")
+    res = {"tokens": out_tok, "num_accepted": out_n, "path": path}
     if am is not None:
         res.update(accept_margin=am, sample_margin=sm, target_info=ti)
     return res

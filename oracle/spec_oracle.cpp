@@ -518,4 +518,152 @@ int oracle_verify_point(const void* target, int target_dtype,
     return 0;
 }
 
+int oracle_verify_tree(const void* target, int target_dtype,
+                       const int32_t* node_tokens, const int32_t* parents, int B,
+                       int N, int V, double temperature, int top_k, double top_p,
+                       uint64_t seed, int seq_base, int32_t* out_tokens,
+                       int32_t* out_num_accepted, int32_t* out_path,
+                       double* accept_margin, double* sample_margin,
+                       oracle_row_info* target_info) {
+    if (B < 0 || N < 0 || V < 1 || seq_base < 0) return 1;
+    if (!dtype_ok(target_dtype)) return 1;
+    if (!(temperature >= 0.0) || !std::isfinite(temperature)) return 1;
+    if (!(top_p > 0.0 && top_p <= 1.0)) return 1;
+    if (B == 0) return 0;
+    if (!target || !out_tokens || !out_num_accepted) return 1;
+    if (N > 0 && (!node_tokens || !parents)) return 1;
+    const size_t tsz = dtype_size(target_dtype);
+    const bool greedy = temperature == 0.0;
+
+    for (int b = 0; b < B; ++b) {
+        const uint32_t gb = static_cast<uint32_t>(seq_base + b);
+        const int32_t* tok = node_tokens + static_cast<size_t>(b) * N;
+        const int32_t* par = parents + static_cast<size_t>(b) * N;
+        auto row_of = [&](int r) {
+            return static_cast<const char*>(target) +
+                   (static_cast<size_t>(b) * (N + 1) + r) * V * tsz;
+        };
+        /* children of node u (u = -1: the root) in index order; a node is
+         * a child of its parent only if the parent index is below its own */
+        auto children = [&](int u) {
+            std::vector<int> c;
+            for (int i = u + 1; i < N; ++i)
+                if (par[i] == u) c.push_back(i);
+            return c;
+        };
+        if (accept_margin)
+            for (int i = 0; i < N; ++i) accept_margin[static_cast<size_t>(b) * N + i] = kNaN;
+
+        std::vector<int> path;
+        int u = -1;  // current node
+        int y = -1;  // the last token
+        double margin = 0.0;
+        if (greedy) {
+            for (;;) {
+                /* argmax of the current row, lowest index among equal maxima */
+                const char* row = row_of(u + 1);
+                int g = 0;
+                double gv = load_logit(row, target_dtype, 0);
+                for (int i = 1; i < V; ++i) {
+                    const double v = load_logit(row, target_dtype, i);
+                    if (v > gv) {
+                        gv = v;
+                        g = i;
+                    }
+                }
+                int next = -1;
+                for (int c : children(u))
+                    if (tok[c] == g) {
+                        next = c;
+                        break;
+                    }
+                if (next < 0) {
+                    y = g;
+                    break;
+                }
+                path.push_back(next);
+                u = next;
+            }
+        } else {
+            std::vector<Row> P(N + 1);
+            for (int r = 0; r <= N; ++r)
+                if (process_row(row_of(r), target_dtype, V, temperature, top_k, top_p, P[r]))
+                    return 2;
+            std::vector<double> p;
+            for (;;) {
+                const int r = u + 1;
+                p = P[r].prob;
+                int next = -1;
+                for (int c : children(u)) {
+                    const int x = tok[c];
+                    const double px = (x >= 0 && x < V) ? p[x] : 0.0;
+                    const double uc = oracle_u24(seed, gb, static_cast<uint32_t>(c),
+                                                 ORACLE_PURPOSE_ACCEPT);
+                    if (accept_margin)
+                        accept_margin[static_cast<size_t>(b) * N + c] = std::fabs(uc - px);
+                    if (uc < px) {
+                        next = c;
+                        break;
+                    }
+                    /* rejected: remove x and renormalise what is left */
+                    if (x >= 0 && x < V && p[x] > 0.0) {
+                        p[x] = 0.0;
+                        double s = 0.0;
+                        for (int i = 0; i < V; ++i) s += p[i];
+                        if (s > 0.0)
+                            for (int i = 0; i < V; ++i) p[i] /= s;
+                    }
+                }
+                if (next < 0) break;
+                path.push_back(next);
+                u = next;
+            }
+            /* the draw: from what is left of p, or the row itself when no
+             * mass is left (a leaf has p equal to its row) */
+            const int r = u + 1;
+            double S = 0.0;
+            for (int i = 0; i < V; ++i) S += p[i];
+            if (!(S > 0.0)) {
+                p = P[r].prob;
+                S = 0.0;
+                for (int i = 0; i < V; ++i) S += p[i];
+            }
+            const double t = oracle_u53(seed, gb, static_cast<uint32_t>(r),
+                                        ORACLE_PURPOSE_SAMPLE) * S;
+            int last_pos = -1;
+            double cum = 0.0;
+            for (int i = 0; i < V; ++i) {
+                if (!(p[i] > 0.0)) continue;
+                last_pos = i;
+                const double prev = cum;
+                cum += p[i];
+                if (y < 0 && cum > t) {
+                    y = i;
+                    margin = std::min(t - prev, cum - t) / S;
+                }
+            }
+            if (y < 0) {
+                y = last_pos;
+                margin = 0.0;
+            }
+            if (target_info)
+                for (int k = 0; k <= N; ++k)
+                    target_info[static_cast<size_t>(b) * (N + 1) + k] = P[k].info;
+        }
+        if (sample_margin) sample_margin[b] = margin;
+
+        const int n = static_cast<int>(path.size());
+        int32_t* out = out_tokens + static_cast<size_t>(b) * (N + 1);
+        for (int k = 0; k < n; ++k) out[k] = tok[path[k]];
+        out[n] = y;
+        for (int k = n + 1; k <= N; ++k) out[k] = -1;
+        out_num_accepted[b] = n;
+        if (out_path) {
+            int32_t* op = out_path + static_cast<size_t>(b) * N;
+            for (int k = 0; k < N; ++k) op[k] = k < n ? path[k] : -1;
+        }
+    }
+    return 0;
+}
+
 }  // extern "C"

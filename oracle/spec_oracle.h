@@ -112,6 +112,41 @@ int oracle_verify_point(const void* target, int target_dtype,
                         int32_t* out_num_accepted, double* accept_margin,
                         double* sample_margin, oracle_row_info* target_info);
 
+/* Token-tree verification (multi-head / tree speculation: "Speculative
+ * decoding and multi-token prediction: how LLMs generate faster", section
+ * "Multi-head and tree speculation": one pass scores every branch and the
+ * best-accepted path is kept).  Each sequence holds N nodes; node i carries
+ * token node_tokens[i] and parent parents[i], which is -1 (the committed
+ * context, the root) or a node index below i; any other value makes node i
+ * unreachable.  Target rows are [B][N+1][V]: row 0 is the root's
+ * distribution, row i+1 the distribution after node i.
+ * The children of a node are proposed with certainty (deterministic top-k or
+ * n-gram trees), so each child is a point-mass draft.  The walk starts at the
+ * root with p = its processed row; its children are tested in index order:
+ * child c is accepted when u_c < p(x_c), u_c the accept uniform of counter
+ * (sequence, c); on a rejection p(x_c) is set to 0 and p is renormalised
+ * before the next sibling.  An accepted child becomes the current node.
+ * When every child is rejected, the last token is drawn from the current
+ * (renormalised) p, or from the node's processed row if no mass is left;
+ * a leaf gives the bonus draw from its own row.  The draw uses the sample
+ * uniform of counter (sequence, r), r the row of the node where the walk
+ * stopped.  temperature == 0 gives the greedy tree walk: follow the first
+ * child whose token is the argmax of the current row (lowest index among
+ * equal maxima), then emit that argmax.
+ * Outputs: out_tokens [B][N+1] (the path's tokens, the last token, then -1),
+ * out_num_accepted [B] (path length), out_path [B][N] (node indices of the
+ * path, then -1; may be NULL).  accept_margin [B][N]: |u_c - p(x_c)| of every
+ * test evaluated (p renormalised), NaN for nodes not tested; sample_margin
+ * [B]: distance of the draw from the nearest cumulative boundary over the
+ * weights' sum.  Returns 0 on success. */
+int oracle_verify_tree(const void* target, int target_dtype,
+                       const int32_t* node_tokens, const int32_t* parents, int B,
+                       int N, int V, double temperature, int top_k, double top_p,
+                       uint64_t seed, int seq_base, int32_t* out_tokens,
+                       int32_t* out_num_accepted, int32_t* out_path,
+                       double* accept_margin, double* sample_margin,
+                       oracle_row_info* target_info);
+
 /* Greedy verification: g_k = argmax of target row k (lowest index among
  * equal maxima), accept while d_k == g_k, then emit g_j. */
 int oracle_verify_greedy(const void* target, int target_dtype,

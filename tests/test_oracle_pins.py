@@ -599,3 +599,208 @@ def test_ragged_lengths_tokens_per_pass_and_counters():
         tk, ak = r["tested"][k], r["accepted"][k]
         assert tk == ((lens > k) & (n >= k)).sum() and ak == (n > k).sum()
         assert abs(ak / tk - alpha) < 5 * np.sqrt(alpha * (1 - alpha) / tk), k
+
+
+# ---------------------------------------------------------------------------
+# Token trees (multi-head / tree speculation: "Speculative decoding and
+# multi-token prediction: how LLMs generate faster", section "Multi-head and
+# tree speculation").  Reading: the children of a node are point-mass
+# proposals tested in index order, each rejected one removed from p.
+# ---------------------------------------------------------------------------
+
+def _chain_parents(B, N):
+    return np.ascontiguousarray(np.broadcast_to(np.arange(-1, N - 1, dtype=np.int32), (B, N)))
+
+
+@pytest.mark.parametrize("T,top_k,top_p", [(0.8, 0, 1.0), (1.0, 5, 1.0), (0.7, 0, 0.9), (0.0, 0, 1.0)])
+def test_tree_chain_equals_point_verification(T, top_k, top_p):
+    """A tree that is a single chain (parent of node i is i-1) is a point-mass
+    draft of K = N tokens: same tokens, counts and (same counters) draws."""
+    rng = np.random.default_rng(41)
+    B, N, V = 64, 5, 40
+    target = (rng.standard_normal((B, N + 1, V)) * 2.0).astype(np.float32)
+    P0 = np.argmax(target, axis=2)
+    # half the proposals are the row's argmax, so paths of every length occur
+    toks = np.where(rng.random((B, N)) < 0.7, P0[:, :N], rng.integers(0, V, (B, N))).astype(np.int32)
+    par = _chain_parents(B, N)
+    r = oracle.verify_tree(target, toks, par, T, top_k, top_p, seed=9, diagnostics=False)
+    if T == 0:
+        q = oracle.verify_greedy(target, toks)
+    else:
+        q = oracle.verify_point(target, toks, T, top_k, top_p, seed=9, diagnostics=False)
+    np.testing.assert_array_equal(r["tokens"], q["tokens"])
+    np.testing.assert_array_equal(r["num_accepted"], q["num_accepted"])
+    n = r["num_accepted"]
+    for b in range(B):
+        np.testing.assert_array_equal(r["path"][b], [i if i < n[b] else -1 for i in range(N)])
+    assert 0 < n.min() or n.max() > 0
+
+
+def _small_tree():
+    """Root with children 0, 1, 2; node 0 with children 3, 4; node 1 with
+    child 5; node 3 with child 6.  Breadth-first numbering mixed with a
+    deeper branch."""
+    return np.array([-1, -1, -1, 0, 0, 1, 3], np.int32)
+
+
+def test_tree_output_distribution_equals_target():
+    """Every emitted token is distributed as the target row of the node it
+    follows: the first token as p_root, the second, among sequences whose
+    first token was node c's, as p_{c+1}; the first level accepts child c_j
+    with probability p(x_cj) (distinct tokens), and a draw after rejecting
+    every root child follows p_root with those tokens removed."""
+    rng = np.random.default_rng(23)
+    V, B = 8, 1 << 18
+    par = _small_tree()
+    N = len(par)
+    T, top_k, top_p = 0.9, 0, 0.95
+    t_log = (rng.standard_normal((N + 1, V)) * 1.5).astype(np.float32)
+    P = np.stack([brute_force_processed(t_log[r], T, top_k, top_p) for r in range(N + 1)])
+    # each node proposes a likely-but-not-top token of its parent's row,
+    # siblings distinct
+    tok = np.zeros(N, np.int32)
+    for u in range(-1, N):
+        kids = [i for i in range(N) if par[i] == u]
+        order = np.argsort(P[u + 1])[::-1]
+        for j, c in enumerate(kids):
+            tok[c] = int(order[j + 1])
+    target = np.ascontiguousarray(np.broadcast_to(t_log, (B, N + 1, V)))
+    r = oracle.verify_tree(target, np.broadcast_to(tok, (B, N)), np.broadcast_to(par, (B, N)), T,
+                           top_k, top_p, seed=3, diagnostics=False)
+    out, n, path = r["tokens"], r["num_accepted"], r["path"]
+    assert chi2_pvalue(out[:, 0], P[0]) > 1e-6
+    root_kids = [0, 1, 2]
+    for c in root_kids:
+        f = (path[:, 0] == c).mean()
+        pc = P[0][tok[c]]
+        assert abs(f - pc) < 5 * np.sqrt(pc * (1 - pc) / B), c
+        sel = path[:, 0] == c
+        assert chi2_pvalue(out[sel, 1], P[c + 1]) > 1e-6, c
+    rej = n == 0
+    resid = P[0].copy()
+    resid[tok[root_kids]] = 0.0
+    assert chi2_pvalue(out[rej, 0], resid / resid.sum()) > 1e-6
+    # the path follows parent links
+    for b in range(0, B, 997):
+        for k in range(1, n[b]):
+            assert par[path[b, k]] == path[b, k - 1]
+
+
+def _expected_depth(par, tok, P):
+    """E[path length] = sum over distinct children c of u of
+    p_u(x_c) (1 + E[c]) (each child's token is emitted with its own target
+    probability, so the chance of entering c is p_u(x_c))."""
+    N = len(par)
+
+    def E(u):
+        seen, e = set(), 0.0
+        for c in range(u + 1, N):
+            if par[c] == u and int(tok[c]) not in seen:
+                seen.add(int(tok[c]))
+                e += P[u + 1][tok[c]] * (1.0 + E(c))
+        return e
+    return E(-1)
+
+
+def test_tree_expected_path_length_closed_form():
+    """Mean path length against its closed form, with a duplicated sibling
+    token (never followed: after its first copy is rejected its p is 0)."""
+    rng = np.random.default_rng(5)
+    V, B = 6, 1 << 18
+    par = np.array([-1, -1, -1, 0, 0, 2], np.int32)
+    N = len(par)
+    T = 1.1
+    t_log = (rng.standard_normal((N + 1, V)) * 1.2).astype(np.float32)
+    P = np.stack([brute_force_processed(t_log[r], T, 0, 1.0) for r in range(N + 1)])
+    tok = np.array([1, 3, 1, 0, 2, 4], np.int32)  # nodes 0 and 2 share token 1
+    target = np.ascontiguousarray(np.broadcast_to(t_log, (B, N + 1, V)))
+    r = oracle.verify_tree(target, np.broadcast_to(tok, (B, N)), np.broadcast_to(par, (B, N)), T,
+                           seed=11, diagnostics=False)
+    n = r["num_accepted"]
+    E = _expected_depth(par, tok, P)
+    assert abs(n.mean() - E) < 5 * n.std() / np.sqrt(B), (n.mean(), E)
+    assert not (r["path"] == 2).any()
+    assert not (r["path"] == 5).any()
+
+
+def _greedy_brute(t_log, tok, par):
+    """Greedy tree walk by enumeration: the nodes whose whole ancestor chain
+    matches the argmax of each parent row form a path (siblings carry
+    distinct tokens); the answer is that path and the argmax after it."""
+    N = len(par)
+    g = np.argmax(t_log, axis=1)
+
+    def chain_ok(i):
+        while i >= 0:
+            if tok[i] != g[par[i] + 1]:
+                return False
+            i = par[i]
+        return True
+    good = [i for i in range(N) if chain_ok(i)]
+    # order the matching nodes by depth
+    depth = {}
+    for i in good:
+        d, j = 0, i
+        while j >= 0:
+            d, j = d + 1, par[j]
+        depth[i] = d
+    path = sorted(good, key=lambda i: depth[i])
+    last = path[-1] if path else -1
+    return path, int(g[last + 1])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_tree_greedy_is_argmax_path(seed):
+    rng = np.random.default_rng(100 + seed)
+    N, V = 12, 9
+    par = np.array([-1] + [int(rng.integers(-1, i)) for i in range(1, N)], np.int32)
+    t_log = rng.standard_normal((N + 1, V)).astype(np.float32)
+    g = np.argmax(t_log, axis=1)
+    tok = np.zeros(N, np.int32)
+    for u in range(-1, N):
+        kids = [i for i in range(N) if par[i] == u]
+        # distinct sibling tokens, the argmax among them with probability 0.7
+        choices = list(rng.permutation(V))
+        if rng.random() < 0.7:
+            choices.remove(g[u + 1])
+            choices.insert(int(rng.integers(0, len(kids) + 1)) if kids else 0, g[u + 1])
+        for j, c in enumerate(kids):
+            tok[c] = choices[j]
+    path, last = _greedy_brute(t_log, tok, par)
+    r = oracle.verify_tree(t_log[None], tok[None], par[None], 0.0)
+    n = int(r["num_accepted"][0])
+    assert r["path"][0, :n].tolist() == path
+    assert r["tokens"][0, :n].tolist() == [int(tok[i]) for i in path]
+    assert int(r["tokens"][0, n]) == last
+    assert (r["tokens"][0, n + 1:] == -1).all() and (r["path"][0, n:] == -1).all()
+
+
+def test_tree_edge_cases():
+    """N = 0 is the bonus draw from the root row (point drafts with K = 0);
+    a parent index outside [-1, i) makes a node unreachable; a token outside
+    [0, V) is rejected; when a node's children cover the whole kept set the
+    last of them is left with p = 1 after the removals and is accepted."""
+    rng = np.random.default_rng(8)
+    V = 16
+    t0 = rng.standard_normal((3, 1, V)).astype(np.float32)
+    r = oracle.verify_tree(t0, np.zeros((3, 0), np.int32), np.zeros((3, 0), np.int32), 0.8, seed=4)
+    q = oracle.verify_point(t0, np.zeros((3, 0), np.int32), 0.8, seed=4)
+    np.testing.assert_array_equal(r["tokens"], q["tokens"])
+    N = 4
+    t = (rng.standard_normal((1, N + 1, V)) * 0.1).astype(np.float32)
+    g = int(np.argmax(t[0, 0]))
+    # node 1 points at itself, node 2 at a later node, node 3 at -2
+    par = np.array([[-1, 1, 3, -2]], np.int32)
+    tok = np.array([[V + 3, g, g, g]], np.int32)
+    for T in (0.0, 0.9):
+        r = oracle.verify_tree(t, tok, par, T, seed=1)
+        assert int(r["num_accepted"][0]) == 0
+        assert (r["path"] == -1).all()
+    # top-k 2 with both kept tokens as the root's children
+    top2 = np.argsort(t[0, 0])[-2:]
+    par2 = np.array([[-1, -1, 0, 1]], np.int32)
+    tok2 = np.array([[top2[0], top2[1], 0, 0]], np.int32)
+    for s in range(20):
+        r = oracle.verify_tree(t, tok2, par2, 1.0, top_k=2, seed=s)
+        assert int(r["tokens"][0, 0]) in top2.tolist()
+        assert int(r["num_accepted"][0]) >= 1

@@ -26,7 +26,8 @@ ROW_STATS_FIELDS = [("max_logit", "<f4"), ("thresh", "<f4"), ("n_kept", "<i4"),
                     ("flags", "<i4"), ("z_kept", "<f8"), ("prob_at_token", "<f8")]
 ROW_STATS_BYTES = 32
 
-EXPORTS = ["spec_verify", "spec_verify_ragged", "spec_verify_point", "spec_verify_greedy", "spec_verify_stats",
+EXPORTS = ["spec_verify", "spec_verify_ragged", "spec_verify_point", "spec_verify_tree", "spec_verify_greedy",
+           "spec_verify_stats",
            "spec_rng_uniforms", "spec_profile_events", "spec_status_string", "spec_release_workspace"]
 
 _lib = None
@@ -55,6 +56,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     L.spec_verify_ragged.restype = i32
     L.spec_verify_point.argtypes = [vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32]
     L.spec_verify_point.restype = i32
+    L.spec_verify_tree.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, vp, i32]
+    L.spec_verify_tree.restype = i32
     L.spec_verify_greedy.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32]
     L.spec_verify_greedy.restype = i32
     L.spec_verify_stats.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp,
@@ -186,6 +189,31 @@ def spec_verify_point(target: torch.Tensor, tokens: torch.Tensor | None, tempera
                                   _stream_handle(stream), _dtype_code(target))
     _check(rc)
     return out_tokens, out_num
+
+
+def spec_verify_tree(target: torch.Tensor, tokens: torch.Tensor | None, parents: torch.Tensor | None,
+                     temperature: float, top_k: int = 0, top_p: float = 1.0, seed: int = 0,
+                     path: bool = True, stream=None):
+    """Verify a token tree per sequence: target [B, N+1, V] (row 0 the root,
+    row i+1 after node i), tokens [B, N] and parents [B, N] int32 (-1 = root,
+    else an index below the node's own).  Returns (out_tokens [B, N+1],
+    out_num_accepted [B], out_path [B, N] or None)."""
+    _dev(target, "target_logits")
+    B, N1, V = target.shape
+    N = N1 - 1
+    if N > 0:
+        for t, name in ((tokens, "node_tokens"), (parents, "parents")):
+            assert t is not None and t.dtype == torch.int32 and tuple(t.shape) == (B, N), name
+            _dev(t, name)
+    out_tokens, out_num = _outputs(B, N, target.device, None, None)
+    out_path = torch.empty((B, N), dtype=torch.int32, device=target.device) if path else None
+    rc = load().spec_verify_tree(_ptr(target), _ptr(tokens) if N > 0 else None,
+                                 _ptr(parents) if N > 0 else None, B, N, V, float(temperature), int(top_k),
+                                 float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out_tokens),
+                                 _ptr(out_num), _ptr(out_path) if N > 0 else None, _stream_handle(stream),
+                                 _dtype_code(target))
+    _check(rc)
+    return out_tokens, out_num, out_path
 
 
 def spec_verify_greedy(target: torch.Tensor, tokens: torch.Tensor | None, out_tokens=None,

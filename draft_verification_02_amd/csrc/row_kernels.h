@@ -99,8 +99,9 @@ __device__ __forceinline__ bool row_live(const Shape& sh, int row) {
     const int r = row - sh.n_trows;
     return r % sh.K < seq_len(sh, r / sh.K);
 }
+// Rows of a token tree carry no token of their own (tokens is null there).
 __device__ __forceinline__ bool row_has_token(const Shape& sh, int row) {
-    return row >= sh.n_trows || (row % (sh.K + 1)) < seq_len(sh, row / (sh.K + 1));
+    return sh.tokens && (row >= sh.n_trows || (row % (sh.K + 1)) < seq_len(sh, row / (sh.K + 1)));
 }
 __device__ __forceinline__ int row_token(const Shape& sh, int row) {
     if (row < sh.n_trows) {

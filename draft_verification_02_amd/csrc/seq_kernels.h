@@ -10,6 +10,11 @@
 //                   the whole vocabulary: chunk sums over the stop row pair in
 //                   fp64, then one workgroup per sequence locates the draw.
 //  k_greedy_prefix : greedy prefix match from the per-row argmax.
+//
+// The draw kernels also serve token trees: there a walk kernel has already
+// fixed each sequence's stop row, the depth of its accepted path and the
+// tokens of the stop node's children (all rejected), which the draw removes
+// from p_j the way a point-mass draft's token is removed.
 #pragma once
 
 #include <type_traits>
@@ -21,6 +26,13 @@ namespace sv {
 constexpr int kSB = 256;                 // threads per sequence workgroup
 constexpr int kChunk = 1024;             // tokens per draw chunk
 constexpr int kCPT = kChunk / kSB;       // 4 contiguous tokens per thread
+
+// Where the walk of a token tree stopped: the target row of the stop node,
+// the number of accepted nodes, and how many children (all rejected) the
+// stop node has; none means the draw is the bonus draw from p of that row.
+struct TreeStop {
+    int row, depth, n_ex, pad;
+};
 
 struct SeqArgs {
     Shape sh;
@@ -36,6 +48,8 @@ struct SeqArgs {
     int32_t* out_tokens;
     int32_t* out_num;
     int point;            // drafts are point masses at the drafted tokens (no draft rows)
+    const TreeStop* tstop; // token trees: per-sequence stop (null for drafted sequences)
+    const int32_t* tex;    // token trees: [B][K] tokens of the stop node's children
 };
 
 // Stop position of sequence b: first k with !(u_k * q_k(d_k) < p_k(d_k)),
@@ -60,6 +74,15 @@ __device__ __forceinline__ int first_rejection(const SeqArgs& a, int b) {
     return Kb;
 }
 
+// The stop row of sequence b: fixed by the walk for a token tree, else the
+// first rejection.  Executed by one wave.
+__device__ __forceinline__ int stop_of(const SeqArgs& a, int b) {
+    return a.tstop ? a.tstop[b].row : first_rejection(a, b);
+}
+__device__ __forceinline__ bool stop_is_bonus(const SeqArgs& a, int b, int j) {
+    return a.tstop ? a.tstop[b].n_ex == 0 : j >= seq_len(a.sh, b);
+}
+
 // The stop row pair of a sequence: target row j, draft row j when j < K_b
 // (or, for point-mass drafts, the drafted token dtok, where q = 1).
 struct StopRow {
@@ -71,7 +94,16 @@ struct StopRow {
     bool has_draft;
     bool bonus;  // j is the sequence's draft length: the bonus row, drawn from p_j
     int dtok;    // -1 unless the draft is a point mass at dtok
+    const int32_t* ex;  // token trees: tokens removed from p_j (the rejected children)
+    int n_ex;
 };
+
+// Whether token i is one of the stop row's removed tokens.
+__device__ __forceinline__ bool in_ex(const StopRow& s, int i) {
+    for (int e = 0; e < s.n_ex; ++e)
+        if (s.ex[e] == i) return true;
+    return false;
+}
 
 __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
     StopRow s;
@@ -83,10 +115,20 @@ __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
     s.Mt = Rt.s.max_logit;
     s.thr_t = Rt.s.thresh;
     s.zt = Rt.s.z_kept;
-    const int Kb = seq_len(a.sh, b);
-    s.bonus = j >= Kb;
-    s.has_draft = j < Kb && !a.point;
-    s.dtok = j < Kb && a.point ? a.sh.tokens[(size_t)b * K + j] : -1;
+    s.n_ex = 0;
+    s.ex = nullptr;
+    if (a.tstop) {
+        s.n_ex = a.tstop[b].n_ex;
+        s.ex = a.tex + (size_t)b * K;
+        s.bonus = s.n_ex == 0;
+        s.has_draft = false;
+        s.dtok = -1;
+    } else {
+        const int Kb = seq_len(a.sh, b);
+        s.bonus = j >= Kb;
+        s.has_draft = j < Kb && !a.point;
+        s.dtok = j < Kb && a.point ? a.sh.tokens[(size_t)b * K + j] : -1;
+    }
     if (s.has_draft) {
         const int rd = a.sh.n_trows + b * K + j;
         const RowRec& Rd = a.rec[rd];
@@ -110,7 +152,7 @@ __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
 __device__ __forceinline__ void stop_terms_x(const StopRow& s, double inv_T, int i, float xt,
                                              double& p, double& r) {
     p = xt >= s.thr_t ? exp(((double)xt - (double)s.Mt) * inv_T) / s.zt : 0.0;
-    double q = i == s.dtok ? 1.0 : 0.0;
+    double q = (i == s.dtok || in_ex(s, i)) ? 1.0 : 0.0;
     if (s.has_draft) {
         const float xd = load_logit(s.dp, s.ddt, i);
         q = xd >= s.thr_d ? exp(((double)xd - (double)s.Md) * inv_T) / s.zd : 0.0;
@@ -186,6 +228,10 @@ __device__ __forceinline__ void count_accepts(const Shape& sh, int b, int j) {
 
 __device__ __forceinline__ void write_outputs(const SeqArgs& a, int b, int j, int y) {
     const int K = a.sh.K;
+    if (a.tstop) {  // the walk wrote the path, the count and the padding
+        a.out_tokens[(size_t)b * (K + 1) + a.tstop[b].depth] = y;
+        return;
+    }
     int32_t* out = a.out_tokens + (size_t)b * (K + 1);
     for (int k = 0; k < j; ++k) out[k] = a.sh.tokens[(size_t)b * K + k];
     out[j] = y;
@@ -334,7 +380,11 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     __shared__ int s_j, s_tau, s_y;
     __shared__ int s_last[kSB / 64], s_first[kSB / 64];
     const int K = a.sh.K;
-    const int b = blockIdx.x / (K + 1), jc = blockIdx.x % (K + 1);
+    // drafted sequences: one workgroup per (sequence, candidate stop row);
+    // token trees: one per sequence, at the row where its walk stopped
+    const bool tree = a.tstop != nullptr;
+    const int b = tree ? (int)blockIdx.x : (int)blockIdx.x / (K + 1);
+    const int jc = tree ? a.tstop[b].row : (int)blockIdx.x % (K + 1);
     const int rt = b * (K + 1) + jc;
     const int n = a.kept_n[rt];
     const uint2* L = a.kept + (size_t)rt * kListMax;
@@ -357,13 +407,15 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     }
     const StopRow s = stop_row(a, b, jc);
     // the accepted drafted tokens, one per thread, for the output row
-    const int tok = (int)threadIdx.x < jc ? a.sh.tokens[(size_t)b * K + threadIdx.x] : -1;
-    if (threadIdx.x < 64) {
-        const int j = first_rejection(a, b);
-        if (threadIdx.x == 0) s_j = j;
+    const int tok = !tree && (int)threadIdx.x < jc ? a.sh.tokens[(size_t)b * K + threadIdx.x] : -1;
+    if (!tree) {
+        if (threadIdx.x < 64) {
+            const int j = first_rejection(a, b);
+            if (threadIdx.x == 0) s_j = j;
+        }
+        __syncthreads();
+        if (s_j != jc) return;
     }
-    __syncthreads();
-    if (s_j != jc) return;
     if (n < 0) {
         draw_full_row(a, b, jc, s_val, s_excl, &s_total, &s_tau);
         return;
@@ -386,7 +438,7 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         const bool in = threadIdx.x * kLPT + e < n;
         const bool qd = in && xd >= s.thr_d;
         const double q = qd ? exp(((double)xd - (double)s.Md) * a.inv_T) * inv_zd
-                            : (in && (int)ent[e].x == s.dtok ? 1.0 : 0.0);
+                            : (in && ((int)ent[e].x == s.dtok || in_ex(s, (int)ent[e].x)) ? 1.0 : 0.0);
         const double d = pr[e] - q;
         rr[e] = d > 0.0 ? d : 0.0;
         sr += rr[e];
@@ -432,6 +484,10 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         s_y = y >= 0 ? y : last;
     }
     __syncthreads();
+    if (tree) {
+        if (threadIdx.x == 0) write_outputs(a, b, jc, s_y);
+        return;
+    }
     // output row: accepted drafts, the drawn token, then -1
     int32_t* out = a.out_tokens + (size_t)b * (K + 1);
     for (int k = threadIdx.x; k <= K; k += kSB)
@@ -471,11 +527,17 @@ __device__ __forceinline__ void run_terms(const StopRow& s, double inv_T, int lo
     // without a draft row the target row is read again and ignored
     load_run<DDT>(s.has_draft ? s.dp : s.tp, lo, V, xd);
     const double inv_zt = 1.0 / s.zt, inv_zd = 1.0 / s.zd;
+    // removed tokens of a tree's stop row inside [lo, lo + kCPT)
+    uint32_t exm = 0u;
+    for (int e = 0; e < s.n_ex; ++e) {
+        const uint32_t d = (uint32_t)(s.ex[e] - lo);
+        if (d < (uint32_t)kCPT) exm |= 1u << d;
+    }
 #pragma unroll
     for (int e = 0; e < kCPT; ++e) {
         p[e] = xt[e] >= s.thr_t ? exp(((double)xt[e] - (double)s.Mt) * inv_T) * inv_zt : 0.0;
         const double q = (s.has_draft && xd[e] >= s.thr_d) ? exp(((double)xd[e] - (double)s.Md) * inv_T) * inv_zd
-                                                           : (lo + e == s.dtok ? 1.0 : 0.0);
+                                                           : ((lo + e == s.dtok || ((exm >> e) & 1u)) ? 1.0 : 0.0);
         const double d = p[e] - q;
         r[e] = d > 0.0 ? d : 0.0;
     }
@@ -501,7 +563,7 @@ __global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
     const int b = blockIdx.x / a.n_chunks;
     const int c = blockIdx.x % a.n_chunks;
     if (threadIdx.x < 64) {
-        const int j = first_rejection(a, b);
+        const int j = stop_of(a, b);
         if (threadIdx.x == 0) s_j = j;
     }
     __syncthreads();
@@ -532,7 +594,7 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
     const int b = blockIdx.x;
     const int K = a.sh.K, V = a.sh.V;
     if (threadIdx.x < 64) {
-        const int j = first_rejection(a, b);
+        const int j = stop_of(a, b);
         if (threadIdx.x == 0) {
             s_j = j;
             s_cstar = 0;  // stays if no chunk holds mass
@@ -552,7 +614,7 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
     double er, ep, tr, tp;
     seq_excl_scan2(mr, mp, s_wa, s_wb, er, ep, tr, tp);  // (its barrier also publishes s_j)
     const int j = s_j;
-    const bool usep = j >= seq_len(a.sh, b) || !(tr > 0.0);
+    const bool usep = stop_is_bonus(a, b, j) || !(tr > 0.0);
     const double S = usep ? tp : tr;
     const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -10,7 +10,7 @@
 #include <utility>
 
 #include "../../include/spec_verify.h"
-#include "seq_kernels.h"
+#include "tree_kernels.h"
 
 namespace {
 
@@ -18,12 +18,12 @@ using namespace sv;
 
 // Library-owned scratch for one (device, stream): row records, kept lists of
 // filtered target rows (with p and the draft logit of each listed token), greedy
-// argmax indices and draw chunk sums.  Every
+// argmax indices, draw chunk sums and the stops of token-tree walks.  Every
 // kernel writes what it later reads within the same call, so nothing needs
 // clearing between calls.
 struct Workspace {
     void* base = nullptr;
-    size_t cap_rows = 0, cap_trows = 0, cap_chunks = 0;
+    size_t cap_rows = 0, cap_trows = 0, cap_chunks = 0, cap_seqs = 0, cap_nodes = 0;
     RowRec* rec = nullptr;
     uint2* kept = nullptr;
     int* kept_n = nullptr;
@@ -32,6 +32,8 @@ struct Workspace {
     int32_t* gidx = nullptr;
     double2* chunk_sum = nullptr;
     PartRec* prec = nullptr;
+    TreeStop* tstop = nullptr;
+    int32_t* tex = nullptr;
 };
 
 std::mutex g_mu;
@@ -41,12 +43,14 @@ void* g_ev_after = nullptr;
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, Workspace** out) {
+int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, Workspace** out,
+                  size_t seqs = 0, size_t nodes = 0) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_LAUNCH;
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace& w = g_ws[{dev, stream}];
-    if (w.base && rows <= w.cap_rows && trows <= w.cap_trows && chunks <= w.cap_chunks) {
+    if (w.base && rows <= w.cap_rows && trows <= w.cap_trows && chunks <= w.cap_chunks && seqs <= w.cap_seqs &&
+        nodes <= w.cap_nodes) {
         *out = &w;
         return SPEC_OK;
     }
@@ -54,6 +58,8 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     nw.cap_rows = std::max(rows, w.cap_rows);
     nw.cap_trows = std::max(trows, w.cap_trows);
     nw.cap_chunks = std::max(chunks, w.cap_chunks);
+    nw.cap_seqs = std::max(seqs, w.cap_seqs);
+    nw.cap_nodes = std::max(nodes, w.cap_nodes);
     size_t off = 0;
     const size_t o_rec = off; off = align_up(off + nw.cap_rows * sizeof(RowRec));
     const size_t o_kept = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(uint2));
@@ -63,6 +69,8 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     const size_t o_g = off; off = align_up(off + nw.cap_trows * sizeof(int32_t));
     const size_t o_cs = off; off = align_up(off + nw.cap_chunks * sizeof(double2));
     const size_t o_pr = off; off = align_up(off + nw.cap_rows * (size_t)kMaxParts * sizeof(PartRec));
+    const size_t o_ts = off; off = align_up(off + nw.cap_seqs * sizeof(TreeStop));
+    const size_t o_tx = off; off = align_up(off + nw.cap_nodes * sizeof(int32_t));
     if (w.base) {
         // the old buffer may still be in use by work queued on this stream
         if (hipStreamSynchronize(stream) != hipSuccess) return SPEC_E_LAUNCH;
@@ -79,6 +87,8 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
     nw.gidx = reinterpret_cast<int32_t*>(b + o_g);
     nw.chunk_sum = reinterpret_cast<double2*>(b + o_cs);
     nw.prec = reinterpret_cast<PartRec*>(b + o_pr);
+    nw.tstop = reinterpret_cast<TreeStop*>(b + o_ts);
+    nw.tex = reinterpret_cast<int32_t*>(b + o_tx);
     w = nw;
     *out = &w;
     return SPEC_OK;
@@ -137,11 +147,48 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     return launch_status();
 }
 
+int run_tree_greedy(const void* target, const int32_t* tokens, const int32_t* parents, int B, int N, int V,
+                    int32_t* out_tokens, int32_t* out_num, int32_t* out_path, hipStream_t stream, int tdt) {
+    int tsz;
+    if (!dtype_size(tdt, &tsz)) return SPEC_E_UNSUPPORTED;
+    int rc = check_sizes(B, N, V);
+    if (rc) return rc;
+    if (N > kTreeMax) return SPEC_E_INVALID;
+    if (B == 0) return SPEC_OK;
+    if (!target || !out_tokens || !out_num || (N > 0 && (!tokens || !parents))) return SPEC_E_INVALID;
+    const int n_trows = B * (N + 1);
+    Workspace* ws;
+    rc = get_workspace(stream, 0, n_trows, 0, &ws);
+    if (rc) return rc;
+    const Shape sh{static_cast<const char*>(target), nullptr, nullptr, B, N, V, tdt, 0, tsz, 0, n_trows, 0,
+                   nullptr, nullptr, nullptr};
+    void *evb, *eva;
+    take_events(&evb, &eva);
+    if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
+    hipLaunchKernelGGL(k_row_argmax, dim3(n_trows), dim3(kRB), 0, stream, sh, ws->gidx);
+    if ((rc = launch_status())) return rc;
+    if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
+    TreeArgs ta{};
+    ta.sh = sh;
+    ta.tok = tokens;
+    ta.par = parents;
+    ta.gidx = ws->gidx;
+    ta.out_tokens = out_tokens;
+    ta.out_num = out_num;
+    ta.out_path = out_path;
+    hipLaunchKernelGGL(k_tree_greedy, dim3(B), dim3(64), 0, stream, ta);
+    return launch_status();
+}
+
 int run_sampling(const void* target, const void* draft, const int32_t* tokens, int B, int K, int V,
                  float temperature, int top_k, float top_p, uint64_t seed, int32_t* out_tokens,
                  int32_t* out_num, hipStream_t stream, int tdt, int ddt, spec_row_stats_t* tstats,
                  spec_row_stats_t* dstats, bool point, const int32_t* lens = nullptr,
-                 int32_t* tested = nullptr, int32_t* accepted = nullptr) {
+                 int32_t* tested = nullptr, int32_t* accepted = nullptr, const int32_t* parents = nullptr,
+                 int32_t* out_path = nullptr) {
+    // token trees (parents given): K is the node count, tokens the node
+    // tokens; the rows carry no token of their own and a walk fixes the stop
+    const bool tree = parents != nullptr;
     int tsz, dsz = 4;
     if (!dtype_size(tdt, &tsz)) return SPEC_E_UNSUPPORTED;
     if (K > 0 && !point && !dtype_size(ddt, &dsz)) return SPEC_E_UNSUPPORTED;
@@ -155,6 +202,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     if (!target || !out_tokens || !out_num) return SPEC_E_INVALID;
     if (K > 0 && ((!point && !draft) || !tokens)) return SPEC_E_INVALID;
     if (point) draft = nullptr;
+    if (tree && K > kTreeMax) return SPEC_E_INVALID;
 
     // point-mass drafts have no draft rows
     const int n_trows = B * (K + 1);
@@ -165,11 +213,12 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     const bool filtered = use_k || use_p;
     const int n_chunks = (int)ceil_div(V, kChunk);
     Workspace* ws;
-    rc = get_workspace(stream, rows, filtered ? n_trows : 0, filtered ? 0 : (size_t)B * n_chunks, &ws);
+    rc = get_workspace(stream, rows, filtered ? n_trows : 0, filtered ? 0 : (size_t)B * n_chunks, &ws,
+                       tree ? (size_t)B : 0, tree ? (size_t)B * K : 0);
     if (rc) return rc;
 
-    const Shape sh{static_cast<const char*>(target), static_cast<const char*>(draft), tokens, B, K, V,
-                   tdt, ddt, tsz, dsz, n_trows, n_drows, lens, tested, accepted};
+    const Shape sh{static_cast<const char*>(target), static_cast<const char*>(draft), tree ? nullptr : tokens,
+                   B, K, V, tdt, ddt, tsz, dsz, n_trows, n_drows, lens, tested, accepted};
     RowArgs ra;
     ra.sh = sh;
     // c = c_hi + c_lo with c_hi the largest float below c (so c_hi > 0 and
@@ -231,8 +280,31 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     sa.out_tokens = out_tokens;
     sa.out_num = out_num;
     sa.point = point ? 1 : 0;
+    sa.tstop = nullptr;
+    sa.tex = nullptr;
+    if (tree) {
+        TreeArgs ta;
+        ta.sh = sh;
+        ta.tok = tokens;
+        ta.par = parents;
+        ta.inv_T = inv_T;
+        ta.seed = seed;
+        ta.rec = ws->rec;
+        ta.gidx = nullptr;
+        ta.tstop = ws->tstop;
+        ta.tex = ws->tex;
+        ta.out_tokens = out_tokens;
+        ta.out_num = out_num;
+        ta.out_path = out_path;
+        hipLaunchKernelGGL(k_tree_walk, dim3(B), dim3(64), 0, stream, ta);
+        if ((rc = launch_status())) return rc;
+        sa.tstop = ws->tstop;
+        sa.tex = ws->tex;
+    }
     if (filtered) {
-        hipLaunchKernelGGL(k_seq_filtered, dim3((unsigned)((long long)B * (K + 1))), dim3(kSB), 0, stream, sa);
+        // a tree's stop row is known: one workgroup per sequence
+        const long long nwg = tree ? (long long)B : (long long)B * (K + 1);
+        hipLaunchKernelGGL(k_seq_filtered, dim3((unsigned)nwg), dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
     } else {
         hipLaunchKernelGGL(k_draw_sums, dim3((unsigned)((long long)B * n_chunks)), dim3(kSB), 0, stream, sa);
@@ -296,6 +368,28 @@ int spec_verify_ragged(const void* target_logits, const void* draft_logits, cons
     return run_sampling(target_logits, draft_logits, draft_tokens, B, K, V, temperature, top_k, top_p,
                         seed, out_tokens, out_num_accepted, s, target_dtype, draft_dtype, nullptr,
                         nullptr, false, draft_lens, pos_tested, pos_accepted);
+}
+
+int spec_verify_tree(const void* target_logits, const int32_t* node_tokens, const int32_t* parents, int B,
+                     int N, int V, float temperature, int top_k, float top_p, uint64_t seed,
+                     int32_t* out_tokens, int32_t* out_num_accepted, int32_t* out_path, void* stream,
+                     int target_dtype) {
+    if (!std::isfinite(temperature) || temperature < 0.0f) return SPEC_E_INVALID;
+    if (!(top_p > 0.0f && top_p <= 1.0f)) return SPEC_E_INVALID;
+    if (N > kTreeMax) return SPEC_E_INVALID;
+    if (B > 0 && N > 0 && !parents) return SPEC_E_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (temperature == 0.0f)
+        return run_tree_greedy(target_logits, node_tokens, parents, B, N, V, out_tokens, out_num_accepted,
+                               out_path, s, target_dtype);
+    // a tree with no nodes is the bonus draw from the root row: a point-mass
+    // call with no drafts (the same row, the same sample counter)
+    if (N == 0)
+        return run_sampling(target_logits, nullptr, nullptr, B, 0, V, temperature, top_k, top_p, seed, out_tokens,
+                            out_num_accepted, s, target_dtype, SPEC_DTYPE_F32, nullptr, nullptr, true);
+    return run_sampling(target_logits, nullptr, node_tokens, B, N, V, temperature, top_k, top_p, seed,
+                        out_tokens, out_num_accepted, s, target_dtype, SPEC_DTYPE_F32, nullptr, nullptr, true,
+                        nullptr, nullptr, nullptr, parents, out_path);
 }
 
 int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int K, int V,

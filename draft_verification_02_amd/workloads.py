@@ -35,6 +35,7 @@ _S_BOOST = 2
 _S_DRAFT = 3
 _S_DRAFT_SAMPLE = 4
 _S_RHO = 5
+_S_TREE = 6
 
 
 def gen_seed(cfg: int, rnd: int = 0) -> int:
@@ -112,20 +113,21 @@ def make(B: int, K: int, V: int, *, target_dtype: int = BF16, draft_dtype: int =
          temperature: float = 1.0, top_k: int = 0, top_p: float = 1.0,
          dist: str = "gauss", sigma: float = 3.0, rho=0.9, n_boost: int = 0,
          boost: float = 8.0, seed: int = 1, vseed: int | None = None,
-         name: str = "custom", threads: int | None = None) -> Workload:
+         name: str = "custom", threads: int | None = None, with_draft: bool = True) -> Workload:
     """Draw one workload.
 
     dist="gauss": target x = N(0, sigma^2) (+ ``boost`` on ``n_boost`` distinct
     uniform ids per row), draft d = rho * x_stored + sqrt(1 - rho^2) * N(0, sigma^2).
     dist="t3": target x = sigma * t_3, draft d = rho * x_stored + sqrt(1-rho^2) * sigma * t_3'.
     rho: a number, or a pair (lo, hi) to draw one rho per sequence from U(lo, hi).
-    The draft is built from the stored (rounded) target value.
+    The draft is built from the stored (rounded) target value.  with_draft=False
+    draws the target rows only (draft None, tokens zero).
     """
     if dist not in ("gauss", "t3"):
         raise ValueError(dist)
     target = np.empty((B, K + 1, V), dtype=np.uint16 if target_dtype == BF16 else np.float32)
-    draft = np.empty((B, K, V), dtype=np.uint16 if draft_dtype == BF16 else np.float32)
-    tokens = np.empty((B, K), dtype=np.int32)
+    draft = np.empty((B, K, V) if with_draft else (0,), dtype=np.uint16 if draft_dtype == BF16 else np.float32)
+    tokens = np.zeros((B, K), dtype=np.int32)
     if isinstance(rho, (tuple, list)):
         rr = _rng(seed, _S_RHO, 0)
         rhos = rr.uniform(rho[0], rho[1], size=B)
@@ -148,7 +150,7 @@ def make(B: int, K: int, V: int, *, target_dtype: int = BF16, draft_dtype: int =
                 target[b, k] = f32_to_bf16_bits(x32)
             else:
                 target[b, k] = x32
-            if k == K:
+            if k == K or not with_draft:
                 continue
             stored = as_f32(target[b, k]).astype(np.float64)
             drow = b * K + k
@@ -177,11 +179,62 @@ def make(B: int, K: int, V: int, *, target_dtype: int = BF16, draft_dtype: int =
     else:
         with ThreadPoolExecutor(max_workers=nthreads) as ex:
             list(ex.map(one_sequence, range(B)))
-    return Workload(name=name, B=B, K=K, V=V, target=target, draft=draft if K > 0 else None,
+    return Workload(name=name, B=B, K=K, V=V, target=target, draft=draft if K > 0 and with_draft else None,
                     tokens=tokens, temperature=float(temperature), top_k=int(top_k),
                     top_p=float(top_p), seed=vseed if vseed is not None else seed,
                     meta={"dist": dist, "sigma": sigma, "rho": rho, "n_boost": n_boost,
                           "rhos": rhos})
+
+
+def tree_shape(branching) -> np.ndarray:
+    """Parent indices of a static token tree in breadth-first order: the root
+    has branching[0] children, every node at depth d (1-based) has
+    branching[d] children.  Returns int32 [N] (-1 = child of the root)."""
+    par, level = [], [-1]
+    for m in branching:
+        nxt = []
+        for u in level:
+            for _ in range(m):
+                par.append(u)
+                nxt.append(len(par) - 1)
+        level = nxt
+    return np.asarray(par, dtype=np.int32)
+
+
+def make_tree(B: int, branching, V: int, *, target_dtype: int = BF16, temperature: float = 1.0,
+              top_k: int = 0, top_p: float = 1.0, sigma: float = 3.0, rho=0.9, n_boost: int = 0,
+              boost: float = 8.0, seed: int = 1, vseed: int | None = None,
+              name: str = "tree") -> Workload:
+    """A batch of token trees (multi-head / tree speculation).  The target rows
+    [B, N+1, V] are drawn as in ``make`` with K = N (row 0 for the root, row
+    i+1 after node i); every sequence shares the tree shape of
+    ``tree_shape(branching)``, and the children of node u carry the
+    ``m`` distinct tokens ranked highest by a proposer's noisy copy of row
+    u+1, rho * x + sqrt(1 - rho^2) * sigma * N(0, 1), as draft heads propose
+    their top candidates.  ``meta['parents']`` holds the parents [B, N]."""
+    par = tree_shape(branching)
+    N = len(par)
+    w = make(B, N, V, target_dtype=target_dtype, draft_dtype=F32, temperature=temperature,
+             top_k=top_k, top_p=top_p, sigma=sigma, rho=rho, n_boost=n_boost, boost=boost,
+             seed=seed, vseed=vseed, name=name, with_draft=False)
+    kids = [[i for i in range(N) if par[i] == u] for u in range(-1, N)]
+    tokens = np.zeros((B, N), dtype=np.int32)
+    for b in range(B):
+        r = float(w.meta["rhos"][b])
+        for u in range(-1, N):
+            if not kids[u + 1]:
+                continue
+            x = as_f32(w.target[b, u + 1]).astype(np.float64)
+            g = _rng(seed, _S_TREE, b * (N + 1) + u + 1)
+            prop = r * x + np.sqrt(max(0.0, 1.0 - r * r)) * sigma * g.standard_normal(V)
+            m = len(kids[u + 1])
+            top = np.argpartition(-prop, m - 1)[:m]
+            top = top[np.argsort(-prop[top], kind="stable")]
+            tokens[b, kids[u + 1]] = top
+    w.tokens = tokens
+    w.meta["parents"] = np.ascontiguousarray(np.broadcast_to(par, (B, N)))
+    w.meta["branching"] = list(branching)
+    return w
 
 
 # The five measured workloads (shapes, dtypes, distributions and processing).

@@ -177,6 +177,44 @@ int spec_verify_point(const void* target_logits, const int32_t* draft_tokens,
                       int target_dtype);
 
 /*
+ * Token-tree verification (multi-head / tree speculation: "Speculative
+ * decoding and multi-token prediction: how LLMs generate faster", section
+ * "Multi-head and tree speculation": one target pass scores every branch of a
+ * tree of proposals and the best-accepted path is kept).  The pages leave the
+ * rule for several candidates at one node open; the reading taken extends
+ * the point-mass rule of spec_verify_point to siblings:
+ *   node_tokens [B][N] int32 device array: token of node i.
+ *   parents     [B][N] int32 device array: parent of node i, -1 for the root
+ *               (the committed context) or a node index below i; any other
+ *               value leaves node i unreachable.  N <= 1024.
+ *   target_logits [B][N+1][V]: row 0 is the root's distribution, row i+1 the
+ *               distribution after node i (the tree-attention pass).
+ * From the root, the current node's children are tested in index order:
+ * child c is accepted when u_c < p(x_c), where p is the current node's
+ * processed row with the tokens of the siblings rejected before c removed
+ * and renormalised (a repeated sibling token is therefore never accepted,
+ * and a token outside [0, V) is always rejected).  An accepted child becomes
+ * the current node.  When all children are rejected, the last token is drawn
+ * from that remaining distribution (from the full row if nothing remains);
+ * a leaf gives the bonus draw from its row.  u_c is the accept uniform of
+ * counter (sequence, c); the draw uses the sample uniform of counter
+ * (sequence, r), r the row of the node where the walk stopped; so a tree
+ * that is one chain reproduces spec_verify_point.  temperature == 0: follow
+ * the first child whose token is the row's argmax (lowest index among equal
+ * maxima), then emit that argmax.
+ * Outputs (device arrays): out_tokens [B][N+1] (the path's tokens, the last
+ * token, then -1); out_num_accepted [B] (path length); out_path [B][N] (node
+ * indices of the path, then -1; may be NULL).  Temperature, top-k, top-p,
+ * seed, stream, dtype and error codes as spec_verify.  Reads the target
+ * logits once: B*(N+1)*V*sizeof(target) bytes.
+ */
+int spec_verify_tree(const void* target_logits, const int32_t* node_tokens,
+                     const int32_t* parents, int B, int N, int V,
+                     float temperature, int top_k, float top_p, uint64_t seed,
+                     int32_t* out_tokens, int32_t* out_num_accepted,
+                     int32_t* out_path, void* stream, int target_dtype);
+
+/*
  * Greedy verification: g_k = argmax of target row k (lowest index among equal
  * maxima), accept while d_k == g_k, emit g_j at the first mismatch j (or the
  * bonus argmax g_K).  Reads target logits only.  Same conventions as

@@ -278,3 +278,88 @@ def check_ragged(w: wl.Workload, lens: np.ndarray, seqs=None, report=None) -> Re
         rep.mismatch_tolerated += 1
     assert rep.mismatch_tolerated <= 1e-6 * max(1, rep.decisions), rep
     return rep
+
+
+def tree_inputs(w: wl.Workload, dev="cuda"):
+    t = to_device(w.target, dev)
+    k = torch.from_numpy(np.ascontiguousarray(w.tokens, dtype=np.int32)).to(dev)
+    p = torch.from_numpy(np.ascontiguousarray(w.meta["parents"], dtype=np.int32)).to(dev)
+    return t, k, p
+
+
+def gpu_tree(w: wl.Workload):
+    t, k, p = tree_inputs(w)
+    g_tok, g_num, g_path = binding.spec_verify_tree(t, k, p, w.temperature, w.top_k, w.top_p, w.seed)
+    torch.cuda.synchronize()
+    return g_tok.cpu().numpy(), g_num.cpu().numpy(), g_path.cpu().numpy()
+
+
+def check_tree_structure(w: wl.Workload, g_tok, g_num, g_path):
+    """What holds for every sequence whatever the random draws: the path
+    starts at a root child and follows parent links, its tokens are the
+    nodes' tokens, the padding is -1 and the last token is in [0, V)."""
+    N = w.K
+    par = w.meta["parents"]
+    for b in range(w.B):
+        n = int(g_num[b])
+        assert 0 <= n <= N, b
+        path = g_path[b, :n].tolist()
+        prev = -1
+        for c in path:
+            assert 0 <= c < N and par[b, c] == prev and c > prev, (b, path)
+            prev = c
+        assert (g_path[b, n:] == -1).all(), b
+        assert g_tok[b, :n].tolist() == [int(w.tokens[b, c]) for c in path], b
+        assert 0 <= g_tok[b, n] < w.V, b
+        assert (g_tok[b, n + 1:] == -1).all(), b
+
+
+def check_tree(w: wl.Workload, seqs=None, report=None) -> Report:
+    """spec_verify_tree on the GPU against oracle.verify_tree.  Greedy: path,
+    tokens and counts bit-exact.  Sampling: exact, except where the first
+    differing decision is ambiguous: a sibling test at the node where the
+    paths part with |u - p'| <= 1e-5, a nucleus boundary within 1e-6 on that
+    row, or a draw within 1e-12 * S of a cumulative boundary; at most 1e-6 of
+    the decisions."""
+    rep = report or Report()
+    g_tok, g_num, g_path = gpu_tree(w)
+    check_tree_structure(w, g_tok, g_num, g_path)
+    if seqs is None:
+        seqs = range(w.B)
+    par = w.meta["parents"]
+    for b in seqs:
+        r = oracle.verify_tree(w.target[b:b + 1], w.tokens[b:b + 1], par[b:b + 1], f32(w.temperature),
+                               w.top_k, f32(w.top_p), w.seed, seq_base=int(b))
+        o_tok, o_num, o_path = r["tokens"][0], int(r["num_accepted"][0]), r["path"][0]
+        j_g = int(g_num[b])
+        if w.temperature == 0:
+            assert j_g == o_num and np.array_equal(g_tok[b], o_tok) and np.array_equal(g_path[b], o_path), (
+                b, g_tok[b].tolist(), o_tok.tolist())
+            rep.decisions += o_num + 1
+            continue
+        am = r["accept_margin"][0]
+        rep.decisions += int(np.isfinite(am).sum()) + 1
+        if j_g == o_num and np.array_equal(g_tok[b], o_tok) and np.array_equal(g_path[b], o_path):
+            continue
+        # the node where the two walks part
+        d = 0
+        while d < min(j_g, o_num) and g_path[b, d] == o_path[d]:
+            d += 1
+        u = -1 if d == 0 else int(o_path[d - 1])
+        amb_row = r["target_info"][0][u + 1]["nucleus_margin"] <= NUCLEUS_BAND
+        if d < max(j_g, o_num) or j_g != o_num:
+            kids = [c for c in range(u + 1, w.K) if par[b, c] == u]
+            margins = [am[c] for c in kids if np.isfinite(am[c])]
+            m = min(margins) if margins else np.inf
+            ok = m <= ACCEPT_BAND or amb_row
+            why = f"sibling tests below node {u}: smallest margin {m:.3g}"
+        else:
+            sm = r["sample_margin"][0]
+            ok = sm <= SAMPLE_BAND or amb_row
+            why = f"draw after node {u}: margin {sm:.3g}"
+        assert ok, (f"sequence {b}: GPU {g_tok[b].tolist()} path {g_path[b].tolist()} vs oracle "
+                    f"{o_tok.tolist()} path {o_path.tolist()}; {why} is outside every band")
+        rep.mismatch_tolerated += 1
+        rep.details.append((b, why))
+    assert rep.mismatch_tolerated <= 1e-6 * rep.decisions, rep
+    return rep

@@ -92,6 +92,25 @@ def test_ragged_entry_rejects_invalid_arguments_on_host(lib):
     assert call(B=0, lens=None) == 0
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(T=-1.0), 1), (dict(T=float("nan")), 1), (dict(top_p=0.0), 1), (dict(top_p=2.0), 1),
+    (dict(B=-1), 1), (dict(N=-1), 1), (dict(V=0), 1), (dict(tdt=5), 2), (dict(N=1025), 1),
+    (dict(target=None), 1), (dict(out=None), 1), (dict(tokens=None), 1), (dict(parents=None), 1),
+    (dict(T=0.0, N=1025), 1), (dict(T=0.0, parents=None), 1), (dict(T=0.0, tdt=5), 2),
+    (dict(T=0.0, tokens=None), 1),
+])
+def test_tree_entry_rejects_invalid_arguments_on_host(lib, kw, code):
+    a = dict(target=ctypes.c_void_p(16), tokens=ctypes.c_void_p(16), parents=ctypes.c_void_p(16), B=1, N=2,
+             V=4, T=1.0, top_k=0, top_p=1.0, seed=0, out=ctypes.c_void_p(16), num=ctypes.c_void_p(16),
+             path=None, stream=None, tdt=0)
+    a.update(kw)
+    assert lib.spec_verify_tree(a["target"], a["tokens"], a["parents"], a["B"], a["N"], a["V"], a["T"],
+                                a["top_k"], a["top_p"], a["seed"], a["out"], a["num"], a["path"],
+                                a["stream"], a["tdt"]) == code
+
+
 def test_empty_batch_returns_ok_without_device_work(lib):
     assert _call(lib, B=0, target=None, draft=None, tokens=None, out=None, num=None) == 0
     assert lib.spec_verify_greedy(None, None, 0, 3, 10, None, None, None, 1) == 0
+    for T in (0.0, 0.8):
+        assert lib.spec_verify_tree(None, None, None, 0, 5, 10, T, 0, 1.0, 0, None, None, None, None, 1) == 0

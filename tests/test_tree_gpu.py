@@ -1,0 +1,162 @@
+"""GPU parity of token-tree verification (spec_verify_tree) against the CPU
+oracle: static breadth-first trees of the multi-head / tree speculation kind,
+small cases across dtypes, filters and temperatures checked on every
+sequence, the concurrent-batch shape at full vocabulary on a sample of
+sequences (every sequence's structure checked), and the degenerate trees."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from draft_verification_02_amd import binding
+from draft_verification_02_amd import workloads as wl
+
+from parity import (Report, check_tree, check_tree_structure, f32, gpu_tree, point_tokens, to_device,
+                    tree_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _print_case(name):
+    print(f"[case] {name}", flush=True)
+
+
+def _tree(B, branching, V, **kw):
+    return wl.make_tree(B, branching, V, **kw)
+
+
+@pytest.mark.parametrize("T,top_k,top_p", [(0.0, 0, 1.0), (1.0, 0, 1.0), (0.7, 0, 0.9), (1.0, 20, 1.0),
+                                           (0.8, 50, 0.95)])
+@pytest.mark.parametrize("tdt,V", [(wl.F32, 1000), (wl.BF16, 4099)])
+def test_tree_small_all_sequences(T, top_k, top_p, tdt, V):
+    _print_case(f"tree small T={T} k={top_k} p={top_p} tdt={tdt} V={V}")
+    w = _tree(16, [3, 2, 2], V, target_dtype=tdt, temperature=T, top_k=top_k, top_p=top_p, rho=(0.5, 0.98),
+              seed=V + tdt + int(T * 10), vseed=V * 3 + top_k)
+    print(check_tree(w))
+
+
+def test_tree_c3_shape_full_size_sampled():
+    """The concurrent-batch workload's target rows and filters (B = 32,
+    V = 151936, bf16, T = 0.7, top-p 0.9) over a 44-node tree with 4, 2, 2, 1
+    children per level: every sequence's structure, 6 sequences against the
+    oracle."""
+    _print_case("tree c3 full, 6 sequences checked")
+    spec = wl.CONFIG_SPECS[3]
+    w = _tree(32, [4, 2, 2, 1], spec["V"], target_dtype=spec["target_dtype"], temperature=spec["temperature"],
+              top_p=spec["top_p"], sigma=spec["sigma"], rho=spec["rho"], n_boost=spec["n_boost"],
+              seed=wl.gen_seed(3), vseed=wl.verify_seed(3))
+    print(check_tree(w, seqs=[0, 5, 11, 17, 24, 31]))
+
+
+@pytest.mark.parametrize("T,top_k,top_p,sigma", [(1.0, 0, 1.0, 3.0), (0.9, 0, 0.999, 0.5),
+                                                 (1.0, 0, 0.98, 1.0)])
+def test_tree_full_vocabulary_draw_paths(T, top_k, top_p, sigma):
+    """Unfiltered rows (chunked draw over the whole vocabulary), kept lists
+    longer than the stored limit (draw over the full row) and longer than one
+    workgroup's speculative load."""
+    _print_case(f"tree V=151936 T={T} p={top_p} sigma={sigma}")
+    w = _tree(4, [3, 2], 151936, target_dtype=wl.BF16, temperature=T, top_k=top_k, top_p=top_p, sigma=sigma,
+              rho=0.9, seed=int(sigma * 100) + 7, vseed=11)
+    print(check_tree(w))
+
+
+def test_tree_that_is_a_chain_equals_point_verification():
+    """Parents i-1: the tree walk and the point-mass path give the same
+    outputs on the GPU (same rows, same counters)."""
+    _print_case("tree chain vs point")
+    w = wl.config(3, B=8)
+    toks = point_tokens(w)
+    K = w.K
+    t = to_device(w.target)
+    k = torch.from_numpy(np.ascontiguousarray(toks, dtype=np.int32)).cuda()
+    par = torch.arange(-1, K - 1, dtype=torch.int32).repeat(w.B, 1).contiguous().cuda()
+    a_tok, a_num, a_path = binding.spec_verify_tree(t, k, par, w.temperature, w.top_k, w.top_p, w.seed)
+    b_tok, b_num = binding.spec_verify_point(t, k, w.temperature, w.top_k, w.top_p, w.seed)
+    torch.cuda.synchronize()
+    assert torch.equal(a_tok, b_tok) and torch.equal(a_num, b_num)
+    n = a_num.cpu().numpy()
+    for b in range(w.B):
+        assert a_path[b].cpu().tolist() == [i if i < n[b] else -1 for i in range(K)]
+
+
+def test_tree_wide_and_deep():
+    """A root with 150 children (three ballot chunks per level) and a chain of
+    300 nodes below the first child, sibling tokens repeated on purpose."""
+    _print_case("tree wide and deep")
+    V, B = 512, 6
+    par = np.concatenate([np.full(150, -1), [0], np.arange(150, 150 + 299)]).astype(np.int32)
+    N = len(par)
+    w = wl.make(B, N, V, target_dtype=wl.F32, temperature=1.0, sigma=1.0, seed=77, vseed=78, with_draft=False)
+    rng = np.random.default_rng(5)
+    tok = rng.integers(0, V, (B, N)).astype(np.int32)
+    # repeats among the root's children; the chain follows each row's argmax
+    # most of the time
+    tok[:, 100:150] = tok[:, 0:50]
+    x = np.stack([wl.as_f32(w.target[b]) for b in range(B)])
+    for i in range(150, N):
+        tok[:, i] = np.where(rng.random(B) < 0.9, np.argmax(x[:, par[i] + 1], axis=1), tok[:, i])
+    w.tokens = tok
+    w.meta["parents"] = np.ascontiguousarray(np.broadcast_to(par, (B, N)))
+    for T in (0.0, 1.0, 0.6):
+        w.temperature = T
+        w.top_p = 0.9 if T == 0.6 else 1.0
+        print(T, check_tree(w))
+
+
+def test_tree_degenerate_inputs():
+    """N = 0 (the bonus draw from the root row), parents that point at the
+    node itself, at a later node or below -1 (unreachable nodes), tokens
+    outside [0, V) (always rejected), and the largest tree (1024 nodes)."""
+    _print_case("tree degenerate")
+    V = 300
+    w0 = wl.make(5, 0, V, target_dtype=wl.BF16, temperature=0.9, seed=3, with_draft=False)
+    t0 = to_device(w0.target)
+    for T in (0.0, 0.9):
+        g_tok, g_num, g_path = binding.spec_verify_tree(t0, None, None, T, 0, 1.0, w0.seed)
+        r = oracle.verify_tree(w0.target, np.zeros((5, 0), np.int32), np.zeros((5, 0), np.int32), T,
+                               seed=w0.seed)
+        assert np.array_equal(g_tok.cpu().numpy(), r["tokens"]) and (g_num.cpu().numpy() == 0).all()
+    B, N = 4, 6
+    w = wl.make(B, N, V, target_dtype=wl.F32, temperature=1.0, seed=9, vseed=10, with_draft=False)
+    x = np.stack([wl.as_f32(w.target[b]) for b in range(B)])
+    par = np.array([-1, 1, 5, -7, 0, 0], np.int32)
+    tok = np.zeros((B, N), np.int32)
+    tok[:, 0] = np.argmax(x[:, 0], axis=1)
+    tok[:, 1:4] = tok[:, :1]
+    tok[:, 4] = -3
+    tok[:, 5] = V + 1
+    w.tokens = tok
+    w.meta["parents"] = np.ascontiguousarray(np.broadcast_to(par, (B, N)))
+    for T, p in ((0.0, 1.0), (1.0, 1.0), (0.5, 0.9)):
+        w.temperature, w.top_p = T, p
+        print(check_tree(w))
+        _, g_num, g_path = gpu_tree(w)
+        assert set(g_path[g_path >= 0].tolist()) <= {0}
+    # the largest tree: 1024 nodes, 8 children per node breadth-first
+    N = 1024
+    par = np.array([(i // 8) - 1 for i in range(N)], np.int32)
+    w = wl.make(2, N, 64, target_dtype=wl.F32, temperature=1.0, sigma=4.0, seed=12, vseed=13, with_draft=False)
+    x = np.stack([wl.as_f32(w.target[b]) for b in range(2)])
+    order = np.argsort(-x, axis=2)
+    tok = np.zeros((2, N), np.int32)
+    for i in range(N):
+        tok[:, i] = order[:, par[i] + 1, i % 8]
+    w.tokens = tok
+    w.meta["parents"] = np.ascontiguousarray(np.broadcast_to(par, (2, N)))
+    for T in (0.0, 1.0):
+        w.temperature = T
+        print(check_tree(w))
+
+
+def test_tree_repeated_calls_and_buffer_reuse():
+    """Two tree calls of different sizes on one stream, then a drafted call:
+    the workspace regrows and the second tree's outputs match the oracle."""
+    _print_case("tree reuse")
+    a = _tree(3, [2, 2], 700, target_dtype=wl.F32, temperature=1.0, seed=31, vseed=32)
+    b = _tree(9, [5, 3, 1], 2000, target_dtype=wl.BF16, temperature=0.8, top_p=0.9, seed=33, vseed=34)
+    check_tree(a)
+    check_tree(b)
+    c = wl.config(1)
+    from parity import check_sampling
+    check_sampling(c)
+    check_tree(a)

@@ -17,6 +17,11 @@ greedy draft head) and no draft logits read.
 --mode ragged measures spec_verify_ragged with per-sequence draft lengths
 drawn uniformly from 0..K (seeded) and the per-position acceptance counters
 on; the bytes counted are those of the rows inside each sequence's length.
+
+--mode tree measures spec_verify_tree: the same target-row distributions and
+processing over a static 44-node token tree per sequence (4 children of the
+root, then 2, 2 and 1 per node), 45 target rows per sequence, the children's
+tokens the top candidates of a proposer's noisy copy of the parent row.
 """
 from __future__ import annotations
 
@@ -38,6 +43,9 @@ METRIC_RAGGED = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K<=7 
                  "per-sequence draft lengths U{0..7} (spec_verify_ragged)")
 METRIC_POINT = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936, 1 GPU, "
                 "point-mass drafts (spec_verify_point)")
+METRIC_TREE = ("verified tree nodes/sec + HBM GB/s (% peak) at B=32 N=44 V=151936, 1 GPU, "
+               "token trees 4-2-2-1 (spec_verify_tree)")
+TREE_BRANCHING = [4, 2, 2, 1]
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -81,11 +89,22 @@ def traffic_from_profiles(config_name: str, src_hash: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, max_seqs: int, point_tokens=None, lens=None):
+def cpu_baseline(w, max_seqs: int, point_tokens=None, lens=None, tree=False):
     import oracle  # CPU baseline leg only
 
     seqs = list(range(min(w.B, max_seqs)))
     t0 = time.perf_counter()
+    if tree:
+        par = w.meta["parents"]
+        for b in seqs:
+            oracle.verify_tree(w.target[b:b + 1], w.tokens[b:b + 1], par[b:b + 1],
+                               float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p)),
+                               w.seed, seq_base=b, diagnostics=False)
+        dt = time.perf_counter() - t0
+        return {"value": round(len(seqs) * w.K / dt, 3), "unit": "verified tree nodes/s",
+                "cores": 1, "kind": "oracle",
+                "sample": f"{len(seqs)} of {w.B} sequences of the same workload, single-threaded "
+                          f"fp64 C++ oracle, {dt:.2f} s"}
     if lens is not None:
         sub = slice(0, len(seqs))
         oracle.verify_ragged(w.target[sub], w.draft[sub], w.tokens[sub], lens[sub],
@@ -120,11 +139,11 @@ def main():
     ap.add_argument("--no-settle", dest="settle", action="store_false",
                     help="skip the untimed settle phase after the warmup steps")
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--mode", choices=["general", "point", "ragged"], default="general",
+    ap.add_argument("--mode", choices=["general", "point", "ragged", "tree"], default="general",
                     help="general: spec_verify with draft logits (the headline); point: "
                          "spec_verify_point with point-mass drafts")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
-    ap.add_argument("--cpu-seqs", type=int, default=32)
+    ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences of the CPU baseline (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (3 times), for "
@@ -149,15 +168,25 @@ def main():
     import torch
     from draft_verification_02_amd import binding, workloads as wl
 
-    w = wl.config(args.config)
+    point = args.mode == "point"
+    ragged = args.mode == "ragged"
+    tree = args.mode == "tree"
+    if tree:
+        spec = dict(wl.CONFIG_SPECS[args.config])
+        w = wl.make_tree(spec["B"], TREE_BRANCHING, spec["V"], target_dtype=spec["target_dtype"],
+                         temperature=spec["temperature"], top_k=spec.get("top_k", 0),
+                         top_p=spec.get("top_p", 1.0), sigma=spec["sigma"], rho=spec["rho"],
+                         n_boost=spec["n_boost"], seed=wl.gen_seed(args.config),
+                         vseed=wl.verify_seed(args.config),
+                         name=spec["name"].split(" ")[0] + f" tree B{spec['B']} N44 4-2-2-1")
+    else:
+        w = wl.config(args.config)
     if w.greedy:
         raise SystemExit("the headline workload is a sampling workload")
     dev = torch.device("cuda:0")
-    point = args.mode == "point"
-    ragged = args.mode == "ragged"
     # point-mass drafts: the draft rows' argmax, a greedy draft head's proposals
     ptoks = np.argmax(wl.as_f32(w.draft), axis=2).astype(np.int32) if point else None
-    ideal = w.target.nbytes if point else w.ideal_bytes()
+    ideal = w.target.nbytes if (point or tree) else w.ideal_bytes()
     lens_np = None
     if ragged:
         lens_np = np.random.default_rng(w.seed & 0xFFFFFFFF).integers(0, w.K + 1, w.B).astype(np.int32)
@@ -171,8 +200,10 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    sets = [(up(w.target), None if point else up(w.draft), up(ptoks if point else w.tokens))
+    sets = [(up(w.target), None if (point or tree) else up(w.draft), up(ptoks if point else w.tokens))
             for _ in range(n_sets)]
+    par_t = up(np.ascontiguousarray(w.meta["parents"])) if tree else None
+    out_p = torch.empty((w.B, w.K), dtype=torch.int32, device=dev) if tree else None
     lens_t = up(lens_np) if ragged else None
     out_t = torch.empty((w.B, w.K + 1), dtype=torch.int32, device=dev)
     out_n = torch.empty((w.B,), dtype=torch.int32, device=dev)
@@ -180,6 +211,10 @@ def main():
 
     def step(i):
         t, d, k = sets[i % n_sets]
+        if tree:
+            binding.spec_verify_tree(t, k, par_t, w.temperature, w.top_k, w.top_p, w.seed, stream=stream,
+                                     out_tokens=out_t, out_num_accepted=out_n, out_path=out_p)
+            return
         if point:
             binding.spec_verify_point(t, k, w.temperature, w.top_k, w.top_p, w.seed, out_t, out_n,
                                       stream=stream)
@@ -245,13 +280,14 @@ def main():
 
     src_hash = kernel_source_hash()
     achieved = ideal / (k_ms * 1e-3) / 1e9
-    traffic = None if (point or ragged) else traffic_from_profiles(w.name, src_hash)
+    traffic = None if (point or ragged or tree) else traffic_from_profiles(w.name, src_hash)
     positions = int(lens_np.sum()) if ragged else w.B * w.K
     value = positions / (ms * 1e-3)
+    metric = METRIC_TREE if tree else (METRIC_POINT if point else (METRIC_RAGGED if ragged else METRIC))
     line = {
-        "metric": METRIC_POINT if point else (METRIC_RAGGED if ragged else METRIC),
+        "metric": metric,
         "value": round(value, 1),
-        "unit": "verified draft positions/s",
+        "unit": "verified tree nodes/s" if tree else "verified draft positions/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -263,8 +299,8 @@ def main():
         "dtype": "f32+f64",
         "data": "synthetic",
         "config": {"workload": w.name + ("-point" if point else ("-ragged" if ragged else "")),
-                   "B": w.B, "K": w.K, "V": w.V,
-                   "target": "bf16", "draft": "point mass" if point else "f32",
+                   "B": w.B, ("N" if tree else "K"): w.K, "V": w.V,
+                   "target": "bf16", "draft": "point mass" if (point or tree) else "f32",
                    "temperature": w.temperature, "top_k": w.top_k,
                    "top_p": w.top_p, "input_sets_rotated": n_sets, "ideal_bytes": ideal},
         "hbm_gbs_step": round(ideal / (ms * 1e-3) / 1e9, 1),
@@ -277,8 +313,12 @@ def main():
     }
     if ragged:
         line["config"]["draft_lens_total"] = positions
+    if tree:
+        line["config"]["branching"] = TREE_BRANCHING
+        line["mean_accepted_path"] = round(float(out_n.float().mean().item()), 3)
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, args.cpu_seqs, ptoks, lens_np)
+        cpu_seqs = args.cpu_seqs or (8 if tree else 32)
+        line["cpu_baseline"] = cpu_baseline(w, cpu_seqs, ptoks, lens_np, tree)
     print(json.dumps(line), flush=True)
 
 

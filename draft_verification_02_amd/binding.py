@@ -193,7 +193,8 @@ def spec_verify_point(target: torch.Tensor, tokens: torch.Tensor | None, tempera
 
 def spec_verify_tree(target: torch.Tensor, tokens: torch.Tensor | None, parents: torch.Tensor | None,
                      temperature: float, top_k: int = 0, top_p: float = 1.0, seed: int = 0,
-                     path: bool = True, stream=None):
+                     path: bool = True, stream=None, out_tokens=None, out_num_accepted=None,
+                     out_path=None):
     """Verify a token tree per sequence: target [B, N+1, V] (row 0 the root,
     row i+1 after node i), tokens [B, N] and parents [B, N] int32 (-1 = root,
     else an index below the node's own).  Returns (out_tokens [B, N+1],
@@ -205,8 +206,12 @@ def spec_verify_tree(target: torch.Tensor, tokens: torch.Tensor | None, parents:
         for t, name in ((tokens, "node_tokens"), (parents, "parents")):
             assert t is not None and t.dtype == torch.int32 and tuple(t.shape) == (B, N), name
             _dev(t, name)
-    out_tokens, out_num = _outputs(B, N, target.device, None, None)
-    out_path = torch.empty((B, N), dtype=torch.int32, device=target.device) if path else None
+    out_tokens, out_num = _outputs(B, N, target.device, out_tokens, out_num_accepted)
+    if out_path is None and path:
+        out_path = torch.empty((B, N), dtype=torch.int32, device=target.device)
+    if out_path is not None:
+        assert out_path.dtype == torch.int32 and out_path.numel() == B * N
+        _dev(out_path, "out_path")
     rc = load().spec_verify_tree(_ptr(target), _ptr(tokens) if N > 0 else None,
                                  _ptr(parents) if N > 0 else None, B, N, V, float(temperature), int(top_k),
                                  float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out_tokens),

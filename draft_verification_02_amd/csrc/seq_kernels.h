@@ -75,12 +75,17 @@ __device__ __forceinline__ int first_rejection(const SeqArgs& a, int b) {
 }
 
 // The stop row of sequence b: fixed by the walk for a token tree, else the
-// first rejection.  Executed by one wave.
+// first rejection.  Executed by one wave.  The kernels take the tree case as
+// a template parameter, so the drafted-sequence code carries none of it.
+template <bool kTree>
 __device__ __forceinline__ int stop_of(const SeqArgs& a, int b) {
-    return a.tstop ? a.tstop[b].row : first_rejection(a, b);
+    if constexpr (kTree) return a.tstop[b].row;
+    else return first_rejection(a, b);
 }
+template <bool kTree>
 __device__ __forceinline__ bool stop_is_bonus(const SeqArgs& a, int b, int j) {
-    return a.tstop ? a.tstop[b].n_ex == 0 : j >= seq_len(a.sh, b);
+    if constexpr (kTree) return a.tstop[b].n_ex == 0;
+    else return j >= seq_len(a.sh, b);
 }
 
 // The stop row pair of a sequence: target row j, draft row j when j < K_b
@@ -105,6 +110,7 @@ __device__ __forceinline__ bool in_ex(const StopRow& s, int i) {
     return false;
 }
 
+template <bool kTree>
 __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
     StopRow s;
     const int K = a.sh.K;
@@ -117,7 +123,7 @@ __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
     s.zt = Rt.s.z_kept;
     s.n_ex = 0;
     s.ex = nullptr;
-    if (a.tstop) {
+    if constexpr (kTree) {
         s.n_ex = a.tstop[b].n_ex;
         s.ex = a.tex + (size_t)b * K;
         s.bonus = s.n_ex == 0;
@@ -226,9 +232,10 @@ __device__ __forceinline__ void count_accepts(const Shape& sh, int b, int j) {
         for (int k = 0; k < j; ++k) atomicAdd(&sh.accepted[k], 1);
 }
 
+template <bool kTree>
 __device__ __forceinline__ void write_outputs(const SeqArgs& a, int b, int j, int y) {
     const int K = a.sh.K;
-    if (a.tstop) {  // the walk wrote the path, the count and the padding
+    if constexpr (kTree) {  // the walk wrote the path, the count and the padding
         a.out_tokens[(size_t)b * (K + 1) + a.tstop[b].depth] = y;
         return;
     }
@@ -242,9 +249,10 @@ __device__ __forceinline__ void write_outputs(const SeqArgs& a, int b, int j, in
 
 // Draw over the whole stop row pair with one workgroup (thread-contiguous
 // token ranges).  Used when no kept list is available.
+template <bool kTree>
 __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, double* s_val, double* s_excl,
                               double* s_total, int* s_tau) {
-    const StopRow s = stop_row(a, b, j);
+    const StopRow s = stop_row<kTree>(a, b, j);
     const int V = a.sh.V;
     const int per = (V + kSB - 1) / kSB;
     const int lo = threadIdx.x * per, hi = min(lo + per, V);
@@ -280,7 +288,7 @@ __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, do
                 }
             }
         }
-        write_outputs(a, b, j, y >= 0 ? y : last);
+        write_outputs<kTree>(a, b, j, y >= 0 ? y : last);
     }
 }
 
@@ -288,6 +296,7 @@ __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, do
 // slices of up to kListMax / kSB entries, read and gathered now.
 constexpr int kListPT = kListMax / kSB;  // 16
 
+template <bool kTree>
 __device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, int n, const uint2* L,
                                                const StopRow& s, double* s_val, double* s_excl,
                                                double* s_total, int* s_tau) {
@@ -331,7 +340,7 @@ __device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, i
                 if (acc > t) y = ix[e];
             }
         }
-        write_outputs(a, b, j, y >= 0 ? y : last);
+        write_outputs<kTree>(a, b, j, y >= 0 ? y : last);
     }
 }
 
@@ -374,6 +383,7 @@ __device__ __forceinline__ void seq_excl_scan2(double a, double b, double* s_wa,
     eb = pb + xb;
 }
 
+template <bool kTree>
 __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     __shared__ double s_val[kSB], s_excl[kSB], s_total;
     __shared__ double s_wa[kSB / 64], s_wb[kSB / 64];
@@ -382,9 +392,9 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     const int K = a.sh.K;
     // drafted sequences: one workgroup per (sequence, candidate stop row);
     // token trees: one per sequence, at the row where its walk stopped
-    const bool tree = a.tstop != nullptr;
-    const int b = tree ? (int)blockIdx.x : (int)blockIdx.x / (K + 1);
-    const int jc = tree ? a.tstop[b].row : (int)blockIdx.x % (K + 1);
+    constexpr bool tree = kTree;
+    const int b = tree ? blockIdx.x : blockIdx.x / (K + 1);
+    const int jc = tree ? a.tstop[b].row : blockIdx.x % (K + 1);
     const int rt = b * (K + 1) + jc;
     const int n = a.kept_n[rt];
     const uint2* L = a.kept + (size_t)rt * kListMax;
@@ -405,10 +415,10 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
             pl[e] = LP[threadIdx.x * kLPT + e];
         }
     }
-    const StopRow s = stop_row(a, b, jc);
+    const StopRow s = stop_row<kTree>(a, b, jc);
     // the accepted drafted tokens, one per thread, for the output row
     const int tok = !tree && (int)threadIdx.x < jc ? a.sh.tokens[(size_t)b * K + threadIdx.x] : -1;
-    if (!tree) {
+    if constexpr (!tree) {
         if (threadIdx.x < 64) {
             const int j = first_rejection(a, b);
             if (threadIdx.x == 0) s_j = j;
@@ -417,11 +427,11 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         if (s_j != jc) return;
     }
     if (n < 0) {
-        draw_full_row(a, b, jc, s_val, s_excl, &s_total, &s_tau);
+        draw_full_row<kTree>(a, b, jc, s_val, s_excl, &s_total, &s_tau);
         return;
     }
     if (n > kSpec) {
-        draw_long_list(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
+        draw_long_list<kTree>(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
         return;
     }
     const double inv_zd = 1.0 / s.zd;
@@ -484,8 +494,8 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         s_y = y >= 0 ? y : last;
     }
     __syncthreads();
-    if (tree) {
-        if (threadIdx.x == 0) write_outputs(a, b, jc, s_y);
+    if constexpr (tree) {
+        if (threadIdx.x == 0) write_outputs<kTree>(a, b, jc, s_y);
         return;
     }
     // output row: accepted drafts, the drawn token, then -1
@@ -557,17 +567,18 @@ __device__ __forceinline__ void with_dtypes(const StopRow& s, F&& f) {
     }
 }
 
+template <bool kTree>
 __global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
     __shared__ double s_wa[kSB / 64], s_wb[kSB / 64];
     __shared__ int s_j;
     const int b = blockIdx.x / a.n_chunks;
     const int c = blockIdx.x % a.n_chunks;
     if (threadIdx.x < 64) {
-        const int j = stop_of(a, b);
+        const int j = stop_of<kTree>(a, b);
         if (threadIdx.x == 0) s_j = j;
     }
     __syncthreads();
-    const StopRow s = stop_row(a, b, s_j);
+    const StopRow s = stop_row<kTree>(a, b, s_j);
     const int lo = c * kChunk + threadIdx.x * kCPT;
     double sr = 0.0, sp = 0.0;
     with_dtypes(s, [&](auto tt, auto dt) {
@@ -587,6 +598,7 @@ __global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
 // One workgroup per sequence: the chunk holding the draw point (chunk sums
 // in chunk order, thread t holding chunks t, t + kSB, ...), then the token
 // inside it from the same per-thread terms.
+template <bool kTree>
 __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
     __shared__ double s_wa[kSB / 64], s_wb[kSB / 64], s_run;
     __shared__ int s_j, s_cstar;
@@ -594,7 +606,7 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
     const int b = blockIdx.x;
     const int K = a.sh.K, V = a.sh.V;
     if (threadIdx.x < 64) {
-        const int j = stop_of(a, b);
+        const int j = stop_of<kTree>(a, b);
         if (threadIdx.x == 0) {
             s_j = j;
             s_cstar = 0;  // stays if no chunk holds mass
@@ -614,7 +626,7 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
     double er, ep, tr, tp;
     seq_excl_scan2(mr, mp, s_wa, s_wb, er, ep, tr, tp);  // (its barrier also publishes s_j)
     const int j = s_j;
-    const bool usep = stop_is_bonus(a, b, j) || !(tr > 0.0);
+    const bool usep = stop_is_bonus<kTree>(a, b, j) || !(tr > 0.0);
     const double S = usep ? tp : tr;
     const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -664,7 +676,7 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
     __syncthreads();
     const int cstar = s_cstar;
     const double run = s_run;
-    const StopRow s = stop_row(a, b, j);
+    const StopRow s = stop_row<kTree>(a, b, j);
     const int lo = cstar * kChunk + threadIdx.x * kCPT;
     with_dtypes(s, [&](auto tt, auto dt) {
         double p[kCPT], r[kCPT];
@@ -692,7 +704,7 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
                     if (acc > t) y = lo + e;
                 }
             }
-            write_outputs(a, b, j, y >= 0 ? y : last);
+            write_outputs<kTree>(a, b, j, y >= 0 ? y : last);
         }
     });
 }

@@ -304,12 +304,22 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     if (filtered) {
         // a tree's stop row is known: one workgroup per sequence
         const long long nwg = tree ? (long long)B : (long long)B * (K + 1);
-        hipLaunchKernelGGL(k_seq_filtered, dim3((unsigned)nwg), dim3(kSB), 0, stream, sa);
+        if (tree)
+            hipLaunchKernelGGL(k_seq_filtered<true>, dim3((unsigned)nwg), dim3(kSB), 0, stream, sa);
+        else
+            hipLaunchKernelGGL(k_seq_filtered<false>, dim3((unsigned)nwg), dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
     } else {
-        hipLaunchKernelGGL(k_draw_sums, dim3((unsigned)((long long)B * n_chunks)), dim3(kSB), 0, stream, sa);
+        const dim3 g_sums((unsigned)((long long)B * n_chunks));
+        if (tree)
+            hipLaunchKernelGGL(k_draw_sums<true>, g_sums, dim3(kSB), 0, stream, sa);
+        else
+            hipLaunchKernelGGL(k_draw_sums<false>, g_sums, dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
-        hipLaunchKernelGGL(k_draw_pick, dim3(B), dim3(kSB), 0, stream, sa);
+        if (tree)
+            hipLaunchKernelGGL(k_draw_pick<true>, dim3(B), dim3(kSB), 0, stream, sa);
+        else
+            hipLaunchKernelGGL(k_draw_pick<false>, dim3(B), dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
     }
     if (tstats || dstats) {

@@ -367,6 +367,7 @@ struct RowArgs {
     int* kept_n;        // [n_trows]; -1 when the list was not stored
     float* kept_d;      // [n_trows][kListMax] draft logit of each listed token (rows with a draft row)
     double* kept_p;     // [n_trows][kListMax] p of each listed token
+    int want_list;      // target rows store their kept lists (else the draw reads the row itself)
     int parts;          // > 1: unfiltered rows split into this many parts (one workgroup each)
     PartRec* prec;      // [rows][parts]
 };
@@ -1430,7 +1431,7 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
         // indices below it.  Exact path: gather the kept logits in a pass over
         // the row, bucket them by tile and rank each inside its bucket.  Both
         // orders are deterministic.
-        if (row < a.sh.n_trows) {
+        if (row < a.sh.n_trows && a.want_list) {
             const int list_n = (n_kept <= kListMax && st.nt <= kNB) ? n_kept : -1;
             const uint32_t tk = fkey(thr);
             uint2* out = a.kept + (size_t)row * kListMax;

@@ -11,10 +11,11 @@
 //                   fp64, then one workgroup per sequence locates the draw.
 //  k_greedy_prefix : greedy prefix match from the per-row argmax.
 //
-// The draw kernels also serve token trees: there a walk kernel has already
-// fixed each sequence's stop row, the depth of its accepted path and the
-// tokens of the stop node's children (all rejected), which the draw removes
-// from p_j the way a point-mass draft's token is removed.
+// k_draw_sums / k_draw_pick also serve token trees (filtered or not): there a
+// walk kernel has already fixed each sequence's stop row, the depth of its
+// accepted path and the tokens of the stop node's children (all rejected),
+// which the draw removes from p_j the way a point-mass draft's token is
+// removed.
 #pragma once
 
 #include <type_traits>
@@ -103,12 +104,6 @@ struct StopRow {
     int n_ex;
 };
 
-// Whether token i is one of the stop row's removed tokens.
-__device__ __forceinline__ bool in_ex(const StopRow& s, int i) {
-    for (int e = 0; e < s.n_ex; ++e)
-        if (s.ex[e] == i) return true;
-    return false;
-}
 
 template <bool kTree>
 __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
@@ -158,7 +153,7 @@ __device__ __forceinline__ StopRow stop_row(const SeqArgs& a, int b, int j) {
 __device__ __forceinline__ void stop_terms_x(const StopRow& s, double inv_T, int i, float xt,
                                              double& p, double& r) {
     p = xt >= s.thr_t ? exp(((double)xt - (double)s.Mt) * inv_T) / s.zt : 0.0;
-    double q = (i == s.dtok || in_ex(s, i)) ? 1.0 : 0.0;
+    double q = i == s.dtok ? 1.0 : 0.0;
     if (s.has_draft) {
         const float xd = load_logit(s.dp, s.ddt, i);
         q = xd >= s.thr_d ? exp(((double)xd - (double)s.Md) * inv_T) / s.zd : 0.0;
@@ -249,10 +244,9 @@ __device__ __forceinline__ void write_outputs(const SeqArgs& a, int b, int j, in
 
 // Draw over the whole stop row pair with one workgroup (thread-contiguous
 // token ranges).  Used when no kept list is available.
-template <bool kTree>
 __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, double* s_val, double* s_excl,
                               double* s_total, int* s_tau) {
-    const StopRow s = stop_row<kTree>(a, b, j);
+    const StopRow s = stop_row<false>(a, b, j);
     const int V = a.sh.V;
     const int per = (V + kSB - 1) / kSB;
     const int lo = threadIdx.x * per, hi = min(lo + per, V);
@@ -288,7 +282,7 @@ __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, do
                 }
             }
         }
-        write_outputs<kTree>(a, b, j, y >= 0 ? y : last);
+        write_outputs<false>(a, b, j, y >= 0 ? y : last);
     }
 }
 
@@ -296,7 +290,6 @@ __device__ __forceinline__ void draw_full_row(const SeqArgs& a, int b, int j, do
 // slices of up to kListMax / kSB entries, read and gathered now.
 constexpr int kListPT = kListMax / kSB;  // 16
 
-template <bool kTree>
 __device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, int n, const uint2* L,
                                                const StopRow& s, double* s_val, double* s_excl,
                                                double* s_total, int* s_tau) {
@@ -340,7 +333,7 @@ __device__ __forceinline__ void draw_long_list(const SeqArgs& a, int b, int j, i
                 if (acc > t) y = ix[e];
             }
         }
-        write_outputs<kTree>(a, b, j, y >= 0 ? y : last);
+        write_outputs<false>(a, b, j, y >= 0 ? y : last);
     }
 }
 
@@ -383,18 +376,13 @@ __device__ __forceinline__ void seq_excl_scan2(double a, double b, double* s_wa,
     eb = pb + xb;
 }
 
-template <bool kTree>
 __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
     __shared__ double s_val[kSB], s_excl[kSB], s_total;
     __shared__ double s_wa[kSB / 64], s_wb[kSB / 64];
     __shared__ int s_j, s_tau, s_y;
     __shared__ int s_last[kSB / 64], s_first[kSB / 64];
     const int K = a.sh.K;
-    // drafted sequences: one workgroup per (sequence, candidate stop row);
-    // token trees: one per sequence, at the row where its walk stopped
-    constexpr bool tree = kTree;
-    const int b = tree ? blockIdx.x : blockIdx.x / (K + 1);
-    const int jc = tree ? a.tstop[b].row : blockIdx.x % (K + 1);
+    const int b = blockIdx.x / (K + 1), jc = blockIdx.x % (K + 1);
     const int rt = b * (K + 1) + jc;
     const int n = a.kept_n[rt];
     const uint2* L = a.kept + (size_t)rt * kListMax;
@@ -415,23 +403,21 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
             pl[e] = LP[threadIdx.x * kLPT + e];
         }
     }
-    const StopRow s = stop_row<kTree>(a, b, jc);
+    const StopRow s = stop_row<false>(a, b, jc);
     // the accepted drafted tokens, one per thread, for the output row
-    const int tok = !tree && (int)threadIdx.x < jc ? a.sh.tokens[(size_t)b * K + threadIdx.x] : -1;
-    if constexpr (!tree) {
-        if (threadIdx.x < 64) {
-            const int j = first_rejection(a, b);
-            if (threadIdx.x == 0) s_j = j;
-        }
-        __syncthreads();
-        if (s_j != jc) return;
+    const int tok = (int)threadIdx.x < jc ? a.sh.tokens[(size_t)b * K + threadIdx.x] : -1;
+    if (threadIdx.x < 64) {
+        const int j = first_rejection(a, b);
+        if (threadIdx.x == 0) s_j = j;
     }
+    __syncthreads();
+    if (s_j != jc) return;
     if (n < 0) {
-        draw_full_row<kTree>(a, b, jc, s_val, s_excl, &s_total, &s_tau);
+        draw_full_row(a, b, jc, s_val, s_excl, &s_total, &s_tau);
         return;
     }
     if (n > kSpec) {
-        draw_long_list<kTree>(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
+        draw_long_list(a, b, jc, n, L, s, s_val, s_excl, &s_total, &s_tau);
         return;
     }
     const double inv_zd = 1.0 / s.zd;
@@ -448,7 +434,7 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         const bool in = threadIdx.x * kLPT + e < n;
         const bool qd = in && xd >= s.thr_d;
         const double q = qd ? exp(((double)xd - (double)s.Md) * a.inv_T) * inv_zd
-                            : (in && ((int)ent[e].x == s.dtok || in_ex(s, (int)ent[e].x)) ? 1.0 : 0.0);
+                            : (in && (int)ent[e].x == s.dtok ? 1.0 : 0.0);
         const double d = pr[e] - q;
         rr[e] = d > 0.0 ? d : 0.0;
         sr += rr[e];
@@ -494,10 +480,6 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
         s_y = y >= 0 ? y : last;
     }
     __syncthreads();
-    if constexpr (tree) {
-        if (threadIdx.x == 0) write_outputs<kTree>(a, b, jc, s_y);
-        return;
-    }
     // output row: accepted drafts, the drawn token, then -1
     int32_t* out = a.out_tokens + (size_t)b * (K + 1);
     for (int k = threadIdx.x; k <= K; k += kSB)

@@ -213,7 +213,10 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     const bool filtered = use_k || use_p;
     const int n_chunks = (int)ceil_div(V, kChunk);
     Workspace* ws;
-    rc = get_workspace(stream, rows, filtered ? n_trows : 0, filtered ? 0 : (size_t)B * n_chunks, &ws,
+    // drafted sequences with filters draw from kept lists; unfiltered rows
+    // and trees draw with chunk sums
+    const bool lists = filtered && !tree;
+    rc = get_workspace(stream, rows, lists ? n_trows : 0, lists ? 0 : (size_t)B * n_chunks, &ws,
                        tree ? (size_t)B : 0, tree ? (size_t)B * K : 0);
     if (rc) return rc;
 
@@ -243,6 +246,9 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     ra.kept_n = ws->kept_n;
     ra.kept_d = ws->kept_d;
     ra.kept_p = ws->kept_p;
+    // A tree's walk needs only the row records; the one stop row per
+    // sequence is drawn by the chunked kernels, which read it again.
+    ra.want_list = lists ? 1 : 0;
     // Few unfiltered rows: split each across workgroups (at most kPartTiles
     // tiles each) so that about 512 workgroups stream, then merge per row.
     ra.parts = 1;
@@ -301,13 +307,9 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
         sa.tstop = ws->tstop;
         sa.tex = ws->tex;
     }
-    if (filtered) {
-        // a tree's stop row is known: one workgroup per sequence
-        const long long nwg = tree ? (long long)B : (long long)B * (K + 1);
-        if (tree)
-            hipLaunchKernelGGL(k_seq_filtered<true>, dim3((unsigned)nwg), dim3(kSB), 0, stream, sa);
-        else
-            hipLaunchKernelGGL(k_seq_filtered<false>, dim3((unsigned)nwg), dim3(kSB), 0, stream, sa);
+    if (lists) {
+        hipLaunchKernelGGL(k_seq_filtered, dim3((unsigned)((long long)B * (K + 1))), dim3(kSB), 0, stream,
+                           sa);
         if ((rc = launch_status())) return rc;
     } else {
         const dim3 g_sums((unsigned)((long long)B * n_chunks));

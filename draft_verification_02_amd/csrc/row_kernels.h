@@ -368,6 +368,7 @@ struct RowArgs {
     float* kept_d;      // [n_trows][kListMax] draft logit of each listed token (rows with a draft row)
     double* kept_p;     // [n_trows][kListMax] p of each listed token
     int want_list;      // target rows store their kept lists (else the draw reads the row itself)
+    int drafts_first;   // draft rows take the first workgroups (see k_row)
     int parts;          // > 1: unfiltered rows split into this many parts (one workgroup each)
     PartRec* prec;      // [rows][parts]
 };
@@ -1762,7 +1763,12 @@ __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
             row_part_plain<DT_F32>(a, S, row, part);
         return;
     }
-    const int row = blockIdx.x;
+    // With more rows than the GPU holds workgroups at once, the draft rows
+    // (the longer streams) go first and the shorter target rows fill the
+    // tail; with one round, the target rows go first so that their heavier
+    // finalize (kept lists) overlaps the draft rows' streams.
+    const int nr = a.sh.n_trows + a.sh.n_drows;
+    const int row = a.drafts_first ? (int)((blockIdx.x + (unsigned)a.sh.n_trows) % (unsigned)nr) : (int)blockIdx.x;
     if (!row_live(a.sh, row)) return;  // past its sequence's draft length
     const bool bf = row_dt(a.sh, row) == DT_BF16;
     if (a.use_k) {

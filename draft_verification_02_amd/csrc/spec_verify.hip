@@ -34,6 +34,7 @@ struct Workspace {
     PartRec* prec = nullptr;
     TreeStop* tstop = nullptr;
     int32_t* tex = nullptr;
+    int n_cu = 0;  // compute units of the device
 };
 
 std::mutex g_mu;
@@ -77,6 +78,9 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
         (void)hipFree(w.base);
         w = Workspace();
     }
+    if (hipDeviceGetAttribute(&nw.n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        nw.n_cu <= 0)
+        return SPEC_E_LAUNCH;
     if (hipMalloc(&nw.base, std::max<size_t>(off, 256)) != hipSuccess) return SPEC_E_NOMEM;
     char* b = static_cast<char*>(nw.base);
     nw.rec = reinterpret_cast<RowRec*>(b + o_rec);
@@ -249,6 +253,8 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     // A tree's walk needs only the row records; the one stop row per
     // sequence is drawn by the chunked kernels, which read it again.
     ra.want_list = lists ? 1 : 0;
+    // two row workgroups fit on a compute unit (their LDS)
+    ra.drafts_first = n_drows > 0 && rows > 2 * ws->n_cu ? 1 : 0;
     // Few unfiltered rows: split each across workgroups (at most kPartTiles
     // tiles each) so that about 512 workgroups stream, then merge per row.
     ra.parts = 1;

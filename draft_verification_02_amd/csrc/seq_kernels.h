@@ -549,6 +549,9 @@ __device__ __forceinline__ void with_dtypes(const StopRow& s, F&& f) {
     }
 }
 
+// Chunk sums of the stop row pair: one workgroup per (sequence, chunk).
+// (Four chunks per workgroup, one round of workgroups for large batches, was
+// slower: each workgroup's chain of loads, scans and barriers grew.)
 template <bool kTree>
 __global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
     __shared__ double s_wa[kSB / 64], s_wb[kSB / 64];
@@ -561,20 +564,20 @@ __global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
     }
     __syncthreads();
     const StopRow s = stop_row<kTree>(a, b, s_j);
-    const int lo = c * kChunk + threadIdx.x * kCPT;
-    double sr = 0.0, sp = 0.0;
     with_dtypes(s, [&](auto tt, auto dt) {
         double p[kCPT], r[kCPT];
-        run_terms<decltype(tt)::value, decltype(dt)::value>(s, a.inv_T, lo, a.sh.V, p, r);
+        run_terms<decltype(tt)::value, decltype(dt)::value>(s, a.inv_T, c * kChunk + threadIdx.x * kCPT, a.sh.V, p,
+                                                             r);
+        double sr = 0.0, sp = 0.0;
 #pragma unroll
         for (int e = 0; e < kCPT; ++e) {
             sr += r[e];
             sp += p[e];
         }
+        double er, ep, tr, tp;
+        seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
+        if (threadIdx.x == 0) a.chunk_sum[(size_t)b * a.n_chunks + c] = make_double2(tr, tp);
     });
-    double er, ep, tr, tp;
-    seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
-    if (threadIdx.x == 0) a.chunk_sum[(size_t)b * a.n_chunks + c] = make_double2(tr, tp);
 }
 
 // One workgroup per sequence: the chunk holding the draw point (chunk sums

@@ -404,3 +404,18 @@ def test_long_drafts_and_wide_batches():
     w = wl.make(512, 2, 1000, target_dtype=wl.F32, temperature=0.9, top_k=20, rho=0.8,
                 seed=512, vseed=513)
     print(check_sampling(w, check_stats=False))
+
+
+def test_more_rows_than_one_round_of_workgroups():
+    """Batches with more rows than the GPU runs at once (draft rows take the
+    first workgroups): general and ragged calls with filters, every sequence
+    against the oracle, at a small vocabulary."""
+    from parity import check_ragged
+    _print_case("rows > one round: B=96 K=7 V=3001")
+    w = wl.make(96, 7, 3001, target_dtype=wl.BF16, draft_dtype=wl.F32, temperature=0.7, top_p=0.9,
+                rho=(0.6, 0.95), n_boost=4, seed=9601, vseed=9602)
+    print(check_sampling(w))
+    print(check_ragged(w, _lens(w.B, w.K, 96)))
+    w = wl.make(64, 7, 2500, target_dtype=wl.F32, draft_dtype=wl.BF16, temperature=1.0, top_k=40,
+                rho=0.8, seed=6401, vseed=6402)
+    print(check_sampling(w))

@@ -14,14 +14,18 @@
 //              streams.  After the stream the kept set is resolved exactly
 //              from the candidates and, if they cannot decide (overflow, too
 //              few), by re-reading the row.  Writes the row record (M, Z,
-//              threshold, p(d_k) or q(d_k)) and, for target rows, the kept
-//              tokens sorted by index.
+//              threshold, p(d_k) or q(d_k)) and, for target rows of drafted
+//              sequences, the kept tokens sorted by index (token trees draw
+//              from the stop row itself and skip the lists).
 //  k_row_merge  : the record of an unfiltered row split over workgroups.
 //  k_row_argmax : greedy mode, lowest-index argmax of a target row.
 //
 // Row numbering: rows [0, B*(K+1)) are target rows b*(K+1)+k, rows
-// [B*(K+1), B*(2K+1)) are draft rows b*K+k (none for point-mass drafts).
+// [B*(K+1), B*(2K+1)) are draft rows b*K+k (none for point-mass drafts; for
+// a token tree K is the node count and target row k+1 follows node k).
 // With per-sequence draft lengths, rows past a sequence's length exit at once.
+// Workgroup i takes row i, or, when rows outnumber what the GPU runs at once,
+// the draft rows first (k_row).
 #pragma once
 
 #include <type_traits>

@@ -1,7 +1,8 @@
 // tree_kernels.h — token-tree verification ("Speculative decoding and
 // multi-token prediction: how LLMs generate faster", section "Multi-head and
-// tree speculation": one target pass scores every branch of a tree of
-// proposals and the best-accepted path is kept).
+// tree speculation": the target model evaluates all branches of a tree of
+// proposals in a single forward pass, and verification returns the one root
+// path that survives).
 //
 // A sequence's tree has N nodes; node i carries a token and a parent index,
 // -1 (the committed context, the root) or a node below i (any other value

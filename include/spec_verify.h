@@ -179,8 +179,8 @@ int spec_verify_point(const void* target_logits, const int32_t* draft_tokens,
 /*
  * Token-tree verification (multi-head / tree speculation: "Speculative
  * decoding and multi-token prediction: how LLMs generate faster", section
- * "Multi-head and tree speculation": one target pass scores every branch of a
- * tree of proposals and the best-accepted path is kept).  The pages leave the
+ * "Multi-head and tree speculation": the target evaluates all branches of a
+ * proposal tree in one forward pass and the output follows one root path).  The pages leave the
  * rule for several candidates at one node open; the reading taken extends
  * the point-mass rule of spec_verify_point to siblings:
  *   node_tokens [B][N] int32 device array: token of node i.

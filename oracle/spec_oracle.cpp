@@ -251,8 +251,8 @@ int oracle_verify_greedy(const void* target, int target_dtype,
             g[k] = best;
         }
         /* Accept the longest prefix where the draft equals the target's
-         * argmax, then emit the target's own token at the first mismatch
-         * (or the bonus argmax of row K when all K match). */
+         * argmax; at the first mismatch the output is the target argmax of
+         * that row (row K's argmax, the bonus, when all K match). */
         int j = K;
         for (int k = 0; k < K; ++k)
             if (draft_tokens[static_cast<size_t>(b) * K + k] != g[k]) {

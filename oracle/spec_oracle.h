@@ -114,11 +114,11 @@ int oracle_verify_point(const void* target, int target_dtype,
 
 /* Token-tree verification (multi-head / tree speculation: "Speculative
  * decoding and multi-token prediction: how LLMs generate faster", section
- * "Multi-head and tree speculation": one pass scores every branch and the
- * best-accepted path is kept).  Each sequence holds N nodes; node i carries
- * token node_tokens[i] and parent parents[i], which is -1 (the committed
- * context, the root) or a node index below i; any other value makes node i
- * unreachable.  Target rows are [B][N+1][V]: row 0 is the root's
+ * "Multi-head and tree speculation": the target evaluates all branches of a
+ * proposal tree together and the verified output is one root path).  Each
+ * sequence holds N nodes; node i carries token node_tokens[i] and parent
+ * parents[i], which is -1 (the committed context, the root) or a node index
+ * below i; any other value makes node i unreachable.  Target rows are [B][N+1][V]: row 0 is the root's
  * distribution, row i+1 the distribution after node i.
  * The children of a node are proposed with certainty (deterministic top-k or
  * n-gram trees), so each child is a point-mass draft.  The walk starts at the

@@ -284,6 +284,9 @@ def main():
     positions = int(lens_np.sum()) if ragged else w.B * w.K
     value = positions / (ms * 1e-3)
     metric = METRIC_TREE if tree else (METRIC_POINT if point else (METRIC_RAGGED if ragged else METRIC))
+    if args.config != 3:  # the metric strings above name the concurrent-batch workload
+        metric = (f"verified {'tree nodes' if tree else 'draft positions'}/sec + HBM GB/s (% peak) at "
+                  f"{w.name}, 1 GPU" + (f", {args.mode} mode" if args.mode != "general" else ""))
     line = {
         "metric": metric,
         "value": round(value, 1),

@@ -419,3 +419,36 @@ def test_more_rows_than_one_round_of_workgroups():
     w = wl.make(64, 7, 2500, target_dtype=wl.F32, draft_dtype=wl.BF16, temperature=1.0, top_k=40,
                 rho=0.8, seed=6401, vseed=6402)
     print(check_sampling(w))
+
+
+def test_concurrent_streams_have_their_own_workspace():
+    """Calls on two streams at once (each with its own workspace), repeated,
+    give the results of the same calls made one after another; a token tree
+    on a third stream too."""
+    from parity import tree_inputs
+    _print_case("two streams + tree stream")
+    w1 = wl.config(3, B=8, V=40000)
+    w2 = wl.make(5, 3, 30011, target_dtype=wl.F32, draft_dtype=wl.BF16, temperature=1.0, top_k=40, rho=0.8,
+                 seed=71, vseed=72)
+    wt = wl.make_tree(4, [3, 2], 20000, temperature=0.8, top_p=0.95, seed=73, vseed=74)
+    a1, a2 = upload(w1), upload(w2)
+    tt, tk, tp = tree_inputs(wt)
+    torch.cuda.synchronize()
+
+    def call(w, a, stream=None):
+        return binding.spec_verify(*a, w.temperature, w.top_k, w.top_p, w.seed, stream=stream)
+
+    r1, r2 = call(w1, a1), call(w2, a2)
+    rt = binding.spec_verify_tree(tt, tk, tp, wt.temperature, wt.top_k, wt.top_p, wt.seed)
+    torch.cuda.synchronize()
+    s1, s2, s3 = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    for _ in range(3):
+        with torch.cuda.stream(s1):
+            c1 = call(w1, a1, s1)
+        with torch.cuda.stream(s2):
+            c2 = call(w2, a2, s2)
+        with torch.cuda.stream(s3):
+            ct = binding.spec_verify_tree(tt, tk, tp, wt.temperature, wt.top_k, wt.top_p, wt.seed, stream=s3)
+        torch.cuda.synchronize()
+        for x, y in zip(c1 + c2 + ct, r1 + r2 + rt):
+            assert torch.equal(x, y)

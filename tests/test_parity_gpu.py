@@ -452,3 +452,22 @@ def test_concurrent_streams_have_their_own_workspace():
         torch.cuda.synchronize()
         for x, y in zip(c1 + c2 + ct, r1 + r2 + rt):
             assert torch.equal(x, y)
+
+
+def test_drafts_longer_than_a_sequence_workgroup():
+    """K = 300 (> 256 threads of the draw workgroup: the output writer reads
+    the drafted tokens past the first 256 from memory).  top-k 1 keeps only
+    each row's argmax, so argmax proposals are always accepted; sequence 0
+    proposes another token at position 280 (rejected there), sequence 1
+    accepts all 300 (bonus)."""
+    from parity import check_point
+    _print_case("K=300")
+    w = wl.make(2, 300, 257, target_dtype=wl.F32, draft_dtype=wl.F32, temperature=1.0, top_k=1, sigma=3.0,
+                rho=0.9, seed=300, vseed=301)
+    toks = np.argmax(wl.as_f32(w.target[:, :w.K]), axis=2).astype(np.int32)
+    toks[0, 280] = (toks[0, 280] + 1) % w.V
+    print(check_point(w, toks))
+    w.tokens = toks
+    print(check_sampling(w, check_stats=False))
+    r = gpu_sampling(w, stats=False)
+    assert r[1].tolist() == [280, 300], r[1]

@@ -105,7 +105,10 @@ __global__ void __launch_bounds__(64) k_tree_walk(TreeArgs a) {
             for (int e = 0; e < n_ex; ++e) dup |= s_ex[e] == x;
             for (unsigned long long mm = m; mm; mm &= mm - 1ull) {
                 const int l = __ffsll((long long)mm) - 1;
-                dup |= l < lane && __shfl(x, l) == x;
+                // every lane takes part in the shuffle: a read from a lane
+                // that is not active returns 0, which would match token 0
+                const int xl = __shfl(x, l);
+                dup |= l < lane && xl == x;
             }
             const bool live = ch && !dup;
             const double pv = live ? s_p[i] : 0.0;

@@ -283,7 +283,7 @@ def check_ragged(w: wl.Workload, lens: np.ndarray, seqs=None, report=None) -> Re
 def tree_inputs(w: wl.Workload, dev="cuda"):
     t = to_device(w.target, dev)
     k = torch.from_numpy(np.ascontiguousarray(w.tokens, dtype=np.int32)).to(dev)
-    p = torch.from_numpy(np.ascontiguousarray(w.meta["parents"], dtype=np.int32)).to(dev)
+    p = torch.from_numpy(np.array(w.meta["parents"], dtype=np.int32, copy=True)).to(dev)
     return t, k, p
 
 

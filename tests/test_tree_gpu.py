@@ -160,3 +160,35 @@ def test_tree_repeated_calls_and_buffer_reuse():
     from parity import check_sampling
     check_sampling(c)
     check_tree(a)
+
+
+def test_tree_children_proposing_token_zero():
+    """Siblings whose tokens include 0 (and a second sibling after it): the
+    repeated-token check must compare real tokens only.  Each root child
+    proposes one of the row's top tokens, the argmax placed at token 0."""
+    _print_case("tree token 0 among siblings")
+    V, B = 63, 64
+    par = np.array([-1, -1, -1, 0, 1, 2], np.int32)
+    N = len(par)
+    w = wl.make(B, N, V, target_dtype=wl.F32, temperature=1.0, top_k=5, top_p=0.9, sigma=0.5, seed=30, vseed=31,
+                with_draft=False)
+    x = np.stack([wl.as_f32(w.target[b]) for b in range(B)])
+    # make token 0 the argmax of every row
+    for b in range(B):
+        for r in range(N + 1):
+            x[b, r, 0] = x[b, r].max() + 0.05
+    w.target = np.ascontiguousarray(x.astype(np.float32))
+    order = np.argsort(-x, axis=2)
+    tok = np.zeros((B, N), np.int32)
+    tok[:, 0] = order[:, 0, 2]
+    tok[:, 1] = order[:, 0, 1]
+    tok[:, 2] = 0
+    for i in range(3, N):
+        tok[:, i] = order[:, par[i] + 1, 0]
+    w.tokens = tok
+    w.meta["parents"] = np.ascontiguousarray(np.broadcast_to(par, (B, N)))
+    # the oracle enters node 2 (token 0) in some sequences, so the check
+    # below covers the case
+    r = oracle.verify_tree(w.target, w.tokens, w.meta["parents"], 1.0, 5, f32(0.9), w.seed)
+    assert (r["path"][:, 0] == 2).sum() >= 3, r["path"][:, 0]
+    print(check_tree(w))

@@ -1,7 +1,7 @@
 """Seeded sweep of random small configurations on the GPU against the
 oracle: vocabulary sizes from 1 to 20000 (tails that fill no tile), K from 0
 to 12, batch sizes 1 to 12, every dtype pair, temperatures including greedy,
-top-k and top-p on and off, through the general, point-mass, ragged and tree
+top-k and top-p on and off, Gaussian and Student-t logits, through the general, point-mass, ragged and tree
 entry points.  Every sequence is checked.  The parameters of each case are
 printed before it runs."""
 import numpy as np
@@ -25,16 +25,17 @@ def _case(i):
     top_p = float(r.choice([1.0, 1.0, 0.5, 0.9, 0.99]))
     sigma = float(r.choice([0.5, 2.0, 4.0]))
     return dict(V=V, K=K, B=B, tdt=tdt, ddt=ddt, T=T, top_k=top_k, top_p=top_p, sigma=sigma,
-                rho=float(r.uniform(0.3, 0.99)), seed=int(r.integers(1, 1 << 30)))
+                rho=float(r.uniform(0.3, 0.99)), seed=int(r.integers(1, 1 << 30)),
+                dist="t3" if i % 3 == 2 else "gauss")
 
 
-@pytest.mark.parametrize("i", range(40))
+@pytest.mark.parametrize("i", range(80))
 def test_random_configuration(i):
     c = _case(i)
     print(f"[case] random {i}: {c}", flush=True)
     w = wl.make(c["B"], c["K"], c["V"], target_dtype=c["tdt"], draft_dtype=c["ddt"], temperature=c["T"],
                 top_k=c["top_k"], top_p=c["top_p"], sigma=c["sigma"], rho=c["rho"], seed=c["seed"],
-                vseed=c["seed"] + 1)
+                vseed=c["seed"] + 1, dist=c["dist"])
     rep = Report()
     if c["T"] == 0.0:
         check_greedy(w)

@@ -289,3 +289,60 @@ def verify_greedy(target, tokens):
     if rc:
         raise ValueError(f"oracle_verify_greedy failed ({rc})")
     return {"tokens": out_tok, "num_accepted": out_n}
+
+
+# ---------------------------------------------------------------------------
+# Greedy verification from the target's last hidden states (the unembedding
+# product computed here, in float64): "FlashMap: Flow Map Speculative
+# Decoding and the Mathematical Elimination of Suffix Decay", section 3
+# (logits of position k are the hidden state times the unembedding matrix
+# transposed), with the greedy rule of "DFlash", section 4 (accept while the
+# draft equals the target argmax, then emit the target's token).
+# ---------------------------------------------------------------------------
+
+def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
+    """Exact float64 values of bf16 bit patterns (uint16)."""
+    return (np.asarray(bits, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def lm_head_logits(hidden_bits: np.ndarray, w_bits: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """Logits [R, V] = hidden [R, H] @ W^T, W [V, H], both bf16 bit patterns,
+    in float64 (a library matmul over vocabulary chunks)."""
+    h = bf16_to_f64(hidden_bits)
+    V = w_bits.shape[0]
+    out = np.empty((h.shape[0], V), dtype=np.float64)
+    for v0 in range(0, V, chunk):
+        out[:, v0:v0 + chunk] = h @ bf16_to_f64(w_bits[v0:v0 + chunk]).T
+    return out
+
+
+def lm_head_abs_sums(hidden_bits: np.ndarray, w_bits: np.ndarray, chunk: int = 8192) -> np.ndarray:
+    """sum_h |hidden_h * W_vh| for every (row, token): the scale of the
+    rounding error of any summation order of the dot product."""
+    h = np.abs(bf16_to_f64(hidden_bits))
+    V = w_bits.shape[0]
+    out = np.empty((h.shape[0], V), dtype=np.float64)
+    for v0 in range(0, V, chunk):
+        out[:, v0:v0 + chunk] = h @ np.abs(bf16_to_f64(w_bits[v0:v0 + chunk])).T
+    return out
+
+
+def verify_greedy_logits64(logits: np.ndarray, tokens: np.ndarray):
+    """Greedy verification on float64 logits [B, K+1, V]: g_k = argmax of row
+    k (lowest index among equal maxima); accept while d_k == g_k, then emit
+    g_j; pad with -1.  Returns tokens [B, K+1] and num_accepted [B]."""
+    B, K1, V = logits.shape
+    K = K1 - 1
+    out = np.full((B, K + 1), -1, dtype=np.int32)
+    num = np.zeros(B, dtype=np.int32)
+    for b in range(B):
+        g = [int(np.argmax(logits[b, k])) for k in range(K + 1)]  # first occurrence of the maximum
+        j = K
+        for k in range(K):
+            if int(tokens[b, k]) != g[k]:
+                j = k
+                break
+        out[b, :j] = tokens[b, :j]
+        out[b, j] = g[j]
+        num[b] = j
+    return out, num

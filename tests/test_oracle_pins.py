@@ -804,3 +804,54 @@ def test_tree_edge_cases():
         r = oracle.verify_tree(t, tok2, par2, 1.0, top_k=2, seed=s)
         assert int(r["tokens"][0, 0]) in top2.tolist()
         assert int(r["num_accepted"][0]) >= 1
+
+
+# ---------------------------------------------------------------------------
+# Greedy verification from hidden states (the unembedding product in float64)
+# ---------------------------------------------------------------------------
+
+def _bf16_bits(a):
+    return (np.asarray(a, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def test_lm_head_logits_and_abs_sums_brute_force():
+    """The float64 matmul against dot products written out, on bf16 inputs
+    (values that bf16 holds exactly)."""
+    rng = np.random.default_rng(61)
+    R, H, V = 3, 5, 7
+    h = np.round(rng.standard_normal((R, H)) * 8) / 8
+    w = np.round(rng.standard_normal((V, H)) * 16) / 16
+    hb, wb = _bf16_bits(h), _bf16_bits(w)
+    np.testing.assert_array_equal(oracle.bf16_to_f64(hb), h)
+    L = oracle.lm_head_logits(hb, wb, chunk=3)
+    A = oracle.lm_head_abs_sums(hb, wb, chunk=2)
+    for r in range(R):
+        for v in range(V):
+            s = 0.0
+            a = 0.0
+            for i in range(H):
+                s += h[r, i] * w[v, i]
+                a += abs(h[r, i] * w[v, i])
+            assert abs(L[r, v] - s) <= 1e-12 * max(1.0, a)
+            assert abs(A[r, v] - a) <= 1e-12 * max(1.0, a)
+
+
+def test_greedy_from_logits64_equals_the_cpp_greedy_rule():
+    """Integer-valued hidden states and weights give logits that float32
+    holds exactly; greedy verification on the float64 product then equals
+    oracle_verify_greedy (independent C++) fed the same logits as float32,
+    including rows with tied maxima (two equal weight rows)."""
+    rng = np.random.default_rng(62)
+    B, K, H, V = 6, 5, 16, 40
+    h = rng.integers(-4, 5, (B * (K + 1), H)).astype(np.float64)
+    w = rng.integers(-4, 5, (V, H)).astype(np.float64)
+    w[7] = w[3]  # token 3 and 7 always tie; argmax takes 3 when they lead
+    L = oracle.lm_head_logits(_bf16_bits(h), _bf16_bits(w)).reshape(B, K + 1, V)
+    g = np.argmax(L, axis=2)
+    toks = np.where(rng.random((B, K)) < 0.8, g[:, :K], rng.integers(0, V, (B, K))).astype(np.int32)
+    out, num = oracle.verify_greedy_logits64(L, toks)
+    ref = oracle.verify_greedy(np.ascontiguousarray(L.astype(np.float32)), toks)
+    np.testing.assert_array_equal(out, ref["tokens"])
+    np.testing.assert_array_equal(num, ref["num_accepted"])
+    assert (g != 7).all()
+    assert num.max() > 0

@@ -27,6 +27,7 @@ ROW_STATS_FIELDS = [("max_logit", "<f4"), ("thresh", "<f4"), ("n_kept", "<i4"),
 ROW_STATS_BYTES = 32
 
 EXPORTS = ["spec_verify", "spec_verify_ragged", "spec_verify_point", "spec_verify_tree", "spec_verify_greedy",
+           "spec_verify_greedy_hidden",
            "spec_verify_stats",
            "spec_rng_uniforms", "spec_profile_events", "spec_status_string", "spec_release_workspace"]
 
@@ -58,6 +59,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     L.spec_verify_point.restype = i32
     L.spec_verify_tree.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, vp, i32]
     L.spec_verify_tree.restype = i32
+    L.spec_verify_greedy_hidden.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    L.spec_verify_greedy_hidden.restype = i32
     L.spec_verify_greedy.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32]
     L.spec_verify_greedy.restype = i32
     L.spec_verify_stats.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp,
@@ -219,6 +222,29 @@ def spec_verify_tree(target: torch.Tensor, tokens: torch.Tensor | None, parents:
                                  _dtype_code(target))
     _check(rc)
     return out_tokens, out_num, out_path
+
+
+def spec_verify_greedy_hidden(hidden: torch.Tensor, w_unembed: torch.Tensor, tokens: torch.Tensor | None,
+                              out_tokens=None, out_num_accepted=None, stream=None):
+    """Greedy verification from hidden states: hidden [B, K+1, H] bf16, the
+    unembedding matrix w_unembed [V, H] bf16, tokens [B, K] int32.  Returns
+    (out_tokens [B, K+1], out_num_accepted [B])."""
+    _dev(hidden, "hidden")
+    _dev(w_unembed, "w_unembed")
+    if hidden.dtype != torch.bfloat16 or w_unembed.dtype != torch.bfloat16:
+        raise TypeError("hidden states and unembedding matrix must be bfloat16")
+    B, K1, H = hidden.shape
+    K = K1 - 1
+    V, H2 = w_unembed.shape
+    assert H2 == H, "hidden size mismatch"
+    if K > 0:
+        assert tokens is not None and tokens.dtype == torch.int32 and tuple(tokens.shape) == (B, K)
+        _dev(tokens, "draft_tokens")
+    out_tokens, out_num = _outputs(B, K, hidden.device, out_tokens, out_num_accepted)
+    rc = load().spec_verify_greedy_hidden(_ptr(hidden), _ptr(w_unembed), _ptr(tokens) if K > 0 else None, B, K, V,
+                                          H, _ptr(out_tokens), _ptr(out_num), _stream_handle(stream))
+    _check(rc)
+    return out_tokens, out_num
 
 
 def spec_verify_greedy(target: torch.Tensor, tokens: torch.Tensor | None, out_tokens=None,

@@ -1,0 +1,175 @@
+// lmhead_kernels.h — greedy verification straight from the target's hidden
+// states: the unembedding product ("FlashMap: Flow Map Speculative Decoding
+// and the Mathematical Elimination of Suffix Decay", section 3: the logits of
+// a position are its hidden state times the transposed unembedding matrix)
+// is computed tile by tile with matrix-core instructions (bf16 inputs, fp32
+// accumulation) and every tile is reduced in registers to its per-row
+// maximum and the lowest token index holding it, so no logit is written to
+// memory.  The greedy rule of "DFlash", section 4, then runs on the argmax.
+//
+//  k_lmhead_argmax : one 256-thread workgroup per (128 tokens, 128 rows)
+//                    tile; 32-wide steps along the hidden dimension staged
+//                    through LDS; each wave owns a 64 x 64 block (2 x 2
+//                    v_mfma_f32_32x32x8_bf16); writes one (max, index) pair
+//                    per (row, vocabulary tile).
+//  k_lmhead_merge  : one workgroup per row: the argmax over its tile pairs.
+//
+// MFMA 32x32x8 operand layout (lane l, element j of the 4-element operand):
+// A[m = l % 32][k = 4 (l / 32) + j], B[k = 4 (l / 32) + j][n = l % 32];
+// result element i holds D[m = 8 (i / 4) + 4 (l / 32) + i % 4][n = l % 32].
+#pragma once
+
+#include <cstdint>
+
+#include "device_common.h"
+
+namespace sv {
+
+constexpr int kLmM = 128;   // rows per workgroup tile
+constexpr int kLmN = 128;   // tokens per workgroup tile
+constexpr int kLmK = 32;    // hidden elements per step
+constexpr int kLmPad = 8;   // LDS row padding (bf16 elements)
+
+typedef short lm_short4 __attribute__((ext_vector_type(4)));
+typedef float lm_float16 __attribute__((ext_vector_type(16)));
+
+struct LmPart {
+    float v;  // tile maximum of the row
+    int i;    // lowest token index holding it (INT32_MAX: none)
+};
+
+struct LmArgs {
+    const uint16_t* hidden;  // [R][H] bf16
+    const uint16_t* w;       // [V][H] bf16
+    int R, V, H;
+    int n_vt;                // vocabulary tiles, ceil(V / kLmN)
+    LmPart* part;            // [R][n_vt]
+    int32_t* gidx;           // [R]
+};
+
+// (v, i) better than (bv, bi): larger value, or equal value at a lower index.
+__device__ __forceinline__ bool lm_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
+
+__global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t sA[kLmM][kLmK + kLmPad];
+    __shared__ __attribute__((aligned(16))) uint16_t sW[kLmN][kLmK + kLmPad];
+    __shared__ LmPart sP[kLmM][2];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int v0 = blockIdx.x * kLmN, row0 = blockIdx.y * kLmM;
+    lm_float16 acc[2][2];
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 2; ++ni)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
+
+    for (int h0 = 0; h0 < a.H; h0 += kLmK) {
+        // stage 128 x 32 of each operand: 512 pieces of 8 bf16 per operand,
+        // two per thread; rows past R or V and columns past H read as zero
+#pragma unroll
+        for (int q = 0; q < 2; ++q) {
+            const int e = tid + q * 256;
+            const int r = e >> 2, piece = e & 3;
+            const int hh = h0 + piece * 8;
+            uint4 va = make_uint4(0u, 0u, 0u, 0u), vw = make_uint4(0u, 0u, 0u, 0u);
+            if (row0 + r < a.R && hh < a.H) va = *reinterpret_cast<const uint4*>(a.hidden + (size_t)(row0 + r) * a.H + hh);
+            if (v0 + r < a.V && hh < a.H) vw = *reinterpret_cast<const uint4*>(a.w + (size_t)(v0 + r) * a.H + hh);
+            *reinterpret_cast<uint4*>(&sA[r][piece * 8]) = va;
+            *reinterpret_cast<uint4*>(&sW[r][piece * 8]) = vw;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int ks = 0; ks < kLmK / 8; ++ks) {
+            const int kc = ks * 8 + (lane >> 5) * 4;
+            lm_short4 fa[2], fb[2];
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+                fa[mi] = *reinterpret_cast<const lm_short4*>(&sA[wm * 64 + mi * 32 + (lane & 31)][kc]);
+#pragma unroll
+            for (int ni = 0; ni < 2; ++ni)
+                fb[ni] = *reinterpret_cast<const lm_short4*>(&sW[wn * 64 + ni * 32 + (lane & 31)][kc]);
+#pragma unroll
+            for (int mi = 0; mi < 2; ++mi)
+#pragma unroll
+                for (int ni = 0; ni < 2; ++ni)
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+        }
+        __syncthreads();
+    }
+
+    // per row of this wave's block: the best over its 64 tokens (the two
+    // column blocks, then the 32 lanes of the half-wave holding the row)
+#pragma unroll
+    for (int mi = 0; mi < 2; ++mi) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int n0 = v0 + wn * 64 + (lane & 31);
+            float bv = n0 < a.V ? acc[mi][0][i] : -INFINITY;
+            int bi = n0 < a.V ? n0 : INT32_MAX;
+            const int n1 = n0 + 32;
+            if (n1 < a.V && lm_better(acc[mi][1][i], n1, bv, bi)) {
+                bv = acc[mi][1][i];
+                bi = n1;
+            }
+#pragma unroll
+            for (int off = 16; off >= 1; off >>= 1) {
+                const float ov = __shfl_xor(bv, off);
+                const int oi = __shfl_xor(bi, off);
+                if (lm_better(ov, oi, bv, bi)) {
+                    bv = ov;
+                    bi = oi;
+                }
+            }
+            if ((lane & 31) == 0) sP[wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)][wn] = LmPart{bv, bi};
+        }
+    }
+    __syncthreads();
+    if (tid < kLmM && row0 + tid < a.R) {
+        LmPart p = sP[tid][0];
+        const LmPart q = sP[tid][1];
+        if (lm_better(q.v, q.i, p.v, p.i)) p = q;
+        a.part[(size_t)(row0 + tid) * a.n_vt + blockIdx.x] = p;
+    }
+}
+
+__global__ void __launch_bounds__(256) k_lmhead_merge(LmArgs a) {
+    __shared__ float s_v[4];
+    __shared__ int s_i[4];
+    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const LmPart* p = a.part + (size_t)row * a.n_vt;
+    float bv = -INFINITY;
+    int bi = INT32_MAX;
+    for (int t = tid; t < a.n_vt; t += 256) {
+        const LmPart q = p[t];
+        if (lm_better(q.v, q.i, bv, bi)) {
+            bv = q.v;
+            bi = q.i;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (lm_better(ov, oi, bv, bi)) {
+            bv = ov;
+            bi = oi;
+        }
+    }
+    if (lane == 0) {
+        s_v[wave] = bv;
+        s_i[wave] = bi;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int w2 = 1; w2 < 4; ++w2)
+            if (lm_better(s_v[w2], s_i[w2], bv, bi)) {
+                bv = s_v[w2];
+                bi = s_i[w2];
+            }
+        a.gidx[row] = bi;
+    }
+}
+
+}  // namespace sv

@@ -4,6 +4,7 @@
 #include <hip/hip_ext.h>
 
 #include <cmath>
+#include <cstdint>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -11,6 +12,7 @@
 
 #include "../../include/spec_verify.h"
 #include "tree_kernels.h"
+#include "lmhead_kernels.h"
 
 namespace {
 
@@ -408,6 +410,44 @@ int spec_verify_tree(const void* target_logits, const int32_t* node_tokens, cons
     return run_sampling(target_logits, nullptr, node_tokens, B, N, V, temperature, top_k, top_p, seed,
                         out_tokens, out_num_accepted, s, target_dtype, SPEC_DTYPE_F32, nullptr, nullptr, true,
                         nullptr, nullptr, nullptr, parents, out_path);
+}
+
+int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const int32_t* draft_tokens, int B,
+                              int K, int V, int H, int32_t* out_tokens, int32_t* out_num_accepted, void* stream) {
+    if (B < 0 || K < 0 || V < 1 || H < 8 || H % 8 != 0) return SPEC_E_INVALID;
+    const long long R = (long long)B * (K + 1);
+    const long long n_vt = ceil_div(V, kLmN);
+    if (R >= (1LL << 31) || R * n_vt >= (1LL << 40) || ceil_div(R, kLmM) > 65535) return SPEC_E_INVALID;
+    if ((long long)V * H >= (1LL << 40) || R * H >= (1LL << 40) || n_vt >= (1LL << 31)) return SPEC_E_INVALID;
+    if (B == 0) return SPEC_OK;
+    if (!hidden || !w_unembed || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SPEC_E_INVALID;
+    if (((uintptr_t)hidden | (uintptr_t)w_unembed) & 15u) return SPEC_E_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    Workspace* ws;
+    // the tile pairs (8 bytes each) live in the chunk-sum area (16-byte units)
+    int rc = get_workspace(st, 0, (size_t)R, (size_t)ceil_div(R * n_vt, 2), &ws);
+    if (rc) return rc;
+    LmArgs la;
+    la.hidden = static_cast<const uint16_t*>(hidden);
+    la.w = static_cast<const uint16_t*>(w_unembed);
+    la.R = (int)R;
+    la.V = V;
+    la.H = H;
+    la.n_vt = (int)n_vt;
+    la.part = reinterpret_cast<LmPart*>(ws->chunk_sum);
+    la.gidx = ws->gidx;
+    void *evb, *eva;
+    take_events(&evb, &eva);
+    hipExtLaunchKernelGGL(k_lmhead_argmax, dim3((unsigned)n_vt, (unsigned)ceil_div(R, kLmM)), dim3(256), 0, st,
+                          static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, la);
+    if ((rc = launch_status())) return rc;
+    hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)R), dim3(256), 0, st, la);
+    if ((rc = launch_status())) return rc;
+    const Shape sh{nullptr, nullptr, draft_tokens, B, K, V, SPEC_DTYPE_BF16, 0, 2, 0, (int)R, 0, nullptr, nullptr,
+                   nullptr};
+    hipLaunchKernelGGL(k_greedy_prefix, dim3((unsigned)ceil_div(B, 256)), dim3(256), 0, st, sh,
+                       (const int32_t*)ws->gidx, out_tokens, out_num_accepted);
+    return launch_status();
 }
 
 int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int K, int V,

@@ -36,6 +36,8 @@ _S_DRAFT = 3
 _S_DRAFT_SAMPLE = 4
 _S_RHO = 5
 _S_TREE = 6
+_S_HIDDEN = 7
+_S_UNEMBED = 8
 
 
 def gen_seed(cfg: int, rnd: int = 0) -> int:
@@ -235,6 +237,25 @@ def make_tree(B: int, branching, V: int, *, target_dtype: int = BF16, temperatur
     w.meta["parents"] = np.ascontiguousarray(np.broadcast_to(par, (B, N)))
     w.meta["branching"] = list(branching)
     return w
+
+
+def make_hidden(B: int, K: int, V: int, H: int, *, seed: int = 1, w_scale: float | None = None):
+    """Inputs of greedy verification from hidden states: target hidden states
+    [B, K+1, H] ~ N(0, 1) and an unembedding matrix [V, H] ~ N(0, w_scale^2)
+    (random weights; w_scale defaults to 1/sqrt(H)), both as bf16 bit
+    patterns (uint16), drawn one row at a time from their own streams."""
+    if w_scale is None:
+        w_scale = 1.0 / np.sqrt(H)
+    hidden = np.empty((B, K + 1, H), dtype=np.uint16)
+    for r in range(B * (K + 1)):
+        hidden.reshape(-1, H)[r] = f32_to_bf16_bits(_rng(seed, _S_HIDDEN, r).standard_normal(H).astype(np.float32))
+    w = np.empty((V, H), dtype=np.uint16)
+    step = 4096
+    for v0 in range(0, V, step):
+        g = _rng(seed, _S_UNEMBED, v0 // step)
+        n = min(step, V - v0)
+        w[v0:v0 + n] = f32_to_bf16_bits((g.standard_normal((n, H), dtype=np.float32) * np.float32(w_scale)))
+    return hidden, w
 
 
 # The five measured workloads (shapes, dtypes, distributions and processing).

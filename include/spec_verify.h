@@ -220,6 +220,29 @@ int spec_verify_tree(const void* target_logits, const int32_t* node_tokens,
  * bonus argmax g_K).  Reads target logits only.  Same conventions as
  * spec_verify.
  */
+/*
+ * Greedy verification straight from the target's last hidden states, the
+ * unembedding product fused in ("FlashMap: Flow Map Speculative Decoding and
+ * the Mathematical Elimination of Suffix Decay", section 3: a position's
+ * logits are its hidden state times the transposed unembedding matrix; the
+ * greedy rule of "DFlash", section 4, as spec_verify_greedy):
+ *   hidden     [B][K+1][H] bf16 device array: the target's final hidden state
+ *              at each verified position (16-byte aligned);
+ *   w_unembed  [V][H] bf16 device array: the unembedding (LM head) matrix
+ *              (16-byte aligned);
+ *   H          hidden size, a multiple of 8.
+ * The logits hidden . w_unembed^T are computed in tiles on the matrix cores
+ * (bf16 products, fp32 accumulation) and reduced to each row's argmax
+ * (lowest index among equal maxima) without being written to memory; the
+ * accepted prefix and the emitted token are as spec_verify_greedy.  Logits
+ * whose top two values lie within the fp32 accumulation error of each other
+ * may resolve to either.  Outputs, stream and error codes as spec_verify.
+ */
+int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed,
+                              const int32_t* draft_tokens, int B, int K, int V,
+                              int H, int32_t* out_tokens,
+                              int32_t* out_num_accepted, void* stream);
+
 int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens,
                        int B, int K, int V, int32_t* out_tokens,
                        int32_t* out_num_accepted, void* stream,

@@ -109,6 +109,16 @@ def test_tree_entry_rejects_invalid_arguments_on_host(lib, kw, code):
                                 a["stream"], a["tdt"]) == code
 
 
+def test_hidden_greedy_entry_rejects_invalid_arguments_on_host(lib):
+    p = ctypes.c_void_p(16)
+    def call(B=1, K=1, V=10, H=16, hidden=p, w=p, tok=p, out=p):
+        return lib.spec_verify_greedy_hidden(hidden, w, tok, B, K, V, H, out, p, None)
+    assert call(H=12) == 1 and call(H=0) == 1 and call(V=0) == 1 and call(B=-1) == 1 and call(K=-1) == 1
+    assert call(hidden=None) == 1 and call(w=None) == 1 and call(tok=None) == 1 and call(out=None) == 1
+    assert call(hidden=ctypes.c_void_p(24)) == 1  # not 16-byte aligned
+    assert call(B=0, hidden=None, w=None, tok=None, out=None) == 0
+
+
 def test_empty_batch_returns_ok_without_device_work(lib):
     assert _call(lib, B=0, target=None, draft=None, tokens=None, out=None, num=None) == 0
     assert lib.spec_verify_greedy(None, None, 0, 3, 10, None, None, None, 1) == 0

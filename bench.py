@@ -18,6 +18,11 @@ greedy draft head) and no draft logits read.
 drawn uniformly from 0..K (seeded) and the per-position acceptance counters
 on; the bytes counted are those of the rows inside each sequence's length.
 
+--mode hidden measures spec_verify_greedy_hidden: greedy verification of the
+same batch shape straight from the target's hidden states (H = 4096, random
+bf16 unembedding matrix of 151936 x 4096), the unembedding product fused with
+the argmax on the matrix cores.
+
 --mode tree measures spec_verify_tree: the same target-row distributions and
 processing over a static 44-node token tree per sequence (4 children of the
 root, then 2, 2 and 1 per node), 45 target rows per sequence, the children's
@@ -46,6 +51,10 @@ METRIC_POINT = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=
 METRIC_TREE = ("verified tree nodes/sec + HBM GB/s (% peak) at B=32 N=44 V=151936, 1 GPU, "
                "token trees 4-2-2-1 (spec_verify_tree)")
 TREE_BRANCHING = [4, 2, 2, 1]
+METRIC_HIDDEN = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936 H=4096, 1 GPU, "
+                 "greedy from hidden states, unembedding fused (spec_verify_greedy_hidden)")
+HIDDEN_H = 4096
+PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
 
@@ -131,6 +140,104 @@ def cpu_baseline(w, max_seqs: int, point_tokens=None, lens=None, tree=False):
                       f"fp64 C++ oracle, {dt:.2f} s"}
 
 
+def _timed_steps(torch, step, steps, warmup, settle_s=0.04):
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    settle = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < settle_s:
+        step(settle)
+        settle += 1
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, settle
+
+
+def _kernel_ms(torch, binding, step, n):
+    hip = _hip()
+    evs = []
+    for _ in range(2 * n):
+        h = ctypes.c_void_p()
+        assert hip.hipEventCreate(ctypes.byref(h)) == 0
+        evs.append(h)
+    torch.cuda.synchronize()
+    for i in range(n):
+        binding.profile_events(evs[2 * i].value, evs[2 * i + 1].value)
+        step(i)
+    torch.cuda.synchronize()
+    durs = []
+    for i in range(n):
+        f = ctypes.c_float()
+        assert hip.hipEventElapsedTime(ctypes.byref(f), evs[2 * i], evs[2 * i + 1]) == 0
+        durs.append(f.value)
+    for h in evs:
+        hip.hipEventDestroy(h)
+    return float(np.mean(durs))
+
+
+def bench_hidden(args, torch, binding, wl):
+    """Greedy verification from hidden states at the concurrent-batch shape."""
+    spec = wl.CONFIG_SPECS[3]
+    B, K, V, H = spec["B"], spec["K"], spec["V"], HIDDEN_H
+    hidden, w = wl.make_hidden(B, K, V, H, seed=wl.gen_seed(3))
+    tokens = np.random.default_rng(wl.verify_seed(3) & 0xFFFFFFFF).integers(0, V, (B, K)).astype(np.int32)
+    dev = torch.device("cuda:0")
+
+    def up16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    h_t, w_t, k_t = up16(hidden), up16(w), torch.from_numpy(tokens).to(dev)
+    out_t = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
+    out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+
+    def step(i):
+        binding.spec_verify_greedy_hidden(h_t, w_t, k_t, out_t, out_n)
+
+    ms, settle = _timed_steps(torch, step, args.steps, args.warmup)
+    k_ms = _kernel_ms(torch, binding, step, args.steps)
+    R = B * (K + 1)
+    ideal = w.nbytes + hidden.nbytes
+    flops = 2.0 * R * V * H
+    achieved = ideal / (k_ms * 1e-3) / 1e9
+    tflops = flops / (k_ms * 1e-3) / 1e12
+    line = {
+        "metric": METRIC_HIDDEN,
+        "value": round(B * K / (ms * 1e-3), 1),
+        "unit": "verified draft positions/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settle,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 x bf16 -> f32",
+        "data": "synthetic (random bf16 hidden states and unembedding matrix)",
+        "config": {"workload": f"c3 shape greedy from hidden states B{B} K{K} V{V} H{H}", "B": B, "K": K, "V": V,
+                   "H": H, "ideal_bytes": ideal, "flops": flops},
+        "roofline": {"bound": "hbm", "kernel": "k_lmhead_argmax", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": None, "kernel_ms": round(k_ms, 5), "kernel_source_hash": kernel_source_hash(),
+                     "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle  # CPU baseline leg only
+        from threadpoolctl import threadpool_limits
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=1):
+            L = oracle.lm_head_logits(hidden[0], w).reshape(1, K + 1, V)
+            oracle.verify_greedy_logits64(L, tokens[:1])
+        dt = time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(K / dt, 3), "unit": "verified draft positions/s", "cores": 1,
+                                "kind": "oracle",
+                                "sample": f"1 of {B} sequences ({K + 1} rows), float64 product on one thread, "
+                                          f"{dt:.2f} s"}
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -139,7 +246,7 @@ def main():
     ap.add_argument("--no-settle", dest="settle", action="store_false",
                     help="skip the untimed settle phase after the warmup steps")
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--mode", choices=["general", "point", "ragged", "tree"], default="general",
+    ap.add_argument("--mode", choices=["general", "point", "ragged", "tree", "hidden"], default="general",
                     help="general: spec_verify with draft logits (the headline); point: "
                          "spec_verify_point with point-mass drafts")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
@@ -168,6 +275,8 @@ def main():
     import torch
     from draft_verification_02_amd import binding, workloads as wl
 
+    if args.mode == "hidden":
+        return bench_hidden(args, torch, binding, wl)
     point = args.mode == "point"
     ragged = args.mode == "ragged"
     tree = args.mode == "tree"

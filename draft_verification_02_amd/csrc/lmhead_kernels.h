@@ -7,15 +7,16 @@
 // maximum and the lowest token index holding it, so no logit is written to
 // memory.  The greedy rule of "DFlash", section 4, then runs on the argmax.
 //
-//  k_lmhead_argmax : one 256-thread workgroup per (128 tokens, 128 rows)
-//                    tile; 32-wide steps along the hidden dimension staged
-//                    through LDS; each wave owns a 64 x 64 block (2 x 2
-//                    v_mfma_f32_32x32x8_bf16); writes one (max, index) pair
-//                    per (row, vocabulary tile).
+//  k_lmhead_argmax : one 256-thread workgroup per (128 rows, 128 tokens)
+//                    tile; 64-wide steps along the hidden dimension staged
+//                    through LDS, the next step's operands loaded into
+//                    registers while the current one multiplies; each wave
+//                    owns a 64 x 64 block (2 x 2 v_mfma_f32_32x32x16_bf16);
+//                    writes one (max, index) pair per (row, vocabulary tile).
 //  k_lmhead_merge  : one workgroup per row: the argmax over its tile pairs.
 //
-// MFMA 32x32x8 operand layout (lane l, element j of the 4-element operand):
-// A[m = l % 32][k = 4 (l / 32) + j], B[k = 4 (l / 32) + j][n = l % 32];
+// MFMA 32x32x16 operand layout (lane l, element j of the 8-element operand,
+// measured): A[m = l % 32][k = 8 (l / 32) + j], B[k = 8 (l / 32) + j][n = l % 32];
 // result element i holds D[m = 8 (i / 4) + 4 (l / 32) + i % 4][n = l % 32].
 #pragma once
 
@@ -27,10 +28,10 @@ namespace sv {
 
 constexpr int kLmM = 128;   // rows per workgroup tile
 constexpr int kLmN = 128;   // tokens per workgroup tile
-constexpr int kLmK = 32;    // hidden elements per step
+constexpr int kLmK = 64;    // hidden elements per step
 constexpr int kLmPad = 8;   // LDS row padding (bf16 elements)
 
-typedef short lm_short4 __attribute__((ext_vector_type(4)));
+typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float lm_float16 __attribute__((ext_vector_type(16)));
 
 struct LmPart {
@@ -56,7 +57,9 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
     __shared__ LmPart sP[kLmM][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    const int v0 = blockIdx.x * kLmN, row0 = blockIdx.y * kLmM;
+    // row tiles vary fastest, so the row tiles of one vocabulary tile run
+    // side by side and the unembedding rows come from HBM once
+    const int row0 = blockIdx.x * kLmM, v0 = blockIdx.y * kLmN;
     lm_float16 acc[2][2];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -65,36 +68,52 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
 
-    for (int h0 = 0; h0 < a.H; h0 += kLmK) {
-        // stage 128 x 32 of each operand: 512 pieces of 8 bf16 per operand,
-        // two per thread; rows past R or V and columns past H read as zero
+    // one step stages 128 x kLmK of each operand: pieces of 8 bf16, kLmK / 8
+    // per row, kPieces per thread; rows past R or V and columns past H read
+    // as zero (no memory access)
+    constexpr int kPerRow = kLmK / 8;
+    constexpr int kPieces = kLmM * kPerRow / 256;
+    uint4 ra[kPieces], rw[kPieces];
+    auto load = [&](int h0) {
 #pragma unroll
-        for (int q = 0; q < 2; ++q) {
+        for (int q = 0; q < kPieces; ++q) {
             const int e = tid + q * 256;
-            const int r = e >> 2, piece = e & 3;
-            const int hh = h0 + piece * 8;
-            uint4 va = make_uint4(0u, 0u, 0u, 0u), vw = make_uint4(0u, 0u, 0u, 0u);
-            if (row0 + r < a.R && hh < a.H) va = *reinterpret_cast<const uint4*>(a.hidden + (size_t)(row0 + r) * a.H + hh);
-            if (v0 + r < a.V && hh < a.H) vw = *reinterpret_cast<const uint4*>(a.w + (size_t)(v0 + r) * a.H + hh);
-            *reinterpret_cast<uint4*>(&sA[r][piece * 8]) = va;
-            *reinterpret_cast<uint4*>(&sW[r][piece * 8]) = vw;
+            const int r = e / kPerRow, hh = h0 + (e % kPerRow) * 8;
+            ra[q] = make_uint4(0u, 0u, 0u, 0u);
+            rw[q] = make_uint4(0u, 0u, 0u, 0u);
+            if (row0 + r < a.R && hh < a.H) ra[q] = *reinterpret_cast<const uint4*>(a.hidden + (size_t)(row0 + r) * a.H + hh);
+            if (v0 + r < a.V && hh < a.H) rw[q] = *reinterpret_cast<const uint4*>(a.w + (size_t)(v0 + r) * a.H + hh);
         }
-        __syncthreads();
+    };
+    auto store = [&]() {
 #pragma unroll
-        for (int ks = 0; ks < kLmK / 8; ++ks) {
-            const int kc = ks * 8 + (lane >> 5) * 4;
-            lm_short4 fa[2], fb[2];
+        for (int q = 0; q < kPieces; ++q) {
+            const int e = tid + q * 256;
+            const int r = e / kPerRow, c = (e % kPerRow) * 8;
+            *reinterpret_cast<uint4*>(&sA[r][c]) = ra[q];
+            *reinterpret_cast<uint4*>(&sW[r][c]) = rw[q];
+        }
+    };
+    load(0);
+    for (int h0 = 0; h0 < a.H; h0 += kLmK) {
+        store();
+        __syncthreads();
+        load(h0 + kLmK);  // the next step's operands arrive while this one multiplies
+#pragma unroll
+        for (int ks = 0; ks < kLmK / 16; ++ks) {
+            const int kc = ks * 16 + (lane >> 5) * 8;
+            lm_bf16x8 fa[2], fb[2];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
-                fa[mi] = *reinterpret_cast<const lm_short4*>(&sA[wm * 64 + mi * 32 + (lane & 31)][kc]);
+                fa[mi] = __builtin_bit_cast(lm_bf16x8, *reinterpret_cast<const uint4*>(&sA[wm * 64 + mi * 32 + (lane & 31)][kc]));
 #pragma unroll
             for (int ni = 0; ni < 2; ++ni)
-                fb[ni] = *reinterpret_cast<const lm_short4*>(&sW[wn * 64 + ni * 32 + (lane & 31)][kc]);
+                fb[ni] = __builtin_bit_cast(lm_bf16x8, *reinterpret_cast<const uint4*>(&sW[wn * 64 + ni * 32 + (lane & 31)][kc]));
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < 2; ++ni)
-                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+                    acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
         }
         __syncthreads();
     }
@@ -130,7 +149,7 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
         LmPart p = sP[tid][0];
         const LmPart q = sP[tid][1];
         if (lm_better(q.v, q.i, p.v, p.i)) p = q;
-        a.part[(size_t)(row0 + tid) * a.n_vt + blockIdx.x] = p;
+        a.part[(size_t)(row0 + tid) * a.n_vt + blockIdx.y] = p;
     }
 }
 

@@ -417,7 +417,7 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     if (B < 0 || K < 0 || V < 1 || H < 8 || H % 8 != 0) return SPEC_E_INVALID;
     const long long R = (long long)B * (K + 1);
     const long long n_vt = ceil_div(V, kLmN);
-    if (R >= (1LL << 31) || R * n_vt >= (1LL << 40) || ceil_div(R, kLmM) > 65535) return SPEC_E_INVALID;
+    if (R >= (1LL << 31) || R * n_vt >= (1LL << 40) || n_vt > 65535) return SPEC_E_INVALID;
     if ((long long)V * H >= (1LL << 40) || R * H >= (1LL << 40) || n_vt >= (1LL << 31)) return SPEC_E_INVALID;
     if (B == 0) return SPEC_OK;
     if (!hidden || !w_unembed || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SPEC_E_INVALID;
@@ -438,7 +438,7 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     la.gidx = ws->gidx;
     void *evb, *eva;
     take_events(&evb, &eva);
-    hipExtLaunchKernelGGL(k_lmhead_argmax, dim3((unsigned)n_vt, (unsigned)ceil_div(R, kLmM)), dim3(256), 0, st,
+    hipExtLaunchKernelGGL(k_lmhead_argmax, dim3((unsigned)ceil_div(R, kLmM), (unsigned)n_vt), dim3(256), 0, st,
                           static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, la);
     if ((rc = launch_status())) return rc;
     hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)R), dim3(256), 0, st, la);

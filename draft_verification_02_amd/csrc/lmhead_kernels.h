@@ -44,6 +44,7 @@ struct LmArgs {
     const uint16_t* w;       // [V][H] bf16
     int R, V, H;
     int n_vt;                // vocabulary tiles, ceil(V / kLmN)
+    int n_rt;                // row tiles, ceil(R / kLmM)
     LmPart* part;            // [R][n_vt]
     int32_t* gidx;           // [R]
 };
@@ -57,9 +58,15 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
     __shared__ LmPart sP[kLmM][2];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
-    // row tiles vary fastest, so the row tiles of one vocabulary tile run
-    // side by side and the unembedding rows come from HBM once
-    const int row0 = blockIdx.x * kLmM, v0 = blockIdx.y * kLmN;
+    // Workgroups are dispatched to the 8 XCDs in turn (workgroup L to XCD
+    // L mod 8), each XCD with its own L2.  Workgroup L = 8 (n_rt q + rt) + x
+    // takes row tile rt of vocabulary tile 8 q + x, so every row tile of a
+    // vocabulary tile runs on one XCD at about the same time and the
+    // unembedding rows come from HBM once.
+    const int L = blockIdx.x, x = L & 7, qr = L >> 3;
+    const int rt = qr % a.n_rt, vt = (qr / a.n_rt) * 8 + x;
+    if (vt >= a.n_vt) return;
+    const int row0 = rt * kLmM, v0 = vt * kLmN;
     lm_float16 acc[2][2];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
@@ -149,7 +156,7 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
         LmPart p = sP[tid][0];
         const LmPart q = sP[tid][1];
         if (lm_better(q.v, q.i, p.v, p.i)) p = q;
-        a.part[(size_t)(row0 + tid) * a.n_vt + blockIdx.y] = p;
+        a.part[(size_t)(row0 + tid) * a.n_vt + vt] = p;
     }
 }
 

@@ -417,7 +417,8 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     if (B < 0 || K < 0 || V < 1 || H < 8 || H % 8 != 0) return SPEC_E_INVALID;
     const long long R = (long long)B * (K + 1);
     const long long n_vt = ceil_div(V, kLmN);
-    if (R >= (1LL << 31) || R * n_vt >= (1LL << 40) || n_vt > 65535) return SPEC_E_INVALID;
+    if (R >= (1LL << 31) || R * n_vt >= (1LL << 40) || (n_vt + 8) * ceil_div(R, kLmM) >= (1LL << 31))
+        return SPEC_E_INVALID;
     if ((long long)V * H >= (1LL << 40) || R * H >= (1LL << 40) || n_vt >= (1LL << 31)) return SPEC_E_INVALID;
     if (B == 0) return SPEC_OK;
     if (!hidden || !w_unembed || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SPEC_E_INVALID;
@@ -434,11 +435,15 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     la.V = V;
     la.H = H;
     la.n_vt = (int)n_vt;
+    la.n_rt = (int)ceil_div(R, kLmM);
     la.part = reinterpret_cast<LmPart*>(ws->chunk_sum);
     la.gidx = ws->gidx;
     void *evb, *eva;
     take_events(&evb, &eva);
-    hipExtLaunchKernelGGL(k_lmhead_argmax, dim3((unsigned)ceil_div(R, kLmM), (unsigned)n_vt), dim3(256), 0, st,
+    // one workgroup per (row tile, vocabulary tile), the vocabulary tiles
+    // padded to a multiple of 8 (see k_lmhead_argmax)
+    const long long n_wg = ceil_div(n_vt, 8) * 8 * ceil_div(R, kLmM);
+    hipExtLaunchKernelGGL(k_lmhead_argmax, dim3((unsigned)n_wg), dim3(256), 0, st,
                           static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, la);
     if ((rc = launch_status())) return rc;
     hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)R), dim3(256), 0, st, la);

@@ -7,11 +7,11 @@
 // maximum and the lowest token index holding it, so no logit is written to
 // memory.  The greedy rule of "DFlash", section 4, then runs on the argmax.
 //
-//  k_lmhead_argmax : one 256-thread workgroup per (128 rows, 128 tokens)
+//  k_lmhead_argmax : one 256-thread workgroup per (128 rows, 256 tokens)
 //                    tile; 64-wide steps along the hidden dimension staged
 //                    through LDS, the next step's operands loaded into
 //                    registers while the current one multiplies; each wave
-//                    owns a 64 x 64 block (2 x 2 v_mfma_f32_32x32x16_bf16);
+//                    owns a 64 x 128 block (2 x 4 v_mfma_f32_32x32x16_bf16);
 //                    writes one (max, index) pair per (row, vocabulary tile).
 //  k_lmhead_merge  : one workgroup per row: the argmax over its tile pairs.
 //
@@ -27,7 +27,8 @@
 namespace sv {
 
 constexpr int kLmM = 128;   // rows per workgroup tile
-constexpr int kLmN = 128;   // tokens per workgroup tile
+constexpr int kLmN = 256;   // tokens per workgroup tile
+constexpr int kLmNI = kLmN / 64;  // 32-token MFMA blocks per wave (two waves across the tokens)
 constexpr int kLmK = 64;    // hidden elements per step
 constexpr int kLmPad = 8;   // LDS row padding (bf16 elements)
 
@@ -52,7 +53,7 @@ struct LmArgs {
 // (v, i) better than (bv, bi): larger value, or equal value at a lower index.
 __device__ __forceinline__ bool lm_better(float v, int i, float bv, int bi) { return v > bv || (v == bv && i < bi); }
 
-__global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
+__global__ void __launch_bounds__(256, 2) k_lmhead_argmax(LmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t sA[kLmM][kLmK + kLmPad];
     __shared__ __attribute__((aligned(16))) uint16_t sW[kLmN][kLmK + kLmPad];
     __shared__ LmPart sP[kLmM][2];
@@ -67,11 +68,11 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
     const int rt = qr % a.n_rt, vt = (qr / a.n_rt) * 8 + x;
     if (vt >= a.n_vt) return;
     const int row0 = rt * kLmM, v0 = vt * kLmN;
-    lm_float16 acc[2][2];
+    lm_float16 acc[2][kLmNI];
 #pragma unroll
     for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int ni = 0; ni < kLmNI; ++ni)
 #pragma unroll
             for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
 
@@ -79,26 +80,35 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
     // per row, kPieces per thread; rows past R or V and columns past H read
     // as zero (no memory access)
     constexpr int kPerRow = kLmK / 8;
-    constexpr int kPieces = kLmM * kPerRow / 256;
-    uint4 ra[kPieces], rw[kPieces];
+    constexpr int kPiecesA = kLmM * kPerRow / 256;
+    constexpr int kPiecesW = kLmN * kPerRow / 256;
+    uint4 ra[kPiecesA], rw[kPiecesW];
     auto load = [&](int h0) {
 #pragma unroll
-        for (int q = 0; q < kPieces; ++q) {
+        for (int q = 0; q < kPiecesA; ++q) {
             const int e = tid + q * 256;
             const int r = e / kPerRow, hh = h0 + (e % kPerRow) * 8;
             ra[q] = make_uint4(0u, 0u, 0u, 0u);
-            rw[q] = make_uint4(0u, 0u, 0u, 0u);
             if (row0 + r < a.R && hh < a.H) ra[q] = *reinterpret_cast<const uint4*>(a.hidden + (size_t)(row0 + r) * a.H + hh);
+        }
+#pragma unroll
+        for (int q = 0; q < kPiecesW; ++q) {
+            const int e = tid + q * 256;
+            const int r = e / kPerRow, hh = h0 + (e % kPerRow) * 8;
+            rw[q] = make_uint4(0u, 0u, 0u, 0u);
             if (v0 + r < a.V && hh < a.H) rw[q] = *reinterpret_cast<const uint4*>(a.w + (size_t)(v0 + r) * a.H + hh);
         }
     };
     auto store = [&]() {
 #pragma unroll
-        for (int q = 0; q < kPieces; ++q) {
+        for (int q = 0; q < kPiecesA; ++q) {
             const int e = tid + q * 256;
-            const int r = e / kPerRow, c = (e % kPerRow) * 8;
-            *reinterpret_cast<uint4*>(&sA[r][c]) = ra[q];
-            *reinterpret_cast<uint4*>(&sW[r][c]) = rw[q];
+            *reinterpret_cast<uint4*>(&sA[e / kPerRow][(e % kPerRow) * 8]) = ra[q];
+        }
+#pragma unroll
+        for (int q = 0; q < kPiecesW; ++q) {
+            const int e = tid + q * 256;
+            *reinterpret_cast<uint4*>(&sW[e / kPerRow][(e % kPerRow) * 8]) = rw[q];
         }
     };
     load(0);
@@ -109,17 +119,17 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
 #pragma unroll
         for (int ks = 0; ks < kLmK / 16; ++ks) {
             const int kc = ks * 16 + (lane >> 5) * 8;
-            lm_bf16x8 fa[2], fb[2];
+            lm_bf16x8 fa[2], fb[kLmNI];
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
                 fa[mi] = __builtin_bit_cast(lm_bf16x8, *reinterpret_cast<const uint4*>(&sA[wm * 64 + mi * 32 + (lane & 31)][kc]));
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-                fb[ni] = __builtin_bit_cast(lm_bf16x8, *reinterpret_cast<const uint4*>(&sW[wn * 64 + ni * 32 + (lane & 31)][kc]));
+            for (int ni = 0; ni < kLmNI; ++ni)
+                fb[ni] = __builtin_bit_cast(lm_bf16x8, *reinterpret_cast<const uint4*>(&sW[wn * (kLmN / 2) + ni * 32 + (lane & 31)][kc]));
 #pragma unroll
             for (int mi = 0; mi < 2; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < 2; ++ni)
+                for (int ni = 0; ni < kLmNI; ++ni)
                     acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
         }
         __syncthreads();
@@ -131,13 +141,16 @@ __global__ void __launch_bounds__(256) k_lmhead_argmax(LmArgs a) {
     for (int mi = 0; mi < 2; ++mi) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const int n0 = v0 + wn * 64 + (lane & 31);
+            const int n0 = v0 + wn * (kLmN / 2) + (lane & 31);
             float bv = n0 < a.V ? acc[mi][0][i] : -INFINITY;
             int bi = n0 < a.V ? n0 : INT32_MAX;
-            const int n1 = n0 + 32;
-            if (n1 < a.V && lm_better(acc[mi][1][i], n1, bv, bi)) {
-                bv = acc[mi][1][i];
-                bi = n1;
+#pragma unroll
+            for (int ni = 1; ni < kLmNI; ++ni) {
+                const int n1 = n0 + 32 * ni;
+                if (n1 < a.V && lm_better(acc[mi][ni][i], n1, bv, bi)) {
+                    bv = acc[mi][ni][i];
+                    bi = n1;
+                }
             }
 #pragma unroll
             for (int off = 16; off >= 1; off >>= 1) {

@@ -81,3 +81,15 @@ def test_hidden_greedy_rejects_bad_arguments():
     t = torch.zeros((2, 2), dtype=torch.int32, device="cuda")
     with pytest.raises(binding.SpecVerifyError):
         binding.spec_verify_greedy_hidden(h, w, t)
+
+
+@pytest.mark.parametrize("i", range(30))
+def test_hidden_greedy_random_shapes(i):
+    """Seeded random shapes: vocabulary tails, hidden sizes that are not a
+    multiple of the 64-wide step, row counts that fill no tile."""
+    r = np.random.default_rng(7000 + i)
+    B, K = int(r.integers(1, 9)), int(r.integers(0, 10))
+    V = int(r.choice([1, 2, 31, 255, 256, 257, 513, 3000, 9999]))
+    H = int(r.choice([8, 16, 24, 56, 64, 72, 200, 264, 512]))
+    _print_case(f"hidden greedy random {i}: B={B} K={K} V={V} H={H}")
+    print("near ties", _check(B, K, V, H, seed=7000 + i, agree=float(r.uniform(0.3, 1.0))))

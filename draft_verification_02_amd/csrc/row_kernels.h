@@ -657,21 +657,16 @@ __device__ __forceinline__ float first_threshold(RowShared& S, float tm, int ran
     return tau;
 }
 
-// Fixed-point weight 2^(x c - 8 kref) * 2^fx of a candidate (kref: the row's
-// power-of-two reference, so the weight is at most 2^fx).  The exponent is
-// formed in fp64 and split into whole and fractional parts, so the fp32 exp2
-// of the fraction carries the only rounding (relative error near 2^-23,
-// the same as the streaming terms of Z).
-__device__ __forceinline__ u64 grid_weight(float x, float kref, double c, int fx) {
-    const double y = fmax(fma((double)x, c, -8.0 * (double)kref), -2000.0);
-    const double n = floor(y);
-    const float w = __builtin_amdgcn_exp2f((float)(y - n));  // in [1, 2]
-    // w = m 2^(e - 23) with a 24-bit m; the weight is m shifted into place
-    const uint32_t b = __float_as_uint(w);
-    const u64 m = (u64)((b & 0x7FFFFFu) | 0x800000u);
-    const int sh = (int)n + fx - 23 + (int)(b >> 23) - 127;
-    return sh >= 0 ? m << min(sh, 40) : (sh > -24 ? m >> -sh : 0ull);
+// Weight 2^(x c - 8 kref) of a candidate in fp64 (kref: the row's
+// power-of-two reference, so the weight is at most 1 up to the rounding of
+// kref): the exponent is one fp64 FMA and exp2 is the fp64 routine, so the
+// weight carries about one fp64 rounding.  Its fixed-point form (times 2^fx,
+// truncated) drives the top-k / top-p decisions, whose sums must be exact and
+// independent of order; the fp64 form gives the kept mass.
+__device__ __forceinline__ double cand_weight(float x, float kref, double c) {
+    return exp2(fmax(fma((double)x, c, -8.0 * (double)kref), -2000.0));
 }
+__device__ __forceinline__ u64 fixed_weight(double w, int fx) { return (u64)ldexp(w, fx); }
 
 // Resolve top-k / top-p from the candidates.  Entries (up to kOwn per thread:
 // its wave's candidates lane + 64 i) hold every logit >= the capture threshold.
@@ -696,6 +691,7 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
     const u64* mine = S.cand + (tid >> 6) * kCW + lane;  // this thread's candidates: mine[64 i], i < n_own
     uint32_t key[kOwn];
     u64 wt[kOwn];
+    double ew[kOwn];  // fp64 weights (0 for unused slots)
     int bin[kOwn];
     float xmin = INFINITY;
     // every slot is read (those past n_own hold stale entries of the region
@@ -710,7 +706,8 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         const bool use = i < n_own;
         const float x = use ? __uint_as_float((uint32_t)(ent[i] >> 32)) : M;
         key[i] = use ? fkey(x) : 0u;
-        wt[i] = use ? grid_weight(x, kref, a.c64, a.fx_shift) : 0ull;
+        ew[i] = use ? cand_weight(x, kref, a.c64) : 0.0;
+        wt[i] = fixed_weight(ew[i], a.fx_shift);
         xmin = use ? fminf(xmin, x) : xmin;
     }
     // every candidate is >= tau; a row captured whole has tau = -inf
@@ -875,11 +872,20 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         if (!resolve_bin(bk, 0, 0u, cb_k, true, (u64)a.top_k, S.hc[bk], S.hm[bk], tau_k, in_k_cnt, in_k_mass))
             return false;
     }
+    // The kept mass in fp64 (the fixed-point sums decide membership only):
+    // each thread adds its kept candidates' weights in slot order, then the
+    // block in a fixed order.
+    auto kept_mass = [&](uint32_t tk) {
+        double z = 0.0;
+#pragma unroll
+        for (int i = 0; i < kOwn; ++i) z += (i < n_own && key[i] >= tk) ? ew[i] : 0.0;
+        return rb_sum(z, S.red_d);
+    };
     const u64 zk = a.use_k ? mb_k + in_k_mass : 0ull;
     if (!a.use_p) {
         thr_key = tau_k;
         n_kept = (int)(cb_k + in_k_cnt);
-        z_kept = (double)zk / scale;
+        z_kept = kept_mass(tau_k);
         return true;
     }
     // top-p on the (top-k) kept set: kept <=> excl < ceil(top_p * Z * 2^s)
@@ -900,7 +906,7 @@ __device__ __forceinline__ bool resolve_reservoir(const RowArgs& a, RowShared& S
         return false;
     thr_key = kmin;
     n_kept = (int)(cb_p + kcnt);
-    z_kept = (double)(mb_p + kmass) / scale;
+    z_kept = kept_mass(kmin);
     return true;
 }
 
@@ -1420,11 +1426,17 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
                     have_z = true;
                 }
             }
-            thr = key_to_float(thk);
+            // key 0 (no selection applied) keeps every logit
+            thr = thk == 0u ? -INFINITY : key_to_float(thk);
             n_kept = (int)cnt;
-            // kept mass relative to the row maximum (the whole row when no
-            // selection applied)
-            z_kept = have_z ? (double)zfx / scale * zs : Z;
+            // The kept mass relative to the row maximum in fp64: one more pass
+            // over the row, an fp64 exp for each kept logit (each thread adds
+            // its own in a fixed order, then the block).
+            double zt = 0.0;
+            row_for_each<DT>(rowp, V, [&](int, float x) {
+                if (fkey(x) >= thk) zt += exp(((double)x - (double)M) * a.inv_T);
+            });
+            z_kept = rb_sum(zt, S.red_d);
             if (threadIdx.x == 0 && d_tok >= 0 && d_tok < V)
                 ptok = exp(((double)xd - (double)M) * a.inv_T) / z_kept;
         }

@@ -6,12 +6,14 @@
 //                   k_row, so the residual max(0, p_j - q_j) is evaluated on
 //                   that list (with the draft logits stored beside it).  One
 //                   workgroup per (sequence, possible stop position).
-//  k_draw_sums / k_draw_pick : unfiltered rows.  The residual is spread over
-//                   the whole vocabulary: chunk sums over the stop row pair in
-//                   fp64, then one workgroup per sequence locates the draw.
+//  k_draw : unfiltered rows.  The residual is spread over the whole
+//                   vocabulary: one workgroup per (sequence, chunk) sums the
+//                   stop row pair's fp64 weights, and the last of a
+//                   sequence's chunk workgroups to finish takes the exact
+//                   normalisers and locates the draw.
 //  k_greedy_prefix : greedy prefix match from the per-row argmax.
 //
-// k_draw_sums / k_draw_pick also serve token trees (filtered or not): there a
+// k_draw also serves token trees (filtered or not): there a
 // walk kernel has already fixed each sequence's stop row, the depth of its
 // accepted path and the tokens of the stop node's children (all rejected),
 // which the draw removes from p_j the way a point-mass draft's token is
@@ -35,6 +37,8 @@ struct TreeStop {
     int row, depth, n_ex, pad;
 };
 
+struct DrawChunk;
+
 struct SeqArgs {
     Shape sh;
     double inv_T;
@@ -44,7 +48,8 @@ struct SeqArgs {
     const int* kept_n;
     const float* kept_d;  // draft logit of each listed token (stop positions j < K)
     const double* kept_p; // p of each listed token
-    double2* chunk_sum;   // [B][n_chunks] (.x residual, .y p)
+    DrawChunk* chunks;         // [B][n_chunks] chunk records of the unfiltered draw
+    unsigned* draw_cnt;   // [B] arrival counters of the chunk workgroups (zero between calls)
     int n_chunks;
     int32_t* out_tokens;
     int32_t* out_num;
@@ -83,12 +88,6 @@ __device__ __forceinline__ int stop_of(const SeqArgs& a, int b) {
     if constexpr (kTree) return a.tstop[b].row;
     else return first_rejection(a, b);
 }
-template <bool kTree>
-__device__ __forceinline__ bool stop_is_bonus(const SeqArgs& a, int b, int j) {
-    if constexpr (kTree) return a.tstop[b].n_ex == 0;
-    else return j >= seq_len(a.sh, b);
-}
-
 // The stop row pair of a sequence: target row j, draft row j when j < K_b
 // (or, for point-mass drafts, the drafted token dtok, where q = 1).
 struct StopRow {
@@ -491,8 +490,35 @@ __global__ void __launch_bounds__(kSB) k_seq_filtered(SeqArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Unfiltered: chunk sums, then the pick.
+// Unfiltered rows and token trees: the draw over the whole stop row pair.
+//
+// p_j = e_t / Z_t and q_j = e_d / Z_d with e = exp((x - M) / T) in fp64 and
+// Z the fp64 sum of the kept e over the row, so the residual scaled by Z_t is
+// max(0, e_t - rho e_d), rho = Z_t / Z_d: the draw depends on rho alone.  The
+// exact rho is known only once every chunk of the row pair is summed; the
+// row records give an estimate rho~ (fp32 streamed sums, relative error far
+// below kDelta / 2).  Each chunk workgroup sums e_t and e_d over its tokens
+// and, over the tokens whose residual has the same sign for every rho within
+// kDelta / 2 of rho~, the e_t and e_d of the positive ones (their residual
+// mass is then a - rho b for any such rho); the few other tokens are listed
+// with their weights.  The last chunk workgroup of a sequence to finish takes
+// the exact rho, the residual mass of every chunk, the chunk holding the draw
+// point and the token inside it.  If rho lies outside the band, or a chunk
+// holds more unsettled tokens than it lists, every chunk is recomputed with
+// the exact rho (slow, exact).  Point-mass drafts, token trees and the bonus
+// row have no draft row: their residual is e_t without the removed tokens.
 // ---------------------------------------------------------------------------
+constexpr double kDelta = 0x1p-14;
+constexpr int kAmb = 8;
+
+struct DrawChunk {
+    double zt, zd;              // sums of e_t and e_d over the chunk
+    double a, b;                // sums of e_t and e_d over its settled positive tokens
+    double at[kAmb], ad[kAmb];  // e_t and e_d of the unsettled tokens, in token order
+    int n_amb;                  // unsettled tokens (more than kAmb: not all listed)
+    int pad;
+};
+
 // The kCPT logits of row `row` from token lo on (-inf past V): the loads of
 // a thread are issued together and decoded after.
 template <int DT>
@@ -509,29 +535,31 @@ __device__ __forceinline__ void load_run(const char* row, int lo, int V, float (
         x[e] = lo + e < V ? __uint_as_float(DT == DT_F32 ? raw[e] : raw[e] << 16) : -INFINITY;
 }
 
-// p_j and the residual max(0, p_j - q_j) of the kCPT tokens from lo on, in
-// fp64 (the same arithmetic wherever a chunk is summed or searched).
+// fp64 weights of the kCPT tokens from lo on: e_t (0 where the target row
+// does not keep the token), e_d (0 without a draft row or where it does not
+// keep it) and the bit mask of removed tokens (a point-mass draft's token, a
+// token tree's rejected children).  The same arithmetic wherever a chunk is
+// summed or searched.
 template <int TDT, int DDT>
-__device__ __forceinline__ void run_terms(const StopRow& s, double inv_T, int lo, int V, double (&p)[kCPT],
-                                          double (&r)[kCPT]) {
+__device__ __forceinline__ void run_weights(const StopRow& s, double inv_T, int lo, int V, double (&et)[kCPT],
+                                            double (&ed)[kCPT], uint32_t& rm) {
     float xt[kCPT], xd[kCPT];
     load_run<TDT>(s.tp, lo, V, xt);
     // without a draft row the target row is read again and ignored
     load_run<DDT>(s.has_draft ? s.dp : s.tp, lo, V, xd);
-    const double inv_zt = 1.0 / s.zt, inv_zd = 1.0 / s.zd;
-    // removed tokens of a tree's stop row inside [lo, lo + kCPT)
-    uint32_t exm = 0u;
+    rm = 0u;
     for (int e = 0; e < s.n_ex; ++e) {
         const uint32_t d = (uint32_t)(s.ex[e] - lo);
-        if (d < (uint32_t)kCPT) exm |= 1u << d;
+        if (d < (uint32_t)kCPT) rm |= 1u << d;
+    }
+    {
+        const uint32_t d = (uint32_t)(s.dtok - lo);
+        if (s.dtok >= 0 && d < (uint32_t)kCPT) rm |= 1u << d;
     }
 #pragma unroll
     for (int e = 0; e < kCPT; ++e) {
-        p[e] = xt[e] >= s.thr_t ? exp(((double)xt[e] - (double)s.Mt) * inv_T) * inv_zt : 0.0;
-        const double q = (s.has_draft && xd[e] >= s.thr_d) ? exp(((double)xd[e] - (double)s.Md) * inv_T) * inv_zd
-                                                           : ((lo + e == s.dtok || ((exm >> e) & 1u)) ? 1.0 : 0.0);
-        const double d = p[e] - q;
-        r[e] = d > 0.0 ? d : 0.0;
+        et[e] = xt[e] >= s.thr_t ? exp(((double)xt[e] - (double)s.Mt) * inv_T) : 0.0;
+        ed[e] = (s.has_draft && xd[e] >= s.thr_d) ? exp(((double)xd[e] - (double)s.Md) * inv_T) : 0.0;
     }
 }
 
@@ -549,98 +577,220 @@ __device__ __forceinline__ void with_dtypes(const StopRow& s, F&& f) {
     }
 }
 
-// Chunk sums of the stop row pair: one workgroup per (sequence, chunk).
-// (Four chunks per workgroup, one round of workgroups for large batches, was
-// slower: each workgroup's chain of loads, scans and barriers grew.)
-template <bool kTree>
-__global__ void __launch_bounds__(kSB) k_draw_sums(SeqArgs a) {
-    __shared__ double s_wa[kSB / 64], s_wb[kSB / 64];
-    __shared__ int s_j;
-    const int b = blockIdx.x / a.n_chunks;
-    const int c = blockIdx.x % a.n_chunks;
-    if (threadIdx.x < 64) {
-        const int j = stop_of<kTree>(a, b);
-        if (threadIdx.x == 0) s_j = j;
+// Residual weight of one token, scaled by Z_t: max(0, e_t - rho e_d) with a
+// draft row, else e_t unless the token is removed (where q = 1 >= p).
+__device__ __forceinline__ double res_weight(bool has_draft, double et, double ed, bool removed, double rho) {
+    if (has_draft) {
+        const double d = et - rho * ed;
+        return d > 0.0 ? d : 0.0;
     }
-    __syncthreads();
-    const StopRow s = stop_row<kTree>(a, b, s_j);
-    with_dtypes(s, [&](auto tt, auto dt) {
-        double p[kCPT], r[kCPT];
-        run_terms<decltype(tt)::value, decltype(dt)::value>(s, a.inv_T, c * kChunk + threadIdx.x * kCPT, a.sh.V, p,
-                                                             r);
-        double sr = 0.0, sp = 0.0;
-#pragma unroll
-        for (int e = 0; e < kCPT; ++e) {
-            sr += r[e];
-            sp += p[e];
-        }
-        double er, ep, tr, tp;
-        seq_excl_scan2(sr, sp, s_wa, s_wb, er, ep, tr, tp);
-        if (threadIdx.x == 0) a.chunk_sum[(size_t)b * a.n_chunks + c] = make_double2(tr, tp);
-    });
+    return removed ? 0.0 : et;
 }
 
-// One workgroup per sequence: the chunk holding the draw point (chunk sums
-// in chunk order, thread t holding chunks t, t + kSB, ...), then the token
-// inside it from the same per-thread terms.
-template <bool kTree>
-__global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
-    __shared__ double s_wa[kSB / 64], s_wb[kSB / 64], s_run;
-    __shared__ int s_j, s_cstar;
-    __shared__ int s_last[kSB / 64], s_first[kSB / 64];
-    const int b = blockIdx.x;
-    const int K = a.sh.K, V = a.sh.V;
-    if (threadIdx.x < 64) {
-        const int j = stop_of<kTree>(a, b);
-        if (threadIdx.x == 0) {
-            s_j = j;
-            s_cstar = 0;  // stays if no chunk holds mass
-            s_run = 0.0;
-        }
-    }
-    const double2* cs = a.chunk_sum + (size_t)b * a.n_chunks;
-    // this thread's chunks are contiguous: [c0, c1)
-    const int per = (a.n_chunks + kSB - 1) / kSB;
-    const int c0 = min((int)threadIdx.x * per, a.n_chunks), c1 = min(c0 + per, a.n_chunks);
-    double mr = 0.0, mp = 0.0;
-    for (int cc = c0; cc < c1; ++cc) {
-        const double2 v = cs[cc];
-        mr += v.x;
-        mp += v.y;
-    }
-    double er, ep, tr, tp;
-    seq_excl_scan2(mr, mp, s_wa, s_wb, er, ep, tr, tp);  // (its barrier also publishes s_j)
-    const int j = s_j;
-    const bool usep = stop_is_bonus<kTree>(a, b, j) || !(tr > 0.0);
-    const double S = usep ? tp : tr;
-    const double t = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE)) * S;
+// Totals of N doubles over the kSB threads (wave butterflies, then the waves
+// in order): the same values in every thread.  s[n][w] is scratch; the
+// leading barrier lets a previous call's readers finish.
+template <int N>
+__device__ __forceinline__ void seq_totals(double (&v)[N], double (*s)[kSB / 64]) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    // the thread whose chunk range holds t (the last with mass starting at or
-    // before t; else the first with mass), then the chunk inside its range
-    auto locate = [&](double mine, double ex) {
-        const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
-        const unsigned long long mf = __ballot(mine > 0.0);
-        __syncthreads();
-        if (lane == 0) {
-            s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
-            s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
-        }
-        __syncthreads();
-        int tau = -1, first = kSB;
 #pragma unroll
-        for (int w = 0; w < kSB / 64; ++w) {
-            tau = max(tau, s_last[w]);
-            first = min(first, s_first[w]);
-        }
-        return tau >= 0 ? tau : first;
-    };
-    const int tc = locate(usep ? mp : mr, usep ? ep : er);
-    if ((int)threadIdx.x == tc) {
-        double run = usep ? ep : er;
-        int cstar = -1, last_nz = c0;
-        double run_last = run;
+    for (int n = 0; n < N; ++n) v[n] = wave_sum(v[n]);
+    __syncthreads();
+    if (lane == 0)
+#pragma unroll
+        for (int n = 0; n < N; ++n) s[n][wave] = v[n];
+    __syncthreads();
+    static_assert(kSB / 64 == 4, "four waves");
+#pragma unroll
+    for (int n = 0; n < N; ++n) v[n] = (s[n][0] + s[n][1]) + (s[n][2] + s[n][3]);
+}
+
+// Exclusive prefix of one int per thread in thread order, and the total.
+__device__ __forceinline__ int seq_excl_scan_int(int v, int* s, int& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int incl = wave_incl_scan(v);
+    __syncthreads();
+    if (lane == 63) s[wave] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int w = 0; w < kSB / 64; ++w) {
+        before += w < wave ? s[w] : 0;
+        total += s[w];
+    }
+    return before + incl - v;
+}
+
+// Loads of another workgroup's chunk records (written with agent-scope
+// stores before its arrival was counted): agent-scope, so coherent across the
+// GPU's L2 caches.
+__device__ __forceinline__ double ld_agent(const double* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ int ld_agent(const int* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(double* p, double v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_agent(int* p, int v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Waits until this thread's earlier stores are complete (vmcnt 0; the other
+// counters left alone).
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Residual mass of one chunk from its record for an exact rho inside the band
+// (every listed unsettled token is evaluated; the caller has checked that
+// none is missing).
+__device__ __forceinline__ double chunk_res(const DrawChunk* c, bool has_draft, double rho) {
+    const double a = ld_agent(&c->a);
+    if (!has_draft) return a;
+    double r = a - rho * ld_agent(&c->b);
+    r = r > 0.0 ? r : 0.0;
+    const int n = min(ld_agent(&c->n_amb), kAmb);
+    for (int k = 0; k < n; ++k) r += res_weight(true, ld_agent(&c->at[k]), ld_agent(&c->ad[k]), false, rho);
+    return r;
+}
+
+struct DrawShared {
+    double tot[4][kSB / 64];
+    double run;
+    int j, cstar, last, tau;
+    int s_last[kSB / 64], s_first[kSB / 64];
+    int scan[kSB / 64];
+};
+
+// The thread whose mass range holds t: the last one with mass starting at or
+// before t; if rounding put t before all of them, the first one with mass.
+__device__ __forceinline__ int locate_thread(double mine, double ex, double t, DrawShared& S) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const unsigned long long mc = __ballot(mine > 0.0 && ex <= t);
+    const unsigned long long mf = __ballot(mine > 0.0);
+    __syncthreads();
+    if (lane == 0) {
+        S.s_last[wave] = mc ? wave * 64 + 63 - __clzll((long long)mc) : -1;
+        S.s_first[wave] = mf ? wave * 64 + __ffsll((long long)mf) - 1 : kSB;
+    }
+    __syncthreads();
+    int tau = -1, first = kSB;
+#pragma unroll
+    for (int w = 0; w < kSB / 64; ++w) {
+        tau = max(tau, S.s_last[w]);
+        first = min(first, S.s_first[w]);
+    }
+    return tau >= 0 ? tau : first;
+}
+
+// Exclusive prefix (thread order) of one double per thread, and the total.
+__device__ __forceinline__ double seq_excl_scan_d(double v, DrawShared& S, double& total) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const double incl = wave_incl_scan(v);
+    const double ex = wave_shift_up1(incl);
+    __syncthreads();
+    if (lane == 63) S.tot[0][wave] = incl;
+    __syncthreads();
+    double before = 0.0;
+    total = 0.0;
+#pragma unroll
+    for (int w = 0; w < kSB / 64; ++w) {
+        before += w < wave ? S.tot[0][w] : 0.0;
+        total += S.tot[0][w];
+    }
+    return before + ex;
+}
+
+// Mass of chunk cc (residual with the exact rho, or p) recomputed by the
+// whole workgroup.
+template <int TDT, int DDT>
+__device__ __forceinline__ double chunk_mass_recomputed(const StopRow& s, double inv_T, int V, int cc, bool usep,
+                                                        double rho, DrawShared& S) {
+    double et[kCPT], ed[kCPT];
+    uint32_t rm;
+    run_weights<TDT, DDT>(s, inv_T, cc * kChunk + (int)threadIdx.x * kCPT, V, et, ed, rm);
+    double m[1] = {0.0};
+#pragma unroll
+    for (int e = 0; e < kCPT; ++e) m[0] += usep ? et[e] : res_weight(s.has_draft, et[e], ed[e], (rm >> e) & 1u, rho);
+    seq_totals<1>(m, S.tot);
+    return m[0];
+}
+
+// The pick, by the last chunk workgroup of sequence b (stop position j).
+template <bool kTree, int TDT, int DDT>
+__device__ __forceinline__ void draw_pick(const SeqArgs& a, int b, int j, const StopRow& s, double rt, DrawShared& S) {
+    const int n_ch = a.n_chunks, V = a.sh.V;
+    const DrawChunk* cs = a.chunks + (size_t)b * n_ch;
+    // this thread's chunks are contiguous: [c0, c1)
+    const int per = (n_ch + kSB - 1) / kSB;
+    const int c0 = min((int)threadIdx.x * per, n_ch), c1 = min(c0 + per, n_ch);
+    double v[3] = {0.0, 0.0, 0.0};  // sum e_t, sum e_d, unlisted unsettled tokens
+    for (int cc = c0; cc < c1; ++cc) {
+        v[0] += ld_agent(&cs[cc].zt);
+        v[1] += ld_agent(&cs[cc].zd);
+        v[2] += ld_agent(&cs[cc].n_amb) > kAmb ? 1.0 : 0.0;
+    }
+    seq_totals<3>(v, S.tot);
+    const double Zt = v[0];
+    const double rho = s.has_draft ? Zt / v[1] : 0.0;
+    const bool settled = !s.has_draft || (v[2] == 0.0 && fabs(rho - rt) <= 0.5 * kDelta * rt);
+    const double u = uniform53(draw_block(a.seed, (uint32_t)b, (uint32_t)j, PURPOSE_SAMPLE));
+    bool usep;
+    double t;
+    int cstar;
+    double run;
+    if (settled) {
+        // residual mass of this thread's chunks, then the chunk holding t
+        double mr = 0.0, mp = 0.0;
         for (int cc = c0; cc < c1; ++cc) {
-            const double sc = usep ? cs[cc].y : cs[cc].x;
+            mr += chunk_res(&cs[cc], s.has_draft, rho);
+            mp += ld_agent(&cs[cc].zt);
+        }
+        double tr, tp;
+        const double er = seq_excl_scan_d(mr, S, tr);
+        const double ep = seq_excl_scan_d(mp, S, tp);
+        usep = s.bonus || !(tr > 0.0);
+        t = u * (usep ? tp : tr);
+        const int tc = locate_thread(usep ? mp : mr, usep ? ep : er, t, S);
+        if ((int)threadIdx.x == tc) {
+            double r = usep ? ep : er;
+            int cs_ = -1, last_nz = c0;
+            double run_last = r;
+            for (int cc = c0; cc < c1; ++cc) {
+                const double sc = usep ? ld_agent(&cs[cc].zt) : chunk_res(&cs[cc], s.has_draft, rho);
+                if (sc > 0.0) {
+                    if (r + sc > t) {
+                        cs_ = cc;
+                        break;
+                    }
+                    last_nz = cc;
+                    run_last = r;
+                }
+                r += sc;
+            }
+            if (cs_ < 0) {
+                cs_ = last_nz;
+                r = run_last;
+            }
+            S.cstar = cs_;
+            S.run = r;
+        }
+        __syncthreads();
+        cstar = S.cstar;
+        run = S.run;
+    } else {
+        // every chunk recomputed with the exact rho, in chunk order: the
+        // total, then the first chunk whose running sum passes t
+        double tr = 0.0;
+        for (int cc = 0; cc < n_ch; ++cc) tr += chunk_mass_recomputed<TDT, DDT>(s, a.inv_T, V, cc, false, rho, S);
+        usep = s.bonus || !(tr > 0.0);
+        t = u * (usep ? Zt : tr);
+        run = 0.0;
+        cstar = -1;
+        int last_nz = 0;
+        double run_last = 0.0;
+        for (int cc = 0; cc < n_ch; ++cc) {
+            const double sc = chunk_mass_recomputed<TDT, DDT>(s, a.inv_T, V, cc, usep, rho, S);
             if (sc > 0.0) {
                 if (run + sc > t) {
                     cstar = cc;
@@ -655,43 +805,112 @@ __global__ void __launch_bounds__(kSB) k_draw_pick(SeqArgs a) {
             cstar = last_nz;
             run = run_last;
         }
-        s_cstar = cstar;
-        s_run = run;
     }
-    __syncthreads();
-    const int cstar = s_cstar;
-    const double run = s_run;
-    const StopRow s = stop_row<kTree>(a, b, j);
-    const int lo = cstar * kChunk + threadIdx.x * kCPT;
-    with_dtypes(s, [&](auto tt, auto dt) {
-        double p[kCPT], r[kCPT];
-        run_terms<decltype(tt)::value, decltype(dt)::value>(s, a.inv_T, lo, V, p, r);
-        double sr = 0.0, sp = 0.0;
+    // the token inside chunk cstar, from the same per-token weights
+    const int lo = cstar * kChunk + (int)threadIdx.x * kCPT;
+    double et[kCPT], ed[kCPT], w[kCPT];
+    uint32_t rm;
+    run_weights<TDT, DDT>(s, a.inv_T, lo, V, et, ed, rm);
+    double mine = 0.0;
+#pragma unroll
+    for (int e = 0; e < kCPT; ++e) {
+        w[e] = usep ? et[e] : res_weight(s.has_draft, et[e], ed[e], (rm >> e) & 1u, rho);
+        mine += w[e];
+    }
+    double tot;
+    const double ex = run + seq_excl_scan_d(mine, S, tot);
+    const int tau = locate_thread(mine, ex, t, S);
+    if ((int)threadIdx.x == tau) {
+        double acc = ex;
+        int y = -1, last = -1;
 #pragma unroll
         for (int e = 0; e < kCPT; ++e) {
-            sr += r[e];
-            sp += p[e];
+            if (y < 0 && w[e] > 0.0) {
+                last = lo + e;
+                acc += w[e];
+                if (acc > t) y = lo + e;
+            }
         }
-        double er2, ep2, tr2, tp2;
-        seq_excl_scan2(sr, sp, s_wa, s_wb, er2, ep2, tr2, tp2);
-        const double mine = usep ? sp : sr;
-        const double ex = run + (usep ? ep2 : er2);
-        const int tau = locate(mine, ex);
-        if ((int)threadIdx.x == tau) {
-            double acc = ex;
-            int y = -1, last = -1;
+        write_outputs<kTree>(a, b, j, y >= 0 ? y : last);
+    }
+}
+
+// One workgroup per (sequence, chunk of kChunk tokens): the chunk record of
+// the stop row pair, then, in the last of the sequence's chunk workgroups to
+// finish, the pick.  The arrival counter of each sequence is zero between
+// calls (zeroed with the workspace, reset by the last workgroup).
+template <bool kTree>
+__global__ void __launch_bounds__(kSB) k_draw(SeqArgs a) {
+    __shared__ DrawShared S;
+    const int b = blockIdx.x / a.n_chunks;
+    const int c = blockIdx.x % a.n_chunks;
+    if (threadIdx.x < 64) {
+        const int j = stop_of<kTree>(a, b);
+        if (threadIdx.x == 0) S.j = j;
+    }
+    __syncthreads();
+    const int j = S.j;
+    const StopRow s = stop_row<kTree>(a, b, j);
+    // rho~ from the row records
+    const double rt = s.has_draft ? s.zt / s.zd : 0.0;
+    DrawChunk* rec = a.chunks + (size_t)b * a.n_chunks + c;
+    with_dtypes(s, [&](auto tt, auto dt) {
+        constexpr int TDT = decltype(tt)::value, DDT = decltype(dt)::value;
+        double et[kCPT], ed[kCPT];
+        uint32_t rm;
+        run_weights<TDT, DDT>(s, a.inv_T, c * kChunk + (int)threadIdx.x * kCPT, a.sh.V, et, ed, rm);
+        double v[4] = {0.0, 0.0, 0.0, 0.0};  // zt, zd, a, b
+        int amb = 0;                          // this thread's unsettled tokens (bit mask)
 #pragma unroll
-            for (int e = 0; e < kCPT; ++e) {
-                const double w = usep ? p[e] : r[e];
-                if (y < 0 && w > 0.0) {
-                    last = lo + e;
-                    acc += w;
-                    if (acc > t) y = lo + e;
+        for (int e = 0; e < kCPT; ++e) {
+            v[0] += et[e];
+            v[1] += ed[e];
+            if (!s.has_draft) {
+                v[2] += ((rm >> e) & 1u) ? 0.0 : et[e];
+            } else if (ed[e] == 0.0) {
+                v[2] += et[e];
+            } else {
+                const double d = et[e] - rt * ed[e], tol = kDelta * rt * ed[e];
+                if (d > tol) {
+                    v[2] += et[e];
+                    v[3] += ed[e];
+                } else if (d >= -tol) {
+                    amb |= 1 << e;
                 }
             }
-            write_outputs<kTree>(a, b, j, y >= 0 ? y : last);
+        }
+        int n_amb;
+        int slot = seq_excl_scan_int(__popc(amb), S.scan, n_amb);
+#pragma unroll
+        for (int e = 0; e < kCPT; ++e) {
+            if ((amb >> e) & 1) {
+                if (slot < kAmb) {
+                    st_agent(&rec->at[slot], et[e]);
+                    st_agent(&rec->ad[slot], ed[e]);
+                }
+                ++slot;
+            }
+        }
+        seq_totals<4>(v, S.tot);
+        if (threadIdx.x == 0) {
+            st_agent(&rec->zt, v[0]);
+            st_agent(&rec->zd, v[1]);
+            st_agent(&rec->a, v[2]);
+            st_agent(&rec->b, v[3]);
+            st_agent(&rec->n_amb, n_amb);
         }
     });
+    wait_stores();
+    __syncthreads();
+    if (threadIdx.x == 0)
+        S.last = __hip_atomic_fetch_add(&a.draw_cnt[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (unsigned)(a.n_chunks - 1);
+    __syncthreads();
+    if (!S.last) return;
+    with_dtypes(s, [&](auto tt, auto dt) {
+        draw_pick<kTree, decltype(tt)::value, decltype(dt)::value>(a, b, j, s, rt, S);
+    });
+    if (threadIdx.x == 0) a.draw_cnt[b] = 0u;
 }
 
 // ---------------------------------------------------------------------------

@@ -20,19 +20,34 @@ using namespace sv;
 
 // Library-owned scratch for one (device, stream): row records, kept lists of
 // filtered target rows (with p and the draft logit of each listed token), greedy
-// argmax indices, draw chunk sums and the stops of token-tree walks.  Every
-// kernel writes what it later reads within the same call, so nothing needs
-// clearing between calls.
+// argmax indices, chunk records and arrival counters of the unfiltered draw,
+// and the stops of token-tree walks.  Every kernel writes what it later reads
+// within the same call; the arrival counters are zeroed when the workspace is
+// allocated and left at zero by the kernel that counts with them.
+struct Caps {
+    size_t rows = 0;         // row records (and split-row partials)
+    size_t lists = 0;        // target rows with stored kept lists
+    size_t gidx = 0;         // greedy argmax indices
+    size_t chunk_bytes = 0;  // chunk records of the unfiltered draw, or the LM-head tile pairs
+    size_t seqs = 0;         // sequences: arrival counters and token-tree stops
+    size_t nodes = 0;        // token-tree child tokens
+    bool covers(const Caps& o) const {
+        return o.rows <= rows && o.lists <= lists && o.gidx <= gidx && o.chunk_bytes <= chunk_bytes &&
+               o.seqs <= seqs && o.nodes <= nodes;
+    }
+};
+
 struct Workspace {
     void* base = nullptr;
-    size_t cap_rows = 0, cap_trows = 0, cap_chunks = 0, cap_seqs = 0, cap_nodes = 0;
+    Caps cap;
     RowRec* rec = nullptr;
     uint2* kept = nullptr;
     int* kept_n = nullptr;
     float* kept_d = nullptr;
     double* kept_p = nullptr;
     int32_t* gidx = nullptr;
-    double2* chunk_sum = nullptr;
+    void* chunks = nullptr;
+    unsigned* draw_cnt = nullptr;
     PartRec* prec = nullptr;
     TreeStop* tstop = nullptr;
     int32_t* tex = nullptr;
@@ -46,34 +61,35 @@ void* g_ev_after = nullptr;
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
-int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, Workspace** out,
-                  size_t seqs = 0, size_t nodes = 0) {
+int get_workspace(hipStream_t stream, const Caps& need, Workspace** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_LAUNCH;
     std::lock_guard<std::mutex> lock(g_mu);
     Workspace& w = g_ws[{dev, stream}];
-    if (w.base && rows <= w.cap_rows && trows <= w.cap_trows && chunks <= w.cap_chunks && seqs <= w.cap_seqs &&
-        nodes <= w.cap_nodes) {
+    if (w.base && w.cap.covers(need)) {
         *out = &w;
         return SPEC_OK;
     }
     Workspace nw;
-    nw.cap_rows = std::max(rows, w.cap_rows);
-    nw.cap_trows = std::max(trows, w.cap_trows);
-    nw.cap_chunks = std::max(chunks, w.cap_chunks);
-    nw.cap_seqs = std::max(seqs, w.cap_seqs);
-    nw.cap_nodes = std::max(nodes, w.cap_nodes);
+    nw.cap.rows = std::max(need.rows, w.cap.rows);
+    nw.cap.lists = std::max(need.lists, w.cap.lists);
+    nw.cap.gidx = std::max(need.gidx, w.cap.gidx);
+    nw.cap.chunk_bytes = std::max(need.chunk_bytes, w.cap.chunk_bytes);
+    nw.cap.seqs = std::max(need.seqs, w.cap.seqs);
+    nw.cap.nodes = std::max(need.nodes, w.cap.nodes);
+    const Caps& c = nw.cap;
     size_t off = 0;
-    const size_t o_rec = off; off = align_up(off + nw.cap_rows * sizeof(RowRec));
-    const size_t o_kept = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(uint2));
-    const size_t o_kn = off; off = align_up(off + nw.cap_trows * sizeof(int));
-    const size_t o_kd = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(float));
-    const size_t o_kp = off; off = align_up(off + nw.cap_trows * (size_t)kListMax * sizeof(double));
-    const size_t o_g = off; off = align_up(off + nw.cap_trows * sizeof(int32_t));
-    const size_t o_cs = off; off = align_up(off + nw.cap_chunks * sizeof(double2));
-    const size_t o_pr = off; off = align_up(off + nw.cap_rows * (size_t)kMaxParts * sizeof(PartRec));
-    const size_t o_ts = off; off = align_up(off + nw.cap_seqs * sizeof(TreeStop));
-    const size_t o_tx = off; off = align_up(off + nw.cap_nodes * sizeof(int32_t));
+    const size_t o_rec = off; off = align_up(off + c.rows * sizeof(RowRec));
+    const size_t o_kept = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(uint2));
+    const size_t o_kn = off; off = align_up(off + c.lists * sizeof(int));
+    const size_t o_kd = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(float));
+    const size_t o_kp = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(double));
+    const size_t o_g = off; off = align_up(off + c.gidx * sizeof(int32_t));
+    const size_t o_cs = off; off = align_up(off + c.chunk_bytes);
+    const size_t o_cnt = off; off = align_up(off + c.seqs * sizeof(unsigned));
+    const size_t o_pr = off; off = align_up(off + c.rows * (size_t)kMaxParts * sizeof(PartRec));
+    const size_t o_ts = off; off = align_up(off + c.seqs * sizeof(TreeStop));
+    const size_t o_tx = off; off = align_up(off + c.nodes * sizeof(int32_t));
     if (w.base) {
         // the old buffer may still be in use by work queued on this stream
         if (hipStreamSynchronize(stream) != hipSuccess) return SPEC_E_LAUNCH;
@@ -85,13 +101,19 @@ int get_workspace(hipStream_t stream, size_t rows, size_t trows, size_t chunks, 
         return SPEC_E_LAUNCH;
     if (hipMalloc(&nw.base, std::max<size_t>(off, 256)) != hipSuccess) return SPEC_E_NOMEM;
     char* b = static_cast<char*>(nw.base);
+    // the arrival counters start at zero (a synchronous fill, once per allocation)
+    if (c.seqs && hipMemset(b + o_cnt, 0, c.seqs * sizeof(unsigned)) != hipSuccess) {
+        (void)hipFree(nw.base);
+        return SPEC_E_LAUNCH;
+    }
     nw.rec = reinterpret_cast<RowRec*>(b + o_rec);
     nw.kept = reinterpret_cast<uint2*>(b + o_kept);
     nw.kept_n = reinterpret_cast<int*>(b + o_kn);
     nw.kept_d = reinterpret_cast<float*>(b + o_kd);
     nw.kept_p = reinterpret_cast<double*>(b + o_kp);
     nw.gidx = reinterpret_cast<int32_t*>(b + o_g);
-    nw.chunk_sum = reinterpret_cast<double2*>(b + o_cs);
+    nw.chunks = b + o_cs;
+    nw.draw_cnt = reinterpret_cast<unsigned*>(b + o_cnt);
     nw.prec = reinterpret_cast<PartRec*>(b + o_pr);
     nw.tstop = reinterpret_cast<TreeStop*>(b + o_ts);
     nw.tex = reinterpret_cast<int32_t*>(b + o_tx);
@@ -113,7 +135,8 @@ int check_sizes(int B, int K, int V) {
     const long long rows = (long long)B * (2LL * K + 1);
     if (rows >= (1LL << 31)) return SPEC_E_INVALID;
     if (rows * (long long)V >= (1LL << 40)) return SPEC_E_INVALID;
-    if ((long long)V >= (1LL << 30)) return SPEC_E_INVALID;
+    // a row's byte size (V * 4 for f32 logits) fits the 32-bit size of a raw buffer
+    if ((long long)V >= (1LL << 29)) return SPEC_E_INVALID;
     if ((long long)B * ceil_div(V, kChunk) >= (1LL << 31)) return SPEC_E_INVALID;
     return SPEC_OK;
 }
@@ -138,7 +161,9 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     if (!target || !out_tokens || !out_num || (K > 0 && !tokens)) return SPEC_E_INVALID;
     const int n_trows = B * (K + 1);
     Workspace* ws;
-    rc = get_workspace(stream, 0, n_trows, 0, &ws);
+    Caps need;
+    need.gidx = n_trows;
+    rc = get_workspace(stream, need, &ws);
     if (rc) return rc;
     const Shape sh{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0, n_trows, 0, lens,
                    tested, accepted};
@@ -164,7 +189,9 @@ int run_tree_greedy(const void* target, const int32_t* tokens, const int32_t* pa
     if (!target || !out_tokens || !out_num || (N > 0 && (!tokens || !parents))) return SPEC_E_INVALID;
     const int n_trows = B * (N + 1);
     Workspace* ws;
-    rc = get_workspace(stream, 0, n_trows, 0, &ws);
+    Caps need;
+    need.gidx = n_trows;
+    rc = get_workspace(stream, need, &ws);
     if (rc) return rc;
     const Shape sh{static_cast<const char*>(target), nullptr, nullptr, B, N, V, tdt, 0, tsz, 0, n_trows, 0,
                    nullptr, nullptr, nullptr};
@@ -222,8 +249,13 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     // drafted sequences with filters draw from kept lists; unfiltered rows
     // and trees draw with chunk sums
     const bool lists = filtered && !tree;
-    rc = get_workspace(stream, rows, lists ? n_trows : 0, lists ? 0 : (size_t)B * n_chunks, &ws,
-                       tree ? (size_t)B : 0, tree ? (size_t)B * K : 0);
+    Caps need;
+    need.rows = rows;
+    need.lists = lists ? n_trows : 0;
+    need.chunk_bytes = lists ? 0 : (size_t)B * n_chunks * sizeof(DrawChunk);
+    need.seqs = B;
+    need.nodes = tree ? (size_t)B * K : 0;
+    rc = get_workspace(stream, need, &ws);
     if (rc) return rc;
 
     const Shape sh{static_cast<const char*>(target), static_cast<const char*>(draft), tree ? nullptr : tokens,
@@ -289,7 +321,8 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     sa.kept_n = ws->kept_n;
     sa.kept_d = ws->kept_d;
     sa.kept_p = ws->kept_p;
-    sa.chunk_sum = ws->chunk_sum;
+    sa.chunks = static_cast<DrawChunk*>(ws->chunks);
+    sa.draw_cnt = ws->draw_cnt;
     sa.n_chunks = n_chunks;
     sa.out_tokens = out_tokens;
     sa.out_num = out_num;
@@ -320,16 +353,11 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
                            sa);
         if ((rc = launch_status())) return rc;
     } else {
-        const dim3 g_sums((unsigned)((long long)B * n_chunks));
+        const dim3 g_draw((unsigned)((long long)B * n_chunks));
         if (tree)
-            hipLaunchKernelGGL(k_draw_sums<true>, g_sums, dim3(kSB), 0, stream, sa);
+            hipLaunchKernelGGL(k_draw<true>, g_draw, dim3(kSB), 0, stream, sa);
         else
-            hipLaunchKernelGGL(k_draw_sums<false>, g_sums, dim3(kSB), 0, stream, sa);
-        if ((rc = launch_status())) return rc;
-        if (tree)
-            hipLaunchKernelGGL(k_draw_pick<true>, dim3(B), dim3(kSB), 0, stream, sa);
-        else
-            hipLaunchKernelGGL(k_draw_pick<false>, dim3(B), dim3(kSB), 0, stream, sa);
+            hipLaunchKernelGGL(k_draw<false>, g_draw, dim3(kSB), 0, stream, sa);
         if ((rc = launch_status())) return rc;
     }
     if (tstats || dstats) {
@@ -425,8 +453,10 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     if (((uintptr_t)hidden | (uintptr_t)w_unembed) & 15u) return SPEC_E_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
     Workspace* ws;
-    // the tile pairs (8 bytes each) live in the chunk-sum area (16-byte units)
-    int rc = get_workspace(st, 0, (size_t)R, (size_t)ceil_div(R * n_vt, 2), &ws);
+    Caps need;
+    need.gidx = (size_t)R;
+    need.chunk_bytes = (size_t)(R * n_vt) * sizeof(LmPart);
+    int rc = get_workspace(st, need, &ws);
     if (rc) return rc;
     LmArgs la;
     la.hidden = static_cast<const uint16_t*>(hidden);
@@ -436,7 +466,7 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     la.H = H;
     la.n_vt = (int)n_vt;
     la.n_rt = (int)ceil_div(R, kLmM);
-    la.part = reinterpret_cast<LmPart*>(ws->chunk_sum);
+    la.part = static_cast<LmPart*>(ws->chunks);
     la.gidx = ws->gidx;
     void *evb, *eva;
     take_events(&evb, &eva);

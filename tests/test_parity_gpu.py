@@ -69,10 +69,10 @@ def test_c2_many_seeds_small_vocab():
     print(rep)
 
 
-def test_c3_concurrent_batch_full_size_sampled():
-    _print_case("c3 full, 6 sequences checked")
+def test_c3_concurrent_batch_full_size_all_sequences():
+    _print_case("c3 full, all 32 sequences checked")
     w = wl.config(3)
-    print(check_sampling(w, seqs=[0, 5, 11, 17, 26, 31]))
+    print(check_sampling(w))
 
 
 def test_c3_generator_small_batch_all_sequences():
@@ -89,9 +89,9 @@ def test_c4_greedy_full():
 
 
 def test_c5_large_batch_full_size_sampled():
-    _print_case("c5 full, 24 sequences checked")
+    _print_case("c5 full, 64 of 256 sequences checked")
     w = wl.config(5)
-    print(check_sampling(w, seqs=list(range(0, 256, 11))))
+    print(check_sampling(w, seqs=list(range(0, 256, 4))))
 
 
 # ---------------------------------------------------------------------------

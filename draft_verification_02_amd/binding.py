@@ -21,12 +21,15 @@ SPEC_DTYPE_BF16 = 1
 ROW_FILTERED = 0x1
 ROW_EXACT_PATH = 0x2
 
+SPEC_E_SCRATCH = 5
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
 # Layout of spec_row_stats_t (32 bytes), for viewing a stats tensor from numpy.
 ROW_STATS_FIELDS = [("max_logit", "<f4"), ("thresh", "<f4"), ("n_kept", "<i4"),
                     ("flags", "<i4"), ("z_kept", "<f8"), ("prob_at_token", "<f8")]
 ROW_STATS_BYTES = 32
 
-EXPORTS = ["spec_verify", "spec_verify_ragged", "spec_verify_point", "spec_verify_tree", "spec_verify_greedy",
+EXPORTS = ["spec_verify", "spec_verify_noalloc", "spec_verify_ragged", "spec_verify_point", "spec_verify_tree", "spec_verify_greedy",
            "spec_verify_greedy_hidden",
            "spec_verify_stats",
            "spec_rng_uniforms", "spec_profile_events", "spec_status_string", "spec_release_workspace"]
@@ -35,7 +38,9 @@ _lib = None
 
 
 class SpecVerifyError(RuntimeError):
-    pass
+    def __init__(self, msg, status=None):
+        super().__init__(msg)
+        self.status = status
 
 
 def load(path: str = LIB) -> ctypes.CDLL:
@@ -52,6 +57,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
                                ctypes.c_void_p)
     L.spec_verify.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32, i32]
     L.spec_verify.restype = i32
+    L.spec_verify_noalloc.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, i32, i32]
+    L.spec_verify_noalloc.restype = i32
     L.spec_verify_ragged.argtypes = [vp, vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp, vp,
                                      vp, i32, i32]
     L.spec_verify_ragged.restype = i32
@@ -81,7 +88,7 @@ def load(path: str = LIB) -> ctypes.CDLL:
 def _check(rc: int) -> None:
     if rc != 0:
         msg = load().spec_status_string(rc).decode()
-        raise SpecVerifyError(f"spec_verify status {rc}: {msg}")
+        raise SpecVerifyError(f"spec_verify status {rc}: {msg}", rc)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -148,6 +155,27 @@ def spec_verify(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.
                             int(top_k), float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
                             _ptr(out_tokens), _ptr(out_num), _stream_handle(stream),
                             _dtype_code(target), ddt)
+    _check(rc)
+    return out_tokens, out_num
+
+
+def spec_verify_noalloc(target: torch.Tensor, draft: torch.Tensor | None, tokens: torch.Tensor | None,
+                        temperature: float, top_k: int, top_p: float, seed: int,
+                        out_tokens: torch.Tensor, out_num_accepted: torch.Tensor, stream=None):
+    """spec_verify through the allocation-free entry point: the library's
+    scratch is its fixed static device array, and the outputs must be given
+    (this wrapper allocates nothing either).  Raises SpecVerifyError with
+    status SPEC_E_SCRATCH when the problem does not fit."""
+    B, K, V = _shapes(target, draft, tokens, need_draft=temperature > 0)
+    assert out_tokens is not None and out_num_accepted is not None, "outputs must be given"
+    out_tokens, out_num = _outputs(B, K, target.device, out_tokens, out_num_accepted)
+    use_draft = draft is not None and K > 0 and temperature > 0
+    ddt = _dtype_code(draft) if use_draft else SPEC_DTYPE_F32
+    rc = load().spec_verify_noalloc(_ptr(target), _ptr(draft) if use_draft else None,
+                                    _ptr(tokens) if K > 0 else None, B, K, V, float(temperature),
+                                    int(top_k), float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF,
+                                    _ptr(out_tokens), _ptr(out_num), _stream_handle(stream),
+                                    _dtype_code(target), ddt)
     _check(rc)
     return out_tokens, out_num
 

@@ -375,6 +375,8 @@ struct RowArgs {
     int drafts_first;   // draft rows take the first workgroups (see k_row)
     int parts;          // > 1: unfiltered rows split into this many parts (one workgroup each)
     PartRec* prec;      // [rows][parts]
+    unsigned* draw_cnt; // [n_cnt] arrival counters of the draw kernel, cleared by the first workgroup
+    int n_cnt;
 };
 
 struct RowShared {
@@ -1770,6 +1772,9 @@ __global__ void __launch_bounds__(256) k_row_merge(RowArgs a) {
 __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
     __shared__ RowShared S;
     clear_counters(a.sh);
+    // the draw kernel's arrival counters start from zero (it runs after this kernel)
+    if (blockIdx.x == 0)
+        for (int i = threadIdx.x; i < a.n_cnt; i += kRB) a.draw_cnt[i] = 0u;
     if (a.parts > 1) {
         const int row = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
         if (!row_live(a.sh, row)) return;

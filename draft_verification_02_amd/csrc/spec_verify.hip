@@ -61,6 +61,41 @@ void* g_ev_after = nullptr;
 
 size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
+// Byte offsets of the workspace parts for the capacities c; returns the total.
+struct Offsets {
+    size_t rec, kept, kn, kd, kp, g, cs, cnt, pr, ts, tx;
+};
+size_t layout(const Caps& c, Offsets& o) {
+    size_t off = 0;
+    o.rec = off; off = align_up(off + c.rows * sizeof(RowRec));
+    o.kept = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(uint2));
+    o.kn = off; off = align_up(off + c.lists * sizeof(int));
+    o.kd = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(float));
+    o.kp = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(double));
+    o.g = off; off = align_up(off + c.gidx * sizeof(int32_t));
+    o.cs = off; off = align_up(off + c.chunk_bytes);
+    o.cnt = off; off = align_up(off + c.seqs * sizeof(unsigned));
+    o.pr = off; off = align_up(off + c.rows * (size_t)kMaxParts * sizeof(PartRec));
+    o.ts = off; off = align_up(off + c.seqs * sizeof(TreeStop));
+    o.tx = off; off = align_up(off + c.nodes * sizeof(int32_t));
+    return std::max<size_t>(off, 256);
+}
+void carve(char* b, const Caps& c, const Offsets& o, Workspace& w) {
+    w.base = b;
+    w.cap = c;
+    w.rec = reinterpret_cast<RowRec*>(b + o.rec);
+    w.kept = reinterpret_cast<uint2*>(b + o.kept);
+    w.kept_n = reinterpret_cast<int*>(b + o.kn);
+    w.kept_d = reinterpret_cast<float*>(b + o.kd);
+    w.kept_p = reinterpret_cast<double*>(b + o.kp);
+    w.gidx = reinterpret_cast<int32_t*>(b + o.g);
+    w.chunks = b + o.cs;
+    w.draw_cnt = reinterpret_cast<unsigned*>(b + o.cnt);
+    w.prec = reinterpret_cast<PartRec*>(b + o.pr);
+    w.tstop = reinterpret_cast<TreeStop*>(b + o.ts);
+    w.tex = reinterpret_cast<int32_t*>(b + o.tx);
+}
+
 int get_workspace(hipStream_t stream, const Caps& need, Workspace** out) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_LAUNCH;
@@ -70,56 +105,87 @@ int get_workspace(hipStream_t stream, const Caps& need, Workspace** out) {
         *out = &w;
         return SPEC_OK;
     }
-    Workspace nw;
-    nw.cap.rows = std::max(need.rows, w.cap.rows);
-    nw.cap.lists = std::max(need.lists, w.cap.lists);
-    nw.cap.gidx = std::max(need.gidx, w.cap.gidx);
-    nw.cap.chunk_bytes = std::max(need.chunk_bytes, w.cap.chunk_bytes);
-    nw.cap.seqs = std::max(need.seqs, w.cap.seqs);
-    nw.cap.nodes = std::max(need.nodes, w.cap.nodes);
-    const Caps& c = nw.cap;
-    size_t off = 0;
-    const size_t o_rec = off; off = align_up(off + c.rows * sizeof(RowRec));
-    const size_t o_kept = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(uint2));
-    const size_t o_kn = off; off = align_up(off + c.lists * sizeof(int));
-    const size_t o_kd = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(float));
-    const size_t o_kp = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(double));
-    const size_t o_g = off; off = align_up(off + c.gidx * sizeof(int32_t));
-    const size_t o_cs = off; off = align_up(off + c.chunk_bytes);
-    const size_t o_cnt = off; off = align_up(off + c.seqs * sizeof(unsigned));
-    const size_t o_pr = off; off = align_up(off + c.rows * (size_t)kMaxParts * sizeof(PartRec));
-    const size_t o_ts = off; off = align_up(off + c.seqs * sizeof(TreeStop));
-    const size_t o_tx = off; off = align_up(off + c.nodes * sizeof(int32_t));
+    Caps c;
+    c.rows = std::max(need.rows, w.cap.rows);
+    c.lists = std::max(need.lists, w.cap.lists);
+    c.gidx = std::max(need.gidx, w.cap.gidx);
+    c.chunk_bytes = std::max(need.chunk_bytes, w.cap.chunk_bytes);
+    c.seqs = std::max(need.seqs, w.cap.seqs);
+    c.nodes = std::max(need.nodes, w.cap.nodes);
+    Offsets o;
+    const size_t total = layout(c, o);
     if (w.base) {
         // the old buffer may still be in use by work queued on this stream
         if (hipStreamSynchronize(stream) != hipSuccess) return SPEC_E_LAUNCH;
         (void)hipFree(w.base);
         w = Workspace();
     }
-    if (hipDeviceGetAttribute(&nw.n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        nw.n_cu <= 0)
+    int n_cu = 0;
+    if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n_cu <= 0)
         return SPEC_E_LAUNCH;
-    if (hipMalloc(&nw.base, std::max<size_t>(off, 256)) != hipSuccess) return SPEC_E_NOMEM;
-    char* b = static_cast<char*>(nw.base);
-    // the arrival counters start at zero (a synchronous fill, once per allocation)
-    if (c.seqs && hipMemset(b + o_cnt, 0, c.seqs * sizeof(unsigned)) != hipSuccess) {
-        (void)hipFree(nw.base);
-        return SPEC_E_LAUNCH;
-    }
-    nw.rec = reinterpret_cast<RowRec*>(b + o_rec);
-    nw.kept = reinterpret_cast<uint2*>(b + o_kept);
-    nw.kept_n = reinterpret_cast<int*>(b + o_kn);
-    nw.kept_d = reinterpret_cast<float*>(b + o_kd);
-    nw.kept_p = reinterpret_cast<double*>(b + o_kp);
-    nw.gidx = reinterpret_cast<int32_t*>(b + o_g);
-    nw.chunks = b + o_cs;
-    nw.draw_cnt = reinterpret_cast<unsigned*>(b + o_cnt);
-    nw.prec = reinterpret_cast<PartRec*>(b + o_pr);
-    nw.tstop = reinterpret_cast<TreeStop*>(b + o_ts);
-    nw.tex = reinterpret_cast<int32_t*>(b + o_tx);
+    void* base = nullptr;
+    if (hipMalloc(&base, total) != hipSuccess) return SPEC_E_NOMEM;
+    Workspace nw;
+    carve(static_cast<char*>(base), c, o, nw);
+    nw.n_cu = n_cu;
     w = nw;
     *out = &w;
     return SPEC_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of the allocation-free entry point: one static device array
+// per GPU, held until the process ends.  Host code never uses the array's
+// name as an address: each device's address comes from hipGetSymbolAddress,
+// taken once with that device current on its first call.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocBytes = size_t(32) << 20;
+constexpr int kMaxDevices = 64;
+static __device__ __align__(256) unsigned char scratch[kNoAllocBytes];
+
+struct NoAllocDevice {
+    bool ready = false;
+    char* ptr = nullptr;  // device address of `scratch` on this device
+    int n_cu = 0;
+};
+NoAllocDevice g_noalloc[kMaxDevices];
+
+// A workspace carved from the current device's fixed scratch (no allocation).
+int noalloc_workspace(const Caps& need, Workspace* w, Workspace** out) {
+    Offsets o;
+    if (layout(need, o) > kNoAllocBytes) return SPEC_E_SCRATCH;  // checked before any HIP call
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_E_LAUNCH;
+    NoAllocDevice& d = g_noalloc[dev];
+    {
+        std::lock_guard<std::mutex> lock(g_mu);
+        if (!d.ready) {
+            void* p = nullptr;
+            if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return SPEC_E_LAUNCH;
+            int n_cu = 0;
+            if (hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+                n_cu <= 0)
+                return SPEC_E_LAUNCH;
+            d.ptr = static_cast<char*>(p);
+            d.n_cu = n_cu;
+            d.ready = true;
+        }
+    }
+    carve(d.ptr, need, o, *w);
+    w->n_cu = d.n_cu;
+    *out = w;
+    return SPEC_OK;
+}
+
+// Where a call's workspace comes from: the per-(device, stream) allocation,
+// or (noalloc) the device's fixed scratch, described in `local`.
+struct WsSource {
+    bool noalloc = false;
+    Workspace local;
+};
+int acquire(hipStream_t stream, const Caps& need, Workspace** out, WsSource* src) {
+    if (src && src->noalloc) return noalloc_workspace(need, &src->local, out);
+    return get_workspace(stream, need, out);
 }
 
 bool dtype_size(int dt, int* sz) {
@@ -152,7 +218,7 @@ void take_events(void** evb, void** eva) {
 
 int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, int32_t* out_tokens,
                int32_t* out_num, hipStream_t stream, int tdt, const int32_t* lens = nullptr,
-               int32_t* tested = nullptr, int32_t* accepted = nullptr) {
+               int32_t* tested = nullptr, int32_t* accepted = nullptr, WsSource* src = nullptr) {
     int tsz;
     if (!dtype_size(tdt, &tsz)) return SPEC_E_UNSUPPORTED;
     int rc = check_sizes(B, K, V);
@@ -163,7 +229,7 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     Workspace* ws;
     Caps need;
     need.gidx = n_trows;
-    rc = get_workspace(stream, need, &ws);
+    rc = acquire(stream, need, &ws, src);
     if (rc) return rc;
     const Shape sh{static_cast<const char*>(target), nullptr, tokens, B, K, V, tdt, 0, tsz, 0, n_trows, 0, lens,
                    tested, accepted};
@@ -218,7 +284,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
                  int32_t* out_num, hipStream_t stream, int tdt, int ddt, spec_row_stats_t* tstats,
                  spec_row_stats_t* dstats, bool point, const int32_t* lens = nullptr,
                  int32_t* tested = nullptr, int32_t* accepted = nullptr, const int32_t* parents = nullptr,
-                 int32_t* out_path = nullptr) {
+                 int32_t* out_path = nullptr, WsSource* src = nullptr) {
     // token trees (parents given): K is the node count, tokens the node
     // tokens; the rows carry no token of their own and a walk fixes the stop
     const bool tree = parents != nullptr;
@@ -255,7 +321,7 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     need.chunk_bytes = lists ? 0 : (size_t)B * n_chunks * sizeof(DrawChunk);
     need.seqs = B;
     need.nodes = tree ? (size_t)B * K : 0;
-    rc = get_workspace(stream, need, &ws);
+    rc = acquire(stream, need, &ws, src);
     if (rc) return rc;
 
     const Shape sh{static_cast<const char*>(target), static_cast<const char*>(draft), tree ? nullptr : tokens,
@@ -293,6 +359,8 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     // tiles each) so that about 512 workgroups stream, then merge per row.
     ra.parts = 1;
     ra.prec = ws->prec;
+    ra.draw_cnt = ws->draw_cnt;
+    ra.n_cnt = B;
     if (!filtered) {
         const int nt = (int)ceil_div(V, kRTile);
         const int want = (int)std::min<long long>(kMaxParts, ceil_div(512, rows));
@@ -385,6 +453,23 @@ int spec_verify(const void* target_logits, const void* draft_logits, const int32
     return run_sampling(target_logits, draft_logits, draft_tokens, B, K, V, temperature, top_k, top_p,
                         seed, out_tokens, out_num_accepted, s, target_dtype, draft_dtype, nullptr,
                         nullptr, false);
+}
+
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits, const int32_t* draft_tokens, int B,
+                        int K, int V, float temperature, int top_k, float top_p, uint64_t seed,
+                        int32_t* out_tokens, int32_t* out_num_accepted, void* stream, int target_dtype,
+                        int draft_dtype) {
+    if (!std::isfinite(temperature) || temperature < 0.0f) return SPEC_E_INVALID;
+    if (!(top_p > 0.0f && top_p <= 1.0f)) return SPEC_E_INVALID;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    WsSource src;
+    src.noalloc = true;
+    if (temperature == 0.0f)
+        return run_greedy(target_logits, draft_tokens, B, K, V, out_tokens, out_num_accepted, s, target_dtype,
+                          nullptr, nullptr, nullptr, &src);
+    return run_sampling(target_logits, draft_logits, draft_tokens, B, K, V, temperature, top_k, top_p, seed,
+                        out_tokens, out_num_accepted, s, target_dtype, draft_dtype, nullptr, nullptr, false,
+                        nullptr, nullptr, nullptr, nullptr, nullptr, &src);
 }
 
 int spec_verify_point(const void* target_logits, const int32_t* draft_tokens, int B, int K, int V,
@@ -533,6 +618,7 @@ const char* spec_status_string(int status) {
         case SPEC_E_UNSUPPORTED: return "unsupported dtype";
         case SPEC_E_NOMEM: return "workspace allocation failed";
         case SPEC_E_LAUNCH: return "HIP runtime or kernel launch failure";
+        case SPEC_E_SCRATCH: return "problem too large for the fixed scratch of the allocation-free entry point";
         default: return "unknown status";
     }
 }

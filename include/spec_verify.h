@@ -85,7 +85,9 @@ typedef enum {
     SPEC_E_INVALID = 1,     /* bad pointer, size, temperature, top_p, ... */
     SPEC_E_UNSUPPORTED = 2, /* unknown dtype code                         */
     SPEC_E_NOMEM = 3,       /* workspace allocation failed                */
-    SPEC_E_LAUNCH = 4       /* a HIP runtime call or kernel launch failed */
+    SPEC_E_LAUNCH = 4,      /* a HIP runtime call or kernel launch failed */
+    SPEC_E_SCRATCH = 5      /* spec_verify_noalloc: the problem does not fit
+                               the fixed scratch (SPEC_NOALLOC_SCRATCH_BYTES) */
 } spec_status_t;
 
 /* Per-row intermediates written by spec_verify_stats (32 bytes). */
@@ -125,6 +127,30 @@ int spec_verify(const void* target_logits, const void* draft_logits,
                 float temperature, int top_k, float top_p, uint64_t seed,
                 int32_t* out_tokens, int32_t* out_num_accepted, void* stream,
                 int target_dtype, int draft_dtype);
+
+/*
+ * spec_verify for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, results (bitwise), kernels and errors as spec_verify, except
+ * that it never allocates or frees: its scratch (row records, kept lists,
+ * draw records and counters) lives in one fixed static device array of
+ * SPEC_NOALLOC_SCRATCH_BYTES per GPU, which the GPU holds until the process
+ * ends.  A problem whose scratch does not fit returns SPEC_E_SCRATCH before
+ * any launch: with top-k / top-p each target row keeps an 80 KiB kept list,
+ * so about B * (K+1) <= 400 target rows fit (the B = 32, K = 7 batch takes
+ * 21 MB); unfiltered and greedy calls need a few hundred bytes per row and
+ * per 1024 tokens of each sequence's stop row.  Every call on a GPU
+ * shares that GPU's array, so calls that overlap on one GPU (on different
+ * streams or from different threads) race and must be serialised by the
+ * caller.  What must start at zero is cleared by the call's first kernel.
+ */
+#define SPEC_NOALLOC_SCRATCH_BYTES (32u << 20)
+int spec_verify_noalloc(const void* target_logits, const void* draft_logits,
+                        const int32_t* draft_tokens, int B, int K, int V,
+                        float temperature, int top_k, float top_p,
+                        uint64_t seed, int32_t* out_tokens,
+                        int32_t* out_num_accepted, void* stream,
+                        int target_dtype, int draft_dtype);
 
 /*
  * Per-sequence draft lengths (the serving engines' per-request number of
@@ -215,12 +241,6 @@ int spec_verify_tree(const void* target_logits, const int32_t* node_tokens,
                      int32_t* out_path, void* stream, int target_dtype);
 
 /*
- * Greedy verification: g_k = argmax of target row k (lowest index among equal
- * maxima), accept while d_k == g_k, emit g_j at the first mismatch j (or the
- * bonus argmax g_K).  Reads target logits only.  Same conventions as
- * spec_verify.
- */
-/*
  * Greedy verification straight from the target's last hidden states, the
  * unembedding product fused in ("FlashMap: Flow Map Speculative Decoding and
  * the Mathematical Elimination of Suffix Decay", section 3: a position's
@@ -243,6 +263,13 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed,
                               int H, int32_t* out_tokens,
                               int32_t* out_num_accepted, void* stream);
 
+/*
+ * Greedy verification: g_k = argmax of target row k (lowest index among equal
+ * maxima), accept while d_k == g_k, emit g_j at the first mismatch j (or the
+ * bonus argmax g_K).  Reads target logits only.  Same conventions as
+ * spec_verify ("DFlash", section 4: the longest prefix matching the target's
+ * greedy choices).
+ */
 int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens,
                        int B, int K, int V, int32_t* out_tokens,
                        int32_t* out_num_accepted, void* stream,

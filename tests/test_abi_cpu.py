@@ -42,15 +42,16 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     assert lib.spec_status_string(0) == b"ok"
     assert b"invalid" in lib.spec_status_string(1)
+    assert b"scratch" in lib.spec_status_string(binding.SPEC_E_SCRATCH)
     assert lib.spec_status_string(12345) == b"unknown status"
 
 
-def _call(lib, **kw):
+def _call(lib, entry="spec_verify", **kw):
     a = dict(target=ctypes.c_void_p(16), draft=ctypes.c_void_p(16), tokens=ctypes.c_void_p(16),
              B=1, K=1, V=4, T=1.0, top_k=0, top_p=1.0, seed=0, out=ctypes.c_void_p(16),
              num=ctypes.c_void_p(16), stream=None, tdt=0, ddt=0)
     a.update(kw)
-    return lib.spec_verify(a["target"], a["draft"], a["tokens"], a["B"], a["K"], a["V"], a["T"],
+    return getattr(lib, entry)(a["target"], a["draft"], a["tokens"], a["B"], a["K"], a["V"], a["T"],
                            a["top_k"], a["top_p"], a["seed"], a["out"], a["num"], a["stream"],
                            a["tdt"], a["ddt"])
 
@@ -61,10 +62,21 @@ def _call(lib, **kw):
     (dict(B=-1), 1), (dict(K=-1), 1), (dict(V=0), 1),
     (dict(tdt=7), 2), (dict(ddt=9), 2),
     (dict(target=None), 1), (dict(out=None), 1), (dict(draft=None), 1), (dict(tokens=None), 1),
-    (dict(T=1e-39), 1),
+    (dict(T=1e-39), 1), (dict(V=1 << 29), 1),
 ])
-def test_invalid_arguments_rejected_on_host(lib, kw, code):
-    assert _call(lib, **kw) == code
+@pytest.mark.parametrize("entry", ["spec_verify", "spec_verify_noalloc"])
+def test_invalid_arguments_rejected_on_host(lib, kw, code, entry):
+    assert _call(lib, entry, **kw) == code
+
+
+@pytest.mark.parametrize("kw", [
+    dict(B=1000, K=7, V=151936, top_p=0.9),   # 8000 kept lists of 80 KiB
+    dict(B=4096, K=15, V=262144, top_k=50),
+    dict(B=70000, K=0, V=1 << 20),            # chunk records of unfiltered draws
+])
+def test_noalloc_entry_rejects_problems_beyond_its_scratch(lib, kw):
+    """Checked on the host before any HIP call (this container has no GPU)."""
+    assert _call(lib, "spec_verify_noalloc", **kw) == binding.SPEC_E_SCRATCH
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -1,32 +1,36 @@
 """Benchmark: batched speculative-decoding verification on one MI355X.
 
-One step = one spec_verify call over the whole batch of the concurrent-batch
-workload (B=32 sequences, K=7 drafted positions, V=151936, bf16 target / f32
-draft logits, temperature 0.7, top-p 0.9), inputs resident in HBM.  Several
-copies of the inputs are rotated so that the 256 MB Infinity Cache cannot
-serve a step from the previous one.
+One step = one verification call over the whole batch of a workload, inputs
+resident in HBM.  The default is the concurrent-batch workload (B=32
+sequences, K=7 drafted positions, V=151936, bf16 target / f32 draft logits,
+temperature 0.7, top-p 0.9) through spec_verify.  Several copies of the
+inputs are rotated so that the 256 MB Infinity Cache cannot serve a step from
+the previous one.
 
-Prints one JSON line with the headline metric (verified draft positions/s),
-the roofline of the dominant (streaming) kernel measured with HIP events on
-the call's stream, and the CPU oracle timed on the host as a baseline.
+Prints one JSON line: the headline metric (verified draft positions/s) over
+exactly --steps back-to-back steps between two events; the median and p10 /
+p90 of the step and of the dominant kernel over at least 100 calls; the
+roofline of the dominant kernel (its algorithmic bytes over its average
+duration, taken with HIP events attached to its dispatch on the call's
+stream); the acceptance telemetry of the batch (tau = mean accepted + 1, the
+acceptance rate at each position); and the CPU oracle timed on the host, on
+one core and on all the cores the process may use, with its parity summary
+against the GPU's outputs (decisions, ambiguous decisions, token mismatches).
 
---mode point measures spec_verify_point instead: the same target rows, with
-the drafts given as point masses (each draft row's argmax, the proposals of a
-greedy draft head) and no draft logits read.
-
---mode ragged measures spec_verify_ragged with per-sequence draft lengths
-drawn uniformly from 0..K (seeded) and the per-position acceptance counters
-on; the bytes counted are those of the rows inside each sequence's length.
-
---mode hidden measures spec_verify_greedy_hidden: greedy verification of the
-same batch shape straight from the target's hidden states (H = 4096, random
-bf16 unembedding matrix of 151936 x 4096), the unembedding product fused with
-the argmax on the matrix cores.
-
---mode tree measures spec_verify_tree: the same target-row distributions and
-processing over a static 44-node token tree per sequence (4 children of the
-root, then 2, 2 and 1 per node), 45 target rows per sequence, the children's
-tokens the top candidates of a proposer's noisy copy of the parent row.
+--config N picks workload N (1..5; 4 is greedy verification).
+--mode point: spec_verify_point, the drafts given as point masses (each draft
+row's argmax, a greedy draft head's proposals), no draft logits read.
+--mode ragged: spec_verify_ragged with per-sequence draft lengths U{0..K}
+(seeded) and the per-position acceptance counters on; the bytes counted are
+those of the rows inside each sequence's length.
+--mode tree: spec_verify_tree over a static 44-node token tree per sequence
+(4 children of the root, then 2, 2 and 1 per node), 45 target rows per
+sequence, the children's tokens the top candidates of a proposer's noisy copy
+of the parent row.
+--mode hidden: spec_verify_greedy_hidden, greedy verification of the same
+batch shape straight from the target's hidden states (H = 4096, random bf16
+unembedding matrix of 151936 x 4096), the unembedding product fused with the
+argmax on the matrix cores.
 """
 from __future__ import annotations
 
@@ -37,6 +41,7 @@ import json
 import os
 import sys
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 
@@ -57,6 +62,9 @@ HIDDEN_H = 4096
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
 MALL_BYTES = 256 << 20
+DIST_CALLS = 100          # calls behind the medians and percentiles (at least)
+MAX_CPU_THREADS = 16      # the host cores one GPU's share of the box holds
+ACCEPT_BAND, NUCLEUS_BAND, SAMPLE_BAND = 1e-5, 1e-6, 1e-12
 
 
 def _hip():
@@ -85,88 +93,163 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def traffic_from_profiles(config_name: str, src_hash: str):
-    """HBM bytes per launch from the committed PMC summary, only while the
-    kernel sources still match the ones the counters were taken on."""
-    path = os.path.join(ROOT, "profiles", "k_row_c3_traffic.json")
-    if not os.path.exists(path):
+def traffic_from_profiles(config_name: str, src_hash: str, kernel: str):
+    """HBM bytes per launch from a committed PMC summary of this kernel and
+    workload, only while the kernel sources still match the ones the
+    counters were taken on."""
+    pdir = os.path.join(ROOT, "profiles")
+    if not os.path.isdir(pdir):
         return None
-    with open(path) as f:
-        d = json.load(f)
-    if d.get("kernel_source_hash") != src_hash or d.get("workload") != config_name:
-        return None
-    return d.get("hbm_bytes_per_launch")
+    for f in sorted(os.listdir(pdir)):
+        if not f.endswith("_traffic.json"):
+            continue
+        with open(os.path.join(pdir, f)) as fh:
+            d = json.load(fh)
+        if (d.get("kernel_source_hash") == src_hash and d.get("workload") == config_name
+                and d.get("kernel", kernel) == kernel):
+            return d.get("hbm_bytes_per_launch")
+    return None
 
 
-def cpu_baseline(w, max_seqs: int, point_tokens=None, lens=None, tree=False):
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_threads() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(MAX_CPU_THREADS, n))
+
+
+def _oracle_job(w, b, point_tokens=None, lens=None, tree=False, greedy=False):
+    """The oracle on sequence b alone (its own global index in the random
+    stream), with its diagnostics."""
     import oracle  # CPU baseline leg only
-
-    seqs = list(range(min(w.B, max_seqs)))
-    t0 = time.perf_counter()
+    T, tk, tp = float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p))
+    sl = slice(b, b + 1)
+    if greedy:
+        return lambda: oracle.verify_greedy(w.target[sl], w.tokens[sl])
     if tree:
         par = w.meta["parents"]
-        for b in seqs:
-            oracle.verify_tree(w.target[b:b + 1], w.tokens[b:b + 1], par[b:b + 1],
-                               float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p)),
-                               w.seed, seq_base=b, diagnostics=False)
-        dt = time.perf_counter() - t0
-        return {"value": round(len(seqs) * w.K / dt, 3), "unit": "verified tree nodes/s",
-                "cores": 1, "kind": "oracle",
-                "sample": f"{len(seqs)} of {w.B} sequences of the same workload, single-threaded "
-                          f"fp64 C++ oracle, {dt:.2f} s"}
+        return lambda: oracle.verify_tree(w.target[sl], w.tokens[sl], par[sl], T, tk, tp, w.seed, seq_base=b)
+    if point_tokens is not None:
+        return lambda: oracle.verify_point(w.target[sl], point_tokens[sl], T, tk, tp, w.seed, seq_base=b)
     if lens is not None:
-        sub = slice(0, len(seqs))
-        oracle.verify_ragged(w.target[sub], w.draft[sub], w.tokens[sub], lens[sub],
-                             float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p)),
-                             w.seed)
-        dt = time.perf_counter() - t0
-        return {"value": round(int(lens[sub].sum()) / dt, 3), "unit": "verified draft positions/s",
-                "cores": 1, "kind": "oracle",
-                "sample": f"{len(seqs)} of {w.B} sequences of the same workload, single-threaded "
-                          f"fp64 C++ oracle, {dt:.2f} s"}
-    for b in seqs:
-        if point_tokens is not None:
-            oracle.verify_point(w.target[b:b + 1], point_tokens[b:b + 1],
-                                float(np.float32(w.temperature)), w.top_k,
-                                float(np.float32(w.top_p)), w.seed, seq_base=b, diagnostics=False)
-            continue
-        oracle.verify(w.target[b:b + 1], w.draft[b:b + 1], w.tokens[b:b + 1],
-                      float(np.float32(w.temperature)), w.top_k, float(np.float32(w.top_p)),
-                      w.seed, seq_base=b, diagnostics=False)
-    dt = time.perf_counter() - t0
-    return {"value": round(len(seqs) * w.K / dt, 3), "unit": "verified draft positions/s",
-            "cores": 1, "kind": "oracle",
-            "sample": f"{len(seqs)} of {w.B} sequences of the same workload, single-threaded "
-                      f"fp64 C++ oracle, {dt:.2f} s"}
+        kb = int(lens[b])
+
+        def ragged():
+            d = None if kb == 0 else np.ascontiguousarray(w.draft[sl, :kb])
+            return oracle.verify(np.ascontiguousarray(w.target[sl, :kb + 1]), d,
+                                 np.ascontiguousarray(w.tokens[sl, :kb]), T, tk, tp, w.seed, seq_base=b)
+        return ragged
+    return lambda: oracle.verify(w.target[sl], w.draft[sl], w.tokens[sl], T, tk, tp, w.seed, seq_base=b)
 
 
-def _timed_steps(torch, step, steps, warmup, settle_s=0.04):
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    settle = 0
+def cpu_baseline(w, max_seqs: int, point_tokens=None, lens=None, tree=False, greedy=False,
+                 outputs: dict | None = None):
+    """The oracle as it stands, timed on the host over a bounded sample of the
+    workload's sequences: single-threaded, then the same jobs over all the
+    cores the process may use (sequences are independent).  Fills
+    ``outputs`` (sequence -> oracle result) when given."""
+    seqs = list(range(min(w.B, max_seqs)))
+    jobs = [_oracle_job(w, b, point_tokens, lens, tree, greedy) for b in seqs]
     t0 = time.perf_counter()
-    while time.perf_counter() - t0 < settle_s:
-        step(settle)
-        settle += 1
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    e0.record()
-    for i in range(steps):
-        step(i)
-    e1.record()
-    torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / steps, settle
+    res = [j() for j in jobs]
+    dt1 = time.perf_counter() - t0
+    n = cpu_threads()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(max_workers=n) as ex:  # the oracle releases the GIL in its C calls
+        list(ex.map(lambda j: j(), jobs))
+    dtn = time.perf_counter() - t0
+    if outputs is not None:
+        outputs.update(zip(seqs, res))
+    if tree:
+        units, unit = len(seqs) * w.K, "verified tree nodes/s"
+    elif lens is not None:
+        units, unit = int(np.asarray(lens)[:len(seqs)].sum()), "verified draft positions/s"
+    else:
+        units, unit = len(seqs) * w.K, "verified draft positions/s"
+    return {"value": round(units / dt1, 3), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": f"{len(seqs)} of {w.B} sequences of the same workload, fp64 C++ oracle with "
+                      f"diagnostics, {dt1:.2f} s on one core",
+            "all_cores": {"value": round(units / dtn, 3), "cores": n, "seconds": round(dtn, 3)},
+            "cpu_model": cpu_model()}
 
 
-def _kernel_ms(torch, binding, step, n):
-    hip = _hip()
+def parity_summary(w, g_tok, g_num, outs: dict, lens=None, tree=False, greedy=False):
+    """GPU outputs against the oracle on the sequences it ran: decisions
+    (accept tests evaluated + one draw per sequence; greedy: the compares
+    made + the emitted token), the ambiguous ones by the oracle's margins (an
+    accept test with |u q - p| <= 1e-5 q, a draw within 1e-12 S of a
+    cumulative boundary, or either made on a row whose nucleus boundary lies
+    within 1e-6 of top_p) and the sequences whose tokens differ."""
+    dec = amb = bad = 0
+    for b, r in outs.items():
+        n_o = int(r["num_accepted"][0])
+        o_tok = r["tokens"][0]
+        bad += int(int(g_num[b]) != n_o or not np.array_equal(g_tok[b, :len(o_tok)], o_tok))
+        if greedy or w.temperature == 0:
+            kb = w.K if lens is None else int(lens[b])
+            dec += n_o + (1 if n_o < kb else 0) + 1
+            continue
+        am = r["accept_margin"][0]
+        ti = r["target_info"][0]
+        near = lambda info: bool(info["nucleus_margin"] <= NUCLEUS_BAND)  # noqa: E731
+        if tree:
+            tested = np.flatnonzero(np.isfinite(am))
+            dec += len(tested) + 1
+            amb += int((am[tested] <= ACCEPT_BAND).sum())
+            path = [c for c in r["path"][0].tolist() if c >= 0]
+            stop_row = path[-1] + 1 if path else 0
+            amb += int(r["sample_margin"][0] <= SAMPLE_BAND or near(ti[stop_row]))
+            continue
+        di = r["draft_info"][0] if "draft_info" in r else None
+        kb = len(am)
+        for k in range(min(n_o + 1, kb)):
+            dec += 1
+            amb += int(am[k] <= ACCEPT_BAND or near(ti[k]) or (di is not None and near(di[k])))
+        dec += 1
+        amb += int(r["sample_margin"][0] <= SAMPLE_BAND or near(ti[n_o])
+                   or (di is not None and n_o < kb and near(di[n_o])))
+    return {"sequences_checked": len(outs), "decisions": dec, "ambiguous_decisions": amb,
+            "token_mismatches": bad}
+
+
+def acceptance(num: np.ndarray, K: int, lens=None):
+    """tau (mean tokens emitted per sequence: accepted + 1) and the acceptance
+    rate at each position among the sequences whose test there ran."""
+    num = np.asarray(num, dtype=np.int64)
+    kb = np.full_like(num, K) if lens is None else np.minimum(np.maximum(np.asarray(lens), 0), K)
+    rates = []
+    for k in range(K):
+        tested = int(((num >= k) & (k < kb)).sum())
+        rates.append(round(int((num > k).sum()) / tested, 4) if tested else None)
+    return round(float((num + 1).mean()), 4), rates
+
+
+def _events(hip, n):
     evs = []
-    for _ in range(2 * n):
+    for _ in range(n):
         h = ctypes.c_void_p()
         assert hip.hipEventCreate(ctypes.byref(h)) == 0
         evs.append(h)
+    return evs
+
+
+def kernel_durations(torch, binding, step, n):
+    """Durations (ms) of the dominant kernel over n calls: the library
+    attaches a HIP event pair to that kernel's dispatch on the call's stream."""
+    hip = _hip()
+    evs = _events(hip, 2 * n)
     torch.cuda.synchronize()
     for i in range(n):
         binding.profile_events(evs[2 * i].value, evs[2 * i + 1].value)
@@ -179,7 +262,52 @@ def _kernel_ms(torch, binding, step, n):
         durs.append(f.value)
     for h in evs:
         hip.hipEventDestroy(h)
-    return float(np.mean(durs))
+    return durs
+
+
+def step_durations(torch, step, n, stream):
+    """Durations (ms) of n back-to-back calls, an event between each two."""
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+    torch.cuda.synchronize()
+    evs[0].record(stream)
+    for i in range(n):
+        step(i)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    return [evs[i].elapsed_time(evs[i + 1]) for i in range(n)]
+
+
+def dist(xs):
+    a = np.asarray(xs, dtype=np.float64)
+    return {"median": round(float(np.median(a)), 5), "p10": round(float(np.percentile(a, 10)), 5),
+            "p90": round(float(np.percentile(a, 90)), 5), "mean": round(float(a.mean()), 5), "n": len(a)}
+
+
+def timed_steps(torch, step, steps, warmup, stream, settle=True):
+    """W untimed warmup steps, 40 ms more of untimed steps (the GPU takes
+    about 20 ms of sustained work to reach its steady clocks; their count is
+    reported as settle_steps), then exactly `steps` back-to-back steps
+    between two events on the call stream."""
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n_settle = 0
+    t0 = time.perf_counter()
+    while settle and time.perf_counter() - t0 < 0.04:
+        for _ in range(20):
+            step(warmup + n_settle)
+            n_settle += 1
+        torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    t_wall = time.perf_counter()
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps, n_settle, time.perf_counter() - t_wall
 
 
 def bench_hidden(args, torch, binding, wl):
@@ -196,17 +324,22 @@ def bench_hidden(args, torch, binding, wl):
     h_t, w_t, k_t = up16(hidden), up16(w), torch.from_numpy(tokens).to(dev)
     out_t = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     out_n = torch.empty((B,), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
 
     def step(i):
         binding.spec_verify_greedy_hidden(h_t, w_t, k_t, out_t, out_n)
 
-    ms, settle = _timed_steps(torch, step, args.steps, args.warmup)
-    k_ms = _kernel_ms(torch, binding, step, args.steps)
+    ms, settle, t_wall = timed_steps(torch, step, args.steps, args.warmup, stream, args.settle)
+    n_dist = max(DIST_CALLS, args.steps)
+    k_durs = kernel_durations(torch, binding, step, n_dist)
+    s_durs = step_durations(torch, step, n_dist, stream)
+    k_ms = float(np.mean(k_durs))
     R = B * (K + 1)
     ideal = w.nbytes + hidden.nbytes
     flops = 2.0 * R * V * H
     achieved = ideal / (k_ms * 1e-3) / 1e9
     tflops = flops / (k_ms * 1e-3) / 1e12
+    src_hash = kernel_source_hash()
     line = {
         "metric": METRIC_HIDDEN,
         "value": round(B * K / (ms * 1e-3), 1),
@@ -218,23 +351,38 @@ def bench_hidden(args, torch, binding, wl):
         "data": "synthetic (random bf16 hidden states and unembedding matrix)",
         "config": {"workload": f"c3 shape greedy from hidden states B{B} K{K} V{V} H{H}", "B": B, "K": K, "V": V,
                    "H": H, "ideal_bytes": ideal, "flops": flops},
+        "step_ms": dist(s_durs),
         "roofline": {"bound": "hbm", "kernel": "k_lmhead_argmax", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": None, "kernel_ms": round(k_ms, 5), "kernel_source_hash": kernel_source_hash(),
+                     "traffic": traffic_from_profiles("hidden B32 K7 V151936 H4096", src_hash, "k_lmhead_argmax"),
+                     "kernel_ms": round(k_ms, 5), "kernel_ms_dist": dist(k_durs),
+                     "kernel_source_hash": src_hash,
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
+        "wall_s_timed": round(t_wall, 4),
     }
     if not args.no_cpu_baseline:
         import oracle  # CPU baseline leg only
         from threadpoolctl import threadpool_limits
+
+        def one(b):
+            L = oracle.lm_head_logits(hidden[b], w).reshape(1, K + 1, V)
+            return oracle.verify_greedy_logits64(L, tokens[b:b + 1])
+
         t0 = time.perf_counter()
         with threadpool_limits(limits=1):
-            L = oracle.lm_head_logits(hidden[0], w).reshape(1, K + 1, V)
-            oracle.verify_greedy_logits64(L, tokens[:1])
+            one(0)
         dt = time.perf_counter() - t0
+        n = cpu_threads()
+        t0 = time.perf_counter()
+        with threadpool_limits(limits=n):
+            one(1)
+        dtn = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(K / dt, 3), "unit": "verified draft positions/s", "cores": 1,
                                 "kind": "oracle",
                                 "sample": f"1 of {B} sequences ({K + 1} rows), float64 product on one thread, "
-                                          f"{dt:.2f} s"}
+                                          f"{dt:.2f} s",
+                                "all_cores": {"value": round(K / dtn, 3), "cores": n, "seconds": round(dtn, 3)},
+                                "cpu_model": cpu_model()}
     print(json.dumps(line), flush=True)
 
 
@@ -290,8 +438,9 @@ def main():
                          name=spec["name"].split(" ")[0] + f" tree B{spec['B']} N44 4-2-2-1")
     else:
         w = wl.config(args.config)
-    if w.greedy:
-        raise SystemExit("the headline workload is a sampling workload")
+    greedy = w.greedy
+    if greedy and args.mode != "general":
+        raise SystemExit("greedy workloads run in the general mode only")
     dev = torch.device("cuda:0")
     # point-mass drafts: the draft rows' argmax, a greedy draft head's proposals
     ptoks = np.argmax(wl.as_f32(w.draft), axis=2).astype(np.int32) if point else None
@@ -309,7 +458,7 @@ def main():
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    sets = [(up(w.target), None if (point or tree) else up(w.draft), up(ptoks if point else w.tokens))
+    sets = [(up(w.target), None if (point or tree or greedy) else up(w.draft), up(ptoks if point else w.tokens))
             for _ in range(n_sets)]
     par_t = up(np.ascontiguousarray(w.meta["parents"])) if tree else None
     out_p = torch.empty((w.B, w.K), dtype=torch.int32, device=dev) if tree else None
@@ -336,66 +485,31 @@ def main():
         binding.spec_verify(t, d, k, w.temperature, w.top_k, w.top_p, w.seed, out_t, out_n,
                             stream=stream)
 
-    for i in range(args.warmup):
-        step(i)
+    # headline: exactly --steps back-to-back steps between two events
+    ms, settle, t_wall = timed_steps(torch, step, args.steps, args.warmup, stream, args.settle)
+    # distributions over at least DIST_CALLS calls: each step between events,
+    # and the dominant kernel's own event pair
+    n_dist = max(DIST_CALLS, args.steps)
+    s_durs = step_durations(torch, step, n_dist, stream)
+    k_durs = kernel_durations(torch, binding, step, n_dist)
+    k_ms = float(np.mean(k_durs))
+    # the outputs of one call on the first input set
+    step(0)
     torch.cuda.synchronize()
-    # Settle: the GPU takes about 20 ms of sustained work to reach its steady
-    # clocks (measured: the first few hundred steps run up to 15% slower).
-    # Untimed steps continue for 40 ms after the warmup steps; their count is
-    # reported as settle_steps.
-    settle = 0
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < 0.04 and args.settle:
-        for _ in range(20):
-            step(args.warmup + settle)
-            settle += 1
-        torch.cuda.synchronize()
-
-    # headline: K back-to-back steps between two events on the call stream
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    t_wall = time.perf_counter()
-    for i in range(args.steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter() - t_wall
-    ms = e0.elapsed_time(e1) / args.steps
-
-    # dominant kernel: the library records a HIP event pair around its
-    # streaming kernel, once per step, on the same stream
-    hip = _hip()
-    n_ev = args.steps
-    evs = []
-    for _ in range(2 * n_ev):
-        h = ctypes.c_void_p()
-        assert hip.hipEventCreate(ctypes.byref(h)) == 0
-        evs.append(h)
-    torch.cuda.synchronize()
-    for i in range(n_ev):
-        binding.profile_events(evs[2 * i].value, evs[2 * i + 1].value)
-        step(i)
-    torch.cuda.synchronize()
-    durs = []
-    for i in range(n_ev):
-        f = ctypes.c_float()
-        assert hip.hipEventElapsedTime(ctypes.byref(f), evs[2 * i], evs[2 * i + 1]) == 0
-        durs.append(f.value)
-    for h in evs:
-        hip.hipEventDestroy(h)
-    k_ms = float(np.mean(durs))
+    g_tok, g_num = out_t.cpu().numpy(), out_n.cpu().numpy()
 
     src_hash = kernel_source_hash()
+    kernel = "k_row_argmax" if greedy else "k_row"
     achieved = ideal / (k_ms * 1e-3) / 1e9
-    traffic = None if (point or ragged or tree) else traffic_from_profiles(w.name, src_hash)
+    workload = w.name + ("-point" if point else ("-ragged" if ragged else ""))
+    traffic = traffic_from_profiles(workload, src_hash, kernel)
     positions = int(lens_np.sum()) if ragged else w.B * w.K
     value = positions / (ms * 1e-3)
     metric = METRIC_TREE if tree else (METRIC_POINT if point else (METRIC_RAGGED if ragged else METRIC))
     if args.config != 3:  # the metric strings above name the concurrent-batch workload
         metric = (f"verified {'tree nodes' if tree else 'draft positions'}/sec + HBM GB/s (% peak) at "
                   f"{w.name}, 1 GPU" + (f", {args.mode} mode" if args.mode != "general" else ""))
+    tau, rates = acceptance(g_num, w.K, lens_np)
     line = {
         "metric": metric,
         "value": round(value, 1),
@@ -408,29 +522,37 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32+f64",
+        "dtype": "f32+f64" if not greedy else ("bf16" if w.target.dtype == np.uint16 else "f32"),
         "data": "synthetic",
-        "config": {"workload": w.name + ("-point" if point else ("-ragged" if ragged else "")),
+        "config": {"workload": workload,
                    "B": w.B, ("N" if tree else "K"): w.K, "V": w.V,
-                   "target": "bf16", "draft": "point mass" if (point or tree) else "f32",
+                   "target": "bf16" if w.target.dtype == np.uint16 else "f32",
+                   "draft": ("none (greedy)" if greedy else "point mass" if (point or tree) else
+                             ("bf16" if w.draft.dtype == np.uint16 else "f32")),
                    "temperature": w.temperature, "top_k": w.top_k,
                    "top_p": w.top_p, "input_sets_rotated": n_sets, "ideal_bytes": ideal},
         "hbm_gbs_step": round(ideal / (ms * 1e-3) / 1e9, 1),
         "pct_peak_step": round(100 * ideal / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "k_row", "achieved": round(achieved, 1),
+        "step_ms": dist(s_durs),
+        "roofline": {"bound": "hbm", "kernel": kernel, "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic, "kernel_ms": round(k_ms, 5),
+                     "traffic": traffic, "kernel_ms": round(k_ms, 5), "kernel_ms_dist": dist(k_durs),
                      "kernel_source_hash": src_hash},
+        "acceptance": {"tau": tau, "rate_by_position": rates,
+                       "note": "one call's outputs on this batch (tau = mean accepted + 1)"},
         "wall_s_timed": round(t_wall, 4),
     }
     if ragged:
         line["config"]["draft_lens_total"] = positions
     if tree:
         line["config"]["branching"] = TREE_BRANCHING
-        line["mean_accepted_path"] = round(float(out_n.float().mean().item()), 3)
+        line["acceptance"] = {"tau": round(float(g_num.mean()) + 1.0, 4),
+                              "note": "mean accepted path length + 1, one call's outputs"}
     if not args.no_cpu_baseline:
-        cpu_seqs = args.cpu_seqs or (8 if tree else 32)
-        line["cpu_baseline"] = cpu_baseline(w, cpu_seqs, ptoks, lens_np, tree)
+        cpu_seqs = args.cpu_seqs or (8 if tree else (64 if greedy else 32))
+        outs = {}
+        line["cpu_baseline"] = cpu_baseline(w, cpu_seqs, ptoks, lens_np, tree, greedy, outs)
+        line["parity"] = parity_summary(w, g_tok, g_num, outs, lens_np, tree, greedy)
     print(json.dumps(line), flush=True)
 
 

@@ -31,6 +31,10 @@ of the parent row.
 batch shape straight from the target's hidden states (H = 4096, random bf16
 unembedding matrix of 151936 x 4096), the unembedding product fused with the
 argmax on the matrix cores.
+--mode hidden-sample: spec_verify_hidden, sampling verification of the same
+batch shape (T 0.7, top-p 0.9) from target and draft hidden states with the
+shared unembedding matrix: the bf16 logits of all 480 rows in one pass over
+the matrix, then the verification of spec_verify on them.
 """
 from __future__ import annotations
 
@@ -58,6 +62,9 @@ METRIC_TREE = ("verified tree nodes/sec + HBM GB/s (% peak) at B=32 N=44 V=15193
 TREE_BRANCHING = [4, 2, 2, 1]
 METRIC_HIDDEN = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936 H=4096, 1 GPU, "
                  "greedy from hidden states, unembedding fused (spec_verify_greedy_hidden)")
+METRIC_HIDDEN_SAMPLE = ("verified draft positions/sec + HBM GB/s (% peak) at B=32 K=7 V=151936 H=4096, 1 GPU, "
+                        "T 0.7 top-p 0.9 from target and draft hidden states, shared unembedding "
+                        "(spec_verify_hidden)")
 HIDDEN_H = 4096
 PEAK_BF16_TFLOPS = 2500.0
 PEAK_HBM_GBS = 8000.0
@@ -310,38 +317,55 @@ def timed_steps(torch, step, steps, warmup, stream, settle=True):
     return e0.elapsed_time(e1) / steps, n_settle, time.perf_counter() - t_wall
 
 
-def bench_hidden(args, torch, binding, wl):
-    """Greedy verification from hidden states at the concurrent-batch shape."""
+def bench_hidden(args, torch, binding, wl, sample=False):
+    """Verification from hidden states at the concurrent-batch shape: greedy
+    (the argmax fused into the product), or sampling (T 0.7, top-p 0.9) with
+    draft states rho * target + sqrt(1 - rho^2) N(0, 1), rho 0.9."""
     spec = wl.CONFIG_SPECS[3]
     B, K, V, H = spec["B"], spec["K"], spec["V"], HIDDEN_H
-    hidden, w = wl.make_hidden(B, K, V, H, seed=wl.gen_seed(3))
-    tokens = np.random.default_rng(wl.verify_seed(3) & 0xFFFFFFFF).integers(0, V, (B, K)).astype(np.int32)
+    T, top_p, rho = spec["temperature"], spec["top_p"], 0.9
+    # sampling: weights N(0, 9 / H), so the logits spread as the concurrent
+    # batch's rows do (sd 3) and the nucleus is a few hundred tokens
+    hidden, w = wl.make_hidden(B, K, V, H, seed=wl.gen_seed(3), w_scale=3.0 / np.sqrt(H) if sample else None)
+    rng = np.random.default_rng(wl.verify_seed(3) & 0xFFFFFFFF)
+    tokens = rng.integers(0, V, (B, K)).astype(np.int32)
+    draft = None
+    if sample:
+        t32 = wl.bf16_bits_to_f32(hidden)
+        draft = wl.f32_to_bf16_bits((rho * t32[:, :K] + np.sqrt(1 - rho * rho) * rng.standard_normal((B, K, H)))
+                                    .astype(np.float32))
     dev = torch.device("cuda:0")
 
     def up16(a):
         return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
 
     h_t, w_t, k_t = up16(hidden), up16(w), torch.from_numpy(tokens).to(dev)
+    d_t = up16(draft) if sample else None
     out_t = torch.empty((B, K + 1), dtype=torch.int32, device=dev)
     out_n = torch.empty((B,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
-        binding.spec_verify_greedy_hidden(h_t, w_t, k_t, out_t, out_n)
+        if sample:
+            binding.spec_verify_hidden(h_t, d_t, w_t, k_t, T, 0, top_p, wl.verify_seed(3), out_t, out_n)
+        else:
+            binding.spec_verify_greedy_hidden(h_t, w_t, k_t, out_t, out_n)
 
     ms, settle, t_wall = timed_steps(torch, step, args.steps, args.warmup, stream, args.settle)
     n_dist = max(DIST_CALLS, args.steps)
     k_durs = kernel_durations(torch, binding, step, n_dist)
     s_durs = step_durations(torch, step, n_dist, stream)
     k_ms = float(np.mean(k_durs))
-    R = B * (K + 1)
-    ideal = w.nbytes + hidden.nbytes
+    R = B * (K + 1) + (B * K if sample else 0)
+    # the product reads the matrix and the states once; the sampling path
+    # also writes the bf16 logits of its rows
+    ideal = w.nbytes + hidden.nbytes + (draft.nbytes + R * V * 2 if sample else 0)
     flops = 2.0 * R * V * H
     achieved = ideal / (k_ms * 1e-3) / 1e9
     tflops = flops / (k_ms * 1e-3) / 1e12
     src_hash = kernel_source_hash()
     line = {
-        "metric": METRIC_HIDDEN,
+        "metric": METRIC_HIDDEN_SAMPLE if sample else METRIC_HIDDEN,
         "value": round(B * K / (ms * 1e-3), 1),
         "unit": "verified draft positions/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "settle_steps": settle,
@@ -349,12 +373,15 @@ def bench_hidden(args, torch, binding, wl):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 x bf16 -> f32",
         "data": "synthetic (random bf16 hidden states and unembedding matrix)",
-        "config": {"workload": f"c3 shape greedy from hidden states B{B} K{K} V{V} H{H}", "B": B, "K": K, "V": V,
+        "config": {"workload": (f"c3 shape {'T0.7 top-p0.9' if sample else 'greedy'} from hidden states "
+                                f"B{B} K{K} V{V} H{H}"), "B": B, "K": K, "V": V,
                    "H": H, "ideal_bytes": ideal, "flops": flops},
         "step_ms": dist(s_durs),
-        "roofline": {"bound": "hbm", "kernel": "k_lmhead_argmax", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "k_lmhead<store>" if sample else "k_lmhead<argmax>",
+                     "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4),
-                     "traffic": traffic_from_profiles("hidden B32 K7 V151936 H4096", src_hash, "k_lmhead_argmax"),
+                     "traffic": traffic_from_profiles(f"hidden{'-sample' if sample else ''} B32 K7 V151936 H4096",
+                                                      src_hash, "k_lmhead"),
                      "kernel_ms": round(k_ms, 5), "kernel_ms_dist": dist(k_durs),
                      "kernel_source_hash": src_hash,
                      "mfma_tflops": round(tflops, 1), "mfma_frac": round(tflops / PEAK_BF16_TFLOPS, 4)},
@@ -365,6 +392,10 @@ def bench_hidden(args, torch, binding, wl):
         from threadpoolctl import threadpool_limits
 
         def one(b):
+            if sample:
+                return oracle.verify_hidden(hidden[b:b + 1], draft[b:b + 1], w, tokens[b:b + 1],
+                                            float(np.float32(T)), 0, float(np.float32(top_p)), wl.verify_seed(3),
+                                            seq_base=b, diagnostics=False)
             L = oracle.lm_head_logits(hidden[b], w).reshape(1, K + 1, V)
             return oracle.verify_greedy_logits64(L, tokens[b:b + 1])
 
@@ -379,8 +410,8 @@ def bench_hidden(args, torch, binding, wl):
         dtn = time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(K / dt, 3), "unit": "verified draft positions/s", "cores": 1,
                                 "kind": "oracle",
-                                "sample": f"1 of {B} sequences ({K + 1} rows), float64 product on one thread, "
-                                          f"{dt:.2f} s",
+                                "sample": f"1 of {B} sequences ({(2 * K + 1) if sample else K + 1} rows), "
+                                          f"float64 product and oracle on one thread, {dt:.2f} s",
                                 "all_cores": {"value": round(K / dtn, 3), "cores": n, "seconds": round(dtn, 3)},
                                 "cpu_model": cpu_model()}
     print(json.dumps(line), flush=True)
@@ -394,7 +425,8 @@ def main():
     ap.add_argument("--no-settle", dest="settle", action="store_false",
                     help="skip the untimed settle phase after the warmup steps")
     ap.add_argument("--config", type=int, default=3)
-    ap.add_argument("--mode", choices=["general", "point", "ragged", "tree", "hidden"], default="general",
+    ap.add_argument("--mode", choices=["general", "point", "ragged", "tree", "hidden", "hidden-sample"],
+                    default="general",
                     help="general: spec_verify with draft logits (the headline); point: "
                          "spec_verify_point with point-mass drafts")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
@@ -423,8 +455,8 @@ def main():
     import torch
     from draft_verification_02_amd import binding, workloads as wl
 
-    if args.mode == "hidden":
-        return bench_hidden(args, torch, binding, wl)
+    if args.mode in ("hidden", "hidden-sample"):
+        return bench_hidden(args, torch, binding, wl, sample=args.mode == "hidden-sample")
     point = args.mode == "point"
     ragged = args.mode == "ragged"
     tree = args.mode == "tree"

@@ -30,7 +30,7 @@ ROW_STATS_FIELDS = [("max_logit", "<f4"), ("thresh", "<f4"), ("n_kept", "<i4"),
 ROW_STATS_BYTES = 32
 
 EXPORTS = ["spec_verify", "spec_verify_noalloc", "spec_verify_ragged", "spec_verify_point", "spec_verify_tree", "spec_verify_greedy",
-           "spec_verify_greedy_hidden",
+           "spec_verify_greedy_hidden", "spec_lm_head_logits", "spec_verify_hidden",
            "spec_verify_stats",
            "spec_rng_uniforms", "spec_profile_events", "spec_status_string", "spec_release_workspace"]
 
@@ -68,6 +68,10 @@ def load(path: str = LIB) -> ctypes.CDLL:
     L.spec_verify_tree.restype = i32
     L.spec_verify_greedy_hidden.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
     L.spec_verify_greedy_hidden.restype = i32
+    L.spec_lm_head_logits.argtypes = [vp, vp, i32, i32, i32, vp, vp]
+    L.spec_lm_head_logits.restype = i32
+    L.spec_verify_hidden.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp]
+    L.spec_verify_hidden.restype = i32
     L.spec_verify_greedy.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, i32]
     L.spec_verify_greedy.restype = i32
     L.spec_verify_stats.argtypes = [vp, vp, vp, i32, i32, i32, f32, i32, f32, u64, vp, vp, vp,
@@ -271,6 +275,52 @@ def spec_verify_greedy_hidden(hidden: torch.Tensor, w_unembed: torch.Tensor, tok
     out_tokens, out_num = _outputs(B, K, hidden.device, out_tokens, out_num_accepted)
     rc = load().spec_verify_greedy_hidden(_ptr(hidden), _ptr(w_unembed), _ptr(tokens) if K > 0 else None, B, K, V,
                                           H, _ptr(out_tokens), _ptr(out_num), _stream_handle(stream))
+    _check(rc)
+    return out_tokens, out_num
+
+
+def spec_lm_head_logits(hidden: torch.Tensor, w_unembed: torch.Tensor, out=None, stream=None) -> torch.Tensor:
+    """bf16 logits [R, V] of hidden [R, H] (bf16) and w_unembed [V, H] (bf16)."""
+    _dev(hidden, "hidden")
+    _dev(w_unembed, "w_unembed")
+    assert hidden.dtype == torch.bfloat16 and w_unembed.dtype == torch.bfloat16
+    R, H = hidden.shape
+    V, H2 = w_unembed.shape
+    assert H == H2, "hidden and w_unembed disagree on H"
+    if out is None:
+        out = torch.empty((R, V), dtype=torch.bfloat16, device=hidden.device)
+    assert out.dtype == torch.bfloat16 and out.numel() == R * V
+    _dev(out, "out_logits")
+    _check(load().spec_lm_head_logits(_ptr(hidden), _ptr(w_unembed), R, V, H, _ptr(out), _stream_handle(stream)))
+    return out
+
+
+def spec_verify_hidden(target_hidden: torch.Tensor, draft_hidden: torch.Tensor | None, w_unembed: torch.Tensor,
+                       tokens: torch.Tensor | None, temperature: float, top_k: int = 0, top_p: float = 1.0,
+                       seed: int = 0, out_tokens=None, out_num_accepted=None, stream=None):
+    """Verification from hidden states with a shared unembedding: target_hidden
+    [B, K+1, H], draft_hidden [B, K, H], w_unembed [V, H] (all bf16), tokens
+    [B, K] int32.  Returns (out_tokens [B, K+1], out_num_accepted [B])."""
+    _dev(target_hidden, "target_hidden")
+    _dev(w_unembed, "w_unembed")
+    B, K1, H = target_hidden.shape
+    K = K1 - 1
+    V = w_unembed.shape[0]
+    assert target_hidden.dtype == torch.bfloat16 and w_unembed.dtype == torch.bfloat16
+    assert tuple(w_unembed.shape) == (V, H)
+    use_draft = K > 0 and temperature > 0
+    if use_draft:
+        assert draft_hidden is not None and tuple(draft_hidden.shape) == (B, K, H)
+        assert draft_hidden.dtype == torch.bfloat16
+        _dev(draft_hidden, "draft_hidden")
+    if K > 0:
+        assert tokens is not None and tokens.dtype == torch.int32 and tuple(tokens.shape) == (B, K)
+        _dev(tokens, "draft_tokens")
+    out_tokens, out_num = _outputs(B, K, target_hidden.device, out_tokens, out_num_accepted)
+    rc = load().spec_verify_hidden(_ptr(target_hidden), _ptr(draft_hidden) if use_draft else None, _ptr(w_unembed),
+                                   _ptr(tokens) if K > 0 else None, B, K, V, H, float(temperature), int(top_k),
+                                   float(top_p), int(seed) & 0xFFFFFFFFFFFFFFFF, _ptr(out_tokens), _ptr(out_num),
+                                   _stream_handle(stream))
     _check(rc)
     return out_tokens, out_num
 

@@ -436,6 +436,96 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     return SPEC_OK;
 }
 
+// ---------------------------------------------------------------------------
+// The unembedding product (k_lmhead): size checks, arguments, launch.
+// ---------------------------------------------------------------------------
+int lm_check(long long R, int V, int H) {
+    if (R < 0 || V < 1 || H < 8 || H % 8 != 0) return SPEC_E_INVALID;
+    const long long n_vt = ceil_div(V, kLmN);
+    if (R >= (1LL << 31) || R * n_vt >= (1LL << 40) || (n_vt + 8) * ceil_div(R, kLmM) >= (1LL << 31))
+        return SPEC_E_INVALID;
+    if ((long long)V * H >= (1LL << 40) || R * H >= (1LL << 40) || R * V >= (1LL << 40)) return SPEC_E_INVALID;
+    return SPEC_OK;
+}
+
+LmArgs lm_args(const void* hidden, const void* hidden2, long long R1, long long R, const void* w, int V, int H) {
+    LmArgs la{};
+    la.hidden = static_cast<const uint16_t*>(hidden);
+    la.hidden2 = static_cast<const uint16_t*>(hidden2);
+    la.R1 = (int)R1;
+    la.w = static_cast<const uint16_t*>(w);
+    la.R = (int)R;
+    la.V = V;
+    la.H = H;
+    la.n_vt = (int)ceil_div(V, kLmN);
+    la.n_rt = (int)ceil_div(R, kLmM);
+    la.n_tiles = (int)(ceil_div(la.n_vt, 8) * 8 * la.n_rt);
+    return la;
+}
+
+// Persistent launch: the workgroups the GPU holds at once (a multiple of 8,
+// see k_lmhead), or fewer when the tiles are fewer.  A measurement event pair,
+// if armed, is attached to this dispatch.
+int launch_lm(int epi, const LmArgs& la, int n_cu, hipStream_t st) {
+    long long grid = std::min<long long>(la.n_tiles, (long long)kLmPerCU * n_cu);
+    grid = std::max<long long>(8, grid / 8 * 8);
+    void *evb, *eva;
+    take_events(&evb, &eva);
+    if (epi == LM_STORE)
+        hipExtLaunchKernelGGL(k_lmhead<LM_STORE>, dim3((unsigned)grid), dim3(kLmThreads), 0, st,
+                              static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, la);
+    else
+        hipExtLaunchKernelGGL(k_lmhead<LM_ARGMAX>, dim3((unsigned)grid), dim3(kLmThreads), 0, st,
+                              static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, la);
+    return launch_status();
+}
+
+// Compute units of the current device (cached per device).
+int device_cus(int* out) {
+    static int cus[kMaxDevices] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SPEC_E_LAUNCH;
+    if (cus[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return SPEC_E_LAUNCH;
+        cus[dev] = n;
+    }
+    *out = cus[dev];
+    return SPEC_OK;
+}
+
+// The logits of a sampling call from hidden states: one grow-only buffer per
+// (device, stream), apart from the verification workspace.
+struct LogitBuf {
+    void* p = nullptr;
+    size_t cap = 0;
+};
+std::map<std::pair<int, hipStream_t>, LogitBuf> g_lbuf;
+
+int get_logit_buf(hipStream_t stream, size_t bytes, void** out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SPEC_E_LAUNCH;
+    std::lock_guard<std::mutex> lock(g_mu);
+    LogitBuf& b = g_lbuf[{dev, stream}];
+    if (b.p && bytes <= b.cap) {
+        *out = b.p;
+        return SPEC_OK;
+    }
+    if (b.p) {
+        if (hipStreamSynchronize(stream) != hipSuccess) return SPEC_E_LAUNCH;
+        (void)hipFree(b.p);
+        b = LogitBuf();
+    }
+    if (hipMalloc(&b.p, std::max<size_t>(bytes, 256)) != hipSuccess) {
+        b.p = nullptr;
+        return SPEC_E_NOMEM;
+    }
+    b.cap = std::max<size_t>(bytes, 256);
+    *out = b.p;
+    return SPEC_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -525,42 +615,42 @@ int spec_verify_tree(const void* target_logits, const int32_t* node_tokens, cons
                         nullptr, nullptr, nullptr, parents, out_path);
 }
 
+int spec_lm_head_logits(const void* hidden, const void* w_unembed, int R, int V, int H, void* out_logits,
+                        void* stream) {
+    int rc = lm_check(R, V, H);
+    if (rc) return rc;
+    if (R == 0) return SPEC_OK;
+    if (!hidden || !w_unembed || !out_logits) return SPEC_E_INVALID;
+    if (((uintptr_t)hidden | (uintptr_t)w_unembed) & 15u) return SPEC_E_INVALID;
+    int n_cu;
+    if ((rc = device_cus(&n_cu))) return rc;
+    LmArgs la = lm_args(hidden, nullptr, R, R, w_unembed, V, H);
+    la.logits = static_cast<uint16_t*>(out_logits);
+    return launch_lm(LM_STORE, la, n_cu, static_cast<hipStream_t>(stream));
+}
+
 int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const int32_t* draft_tokens, int B,
                               int K, int V, int H, int32_t* out_tokens, int32_t* out_num_accepted, void* stream) {
-    if (B < 0 || K < 0 || V < 1 || H < 8 || H % 8 != 0) return SPEC_E_INVALID;
+    if (B < 0 || K < 0) return SPEC_E_INVALID;
     const long long R = (long long)B * (K + 1);
-    const long long n_vt = ceil_div(V, kLmN);
-    if (R >= (1LL << 31) || R * n_vt >= (1LL << 40) || (n_vt + 8) * ceil_div(R, kLmM) >= (1LL << 31))
-        return SPEC_E_INVALID;
-    if ((long long)V * H >= (1LL << 40) || R * H >= (1LL << 40) || n_vt >= (1LL << 31)) return SPEC_E_INVALID;
+    if (R >= (1LL << 31)) return SPEC_E_INVALID;
+    int rc = lm_check(R, V, H);
+    if (rc) return rc;
     if (B == 0) return SPEC_OK;
     if (!hidden || !w_unembed || !out_tokens || !out_num_accepted || (K > 0 && !draft_tokens)) return SPEC_E_INVALID;
     if (((uintptr_t)hidden | (uintptr_t)w_unembed) & 15u) return SPEC_E_INVALID;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    const long long n_vt = ceil_div(V, kLmN);
     Workspace* ws;
     Caps need;
     need.gidx = (size_t)R;
     need.chunk_bytes = (size_t)(R * n_vt) * sizeof(LmPart);
-    int rc = get_workspace(st, need, &ws);
+    rc = get_workspace(st, need, &ws);
     if (rc) return rc;
-    LmArgs la;
-    la.hidden = static_cast<const uint16_t*>(hidden);
-    la.w = static_cast<const uint16_t*>(w_unembed);
-    la.R = (int)R;
-    la.V = V;
-    la.H = H;
-    la.n_vt = (int)n_vt;
-    la.n_rt = (int)ceil_div(R, kLmM);
+    LmArgs la = lm_args(hidden, nullptr, R, R, w_unembed, V, H);
     la.part = static_cast<LmPart*>(ws->chunks);
     la.gidx = ws->gidx;
-    void *evb, *eva;
-    take_events(&evb, &eva);
-    // one workgroup per (row tile, vocabulary tile), the vocabulary tiles
-    // padded to a multiple of 8 (see k_lmhead_argmax)
-    const long long n_wg = ceil_div(n_vt, 8) * 8 * ceil_div(R, kLmM);
-    hipExtLaunchKernelGGL(k_lmhead_argmax, dim3((unsigned)n_wg), dim3(256), 0, st,
-                          static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, la);
-    if ((rc = launch_status())) return rc;
+    if ((rc = launch_lm(LM_ARGMAX, la, ws->n_cu, st))) return rc;
     hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)R), dim3(256), 0, st, la);
     if ((rc = launch_status())) return rc;
     const Shape sh{nullptr, nullptr, draft_tokens, B, K, V, SPEC_DTYPE_BF16, 0, 2, 0, (int)R, 0, nullptr, nullptr,
@@ -568,6 +658,40 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     hipLaunchKernelGGL(k_greedy_prefix, dim3((unsigned)ceil_div(B, 256)), dim3(256), 0, st, sh,
                        (const int32_t*)ws->gidx, out_tokens, out_num_accepted);
     return launch_status();
+}
+
+int spec_verify_hidden(const void* target_hidden, const void* draft_hidden, const void* w_unembed,
+                       const int32_t* draft_tokens, int B, int K, int V, int H, float temperature, int top_k,
+                       float top_p, uint64_t seed, int32_t* out_tokens, int32_t* out_num_accepted, void* stream) {
+    if (!std::isfinite(temperature) || temperature < 0.0f) return SPEC_E_INVALID;
+    if (!(top_p > 0.0f && top_p <= 1.0f)) return SPEC_E_INVALID;
+    if (temperature == 0.0f)
+        return spec_verify_greedy_hidden(target_hidden, w_unembed, draft_tokens, B, K, V, H, out_tokens,
+                                         out_num_accepted, stream);
+    if (B < 0 || K < 0) return SPEC_E_INVALID;
+    const long long R1 = (long long)B * (K + 1), R = R1 + (long long)B * K;
+    if (R >= (1LL << 31)) return SPEC_E_INVALID;
+    int rc = lm_check(R, V, H);
+    if (rc) return rc;
+    if ((rc = check_sizes(B, K, V))) return rc;
+    if (B == 0) return SPEC_OK;
+    if (!target_hidden || !w_unembed || !out_tokens || !out_num_accepted || (K > 0 && (!draft_hidden || !draft_tokens)))
+        return SPEC_E_INVALID;
+    if (((uintptr_t)target_hidden | (uintptr_t)w_unembed | (uintptr_t)(K > 0 ? draft_hidden : nullptr)) & 15u)
+        return SPEC_E_INVALID;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    // the product of every target and draft row with the shared unembedding
+    // matrix, in bf16, then the same verification as spec_verify on them
+    void* lg = nullptr;
+    if ((rc = get_logit_buf(st, (size_t)R * V * sizeof(uint16_t), &lg))) return rc;
+    int n_cu;
+    if ((rc = device_cus(&n_cu))) return rc;
+    LmArgs la = lm_args(target_hidden, draft_hidden, R1, R, w_unembed, V, H);
+    la.logits = static_cast<uint16_t*>(lg);
+    if ((rc = launch_lm(LM_STORE, la, n_cu, st))) return rc;
+    const uint16_t* tl = static_cast<const uint16_t*>(lg);
+    return run_sampling(tl, tl + (size_t)R1 * V, draft_tokens, B, K, V, temperature, top_k, top_p, seed, out_tokens,
+                        out_num_accepted, st, SPEC_DTYPE_BF16, SPEC_DTYPE_BF16, nullptr, nullptr, false);
 }
 
 int spec_verify_greedy(const void* target_logits, const int32_t* draft_tokens, int B, int K, int V,
@@ -634,6 +758,13 @@ void spec_release_workspace(void) {
         (void)hipFree(kv.second.base);
     }
     g_ws.clear();
+    for (auto& kv : g_lbuf) {
+        if (!kv.second.p) continue;
+        (void)hipSetDevice(kv.first.first);
+        (void)hipStreamSynchronize(kv.first.second);
+        (void)hipFree(kv.second.p);
+    }
+    g_lbuf.clear();
     (void)hipSetDevice(cur);
 }
 

@@ -264,6 +264,51 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed,
                               int32_t* out_num_accepted, void* stream);
 
 /*
+ * The unembedding product: a position's logits are its hidden state times
+ * the transposed unembedding (LM head) matrix ("FlashMap: Flow Map
+ * Speculative Decoding and the Mathematical Elimination of Suffix Decay",
+ * section 3).
+ *   hidden      [R][H] bf16 device array (16-byte aligned)
+ *   w_unembed   [V][H] bf16 device array (16-byte aligned); H a multiple of 8
+ *   out_logits  [R][V] bf16 device array: each logit is the product formed
+ *               with bf16 products accumulated in fp32 on the matrix cores,
+ *               rounded to bf16 (nearest, ties to even), as a bf16 LM head
+ *               outputs its logits.  Exact whenever the fp32 sums are (for
+ *               instance with small-integer inputs); otherwise each logit is
+ *               the bf16 rounding of a value within the fp32 accumulation
+ *               error (at most H * 2^-24 * sum |h w|) of the exact product.
+ * R == 0 is a no-op.  Stream and error codes as spec_verify.
+ */
+int spec_lm_head_logits(const void* hidden, const void* w_unembed, int R,
+                        int V, int H, void* out_logits, void* stream);
+
+/*
+ * Verification from hidden states with the unembedding shared by target and
+ * drafter (FlashMap page, section 5: the drafter's logits come from the
+ * target's LM head; "DFlash" section 5: the drafter shares the target's
+ * token embedding and LM head):
+ *   target_hidden [B][K+1][H] bf16: the target's final hidden state at each
+ *                 verified position;
+ *   draft_hidden  [B][K][H] bf16: the drafter's output state at each drafted
+ *                 position (may be NULL when K == 0);
+ *   w_unembed     [V][H] bf16, the shared unembedding matrix.
+ * The logits of all B(2K+1) rows come from one pass over w_unembed as in
+ * spec_lm_head_logits (bf16), and are then verified exactly as spec_verify
+ * verifies bf16 target and draft logits (temperature, top-k, top-p, seed,
+ * outputs and errors as there; temperature == 0 runs
+ * spec_verify_greedy_hidden on the target rows).  The logits stay in a
+ * library-owned buffer per (device, stream), B(2K+1)*V*2 bytes, written once
+ * and read once: exact top-p needs every logit of a row (or a second pass
+ * over w_unembed, which is larger at these sizes).
+ */
+int spec_verify_hidden(const void* target_hidden, const void* draft_hidden,
+                       const void* w_unembed, const int32_t* draft_tokens,
+                       int B, int K, int V, int H, float temperature,
+                       int top_k, float top_p, uint64_t seed,
+                       int32_t* out_tokens, int32_t* out_num_accepted,
+                       void* stream);
+
+/*
  * Greedy verification: g_k = argmax of target row k (lowest index among equal
  * maxima), accept while d_k == g_k, emit g_j at the first mismatch j (or the
  * bonus argmax g_K).  Reads target logits only.  Same conventions as

@@ -327,6 +327,43 @@ def lm_head_abs_sums(hidden_bits: np.ndarray, w_bits: np.ndarray, chunk: int = 8
     return out
 
 
+def round_bf16(x: np.ndarray) -> np.ndarray:
+    """float64 values rounded to the nearest bfloat16 value (8 significant
+    bits), ties to the even significand, as bf16 bit patterns (uint16).  The
+    inputs are finite and in bf16's normal range (or zero).  The logits of a
+    bf16 LM head are its products rounded this way."""
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)                  # x = m 2^e with 0.5 <= |m| < 1
+    q = np.rint(m * 256.0)              # 8 significant bits, halves to even
+    y = np.ldexp(q, e - 8)              # exact, and exact in float32 too
+    return (y.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def lm_head_logits_bf16(hidden_bits: np.ndarray, w_bits: np.ndarray) -> np.ndarray:
+    """Logits [R, V] = hidden [R, H] @ W^T rounded to bf16 (bit patterns):
+    the float64 product (exact for small-integer inputs) through round_bf16."""
+    return round_bf16(lm_head_logits(hidden_bits, w_bits))
+
+
+def verify_hidden(target_hidden, draft_hidden, w_bits, tokens, temperature, top_k=0, top_p=1.0, seed=0,
+                  seq_base=0, diagnostics=True):
+    """Verification from hidden states with a shared unembedding: the logits
+    of target rows [B, K+1, H] and draft rows [B, K, H] are their products
+    with w [V, H] rounded to bf16, then ``verify`` (greedy at temperature 0).
+    Returns verify's dict plus ``target_logits`` and ``draft_logits``."""
+    B, K1, H = target_hidden.shape
+    K = K1 - 1
+    V = w_bits.shape[0]
+    tl = lm_head_logits_bf16(target_hidden.reshape(-1, H), w_bits).reshape(B, K1, V)
+    dl = None
+    if K > 0 and temperature > 0:
+        dl = lm_head_logits_bf16(draft_hidden.reshape(-1, H), w_bits).reshape(B, K, V)
+    r = verify(tl, dl, tokens, temperature, top_k, top_p, seed, seq_base=seq_base, diagnostics=diagnostics)
+    r["target_logits"] = tl
+    r["draft_logits"] = dl
+    return r
+
+
 def verify_greedy_logits64(logits: np.ndarray, tokens: np.ndarray):
     """Greedy verification on float64 logits [B, K+1, V]: g_k = argmax of row
     k (lowest index among equal maxima); accept while d_k == g_k, then emit

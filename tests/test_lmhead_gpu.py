@@ -93,3 +93,137 @@ def test_hidden_greedy_random_shapes(i):
     H = int(r.choice([8, 16, 24, 56, 64, 72, 200, 264, 512]))
     _print_case(f"hidden greedy random {i}: B={B} K={K} V={V} H={H}")
     print("near ties", _check(B, K, V, H, seed=7000 + i, agree=float(r.uniform(0.3, 1.0))))
+
+
+# ---------------------------------------------------------------------------
+# bf16 logits (spec_lm_head_logits) and sampling verification from hidden
+# states with a shared unembedding (spec_verify_hidden)
+# ---------------------------------------------------------------------------
+
+def _int_inputs(rows, V, H, seed, scale_w=16.0):
+    """Small-integer hidden states and weights / 16: every product and every
+    fp32 partial sum is exact, so the GPU's logits are the exact products and
+    their bf16 rounding equals the oracle's."""
+    r = np.random.default_rng(seed)
+    h = r.integers(-3, 4, (rows, H)).astype(np.float32)
+    w = (r.integers(-3, 4, (V, H)) / scale_w).astype(np.float32)
+    return wl.f32_to_bf16_bits(h), wl.f32_to_bf16_bits(w)
+
+
+@pytest.mark.parametrize("R,V,H", [(1, 1, 8), (37, 5003, 264), (129, 777, 40), (256, 2048, 512), (300, 300, 96)])
+def test_lm_head_logits_exact_on_integer_inputs(R, V, H):
+    _print_case(f"lm head logits R={R} V={V} H={H}")
+    hb, wb = _int_inputs(R, V, H, seed=R + V + H)
+    g = binding.spec_lm_head_logits(_dev16(hb), _dev16(wb))
+    torch.cuda.synchronize()
+    g = g.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(g, oracle.lm_head_logits_bf16(hb, wb))
+
+
+def test_lm_head_logits_full_vocabulary_random():
+    """N(0, 1) hidden states, N(0, 1/H) weights, V = 151936, H = 4096: every
+    logit is the bf16 rounding of a value within the fp32 accumulation bound
+    H 2^-24 sum|h w| of the exact product, so where it differs from the exact
+    product's own rounding it lies within that bound plus half a bf16 step of
+    the exact value; such logits are few."""
+    _print_case("lm head logits R=32 V=151936 H=4096")
+    hidden, w = wl.make_hidden(4, 7, 151936, 4096, seed=91)
+    hb = hidden.reshape(-1, 4096)
+    g = binding.spec_lm_head_logits(_dev16(hb), _dev16(w))
+    torch.cuda.synchronize()
+    g = g.view(torch.int16).cpu().numpy().view(np.uint16)
+    exact = oracle.lm_head_logits(hb, w)
+    o = oracle.round_bf16(exact)
+    diff = np.nonzero(g != o)
+    print("logits differing from the exact product's rounding:", len(diff[0]), "of", g.size)
+    if len(diff[0]):
+        gv = oracle.bf16_to_f64(g[diff])
+        half_step = np.spacing(np.abs(gv).astype(np.float32)).astype(np.float64) * 2.0 ** 15
+        A = oracle.lm_head_abs_sums(hb, w)[diff]
+        err = np.abs(gv - exact[diff])
+        bound = 4096 * 2.0 ** -24 * A + half_step
+        assert (err <= bound * (1 + 1e-9)).all(), (err / bound).max()
+    assert len(diff[0]) <= 1e-3 * g.size
+
+
+def _hidden_workload(B, K, V, H, seed, integer, rho=0.9):
+    r = np.random.default_rng(seed)
+    if integer:
+        th, w = _int_inputs(B * (K + 1), V, H, seed)
+        t = wl.bf16_bits_to_f32(th).reshape(B, K + 1, H)
+        noise = r.integers(-1, 2, (B, K, H)) * (r.random((B, K, H)) < 0.3)
+        dh = wl.f32_to_bf16_bits(np.clip(t[:, :K] + noise, -3, 3).astype(np.float32))
+        th = th.reshape(B, K + 1, H)
+    else:
+        hidden, w = wl.make_hidden(B, K, V, H, seed=seed)
+        th = hidden
+        t = wl.bf16_bits_to_f32(th)
+        dh = wl.f32_to_bf16_bits((rho * t[:, :K] + np.sqrt(1 - rho * rho) * r.standard_normal((B, K, H)))
+                                 .astype(np.float32))
+    return th, dh.reshape(B, K, H), w
+
+
+def _run_hidden(th, dh, w, toks, T, top_k, top_p, seed):
+    out, num = binding.spec_verify_hidden(_dev16(th), _dev16(dh) if dh.shape[1] else None, _dev16(w),
+                                          torch.from_numpy(toks).cuda(), T, top_k, top_p, seed)
+    torch.cuda.synchronize()
+    return out.cpu().numpy(), num.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,top_k,top_p", [(0.8, 0, 0.9), (1.0, 0, 1.0), (0.7, 40, 0.95), (1.3, 5, 1.0),
+                                           (0.0, 0, 1.0)])
+def test_verify_hidden_integer_inputs_match_oracle(T, top_k, top_p):
+    """Exact logits (small-integer inputs): spec_verify_hidden equals the
+    oracle's verification of the rounded products token for token, under the
+    same ambiguity bands as spec_verify.  Drafted tokens are the draft
+    logits' argmax (a greedy draft head), so prefixes are accepted."""
+    from parity import Report, compare_sampling
+    _print_case(f"verify hidden integer T={T} top_k={top_k} top_p={top_p}")
+    B, K, V, H = 6, 5, 20011, 512
+    th, dh, w = _hidden_workload(B, K, V, H, seed=int(T * 10) + top_k, integer=True)
+    dl = oracle.lm_head_logits_bf16(dh.reshape(-1, H), w).reshape(B, K, V)
+    toks = np.argmax(wl.bf16_bits_to_f32(dl), axis=2).astype(np.int32)
+    toks[::3, 1] = (toks[::3, 1] + 7) % V
+    seed = 0xABC + top_k
+    g_tok, g_num = _run_hidden(th, dh, w, toks, T, top_k, top_p, seed)
+    if T == 0:
+        r = oracle.verify_hidden(th, dh, w, toks, 0.0)
+        np.testing.assert_array_equal(g_tok, r["tokens"])
+        np.testing.assert_array_equal(g_num, r["num_accepted"])
+        return
+    outs = [oracle.verify_hidden(th[b:b + 1], dh[b:b + 1], w, toks[b:b + 1], float(np.float32(T)), top_k,
+                                 float(np.float32(top_p)), seed, seq_base=b) for b in range(B)]
+    tl = np.concatenate([o["target_logits"] for o in outs])
+    dlo = np.concatenate([o["draft_logits"] for o in outs])
+    wk = wl.Workload("hidden", B, K, V, tl, dlo, toks, T, top_k, top_p, seed)
+    print(compare_sampling(wk, g_tok, g_num, None, None, list(range(B)), outs, Report(), check_stats=False),
+          "accepted", g_num.tolist())
+
+
+def test_verify_hidden_full_vocabulary():
+    """V = 151936, H = 4096, B = 4, K = 7, random N(0, 1) states (draft states
+    correlated with the target's, rho 0.9), T = 0.7, top-p 0.9.  The call is
+    spec_lm_head_logits over the target and draft rows followed by
+    spec_verify on them (bitwise), and agrees with the oracle run on those
+    logits token for token."""
+    from parity import Report, compare_sampling
+    _print_case("verify hidden V=151936 H=4096")
+    B, K, V, H = 4, 7, 151936, 4096
+    th, dh, w = _hidden_workload(B, K, V, H, seed=5, integer=False)
+    rows = np.concatenate([th.reshape(-1, H), dh.reshape(-1, H)])
+    lg = binding.spec_lm_head_logits(_dev16(rows), _dev16(w))
+    torch.cuda.synchronize()
+    lgn = lg.view(torch.int16).cpu().numpy().view(np.uint16)
+    tl, dl = lgn[:B * (K + 1)].reshape(B, K + 1, V), lgn[B * (K + 1):].reshape(B, K, V)
+    toks = np.argmax(wl.bf16_bits_to_f32(dl), axis=2).astype(np.int32)
+    g_tok, g_num = _run_hidden(th, dh, w, toks, 0.7, 0, 0.9, 77)
+    from parity import to_device
+    s_tok, s_num = binding.spec_verify(to_device(tl), to_device(dl), torch.from_numpy(toks).cuda(), 0.7, 0, 0.9, 77)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(g_tok, s_tok.cpu().numpy())
+    np.testing.assert_array_equal(g_num, s_num.cpu().numpy())
+    outs = [oracle.verify(tl[b:b + 1], dl[b:b + 1], toks[b:b + 1], float(np.float32(0.7)), 0, float(np.float32(0.9)),
+                          77, seq_base=b) for b in range(B)]
+    wk = wl.Workload("hidden", B, K, V, tl, dl, toks, 0.7, 0, 0.9, 77)
+    print(compare_sampling(wk, g_tok, g_num, None, None, list(range(B)), outs, Report(), check_stats=False),
+          "accepted", g_num.tolist())

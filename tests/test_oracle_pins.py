@@ -855,3 +855,62 @@ def test_greedy_from_logits64_equals_the_cpp_greedy_rule():
     np.testing.assert_array_equal(num, ref["num_accepted"])
     assert (g != 7).all()
     assert num.max() > 0
+
+
+# ---------------------------------------------------------------------------
+# Rounding to bf16 (the logits a bf16 LM head outputs) and verification from
+# hidden states with a shared unembedding
+# ---------------------------------------------------------------------------
+
+def _bf16_nearest_by_fractions(x: float) -> float:
+    """The bf16 value nearest to x, ties to the even significand, by exact
+    rational arithmetic: the two bf16 neighbours of x are the multiples of
+    the bf16 spacing at x's binade on either side of it."""
+    from fractions import Fraction
+    import math
+    if x == 0.0:
+        return 0.0
+    fx = Fraction(x)
+    e = math.frexp(abs(x))[1]  # 2^(e-1) <= |x| < 2^e
+    ulp = Fraction(2) ** (e - 8)
+    lo = math.floor(fx / ulp)
+    cands = [lo, lo + 1]
+    best = min(cands, key=lambda q: (abs(fx - q * ulp), q % 2))
+    return float(best * ulp)
+
+
+def test_round_bf16_is_the_nearest_value_ties_to_even():
+    rng = np.random.default_rng(91)
+    x = np.concatenate([rng.standard_normal(3000) * 10.0 ** rng.integers(-6, 6, 3000),
+                        rng.integers(-5000, 5000, 500) / 64.0, [0.0, 1.0, -1.0, 255.0, 257.0]])
+    got = oracle.bf16_to_f64(oracle.round_bf16(x))
+    want = np.array([_bf16_nearest_by_fractions(float(v)) for v in x])
+    np.testing.assert_array_equal(got, want)
+    # exact ties between two bf16 values go to the even significand
+    ties = np.array([1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8, -(2.0 + 2.0 ** -7), 256.0 + 1.0, 258.0 + 1.0])
+    np.testing.assert_array_equal(oracle.bf16_to_f64(oracle.round_bf16(ties)),
+                                  [1.0, 1.0 + 2.0 ** -6, -2.0, 256.0, 260.0])
+    # float32 inputs (no double rounding possible) agree with torch's conversion
+    f = (rng.standard_normal(4000) * 30).astype(np.float32)
+    t = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(oracle.round_bf16(f.astype(np.float64)), t)
+
+
+def test_verify_hidden_is_verify_on_rounded_products():
+    """oracle.verify_hidden takes the products with the shared unembedding
+    through round_bf16 and then the plain rule; on small-integer inputs the
+    product is exact, so the logits are round_bf16 of written-out dot
+    products."""
+    rng = np.random.default_rng(92)
+    B, K, H, V = 3, 4, 24, 300
+    th = rng.integers(-3, 4, (B, K + 1, H)).astype(np.float32)
+    dh = rng.integers(-3, 4, (B, K, H)).astype(np.float32)
+    w = (rng.integers(-3, 4, (V, H)) / 16.0).astype(np.float32)
+    toks = rng.integers(0, V, (B, K)).astype(np.int32)
+    r = oracle.verify_hidden(_bf16_bits(th), _bf16_bits(dh), _bf16_bits(w), toks, 0.8, 0, 0.9, seed=5)
+    exact_t = np.einsum("bkh,vh->bkv", th.astype(np.float64), w.astype(np.float64))
+    np.testing.assert_array_equal(r["target_logits"], oracle.round_bf16(exact_t))
+    ref = oracle.verify(r["target_logits"], r["draft_logits"], toks, 0.8, 0, 0.9, 5)
+    np.testing.assert_array_equal(r["tokens"], ref["tokens"])
+    g = oracle.verify_hidden(_bf16_bits(th), None, _bf16_bits(w), toks, 0.0)
+    np.testing.assert_array_equal(g["tokens"], oracle.verify_greedy(r["target_logits"], toks)["tokens"])

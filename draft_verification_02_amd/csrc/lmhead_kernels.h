@@ -12,17 +12,25 @@
 //  store  : the tile's logits are rounded to bf16 (nearest, ties to even, as
 //           a bf16 LM head outputs them) and stored, for the sampling path.
 //
-// k_lmhead<EPI> is persistent: exactly the workgroups the GPU holds at once,
-// each looping over (128 rows, 256 tokens) tiles in an XCD-aware order.  A
-// tile walks the hidden dimension in 32-wide steps through two LDS buffers:
-// the operands of the next two steps are loaded into registers while the
-// current step multiplies, and the next step's are stored into the other
-// buffer afterwards, so each step needs one barrier.  Each of the 4 waves owns a 64 x 128 block
-// (2 x 4 v_mfma_f32_32x32x16_bf16 per 16-wide slice).
+// k_lmhead<EPI> is persistent: one workgroup of 8 waves per compute unit,
+// each looping over (256 rows, 256 tokens) tiles (see the schedule below).
+// A tile spans 256 rows so that, for up to 256 rows (a batch of 32 sequences
+// of 8 positions), every unembedding row is read from memory by one
+// workgroup only, and 256 tokens so that the hidden states, which every tile
+// re-reads from L2, cost no more than the unembedding rows: the L1's limit on
+// requests in flight, not HBM, bounds how fast a compute unit can be fed, so
+// the bytes per tile are what count.  A tile walks the hidden dimension in
+// 32-wide steps through a ring of three LDS stages that the loads fill
+// directly (global_load_lds_dwordx4: no registers hold loaded data), so two
+// steps are in flight while the third multiplies and each step needs one
+// barrier.  Each wave owns 64 rows x 128 tokens (2 x 4
+// v_mfma_f32_32x32x16_bf16 per 16-wide slice).
 //
 // MFMA 32x32x16 operand layout (lane l, element j of the 8-element operand,
 // measured): A[m = l % 32][k = 8 (l / 32) + j], B[k = 8 (l / 32) + j][n = l % 32];
 // result element i holds D[m = 8 (i / 4) + 4 (l / 32) + i % 4][n = l % 32].
+// A direct-to-LDS load writes lane l's 16 bytes at the wave's LDS base plus
+// 16 l (measured).
 #pragma once
 
 #include <cstdint>
@@ -31,16 +39,26 @@
 
 namespace sv {
 
-constexpr int kLmM = 128;   // rows per tile
+constexpr int kLmM = 256;   // rows per tile
 constexpr int kLmN = 256;   // tokens per tile
-constexpr int kLmNI = kLmN / 64;  // 32-token MFMA blocks per wave (two waves across the tokens)
+constexpr int kLmWM = 4;    // waves across the rows
+constexpr int kLmWN = 2;    // waves across the tokens
+constexpr int kLmMI = kLmM / kLmWM / 32;  // 32-row MFMA blocks per wave
+constexpr int kLmNI = kLmN / kLmWN / 32;  // 32-token MFMA blocks per wave
 constexpr int kLmK = 32;    // hidden elements per step
-constexpr int kLmPad = 8;   // LDS row padding (bf16 elements)
-constexpr int kLmThreads = 256;
-constexpr int kLmPerCU = 2; // workgroups a compute unit holds (LDS)
+constexpr int kLmThreads = 64 * kLmWM * kLmWN;
+constexpr int kLmPerCU = 1; // workgroups a compute unit holds (LDS)
+constexpr int kLmStages = 3;                      // LDS ring depth
+constexpr int kLmChunks = kLmK / 8;               // 16-byte chunks per row and step
+constexpr int kLmStageA = kLmM * kLmChunks;       // chunks of hidden state per stage
+constexpr int kLmStage = (kLmM + kLmN) * kLmChunks;  // chunks per stage (24 KiB)
+constexpr int kLmDmaA = kLmStageA / kLmThreads;   // direct loads per thread and step (hidden)
+constexpr int kLmDmaW = kLmN * kLmChunks / kLmThreads;  // (unembedding)
+constexpr int kLmDma = kLmDmaA + kLmDmaW;
 
 typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float lm_float16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lm_lds_void;
 
 struct LmPart {
     float v;  // tile maximum of the row
@@ -55,7 +73,6 @@ struct LmArgs {
     int R, V, H;
     int n_vt;                 // vocabulary tiles, ceil(V / kLmN)
     int n_rt;                 // row tiles, ceil(R / kLmM)
-    int n_tiles;              // tile slots: ceil(n_vt / 8) * 8 * n_rt
     LmPart* part;             // argmax: [R][n_vt]
     int32_t* gidx;            // argmax: [R]
     uint16_t* logits;         // store: [R][V] bf16
@@ -72,136 +89,170 @@ __device__ __forceinline__ uint16_t lm_bf16_rne(float f) {
     return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+// Sixteen zero bytes: the source of every loaded chunk that lies outside the
+// operands (rows past R or V, columns past H).
+__device__ __attribute__((aligned(16))) const uint4 kLmZero16 = {0u, 0u, 0u, 0u};
+
+// LDS layout of a stage: the hidden rows' chunks, then the unembedding rows'
+// chunks, row-major, with the chunk index of row r XORed with lm_swz(r).
+// An operand fetch reads one chunk from each of 32 consecutive rows; the
+// swizzle spreads any 8 consecutive rows over the 32 banks of 128 bytes and
+// any 16 over 64 banks of 256 bytes (both bank widths are conflict-free).
+__device__ __forceinline__ int lm_swz(int r) {
+    return ((((r >> 2) ^ (r >> 3)) & 1) << 1) | (((r >> 1) ^ (r >> 2)) & 1);
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (direct-to-LDS loads count here), then meet the workgroup.
+// A plain s_barrier, not __syncthreads: the latter's release fence would
+// wait for every load in flight.
+template <int N>
+__device__ __forceinline__ void lm_wait_barrier() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0x0 << 8));
+    __builtin_amdgcn_s_barrier();
+}
+
+// Schedule.  Workgroup g serves XCD x = g % 8 as its member j = g / 8 of
+// GX = grid / 8: workgroups are dispatched to the 8 XCDs in turn (each XCD
+// with its own L2), so this keeps the row tiles of a vocabulary tile, which
+// read the same unembedding rows, on one XCD at about the same time.  XCD x
+// owns the vocabulary tiles vt = x, x + 8, ... and, for each, the n_rt row
+// tiles: its list of n_x tiles u = (vt / 8) n_rt + rt, of which member j
+// takes j, j + GX, ...  (Cutting the last partial round's tiles along the
+// hidden dimension over all members was measured slower: the fp32 partial
+// sums they must exchange through agent-scope memory cost more than the
+// idle members.)  Only the speed, not the result, depends on where the
+// workgroups run.
 template <int EPI>
 __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t sA[2][kLmM][kLmK + kLmPad];
-    __shared__ __attribute__((aligned(16))) uint16_t sW[2][kLmN][kLmK + kLmPad];
-    __shared__ LmPart sP[kLmM][2];
+    // the three ring stages are separate LDS objects, each named statically
+    // where it is used: the compiler then sees that a stage being read is not
+    // the one a load in flight writes, and adds no wait for that load
+    __shared__ __attribute__((aligned(16))) uint4 sT0[kLmStage];
+    __shared__ __attribute__((aligned(16))) uint4 sT1[kLmStage];
+    __shared__ __attribute__((aligned(16))) uint4 sT2[kLmStage];
+    __shared__ LmPart sP[kLmM][kLmWN];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
-    constexpr int kPerRow = kLmK / 8;                        // 16-byte pieces per row and step
-    constexpr int kPiecesA = kLmM * kPerRow / kLmThreads;    // 2
-    constexpr int kPiecesW = kLmN * kPerRow / kLmThreads;    // 4
+    const int wm = wave / kLmWN, wn = wave % kLmWN;
     const int n_steps = (a.H + kLmK - 1) / kLmK;
-    // Tile slot T = 8 (n_rt q + rt) + x holds row tile rt of vocabulary tile
-    // 8 q + x.  Workgroups are dispatched to the 8 XCDs in turn (workgroup L
-    // to XCD L mod 8, each XCD with its own L2) and the grid is a multiple of
-    // 8, so slot T always runs on XCD T mod 8: every row tile of a vocabulary
-    // tile runs on one XCD at about the same time and the unembedding rows
-    // come from HBM once.
-    for (int T = blockIdx.x; T < a.n_tiles; T += gridDim.x) {
-        const int x = T & 7, qr = T >> 3;
-        const int rt = qr % a.n_rt, vt = (qr / a.n_rt) * 8 + x;
-        if (vt >= a.n_vt) continue;  // padding slot (uniform over the workgroup)
+    // operand fetch: per-lane chunk offsets of the two 16-wide slices of a step
+    const int fr = lane & 31, fsw = lm_swz(fr);
+    const int fa0 = (wm * (kLmM / kLmWM) + fr) * kLmChunks, fw0 = kLmStageA + (wn * (kLmN / kLmWN) + fr) * kLmChunks;
+    const int fc0 = (0 + (lane >> 5)) ^ fsw, fc1 = (2 + (lane >> 5)) ^ fsw;
+    const int x = blockIdx.x & 7, j = blockIdx.x >> 3, GX = gridDim.x >> 3;
+    const int n_x = (x < a.n_vt ? (a.n_vt - x + 7) / 8 : 0) * a.n_rt;
+
+    lm_float16 acc[kLmMI][kLmNI];
+
+    // acc = the product of row tile rt and vocabulary tile vt
+    auto run = [&](int rt, int vt) {
         const int row0 = rt * kLmM, v0 = vt * kLmN;
-        lm_float16 acc[2][kLmNI];
 #pragma unroll
-        for (int mi = 0; mi < 2; ++mi)
+        for (int mi = 0; mi < kLmMI; ++mi)
 #pragma unroll
             for (int ni = 0; ni < kLmNI; ++ni)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
-        // rows past R or V and columns past H read as zero (no memory access)
-        struct Stage {
-            uint4 a[kPiecesA], w[kPiecesW];
+        // Direct loads: load q of wave w fills the 64 chunks of block
+        // b = (threads / 64) q + w of its region; lane l takes chunk position
+        // 64 b + l, i.e. row p / 4 and logical chunk (p % 4) ^ lm_swz(row).  A
+        // chunk outside the operands comes from kLmZero16.
+        const uint16_t* src[kLmDma];
+        int col[kLmDma];
+#pragma unroll
+        for (int q = 0; q < kLmDma; ++q) {
+            const bool isA = q < kLmDmaA;
+            const int b = (isA ? q : q - kLmDmaA) * (kLmThreads / 64) + wave, p = b * 64 + lane;
+            const int r = p / kLmChunks;
+            col[q] = ((p % kLmChunks) ^ lm_swz(r)) * 8;
+            if (isA) {
+                const int g = row0 + r;
+                src[q] = g >= a.R ? nullptr : g < a.R1 ? a.hidden + (size_t)g * a.H : a.hidden2 + (size_t)(g - a.R1) * a.H;
+            } else {
+                const int g = v0 + r;
+                src[q] = g >= a.V ? nullptr : a.w + (size_t)g * a.H;
+            }
+        }
+        // The hidden dimension is walked from a step that depends on the
+        // vocabulary tile: the row pitch is usually a large power of two, so
+        // tiles walking in lockstep would all read the same L2 channels.
+        const int rot = (int)(((unsigned)vt * 37u) % (unsigned)n_steps);
+        auto issue = [&](int s, uint4* base) {
+            const int h0 = s < n_steps ? ((s + rot) % n_steps) * kLmK : a.H;  // past the last step: zeros
+#pragma unroll
+            for (int q = 0; q < kLmDma; ++q) {
+                const bool isA = q < kLmDmaA;
+                const int b = (isA ? q : q - kLmDmaA) * (kLmThreads / 64) + wave;
+                const int h = h0 + col[q];
+                const void* g = (src[q] != nullptr && h < a.H) ? (const void*)(src[q] + h) : (const void*)&kLmZero16;
+                __builtin_amdgcn_global_load_lds(g, (lm_lds_void*)(base + (isA ? 0 : kLmStageA) + b * 64), 16, 0, 0);
+            }
         };
-        auto load = [&](int h0, Stage& g) {
-#pragma unroll
-            for (int q = 0; q < kPiecesA; ++q) {
-                const int e = tid + q * kLmThreads;
-                const int r = row0 + e / kPerRow, hh = h0 + (e % kPerRow) * 8;
-                g.a[q] = make_uint4(0u, 0u, 0u, 0u);
-                if (r < a.R && hh < a.H) {
-                    const uint16_t* hp = r < a.R1 ? a.hidden + (size_t)r * a.H : a.hidden2 + (size_t)(r - a.R1) * a.H;
-                    g.a[q] = *reinterpret_cast<const uint4*>(hp + hh);
-                }
-            }
-#pragma unroll
-            for (int q = 0; q < kPiecesW; ++q) {
-                const int e = tid + q * kLmThreads;
-                const int r = v0 + e / kPerRow, hh = h0 + (e % kPerRow) * 8;
-                g.w[q] = make_uint4(0u, 0u, 0u, 0u);
-                if (r < a.V && hh < a.H) g.w[q] = *reinterpret_cast<const uint4*>(a.w + (size_t)r * a.H + hh);
-            }
-        };
-        auto store = [&](int buf, const Stage& g) {
-#pragma unroll
-            for (int q = 0; q < kPiecesA; ++q) {
-                const int e = tid + q * kLmThreads;
-                *reinterpret_cast<uint4*>(&sA[buf][e / kPerRow][(e % kPerRow) * 8]) = g.a[q];
-            }
-#pragma unroll
-            for (int q = 0; q < kPiecesW; ++q) {
-                const int e = tid + q * kLmThreads;
-                *reinterpret_cast<uint4*>(&sW[buf][e / kPerRow][(e % kPerRow) * 8]) = g.w[q];
-            }
-        };
-        auto compute = [&](int cur) {
+        auto compute = [&](const uint4* st) {
 #pragma unroll
             for (int ks = 0; ks < kLmK / 16; ++ks) {
-                const int kc = ks * 16 + (lane >> 5) * 8;
-                lm_bf16x8 fa[2], fb[kLmNI];
+                const int fc = ks == 0 ? fc0 : fc1;
+                lm_bf16x8 fa[kLmMI], fb[kLmNI];
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
-                    fa[mi] = __builtin_bit_cast(
-                        lm_bf16x8, *reinterpret_cast<const uint4*>(&sA[cur][wm * 64 + mi * 32 + (lane & 31)][kc]));
+                for (int mi = 0; mi < kLmMI; ++mi)
+                    fa[mi] = __builtin_bit_cast(lm_bf16x8, st[fa0 + mi * 32 * kLmChunks + fc]);
 #pragma unroll
                 for (int ni = 0; ni < kLmNI; ++ni)
-                    fb[ni] = __builtin_bit_cast(
-                        lm_bf16x8,
-                        *reinterpret_cast<const uint4*>(&sW[cur][wn * (kLmN / 2) + ni * 32 + (lane & 31)][kc]));
+                    fb[ni] = __builtin_bit_cast(lm_bf16x8, st[fw0 + ni * 32 * kLmChunks + fc]);
 #pragma unroll
-                for (int mi = 0; mi < 2; ++mi)
+                for (int mi = 0; mi < kLmMI; ++mi)
 #pragma unroll
                     for (int ni = 0; ni < kLmNI; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
             }
         };
-        // Loads run two steps ahead in two register stages: step s multiplies
-        // buffer s & 1 while the loads of steps s + 1 (issued during step s - 1)
-        // and s + 2 (issued now) are in flight; the stage of step s + 1 is
-        // stored into the other buffer, last read in step s - 1, after the
-        // multiply.  Steps are unrolled in pairs so that the register stages
-        // stay fixed.
-        Stage g0, g1;
-        load(0, g0);
-        if (n_steps > 1) load(kLmK, g1);
-        store(0, g0);
-        __syncthreads();
-        for (int s = 0; s < n_steps; s += 2) {
-            // step s: buffer 0; g1 holds step s + 1
-            if (s + 2 < n_steps) load((s + 2) * kLmK, g0);
-            compute(0);
-            if (s + 1 < n_steps) store(1, g1);
-            __syncthreads();
-            if (s + 1 >= n_steps) break;
-            // step s + 1: buffer 1; g0 holds step s + 2
-            if (s + 3 < n_steps) load((s + 3) * kLmK, g1);
-            compute(1);
-            if (s + 2 < n_steps) store(0, g0);
-            __syncthreads();
+        // Step s multiplies stage s % 3.  Before it, each wave waits
+        // for its own loads of step s (those of step s + 1 stay in flight)
+        // and the barrier makes every wave's loads visible; it also shows
+        // that every wave has finished step s - 1, whose stage then takes the
+        // loads of step s + 2.  Steps run in threes so that each stage is
+        // named statically, and the loop has one exit, at its bottom: the
+        // steps past the last (at most two) load zeros and add nothing.
+        auto step = [&](int s, const uint4* rd, uint4* wr) {
+            lm_wait_barrier<kLmDma>();
+            issue(s + 2, wr);
+            compute(rd);
+        };
+        issue(0, sT0);
+        issue(1, sT1);
+        for (int s = 0; s < n_steps; s += 3) {
+            step(s, sT0, sT2);
+            step(s + 1, sT1, sT0);
+            step(s + 2, sT2, sT1);
         }
+        // Before the ring is refilled: every wave is done reading it and
+        // this wave's loads (and stores) have drained.
+        lm_wait_barrier<0>();
+    };
 
+    auto epilogue = [&](int rt, int vt) {
+        const int row0 = rt * kLmM, v0 = vt * kLmN;
         if constexpr (EPI == LM_STORE) {
             // bf16 logits: lanes of a half-wave hold 32 consecutive tokens of one row
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi)
+            for (int mi = 0; mi < kLmMI; ++mi)
 #pragma unroll
                 for (int ni = 0; ni < kLmNI; ++ni)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int r = row0 + wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                        const int n = v0 + wn * (kLmN / 2) + ni * 32 + (lane & 31);
+                        const int r = row0 + wm * (kLmM / kLmWM) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                        const int n = v0 + wn * (kLmN / kLmWN) + ni * 32 + (lane & 31);
                         if (r < a.R && n < a.V) a.logits[(size_t)r * a.V + n] = lm_bf16_rne(acc[mi][ni][i]);
                     }
         } else {
-            // per row of this wave's block: the best over its 128 tokens (the
-            // four column blocks, then the 32 lanes of the half-wave holding the row)
+            // per row of this wave's block: the best over its tokens (the
+            // column blocks, then the 32 lanes of the half-wave holding the row)
 #pragma unroll
-            for (int mi = 0; mi < 2; ++mi) {
+            for (int mi = 0; mi < kLmMI; ++mi) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int n0 = v0 + wn * (kLmN / 2) + (lane & 31);
+                    const int n0 = v0 + wn * (kLmN / kLmWN) + (lane & 31);
                     float bv = n0 < a.V ? acc[mi][0][i] : -INFINITY;
                     int bi = n0 < a.V ? n0 : INT32_MAX;
 #pragma unroll
@@ -222,18 +273,28 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
                         }
                     }
                     if ((lane & 31) == 0)
-                        sP[wm * 64 + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)][wn] = LmPart{bv, bi};
+                        sP[wm * (kLmM / kLmWM) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)][wn] = LmPart{bv, bi};
                 }
             }
             __syncthreads();
-            if (tid < kLmM && row0 + tid < a.R) {
-                LmPart p = sP[tid][0];
-                const LmPart q = sP[tid][1];
-                if (lm_better(q.v, q.i, p.v, p.i)) p = q;
-                a.part[(size_t)(row0 + tid) * a.n_vt + vt] = p;
+            for (int r = tid; r < kLmM; r += kLmThreads) {
+                if (row0 + r >= a.R) break;
+                LmPart p = sP[r][0];
+#pragma unroll
+                for (int jj = 1; jj < kLmWN; ++jj) {
+                    const LmPart q = sP[r][jj];
+                    if (lm_better(q.v, q.i, p.v, p.i)) p = q;
+                }
+                a.part[(size_t)(row0 + r) * a.n_vt + vt] = p;
             }
             __syncthreads();  // sP is written again by the next tile
         }
+    };
+
+    for (int u = j; u < n_x; u += GX) {
+        const int rt = u % a.n_rt, vt = (u / a.n_rt) * 8 + x;
+        run(rt, vt);
+        epilogue(rt, vt);
     }
 }
 

@@ -459,16 +459,18 @@ LmArgs lm_args(const void* hidden, const void* hidden2, long long R1, long long 
     la.H = H;
     la.n_vt = (int)ceil_div(V, kLmN);
     la.n_rt = (int)ceil_div(R, kLmM);
-    la.n_tiles = (int)(ceil_div(la.n_vt, 8) * 8 * la.n_rt);
     return la;
 }
 
+// Workgroups of a k_lmhead launch: as many as the GPU holds at once, a
+// multiple of 8 (k_lmhead serves the XCDs in turn).
+long long lm_grid(int n_cu) { return std::max<long long>(8, (long long)kLmPerCU * n_cu / 8 * 8); }
+
 // Persistent launch: the workgroups the GPU holds at once (a multiple of 8,
-// see k_lmhead), or fewer when the tiles are fewer.  A measurement event pair,
-// if armed, is attached to this dispatch.
+// see k_lmhead).  A measurement event pair, if armed, is attached to this
+// dispatch.
 int launch_lm(int epi, const LmArgs& la, int n_cu, hipStream_t st) {
-    long long grid = std::min<long long>(la.n_tiles, (long long)kLmPerCU * n_cu);
-    grid = std::max<long long>(8, grid / 8 * 8);
+    const long long grid = lm_grid(n_cu);
     void *evb, *eva;
     take_events(&evb, &eva);
     if (epi == LM_STORE)

@@ -17,7 +17,6 @@
 //              threshold, p(d_k) or q(d_k)) and, for target rows of drafted
 //              sequences, the kept tokens sorted by index (token trees draw
 //              from the stop row itself and skip the lists).
-//  k_row_merge  : the record of an unfiltered row split over workgroups.
 //  k_row_argmax : greedy mode, lowest-index argmax of a target row.
 //
 // Row numbering: rows [0, B*(K+1)) are target rows b*(K+1)+k, rows
@@ -355,6 +354,7 @@ struct PartRec {
 };
 constexpr int kPartTiles = 4;             // tiles of one part, loaded together
 constexpr int kMaxParts = 16;             // parts of one row at most
+constexpr int kSplitRows = 512;           // rows are split only when fewer than this
 
 struct RowArgs {
     Shape sh;
@@ -375,6 +375,7 @@ struct RowArgs {
     int drafts_first;   // draft rows take the first workgroups (see k_row)
     int parts;          // > 1: unfiltered rows split into this many parts (one workgroup each)
     PartRec* prec;      // [rows][parts]
+    unsigned* part_cnt; // [kSplitRows] arrival counters of the parts (zero between calls)
     unsigned* draw_cnt; // [n_cnt] arrival counters of the draw kernel, cleared by the first workgroup
     int n_cnt;
 };
@@ -1687,10 +1688,48 @@ __device__ __forceinline__ void row_body(const RowArgs& a, RowShared& S, int row
     }
 }
 
+// The record of a split unfiltered row from its parts, combined in part
+// order (one thread; the parts' records were stored with agent-scope stores
+// before their arrivals were counted).
+__device__ __forceinline__ void merge_row(const RowArgs& a, int row) {
+    RowTot t{-INFINITY, -INFINITY, 0.0, 0ull};
+    for (int p = 0; p < a.parts; ++p) {
+        const PartRec* q = a.prec + (size_t)row * a.parts + p;
+        const float qm = __hip_atomic_load(&q->m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float qk = __hip_atomic_load(&q->k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const double qz = __hip_atomic_load(&q->z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t = row_tot_combine(t, RowTot{qm, qk, qz, 0ull});
+    }
+    const float M = t.m;
+    const double Z = t.k != -INFINITY ? t.z * exp2(8.0 * (double)t.k - (double)M * (double)a.c_hi) : 0.0;
+    const int V = a.sh.V;
+    RowRec r;
+    r.s.max_logit = M;
+    r.z_all = Z;
+    r.pad = 0.0;
+    r.s.thresh = -INFINITY;
+    r.s.n_kept = V;
+    r.s.flags = 0;
+    r.s.z_kept = Z;
+    double prob = __longlong_as_double(0x7FF8000000000000LL);  // NaN: no drafted token
+    if (row_has_token(a.sh, row)) {
+        prob = 0.0;
+        const int d_tok = row_token(a.sh, row);
+        if (d_tok >= 0 && d_tok < V) {
+            const float xd = load_logit(row_ptr(a.sh, row), row_dt(a.sh, row), d_tok);
+            prob = exp(((double)xd - (double)M) * a.inv_T) / Z;
+        }
+    }
+    r.s.prob_at_token = prob;
+    a.rec[row] = r;
+}
+
 // One part of an unfiltered row (few rows: each is split across `parts`
 // workgroups so that the whole GPU streams).  The part's up to kPartTiles
-// tiles are loaded together; its maximum and power-of-two sum go to prec and
-// k_row_merge combines the parts in order.
+// tiles are loaded together; its maximum and power-of-two sum go to prec,
+// and the last of the row's parts to arrive (an arrival counter per row,
+// reset by that part) builds the row's record from all of them, so that the
+// split costs no launch of its own.
 template <int DT>
 __device__ __forceinline__ void row_part_plain(const RowArgs& a, RowShared& S, int row, int part) {
     const char* rowp = row_ptr(a.sh, row);
@@ -1732,41 +1771,18 @@ __device__ __forceinline__ void row_part_plain(const RowArgs& a, RowShared& S, i
         }
     }
     const RowTot tot = rb_row_totals(RowTot{m_th, k_th, z_th, 0ull}, S);
-    if (threadIdx.x == 0) a.prec[(size_t)row * a.parts + part] = PartRec{tot.m, tot.k, tot.z};
-}
-
-// The record of each split unfiltered row from its parts (combined in part
-// order): one thread per row.
-__global__ void __launch_bounds__(256) k_row_merge(RowArgs a) {
-    const int row = blockIdx.x * blockDim.x + threadIdx.x;
-    if (row >= a.sh.n_trows + a.sh.n_drows || !row_live(a.sh, row)) return;
-    RowTot t{-INFINITY, -INFINITY, 0.0, 0ull};
-    for (int p = 0; p < a.parts; ++p) {
-        const PartRec q = a.prec[(size_t)row * a.parts + p];
-        t = row_tot_combine(t, RowTot{q.m, q.k, q.z, 0ull});
-    }
-    const float M = t.m;
-    const double Z = t.k != -INFINITY ? t.z * exp2(8.0 * (double)t.k - (double)M * (double)a.c_hi) : 0.0;
-    const int V = a.sh.V;
-    RowRec r;
-    r.s.max_logit = M;
-    r.z_all = Z;
-    r.pad = 0.0;
-    r.s.thresh = -INFINITY;
-    r.s.n_kept = V;
-    r.s.flags = 0;
-    r.s.z_kept = Z;
-    double prob = __longlong_as_double(0x7FF8000000000000LL);  // NaN: no drafted token
-    if (row_has_token(a.sh, row)) {
-        prob = 0.0;
-        const int d_tok = row_token(a.sh, row);
-        if (d_tok >= 0 && d_tok < V) {
-            const float xd = load_logit(row_ptr(a.sh, row), row_dt(a.sh, row), d_tok);
-            prob = exp(((double)xd - (double)M) * a.inv_T) / Z;
+    if (threadIdx.x == 0) {
+        PartRec* q = a.prec + (size_t)row * a.parts + part;
+        __hip_atomic_store(&q->m, tot.m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&q->k, tot.k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(&q->z, tot.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_s_waitcnt(0x0F70);  // the stores are complete before the arrival counts
+        const unsigned n = __hip_atomic_fetch_add(&a.part_cnt[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (n == (unsigned)(a.parts - 1)) {
+            merge_row(a, row);
+            __hip_atomic_store(&a.part_cnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
-    r.s.prob_at_token = prob;
-    a.rec[row] = r;
 }
 
 __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {

@@ -21,9 +21,12 @@ using namespace sv;
 // Library-owned scratch for one (device, stream): row records, kept lists of
 // filtered target rows (with p and the draft logit of each listed token), greedy
 // argmax indices, chunk records and arrival counters of the unfiltered draw,
-// and the stops of token-tree walks.  Every kernel writes what it later reads
-// within the same call; the arrival counters are zeroed when the workspace is
-// allocated and left at zero by the kernel that counts with them.
+// the parts of split rows and their arrival counters, and the stops of
+// token-tree walks.  Every kernel writes what it later reads within the same
+// call.  The draw's arrival counters are cleared by the row kernel before the
+// draw runs; the split rows' counters, which the row kernel itself counts
+// with, sit at offset 0 of every layout, are zero when the memory is fresh
+// and are left at zero by the part that merges.
 struct Caps {
     size_t rows = 0;         // row records (and split-row partials)
     size_t lists = 0;        // target rows with stored kept lists
@@ -49,6 +52,7 @@ struct Workspace {
     void* chunks = nullptr;
     unsigned* draw_cnt = nullptr;
     PartRec* prec = nullptr;
+    unsigned* part_cnt = nullptr;
     TreeStop* tstop = nullptr;
     int32_t* tex = nullptr;
     int n_cu = 0;  // compute units of the device
@@ -63,10 +67,12 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 
 // Byte offsets of the workspace parts for the capacities c; returns the total.
 struct Offsets {
-    size_t rec, kept, kn, kd, kp, g, cs, cnt, pr, ts, tx;
+    size_t pc, rec, kept, kn, kd, kp, g, cs, cnt, pr, ts, tx;
 };
+constexpr size_t kPartCntBytes = kSplitRows * sizeof(unsigned);
 size_t layout(const Caps& c, Offsets& o) {
     size_t off = 0;
+    o.pc = off; off = align_up(off + kPartCntBytes);  // first, at a fixed place
     o.rec = off; off = align_up(off + c.rows * sizeof(RowRec));
     o.kept = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(uint2));
     o.kn = off; off = align_up(off + c.lists * sizeof(int));
@@ -92,6 +98,7 @@ void carve(char* b, const Caps& c, const Offsets& o, Workspace& w) {
     w.chunks = b + o.cs;
     w.draw_cnt = reinterpret_cast<unsigned*>(b + o.cnt);
     w.prec = reinterpret_cast<PartRec*>(b + o.pr);
+    w.part_cnt = reinterpret_cast<unsigned*>(b + o.pc);
     w.tstop = reinterpret_cast<TreeStop*>(b + o.ts);
     w.tex = reinterpret_cast<int32_t*>(b + o.tx);
 }
@@ -125,6 +132,10 @@ int get_workspace(hipStream_t stream, const Caps& need, Workspace** out) {
         return SPEC_E_LAUNCH;
     void* base = nullptr;
     if (hipMalloc(&base, total) != hipSuccess) return SPEC_E_NOMEM;
+    if (hipMemsetAsync(base, 0, kPartCntBytes, stream) != hipSuccess) {
+        (void)hipFree(base);
+        return SPEC_E_LAUNCH;
+    }
     Workspace nw;
     carve(static_cast<char*>(base), c, o, nw);
     nw.n_cu = n_cu;
@@ -356,16 +367,18 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     // two row workgroups fit on a compute unit (their LDS)
     ra.drafts_first = n_drows > 0 && rows > 2 * ws->n_cu ? 1 : 0;
     // Few unfiltered rows: split each across workgroups (at most kPartTiles
-    // tiles each) so that about 512 workgroups stream, then merge per row.
+    // tiles each) so that about 512 workgroups stream; the last part of each
+    // row to finish merges them.
     ra.parts = 1;
     ra.prec = ws->prec;
+    ra.part_cnt = ws->part_cnt;
     ra.draw_cnt = ws->draw_cnt;
     ra.n_cnt = B;
     if (!filtered) {
         const int nt = (int)ceil_div(V, kRTile);
         const int want = (int)std::min<long long>(kMaxParts, ceil_div(512, rows));
         const int tpp = (int)ceil_div(nt, std::max(1, want));
-        if (want > 1 && tpp <= kPartTiles) ra.parts = (int)ceil_div(nt, tpp);
+        if (want > 1 && tpp <= kPartTiles && rows < kSplitRows) ra.parts = (int)ceil_div(nt, tpp);
     }
 
     void *evb, *eva;
@@ -375,10 +388,6 @@ int run_sampling(const void* target, const void* draft, const int32_t* tokens, i
     hipExtLaunchKernelGGL(k_row, dim3((unsigned)((long long)rows * ra.parts)), dim3(kRB), 0, stream,
                           static_cast<hipEvent_t>(evb), static_cast<hipEvent_t>(eva), 0, ra);
     if ((rc = launch_status())) return rc;
-    if (ra.parts > 1) {
-        hipLaunchKernelGGL(k_row_merge, dim3((unsigned)ceil_div(rows, 256)), dim3(256), 0, stream, ra);
-        if ((rc = launch_status())) return rc;
-    }
 
     SeqArgs sa;
     sa.sh = sh;

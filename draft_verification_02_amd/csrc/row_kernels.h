@@ -375,8 +375,8 @@ struct RowArgs {
     int drafts_first;   // draft rows take the first workgroups (see k_row)
     int parts;          // > 1: unfiltered rows split into this many parts (one workgroup each)
     PartRec* prec;      // [rows][parts]
-    unsigned* part_cnt; // [kSplitRows] arrival counters of the parts (zero between calls)
-    unsigned* draw_cnt; // [n_cnt] arrival counters of the draw kernel, cleared by the first workgroup
+    unsigned* part_cnt; // [kSplitRows * kCntStride] arrival counters of the parts (zero between calls)
+    unsigned* draw_cnt; // [n_cnt * kCntStride] arrival counters of the draw kernel, cleared by the first workgroup
     int n_cnt;
 };
 
@@ -1777,10 +1777,11 @@ __device__ __forceinline__ void row_part_plain(const RowArgs& a, RowShared& S, i
         __hip_atomic_store(&q->k, tot.k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(&q->z, tot.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __builtin_amdgcn_s_waitcnt(0x0F70);  // the stores are complete before the arrival counts
-        const unsigned n = __hip_atomic_fetch_add(&a.part_cnt[row], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        unsigned* const cnt = a.part_cnt + (size_t)row * kCntStride;
+        const unsigned n = __hip_atomic_fetch_add(cnt, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (n == (unsigned)(a.parts - 1)) {
             merge_row(a, row);
-            __hip_atomic_store(&a.part_cnt[row], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(cnt, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -1790,7 +1791,7 @@ __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
     clear_counters(a.sh);
     // the draw kernel's arrival counters start from zero (it runs after this kernel)
     if (blockIdx.x == 0)
-        for (int i = threadIdx.x; i < a.n_cnt; i += kRB) a.draw_cnt[i] = 0u;
+        for (int i = threadIdx.x; i < a.n_cnt; i += kRB) a.draw_cnt[(size_t)i * kCntStride] = 0u;
     if (a.parts > 1) {
         const int row = blockIdx.x / a.parts, part = blockIdx.x % a.parts;
         if (!row_live(a.sh, row)) return;

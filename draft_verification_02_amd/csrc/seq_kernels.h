@@ -49,7 +49,7 @@ struct SeqArgs {
     const float* kept_d;  // draft logit of each listed token (stop positions j < K)
     const double* kept_p; // p of each listed token
     DrawChunk* chunks;         // [B][n_chunks] chunk records of the unfiltered draw
-    unsigned* draw_cnt;   // [B] arrival counters of the chunk workgroups (zero between calls)
+    unsigned* draw_cnt;   // [B * kCntStride] arrival counters of the chunk workgroups (zero between calls)
     int n_chunks;
     int32_t* out_tokens;
     int32_t* out_num;
@@ -536,26 +536,15 @@ __device__ __forceinline__ void load_run(const char* row, int lo, int V, float (
 }
 
 // fp64 weights of the kCPT tokens from lo on: e_t (0 where the target row
-// does not keep the token), e_d (0 without a draft row or where it does not
-// keep it) and the bit mask of removed tokens (a point-mass draft's token, a
-// token tree's rejected children).  The same arithmetic wherever a chunk is
-// summed or searched.
+// does not keep the token) and e_d (0 without a draft row or where it does
+// not keep it).  The same arithmetic wherever a chunk is summed or searched.
 template <int TDT, int DDT>
 __device__ __forceinline__ void run_weights(const StopRow& s, double inv_T, int lo, int V, double (&et)[kCPT],
-                                            double (&ed)[kCPT], uint32_t& rm) {
+                                            double (&ed)[kCPT]) {
     float xt[kCPT], xd[kCPT];
     load_run<TDT>(s.tp, lo, V, xt);
     // without a draft row the target row is read again and ignored
     load_run<DDT>(s.has_draft ? s.dp : s.tp, lo, V, xd);
-    rm = 0u;
-    for (int e = 0; e < s.n_ex; ++e) {
-        const uint32_t d = (uint32_t)(s.ex[e] - lo);
-        if (d < (uint32_t)kCPT) rm |= 1u << d;
-    }
-    {
-        const uint32_t d = (uint32_t)(s.dtok - lo);
-        if (s.dtok >= 0 && d < (uint32_t)kCPT) rm |= 1u << d;
-    }
 #pragma unroll
     for (int e = 0; e < kCPT; ++e) {
         et[e] = xt[e] >= s.thr_t ? exp(((double)xt[e] - (double)s.Mt) * inv_T) : 0.0;
@@ -660,7 +649,32 @@ struct DrawShared {
     int j, cstar, last, tau;
     int s_last[kSB / 64], s_first[kSB / 64];
     int scan[kSB / 64];
+    uint32_t removed[kChunk / 32];  // bitmap of the removed tokens of one chunk
 };
+
+// Bit e set: token lo + e (e < kCPT) of chunk cc is removed from p: a token
+// tree's rejected children, marked in an LDS bitmap of the chunk (the
+// workgroup shares out the list), or a point-mass draft's token.  Called by
+// the whole workgroup.
+__device__ __forceinline__ uint32_t removed_bits(const StopRow& s, int cc, int lo, DrawShared& S) {
+    uint32_t rm = 0u;
+    if (s.n_ex > 0) {
+        __syncthreads();  // earlier readers of the bitmap are done
+        for (int i = threadIdx.x; i < kChunk / 32; i += kSB) S.removed[i] = 0u;
+        __syncthreads();
+        for (int e = threadIdx.x; e < s.n_ex; e += kSB) {
+            const uint32_t d = (uint32_t)(s.ex[e] - cc * kChunk);
+            if (d < (uint32_t)kChunk) atomicOr(&S.removed[d >> 5], 1u << (d & 31));
+        }
+        __syncthreads();
+        const int off = lo - cc * kChunk;  // a multiple of kCPT: the kCPT bits share a word
+        rm = (S.removed[off >> 5] >> (off & 31)) & ((1u << kCPT) - 1u);
+    }
+    const uint32_t d = (uint32_t)(s.dtok - lo);
+    if (s.dtok >= 0 && d < (uint32_t)kCPT) rm |= 1u << d;
+    return rm;
+}
+static_assert(kChunk % 32 == 0 && 32 % kCPT == 0, "a thread's tokens share a bitmap word");
 
 // The thread whose mass range holds t: the last one with mass starting at or
 // before t; if rounding put t before all of them, the first one with mass.
@@ -707,8 +721,8 @@ template <int TDT, int DDT>
 __device__ __forceinline__ double chunk_mass_recomputed(const StopRow& s, double inv_T, int V, int cc, bool usep,
                                                         double rho, DrawShared& S) {
     double et[kCPT], ed[kCPT];
-    uint32_t rm;
-    run_weights<TDT, DDT>(s, inv_T, cc * kChunk + (int)threadIdx.x * kCPT, V, et, ed, rm);
+    const uint32_t rm = removed_bits(s, cc, cc * kChunk + (int)threadIdx.x * kCPT, S);
+    run_weights<TDT, DDT>(s, inv_T, cc * kChunk + (int)threadIdx.x * kCPT, V, et, ed);
     double m[1] = {0.0};
 #pragma unroll
     for (int e = 0; e < kCPT; ++e) m[0] += usep ? et[e] : res_weight(s.has_draft, et[e], ed[e], (rm >> e) & 1u, rho);
@@ -809,8 +823,8 @@ __device__ __forceinline__ void draw_pick(const SeqArgs& a, int b, int j, const 
     // the token inside chunk cstar, from the same per-token weights
     const int lo = cstar * kChunk + (int)threadIdx.x * kCPT;
     double et[kCPT], ed[kCPT], w[kCPT];
-    uint32_t rm;
-    run_weights<TDT, DDT>(s, a.inv_T, lo, V, et, ed, rm);
+    const uint32_t rm = removed_bits(s, cstar, lo, S);
+    run_weights<TDT, DDT>(s, a.inv_T, lo, V, et, ed);
     double mine = 0.0;
 #pragma unroll
     for (int e = 0; e < kCPT; ++e) {
@@ -857,8 +871,8 @@ __global__ void __launch_bounds__(kSB) k_draw(SeqArgs a) {
     with_dtypes(s, [&](auto tt, auto dt) {
         constexpr int TDT = decltype(tt)::value, DDT = decltype(dt)::value;
         double et[kCPT], ed[kCPT];
-        uint32_t rm;
-        run_weights<TDT, DDT>(s, a.inv_T, c * kChunk + (int)threadIdx.x * kCPT, a.sh.V, et, ed, rm);
+        const uint32_t rm = removed_bits(s, c, c * kChunk + (int)threadIdx.x * kCPT, S);
+        run_weights<TDT, DDT>(s, a.inv_T, c * kChunk + (int)threadIdx.x * kCPT, a.sh.V, et, ed);
         double v[4] = {0.0, 0.0, 0.0, 0.0};  // zt, zd, a, b
         int amb = 0;                          // this thread's unsettled tokens (bit mask)
 #pragma unroll
@@ -903,14 +917,14 @@ __global__ void __launch_bounds__(kSB) k_draw(SeqArgs a) {
     wait_stores();
     __syncthreads();
     if (threadIdx.x == 0)
-        S.last = __hip_atomic_fetch_add(&a.draw_cnt[b], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+        S.last = __hip_atomic_fetch_add(&a.draw_cnt[(size_t)b * kCntStride], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
                  (unsigned)(a.n_chunks - 1);
     __syncthreads();
     if (!S.last) return;
     with_dtypes(s, [&](auto tt, auto dt) {
         draw_pick<kTree, decltype(tt)::value, decltype(dt)::value>(a, b, j, s, rt, S);
     });
-    if (threadIdx.x == 0) a.draw_cnt[b] = 0u;
+    if (threadIdx.x == 0) a.draw_cnt[(size_t)b * kCntStride] = 0u;
 }
 
 // ---------------------------------------------------------------------------

@@ -69,7 +69,7 @@ size_t align_up(size_t x) { return (x + 255) & ~size_t(255); }
 struct Offsets {
     size_t pc, rec, kept, kn, kd, kp, g, cs, cnt, pr, ts, tx;
 };
-constexpr size_t kPartCntBytes = kSplitRows * sizeof(unsigned);
+constexpr size_t kPartCntBytes = (size_t)kSplitRows * kCntStride * sizeof(unsigned);
 size_t layout(const Caps& c, Offsets& o) {
     size_t off = 0;
     o.pc = off; off = align_up(off + kPartCntBytes);  // first, at a fixed place
@@ -80,7 +80,7 @@ size_t layout(const Caps& c, Offsets& o) {
     o.kp = off; off = align_up(off + c.lists * (size_t)kListMax * sizeof(double));
     o.g = off; off = align_up(off + c.gidx * sizeof(int32_t));
     o.cs = off; off = align_up(off + c.chunk_bytes);
-    o.cnt = off; off = align_up(off + c.seqs * sizeof(unsigned));
+    o.cnt = off; off = align_up(off + c.seqs * kCntStride * sizeof(unsigned));
     o.pr = off; off = align_up(off + c.rows * (size_t)kMaxParts * sizeof(PartRec));
     o.ts = off; off = align_up(off + c.seqs * sizeof(TreeStop));
     o.tx = off; off = align_up(off + c.nodes * sizeof(int32_t));

@@ -34,6 +34,7 @@
 #pragma once
 
 #include <cstdint>
+#include <type_traits>
 
 #include "device_common.h"
 
@@ -73,7 +74,7 @@ struct LmArgs {
     int R, V, H;
     int n_vt;                 // vocabulary tiles, ceil(V / kLmN)
     int n_rt;                 // row tiles, ceil(R / kLmM)
-    LmPart* part;             // argmax: [R][n_vt]
+    LmPart* part;             // argmax: [R][2 n_vt], one entry per half tile
     int32_t* gidx;            // argmax: [R]
     uint16_t* logits;         // store: [R][V] bf16
 };
@@ -119,9 +120,10 @@ __device__ __forceinline__ void lm_wait_barrier() {
 // read the same unembedding rows, on one XCD at about the same time.  XCD x
 // owns the vocabulary tiles vt = x, x + 8, ... and, for each, the n_rt row
 // tiles: its list of n_x tiles u = (vt / 8) n_rt + rt, of which member j
-// takes j, j + GX, ...  (Cutting the last partial round's tiles along the
-// hidden dimension over all members was measured slower: the fp32 partial
-// sums they must exchange through agent-scope memory cost more than the
+// takes j, j + GX, ...; the tiles of a last partial round are cut into
+// half tiles when that keeps more members busy (below).  (Cutting them along
+// the hidden dimension instead was measured slower: the fp32 partial sums
+// the pieces must exchange through agent-scope memory cost more than the
 // idle members.)  Only the speed, not the result, depends on where the
 // workgroups run.
 template <int EPI>
@@ -138,30 +140,38 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
     const int n_steps = (a.H + kLmK - 1) / kLmK;
     // operand fetch: per-lane chunk offsets of the two 16-wide slices of a step
     const int fr = lane & 31, fsw = lm_swz(fr);
-    const int fa0 = (wm * (kLmM / kLmWM) + fr) * kLmChunks, fw0 = kLmStageA + (wn * (kLmN / kLmWN) + fr) * kLmChunks;
+    const int fa0 = (wm * (kLmM / kLmWM) + fr) * kLmChunks;
     const int fc0 = (0 + (lane >> 5)) ^ fsw, fc1 = (2 + (lane >> 5)) ^ fsw;
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3, GX = gridDim.x >> 3;
     const int n_x = (x < a.n_vt ? (a.n_vt - x + 7) / 8 : 0) * a.n_rt;
 
     lm_float16 acc[kLmMI][kLmNI];
 
-    // acc = the product of row tile rt and vocabulary tile vt
-    auto run = [&](int rt, int vt) {
-        const int row0 = rt * kLmM, v0 = vt * kLmN;
+    // acc = the product of row tile rt and tokens [t0, t0 + width) of
+    // vocabulary tile vt; width = kLmN, or kLmN / 2 for a half tile (HALF:
+    // only the first half of the unembedding stage is loaded, and each wave
+    // keeps kLmNI / 2 column blocks).
+    auto run = [&](auto half_c, int rt, int vt, int t0) {
+        constexpr bool HALF = decltype(half_c)::value;
+        constexpr int NI = HALF ? kLmNI / 2 : kLmNI;
+        constexpr int DW = HALF ? kLmDmaW / 2 : kLmDmaW;  // unembedding loads per thread and step
+        constexpr int DMA = kLmDmaA + DW;
+        const int row0 = rt * kLmM, v0 = vt * kLmN + t0;
+        const int fw0 = kLmStageA + (wn * (NI * 32) + fr) * kLmChunks;
 #pragma unroll
         for (int mi = 0; mi < kLmMI; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < kLmNI; ++ni)
+            for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
         // Direct loads: load q of wave w fills the 64 chunks of block
         // b = (threads / 64) q + w of its region; lane l takes chunk position
         // 64 b + l, i.e. row p / 4 and logical chunk (p % 4) ^ lm_swz(row).  A
         // chunk outside the operands comes from kLmZero16.
-        const uint16_t* src[kLmDma];
-        int col[kLmDma];
+        const uint16_t* src[DMA];
+        int col[DMA];
 #pragma unroll
-        for (int q = 0; q < kLmDma; ++q) {
+        for (int q = 0; q < DMA; ++q) {
             const bool isA = q < kLmDmaA;
             const int b = (isA ? q : q - kLmDmaA) * (kLmThreads / 64) + wave, p = b * 64 + lane;
             const int r = p / kLmChunks;
@@ -176,12 +186,15 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
         }
         // The hidden dimension is walked from a step that depends on the
         // vocabulary tile: the row pitch is usually a large power of two, so
-        // tiles walking in lockstep would all read the same L2 channels.
+        // tiles walking in lockstep would all read the same L2 channels.  The
+        // order depends on the token alone (both halves of a tile walk alike),
+        // so the logits of a token are the same whatever the rows, the tiling
+        // or the epilogue.
         const int rot = (int)(((unsigned)vt * 37u) % (unsigned)n_steps);
         auto issue = [&](int s, uint4* base) {
             const int h0 = s < n_steps ? ((s + rot) % n_steps) * kLmK : a.H;  // past the last step: zeros
 #pragma unroll
-            for (int q = 0; q < kLmDma; ++q) {
+            for (int q = 0; q < DMA; ++q) {
                 const bool isA = q < kLmDmaA;
                 const int b = (isA ? q : q - kLmDmaA) * (kLmThreads / 64) + wave;
                 const int h = h0 + col[q];
@@ -193,29 +206,29 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
 #pragma unroll
             for (int ks = 0; ks < kLmK / 16; ++ks) {
                 const int fc = ks == 0 ? fc0 : fc1;
-                lm_bf16x8 fa[kLmMI], fb[kLmNI];
+                lm_bf16x8 fa[kLmMI], fb[NI];
 #pragma unroll
                 for (int mi = 0; mi < kLmMI; ++mi)
                     fa[mi] = __builtin_bit_cast(lm_bf16x8, st[fa0 + mi * 32 * kLmChunks + fc]);
 #pragma unroll
-                for (int ni = 0; ni < kLmNI; ++ni)
+                for (int ni = 0; ni < NI; ++ni)
                     fb[ni] = __builtin_bit_cast(lm_bf16x8, st[fw0 + ni * 32 * kLmChunks + fc]);
 #pragma unroll
                 for (int mi = 0; mi < kLmMI; ++mi)
 #pragma unroll
-                    for (int ni = 0; ni < kLmNI; ++ni)
+                    for (int ni = 0; ni < NI; ++ni)
                         acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
             }
         };
-        // Step s multiplies stage s % 3.  Before it, each wave waits
-        // for its own loads of step s (those of step s + 1 stay in flight)
-        // and the barrier makes every wave's loads visible; it also shows
-        // that every wave has finished step s - 1, whose stage then takes the
-        // loads of step s + 2.  Steps run in threes so that each stage is
-        // named statically, and the loop has one exit, at its bottom: the
-        // steps past the last (at most two) load zeros and add nothing.
+        // Step s multiplies stage s % 3.  Before it, each wave waits for its
+        // own loads of step s (those of step s + 1 stay in flight) and the
+        // barrier makes every wave's loads visible; it also shows that every
+        // wave has finished step s - 1, whose stage then takes the loads of
+        // step s + 2.  Steps run in threes so that each stage is named
+        // statically, and the loop has one exit, at its bottom: the steps
+        // past the last (at most two) load zeros and add nothing.
         auto step = [&](int s, const uint4* rd, uint4* wr) {
-            lm_wait_barrier<kLmDma>();
+            lm_wait_barrier<DMA>();
             issue(s + 2, wr);
             compute(rd);
         };
@@ -231,18 +244,23 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
         lm_wait_barrier<0>();
     };
 
-    auto epilogue = [&](int rt, int vt) {
-        const int row0 = rt * kLmM, v0 = vt * kLmN;
+    // The epilogue of run(half, rt, vt, t0).  The argmax parts are kept per
+    // half tile (128 tokens): entry 2 vt + h of a row covers tokens
+    // [vt kLmN + h kLmN / 2, + kLmN / 2).
+    auto epilogue = [&](auto half_c, int rt, int vt, int t0) {
+        constexpr bool HALF = decltype(half_c)::value;
+        constexpr int NI = HALF ? kLmNI / 2 : kLmNI;
+        const int row0 = rt * kLmM, v0 = vt * kLmN + t0;
         if constexpr (EPI == LM_STORE) {
             // bf16 logits: lanes of a half-wave hold 32 consecutive tokens of one row
 #pragma unroll
             for (int mi = 0; mi < kLmMI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < kLmNI; ++ni)
+                for (int ni = 0; ni < NI; ++ni)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int r = row0 + wm * (kLmM / kLmWM) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                        const int n = v0 + wn * (kLmN / kLmWN) + ni * 32 + (lane & 31);
+                        const int n = v0 + wn * (NI * 32) + ni * 32 + (lane & 31);
                         if (r < a.R && n < a.V) a.logits[(size_t)r * a.V + n] = lm_bf16_rne(acc[mi][ni][i]);
                     }
         } else {
@@ -252,11 +270,11 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
             for (int mi = 0; mi < kLmMI; ++mi) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int n0 = v0 + wn * (kLmN / kLmWN) + (lane & 31);
+                    const int n0 = v0 + wn * (NI * 32) + (lane & 31);
                     float bv = n0 < a.V ? acc[mi][0][i] : -INFINITY;
                     int bi = n0 < a.V ? n0 : INT32_MAX;
 #pragma unroll
-                    for (int ni = 1; ni < kLmNI; ++ni) {
+                    for (int ni = 1; ni < NI; ++ni) {
                         const int n1 = n0 + 32 * ni;
                         if (n1 < a.V && lm_better(acc[mi][ni][i], n1, bv, bi)) {
                             bv = acc[mi][ni][i];
@@ -277,24 +295,43 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
                 }
             }
             __syncthreads();
+            static_assert(kLmWN == 2 && kLmN == 256, "a full tile's two wave columns are its two half tiles");
             for (int r = tid; r < kLmM; r += kLmThreads) {
                 if (row0 + r >= a.R) break;
-                LmPart p = sP[r][0];
-#pragma unroll
-                for (int jj = 1; jj < kLmWN; ++jj) {
-                    const LmPart q = sP[r][jj];
+                LmPart* out = a.part + (size_t)(row0 + r) * (2 * a.n_vt) + 2 * vt;
+                if (HALF) {
+                    // the two wave columns split this half tile
+                    LmPart p = sP[r][0];
+                    const LmPart q = sP[r][1];
                     if (lm_better(q.v, q.i, p.v, p.i)) p = q;
+                    out[t0 != 0 ? 1 : 0] = p;
+                } else {
+                    out[0] = sP[r][0];
+                    out[1] = sP[r][1];
                 }
-                a.part[(size_t)(row0 + r) * a.n_vt + vt] = p;
             }
             __syncthreads();  // sP is written again by the next tile
         }
     };
 
-    for (int u = j; u < n_x; u += GX) {
+    // Whole tiles j, j + GX, ... while whole rounds of GX remain.  The Q
+    // tiles left for the last round would keep only Q of the GX members
+    // busy; when 2 Q <= GX they are cut into 2 Q half tiles (128 tokens),
+    // one per member, which costs each of them about three quarters of a
+    // tile (the hidden states are re-read whole) instead of idling the rest.
+    const int F = n_x / GX, Q = n_x - F * GX;
+    const bool halves = 2 * Q <= GX;
+    const int whole = halves ? F * GX : n_x;
+    for (int u = j; u < whole; u += GX) {
         const int rt = u % a.n_rt, vt = (u / a.n_rt) * 8 + x;
-        run(rt, vt);
-        epilogue(rt, vt);
+        run(std::false_type(), rt, vt, 0);
+        epilogue(std::false_type(), rt, vt, 0);
+    }
+    if (halves && j < 2 * Q) {
+        const int u = F * GX + (j >> 1), t0 = (j & 1) * (kLmN / 2);
+        const int rt = u % a.n_rt, vt = (u / a.n_rt) * 8 + x;
+        run(std::true_type(), rt, vt, t0);
+        epilogue(std::true_type(), rt, vt, t0);
     }
 }
 
@@ -302,10 +339,10 @@ __global__ void __launch_bounds__(256) k_lmhead_merge(LmArgs a) {
     __shared__ float s_v[4];
     __shared__ int s_i[4];
     const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-    const LmPart* p = a.part + (size_t)row * a.n_vt;
+    const LmPart* p = a.part + (size_t)row * (2 * a.n_vt);
     float bv = -INFINITY;
     int bi = INT32_MAX;
-    for (int t = tid; t < a.n_vt; t += 256) {
+    for (int t = tid; t < 2 * a.n_vt; t += 256) {
         const LmPart q = p[t];
         if (lm_better(q.v, q.i, bv, bi)) {
             bv = q.v;

@@ -52,7 +52,7 @@ constexpr int kLmPerCU = 1; // workgroups a compute unit holds (LDS)
 constexpr int kLmStages = 3;                      // LDS ring depth
 constexpr int kLmChunks = kLmK / 8;               // 16-byte chunks per row and step
 constexpr int kLmStageA = kLmM * kLmChunks;       // chunks of hidden state per stage
-constexpr int kLmStage = (kLmM + kLmN) * kLmChunks;  // chunks per stage (24 KiB)
+constexpr int kLmStage = (kLmM + kLmN) * kLmChunks;  // chunks per stage (32 KiB)
 constexpr int kLmDmaA = kLmStageA / kLmThreads;   // direct loads per thread and step (hidden)
 constexpr int kLmDmaW = kLmN * kLmChunks / kLmThreads;  // (unembedding)
 constexpr int kLmDma = kLmDmaA + kLmDmaW;
@@ -104,9 +104,9 @@ __device__ __forceinline__ int lm_swz(int r) {
 }
 
 // Wait until at most N of this wave's vector-memory operations are
-// outstanding (direct-to-LDS loads count here), then meet the workgroup.
-// A plain s_barrier, not __syncthreads: the latter's release fence would
-// wait for every load in flight.
+// outstanding (direct-to-LDS loads count here) and its LDS reads are done,
+// then meet the workgroup.  A plain s_barrier, not __syncthreads: the
+// latter's release fence would wait for every load in flight.
 template <int N>
 __device__ __forceinline__ void lm_wait_barrier() {
     static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -134,6 +134,7 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
     __shared__ __attribute__((aligned(16))) uint4 sT0[kLmStage];
     __shared__ __attribute__((aligned(16))) uint4 sT1[kLmStage];
     __shared__ __attribute__((aligned(16))) uint4 sT2[kLmStage];
+    static_assert(kLmStages == 3, "the ring is sT0, sT1, sT2");
     __shared__ LmPart sP[kLmM][kLmWN];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / kLmWN, wn = wave % kLmWN;

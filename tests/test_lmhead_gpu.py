@@ -227,3 +227,38 @@ def test_verify_hidden_full_vocabulary():
     wk = wl.Workload("hidden", B, K, V, tl, dl, toks, 0.7, 0, 0.9, 77)
     print(compare_sampling(wk, g_tok, g_num, None, None, list(range(B)), outs, Report(), check_stats=False),
           "accepted", g_num.tolist())
+
+
+@pytest.mark.parametrize("F,Q,tail", [(1, 0, 0), (1, 20, 37), (2, 5, 200), (0, 20, 0)])
+def test_lm_head_schedule_branches(F, Q, tail):
+    """The product's schedule gives each XCD's GX workgroups F whole rounds
+    of tiles and Q tiles left over; when 2 Q <= GX the leftovers run as half
+    tiles, otherwise whole.  V is derived from the device's compute units so
+    that each case is met (no leftovers; leftovers run whole; half tiles
+    after two rounds; leftovers only), with a ragged last tile.  Integer
+    inputs make every logit exact and tie often, so the greedy tokens (ties
+    to the lowest index) and the bf16 logits must equal the oracle's."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    GX = max(1, n_cu // 8)  # workgroups per XCD of a k_lmhead launch
+    Q = min(Q, GX - 1)
+    n_vt = 8 * (GX * F + Q)
+    if n_vt == 0:
+        pytest.skip("no tiles for this device")
+    V, H, B, K = n_vt * 256 - tail, 64, 2, 2
+    _print_case(f"lm head schedule F={F} Q={Q} GX={GX} V={V}")
+    hb, wb = _int_inputs(B * (K + 1), V, H, seed=V + F)
+    L = oracle.lm_head_logits(hb, wb).reshape(B, K + 1, V)
+    g = np.argmax(L, axis=2)  # first index of the maximum
+    rng = np.random.default_rng(V)
+    tokens = rng.integers(0, V, (B, K)).astype(np.int32)
+    pick = rng.random((B, K)) < 0.7
+    tokens[pick] = g[:, :K][pick]
+    out, num = binding.spec_verify_greedy_hidden(_dev16(hb.reshape(B, K + 1, H)), _dev16(wb),
+                                                 torch.from_numpy(tokens).cuda())
+    lg = binding.spec_lm_head_logits(_dev16(hb), _dev16(wb))
+    torch.cuda.synchronize()
+    o_tok, o_num = oracle.verify_greedy_logits64(L, tokens)
+    np.testing.assert_array_equal(out.cpu().numpy(), o_tok)
+    np.testing.assert_array_equal(num.cpu().numpy(), o_num)
+    np.testing.assert_array_equal(lg.view(torch.int16).cpu().numpy().view(np.uint16),
+                                  oracle.lm_head_logits_bf16(hb, wb))

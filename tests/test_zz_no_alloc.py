@@ -4,8 +4,9 @@ Both run the same kernels; the allocation-free one carves its scratch from a
 fixed static device array instead of a per-stream allocation.  Outputs must
 be bitwise equal to spec_verify's on consecutive calls whose sizes shrink (so
 scratch contents left by a larger call are in the way of a smaller one), over
-the filtered kept-list draw, the unfiltered chunked draw with its arrival
-counters, and greedy mode; a problem beyond the scratch is refused.
+the filtered kept-list draw, rows split over workgroups (merged by their
+last part through per-row counters), the unfiltered chunked draw with its
+arrival counters, and greedy mode; a problem beyond the scratch is refused.
 """
 import numpy as np
 import pytest
@@ -39,6 +40,11 @@ def _check(w, name):
 def test_noalloc_matches_spec_verify_on_shrinking_calls():
     # the concurrent-batch workload (kept lists), then smaller calls
     _check(wl.config(3), "c3 B32 K7 V151936 top-p")
+    # a single stream: its 31 unfiltered rows are split over many workgroups
+    # whose last part merges each row (per-row counters at the scratch's
+    # start, which every call must leave at zero), twice in a row
+    _check(wl.config(2), "c2 B1 K15 V151936 split rows")
+    _check(wl.config(2, rnd=1), "c2 again, next round's inputs")
     _check(wl.make(4, 3, 5003, target_dtype=wl.F32, draft_dtype=wl.BF16, temperature=1.0, rho=0.9,
                    seed=11, vseed=12), "B4 K3 V5003 unfiltered")
     _check(wl.make(3, 2, 4001, temperature=0.8, top_k=30, top_p=0.9, rho=0.85, seed=13, vseed=14),

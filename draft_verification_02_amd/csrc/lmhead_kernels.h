@@ -13,18 +13,19 @@
 //           a bf16 LM head outputs them) and stored, for the sampling path.
 //
 // k_lmhead<EPI> is persistent: one workgroup of 8 waves per compute unit,
-// each looping over (256 rows, 256 tokens) tiles (see the schedule below).
+// each looping over (256 rows, 320 tokens) tiles (see the schedule below).
 // A tile spans 256 rows so that, for up to 256 rows (a batch of 32 sequences
 // of 8 positions), every unembedding row is read from memory by one
-// workgroup only, and 256 tokens so that the hidden states, which every tile
-// re-reads from L2, cost no more than the unembedding rows: the L1's limit on
-// requests in flight, not HBM, bounds how fast a compute unit can be fed, so
-// the bytes per tile are what count.  A tile walks the hidden dimension in
-// 32-wide steps through a ring of three LDS stages that the loads fill
-// directly (global_load_lds_dwordx4: no registers hold loaded data), so two
-// steps are in flight while the third multiplies and each step needs one
-// barrier.  Each wave owns 64 rows x 128 tokens (2 x 4
-// v_mfma_f32_32x32x16_bf16 per 16-wide slice).
+// workgroup only.  What bounds how fast a compute unit is fed is not HBM but
+// its L1's limit on requests in flight, so the bytes a tile pulls in per
+// token it covers are what count: every tile re-reads the hidden states
+// (from L2), and 320 tokens, the widest tile whose accumulators fit the
+// registers of 8 waves, spread that re-read over the most tokens.  A tile
+// walks the hidden dimension in 32-wide steps through a ring of four LDS
+// stages that the loads fill directly (global_load_lds_dwordx4: no registers
+// hold loaded data), so three steps are in flight while the fourth
+// multiplies and each step needs one barrier.  Each wave owns 64 rows x 160
+// tokens (2 x 5 v_mfma_f32_32x32x16_bf16 per 16-wide slice).
 //
 // MFMA 32x32x16 operand layout (lane l, element j of the 8-element operand,
 // measured): A[m = l % 32][k = 8 (l / 32) + j], B[k = 8 (l / 32) + j][n = l % 32];
@@ -41,21 +42,22 @@
 namespace sv {
 
 constexpr int kLmM = 256;   // rows per tile
-constexpr int kLmN = 256;   // tokens per tile
+constexpr int kLmN = 320;   // tokens per tile
 constexpr int kLmWM = 4;    // waves across the rows
 constexpr int kLmWN = 2;    // waves across the tokens
 constexpr int kLmMI = kLmM / kLmWM / 32;  // 32-row MFMA blocks per wave
 constexpr int kLmNI = kLmN / kLmWN / 32;  // 32-token MFMA blocks per wave
 constexpr int kLmK = 32;    // hidden elements per step
 constexpr int kLmThreads = 64 * kLmWM * kLmWN;
+constexpr int kLmWaves = kLmThreads / 64;
 constexpr int kLmPerCU = 1; // workgroups a compute unit holds (LDS)
-constexpr int kLmStages = 3;                      // LDS ring depth
+constexpr int kLmStages = 4;                      // LDS ring depth
 constexpr int kLmChunks = kLmK / 8;               // 16-byte chunks per row and step
 constexpr int kLmStageA = kLmM * kLmChunks;       // chunks of hidden state per stage
-constexpr int kLmStage = (kLmM + kLmN) * kLmChunks;  // chunks per stage (32 KiB)
-constexpr int kLmDmaA = kLmStageA / kLmThreads;   // direct loads per thread and step (hidden)
-constexpr int kLmDmaW = kLmN * kLmChunks / kLmThreads;  // (unembedding)
-constexpr int kLmDma = kLmDmaA + kLmDmaW;
+constexpr int kLmStage = (kLmM + kLmN) * kLmChunks;  // chunks per stage (36 KiB)
+constexpr int kLmBlkW = kLmN * kLmChunks / 64;    // 64-chunk load blocks of unembedding rows per step
+static_assert(kLmM * kLmChunks % (kLmThreads * 2) == 0, "a half tile's hidden rows split evenly over the waves");
+static_assert(kLmN * kLmChunks % 64 == 0, "whole load blocks");
 
 typedef __bf16 lm_bf16x8 __attribute__((ext_vector_type(8)));
 typedef float lm_float16 __attribute__((ext_vector_type(16)));
@@ -74,7 +76,7 @@ struct LmArgs {
     int R, V, H;
     int n_vt;                 // vocabulary tiles, ceil(V / kLmN)
     int n_rt;                 // row tiles, ceil(R / kLmM)
-    LmPart* part;             // argmax: [R][2 n_vt], one entry per half tile
+    LmPart* part;             // argmax: [R][2 n_vt], one entry per tile and wave column
     int32_t* gidx;            // argmax: [R]
     uint16_t* logits;         // store: [R][V] bf16
 };
@@ -128,154 +130,174 @@ __device__ __forceinline__ void lm_wait_barrier() {
 // workgroups run.
 template <int EPI>
 __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
-    // the three ring stages are separate LDS objects, each named statically
-    // where it is used: the compiler then sees that a stage being read is not
-    // the one a load in flight writes, and adds no wait for that load
+    // the ring stages are separate LDS objects, each named statically where
+    // it is used: the compiler then sees that a stage being read is not one
+    // that a load in flight writes, and adds no wait for those loads
     __shared__ __attribute__((aligned(16))) uint4 sT0[kLmStage];
     __shared__ __attribute__((aligned(16))) uint4 sT1[kLmStage];
     __shared__ __attribute__((aligned(16))) uint4 sT2[kLmStage];
-    static_assert(kLmStages == 3, "the ring is sT0, sT1, sT2");
+    __shared__ __attribute__((aligned(16))) uint4 sT3[kLmStage];
+    static_assert(kLmStages == 4, "the ring is sT0 .. sT3");
     __shared__ LmPart sP[kLmM][kLmWN];
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int wm = wave / kLmWN, wn = wave % kLmWN;
     const int n_steps = (a.H + kLmK - 1) / kLmK;
     // operand fetch: per-lane chunk offsets of the two 16-wide slices of a step
     const int fr = lane & 31, fsw = lm_swz(fr);
-    const int fa0 = (wm * (kLmM / kLmWM) + fr) * kLmChunks;
     const int fc0 = (0 + (lane >> 5)) ^ fsw, fc1 = (2 + (lane >> 5)) ^ fsw;
+    const int fw0 = kLmStageA + (wn * (kLmNI * 32) + fr) * kLmChunks;
     const int x = blockIdx.x & 7, j = blockIdx.x >> 3, GX = gridDim.x >> 3;
     const int n_x = (x < a.n_vt ? (a.n_vt - x + 7) / 8 : 0) * a.n_rt;
 
     lm_float16 acc[kLmMI][kLmNI];
 
-    // acc = the product of row tile rt and tokens [t0, t0 + width) of
-    // vocabulary tile vt; width = kLmN, or kLmN / 2 for a half tile (HALF:
-    // only the first half of the unembedding stage is loaded, and each wave
-    // keeps kLmNI / 2 column blocks).
-    auto run = [&](auto half_c, int rt, int vt, int t0) {
+    // acc = the product of rows [r0, r0 + height) of row tile rt and the
+    // tokens of vocabulary tile vt; height = kLmM, or kLmM / 2 for a half
+    // tile (HALF: only that many hidden rows are loaded, and each wave keeps
+    // one 32-row block).
+    auto run = [&](auto half_c, int rt, int vt, int r0) {
         constexpr bool HALF = decltype(half_c)::value;
-        constexpr int NI = HALF ? kLmNI / 2 : kLmNI;
-        constexpr int DW = HALF ? kLmDmaW / 2 : kLmDmaW;  // unembedding loads per thread and step
-        constexpr int DMA = kLmDmaA + DW;
-        const int row0 = rt * kLmM, v0 = vt * kLmN + t0;
-        const int fw0 = kLmStageA + (wn * (NI * 32) + fr) * kLmChunks;
+        constexpr int MI = HALF ? 1 : kLmMI;             // 32-row blocks per wave
+        constexpr int DA = MI * 32 * kLmWM * kLmChunks / kLmThreads;  // hidden loads per thread and step
+        const int row0 = rt * kLmM + r0, v0 = vt * kLmN;
+        const int fa0 = (wm * (MI * 32) + fr) * kLmChunks;
 #pragma unroll
-        for (int mi = 0; mi < kLmMI; ++mi)
+        for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-            for (int ni = 0; ni < NI; ++ni)
+            for (int ni = 0; ni < kLmNI; ++ni)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) acc[mi][ni][i] = 0.f;
-        // Direct loads: load q of wave w fills the 64 chunks of block
-        // b = (threads / 64) q + w of its region; lane l takes chunk position
-        // 64 b + l, i.e. row p / 4 and logical chunk (p % 4) ^ lm_swz(row).  A
-        // chunk outside the operands comes from kLmZero16.
-        const uint16_t* src[DMA];
-        int col[DMA];
-#pragma unroll
-        for (int q = 0; q < DMA; ++q) {
-            const bool isA = q < kLmDmaA;
-            const int b = (isA ? q : q - kLmDmaA) * (kLmThreads / 64) + wave, p = b * 64 + lane;
-            const int r = p / kLmChunks;
-            col[q] = ((p % kLmChunks) ^ lm_swz(r)) * 8;
-            if (isA) {
-                const int g = row0 + r;
-                src[q] = g >= a.R ? nullptr : g < a.R1 ? a.hidden + (size_t)g * a.H : a.hidden2 + (size_t)(g - a.R1) * a.H;
-            } else {
-                const int g = v0 + r;
-                src[q] = g >= a.V ? nullptr : a.w + (size_t)g * a.H;
-            }
-        }
         // The hidden dimension is walked from a step that depends on the
         // vocabulary tile: the row pitch is usually a large power of two, so
         // tiles walking in lockstep would all read the same L2 channels.  The
-        // order depends on the token alone (both halves of a tile walk alike),
-        // so the logits of a token are the same whatever the rows, the tiling
-        // or the epilogue.
+        // order depends on the token alone, so the logits of a token are the
+        // same whatever the rows, the tiling or the epilogue.
         const int rot = (int)(((unsigned)vt * 37u) % (unsigned)n_steps);
-        auto issue = [&](int s, uint4* base) {
-            const int h0 = s < n_steps ? ((s + rot) % n_steps) * kLmK : a.H;  // past the last step: zeros
+        // The loop over the steps, for a wave that issues DW unembedding
+        // loads per step (the 64-chunk blocks of a step do not split evenly
+        // over the waves, and each wave must wait for exactly its own).
+        auto body = [&](auto dw_c) {
+            constexpr int DW = decltype(dw_c)::value;
+            constexpr int DMA = DA + DW;
+            // Direct loads: hidden load q of wave w fills block b = 8 q + w
+            // of the hidden region, unembedding load q block 8 q + w of the
+            // unembedding region; lane l takes chunk position 64 b + l, i.e.
+            // row p / 4 and logical chunk (p % 4) ^ lm_swz(row).  A chunk
+            // outside the operands comes from kLmZero16.
+            const uint16_t* src[DMA];
+            int col[DMA];
 #pragma unroll
             for (int q = 0; q < DMA; ++q) {
-                const bool isA = q < kLmDmaA;
-                const int b = (isA ? q : q - kLmDmaA) * (kLmThreads / 64) + wave;
-                const int h = h0 + col[q];
-                const void* g = (src[q] != nullptr && h < a.H) ? (const void*)(src[q] + h) : (const void*)&kLmZero16;
-                __builtin_amdgcn_global_load_lds(g, (lm_lds_void*)(base + (isA ? 0 : kLmStageA) + b * 64), 16, 0, 0);
+                const bool isA = q < DA;
+                const int b = (isA ? q : q - DA) * kLmWaves + wave, p = b * 64 + lane;
+                const int r = p / kLmChunks;
+                col[q] = ((p % kLmChunks) ^ lm_swz(r)) * 8;
+                if (isA) {
+                    const int g = row0 + r;
+                    src[q] = g >= a.R ? nullptr : g < a.R1 ? a.hidden + (size_t)g * a.H : a.hidden2 + (size_t)(g - a.R1) * a.H;
+                } else {
+                    const int g = v0 + r;
+                    src[q] = g >= a.V ? nullptr : a.w + (size_t)g * a.H;
+                }
             }
-        };
-        auto compute = [&](const uint4* st) {
+            auto issue = [&](int s, uint4* base) {
+                const int h0 = s < n_steps ? ((s + rot) % n_steps) * kLmK : a.H;  // past the last step: zeros
 #pragma unroll
-            for (int ks = 0; ks < kLmK / 16; ++ks) {
-                const int fc = ks == 0 ? fc0 : fc1;
-                lm_bf16x8 fa[kLmMI], fb[NI];
+                for (int q = 0; q < DMA; ++q) {
+                    const bool isA = q < DA;
+                    const int b = (isA ? q : q - DA) * kLmWaves + wave;
+                    const int h = h0 + col[q];
+                    const void* g = (src[q] != nullptr && h < a.H) ? (const void*)(src[q] + h) : (const void*)&kLmZero16;
+                    __builtin_amdgcn_global_load_lds(g, (lm_lds_void*)(base + (isA ? 0 : kLmStageA) + b * 64), 16, 0, 0);
+                }
+            };
+            auto compute = [&](const uint4* st) {
 #pragma unroll
-                for (int mi = 0; mi < kLmMI; ++mi)
-                    fa[mi] = __builtin_bit_cast(lm_bf16x8, st[fa0 + mi * 32 * kLmChunks + fc]);
+                for (int ks = 0; ks < kLmK / 16; ++ks) {
+                    const int fc = ks == 0 ? fc0 : fc1;
+                    lm_bf16x8 fa[MI], fb[kLmNI];
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
-                    fb[ni] = __builtin_bit_cast(lm_bf16x8, st[fw0 + ni * 32 * kLmChunks + fc]);
+                    for (int mi = 0; mi < MI; ++mi)
+                        fa[mi] = __builtin_bit_cast(lm_bf16x8, st[fa0 + mi * 32 * kLmChunks + fc]);
 #pragma unroll
-                for (int mi = 0; mi < kLmMI; ++mi)
+                    for (int ni = 0; ni < kLmNI; ++ni)
+                        fb[ni] = __builtin_bit_cast(lm_bf16x8, st[fw0 + ni * 32 * kLmChunks + fc]);
 #pragma unroll
-                    for (int ni = 0; ni < NI; ++ni)
-                        acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+                    for (int mi = 0; mi < MI; ++mi)
+#pragma unroll
+                        for (int ni = 0; ni < kLmNI; ++ni)
+                            acc[mi][ni] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+                }
+            };
+            // Step s multiplies stage s % 4.  Before it, each wave waits for
+            // its own loads of step s (those of steps s + 1 and s + 2 stay in
+            // flight) and the barrier makes every wave's loads visible; it
+            // also shows that every wave has finished step s - 1, whose stage
+            // then takes the loads of step s + 3.  Steps run in fours so that
+            // each stage is named statically, and the loop has one exit, at
+            // its bottom: the steps past the last (at most three) load zeros
+            // and add nothing.
+            auto step = [&](int s, const uint4* rd, uint4* wr) {
+                lm_wait_barrier<2 * DMA>();
+                issue(s + 3, wr);
+                compute(rd);
+            };
+            issue(0, sT0);
+            issue(1, sT1);
+            issue(2, sT2);
+            for (int s = 0; s < n_steps; s += 4) {
+                step(s, sT0, sT3);
+                step(s + 1, sT1, sT0);
+                step(s + 2, sT2, sT1);
+                step(s + 3, sT3, sT2);
             }
+            // Before the ring is refilled: every wave is done reading it and
+            // this wave's loads (and stores) have drained.
+            lm_wait_barrier<0>();
         };
-        // Step s multiplies stage s % 3.  Before it, each wave waits for its
-        // own loads of step s (those of step s + 1 stay in flight) and the
-        // barrier makes every wave's loads visible; it also shows that every
-        // wave has finished step s - 1, whose stage then takes the loads of
-        // step s + 2.  Steps run in threes so that each stage is named
-        // statically, and the loop has one exit, at its bottom: the steps
-        // past the last (at most two) load zeros and add nothing.
-        auto step = [&](int s, const uint4* rd, uint4* wr) {
-            lm_wait_barrier<DMA>();
-            issue(s + 2, wr);
-            compute(rd);
-        };
-        issue(0, sT0);
-        issue(1, sT1);
-        for (int s = 0; s < n_steps; s += 3) {
-            step(s, sT0, sT2);
-            step(s + 1, sT1, sT0);
-            step(s + 2, sT2, sT1);
+        // waves [0, kLmBlkW % 8) take one unembedding block more than the rest
+        if constexpr (kLmBlkW % kLmWaves == 0) {
+            body(std::integral_constant<int, kLmBlkW / kLmWaves>());
+        } else {
+            if (wave < kLmBlkW % kLmWaves)
+                body(std::integral_constant<int, kLmBlkW / kLmWaves + 1>());
+            else
+                body(std::integral_constant<int, kLmBlkW / kLmWaves>());
         }
-        // Before the ring is refilled: every wave is done reading it and
-        // this wave's loads (and stores) have drained.
-        lm_wait_barrier<0>();
     };
 
-    // The epilogue of run(half, rt, vt, t0).  The argmax parts are kept per
-    // half tile (128 tokens): entry 2 vt + h of a row covers tokens
-    // [vt kLmN + h kLmN / 2, + kLmN / 2).
-    auto epilogue = [&](auto half_c, int rt, int vt, int t0) {
+    // The epilogue of run(half, rt, vt, r0).  The argmax parts are kept per
+    // wave column: entry 2 vt + c of a row covers tokens
+    // [vt kLmN + c kLmN / 2, + kLmN / 2).
+    auto epilogue = [&](auto half_c, int rt, int vt, int r0) {
         constexpr bool HALF = decltype(half_c)::value;
-        constexpr int NI = HALF ? kLmNI / 2 : kLmNI;
-        const int row0 = rt * kLmM, v0 = vt * kLmN + t0;
+        constexpr int MI = HALF ? 1 : kLmMI;
+        constexpr int RT = MI * 32 * kLmWM;  // rows of this tile
+        const int row0 = rt * kLmM + r0, v0 = vt * kLmN;
         if constexpr (EPI == LM_STORE) {
             // bf16 logits: lanes of a half-wave hold 32 consecutive tokens of one row
 #pragma unroll
-            for (int mi = 0; mi < kLmMI; ++mi)
+            for (int mi = 0; mi < MI; ++mi)
 #pragma unroll
-                for (int ni = 0; ni < NI; ++ni)
+                for (int ni = 0; ni < kLmNI; ++ni)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) {
-                        const int r = row0 + wm * (kLmM / kLmWM) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-                        const int n = v0 + wn * (NI * 32) + ni * 32 + (lane & 31);
+                        const int r = row0 + wm * (MI * 32) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+                        const int n = v0 + wn * (kLmNI * 32) + ni * 32 + (lane & 31);
                         if (r < a.R && n < a.V) a.logits[(size_t)r * a.V + n] = lm_bf16_rne(acc[mi][ni][i]);
                     }
         } else {
             // per row of this wave's block: the best over its tokens (the
             // column blocks, then the 32 lanes of the half-wave holding the row)
 #pragma unroll
-            for (int mi = 0; mi < kLmMI; ++mi) {
+            for (int mi = 0; mi < MI; ++mi) {
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    const int n0 = v0 + wn * (NI * 32) + (lane & 31);
+                    const int n0 = v0 + wn * (kLmNI * 32) + (lane & 31);
                     float bv = n0 < a.V ? acc[mi][0][i] : -INFINITY;
                     int bi = n0 < a.V ? n0 : INT32_MAX;
 #pragma unroll
-                    for (int ni = 1; ni < NI; ++ni) {
+                    for (int ni = 1; ni < kLmNI; ++ni) {
                         const int n1 = n0 + 32 * ni;
                         if (n1 < a.V && lm_better(acc[mi][ni][i], n1, bv, bi)) {
                             bv = acc[mi][ni][i];
@@ -292,24 +314,16 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
                         }
                     }
                     if ((lane & 31) == 0)
-                        sP[wm * (kLmM / kLmWM) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)][wn] = LmPart{bv, bi};
+                        sP[wm * (MI * 32) + mi * 32 + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3)][wn] = LmPart{bv, bi};
                 }
             }
             __syncthreads();
-            static_assert(kLmWN == 2 && kLmN == 256, "a full tile's two wave columns are its two half tiles");
-            for (int r = tid; r < kLmM; r += kLmThreads) {
+            static_assert(kLmWN == 2, "two parts per row and tile");
+            for (int r = tid; r < RT; r += kLmThreads) {
                 if (row0 + r >= a.R) break;
                 LmPart* out = a.part + (size_t)(row0 + r) * (2 * a.n_vt) + 2 * vt;
-                if (HALF) {
-                    // the two wave columns split this half tile
-                    LmPart p = sP[r][0];
-                    const LmPart q = sP[r][1];
-                    if (lm_better(q.v, q.i, p.v, p.i)) p = q;
-                    out[t0 != 0 ? 1 : 0] = p;
-                } else {
-                    out[0] = sP[r][0];
-                    out[1] = sP[r][1];
-                }
+                out[0] = sP[r][0];
+                out[1] = sP[r][1];
             }
             __syncthreads();  // sP is written again by the next tile
         }
@@ -317,9 +331,10 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
 
     // Whole tiles j, j + GX, ... while whole rounds of GX remain.  The Q
     // tiles left for the last round would keep only Q of the GX members
-    // busy; when 2 Q <= GX they are cut into 2 Q half tiles (128 tokens),
-    // one per member, which costs each of them about three quarters of a
-    // tile (the hidden states are re-read whole) instead of idling the rest.
+    // busy; when 2 Q <= GX they are cut into 2 Q half tiles (128 rows), one
+    // per member, which costs each of them about three quarters of a tile
+    // (the unembedding rows are read whole) instead of idling the rest.  A
+    // half tile that holds no row (past R) is skipped.
     const int F = n_x / GX, Q = n_x - F * GX;
     const bool halves = 2 * Q <= GX;
     const int whole = halves ? F * GX : n_x;
@@ -329,10 +344,12 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
         epilogue(std::false_type(), rt, vt, 0);
     }
     if (halves && j < 2 * Q) {
-        const int u = F * GX + (j >> 1), t0 = (j & 1) * (kLmN / 2);
+        const int u = F * GX + (j >> 1), r0 = (j & 1) * (kLmM / 2);
         const int rt = u % a.n_rt, vt = (u / a.n_rt) * 8 + x;
-        run(std::true_type(), rt, vt, t0);
-        epilogue(std::true_type(), rt, vt, t0);
+        if (rt * kLmM + r0 < a.R) {
+            run(std::true_type(), rt, vt, r0);
+            epilogue(std::true_type(), rt, vt, r0);
+        }
     }
 }
 

@@ -655,7 +655,7 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     Workspace* ws;
     Caps need;
     need.gidx = (size_t)R;
-    need.chunk_bytes = (size_t)(R * 2 * n_vt) * sizeof(LmPart);  // one part per half tile
+    need.chunk_bytes = (size_t)(R * 2 * n_vt) * sizeof(LmPart);  // one part per tile and wave column
     rc = get_workspace(st, need, &ws);
     if (rc) return rc;
     LmArgs la = lm_args(hidden, nullptr, R, R, w_unembed, V, H);

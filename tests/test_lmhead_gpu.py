@@ -229,22 +229,27 @@ def test_verify_hidden_full_vocabulary():
           "accepted", g_num.tolist())
 
 
-@pytest.mark.parametrize("F,Q,tail", [(1, 0, 0), (1, 20, 37), (2, 5, 200), (0, 20, 0)])
+LM_TILE_TOKENS = 320  # tokens per tile of the unembedding product
+
+
+@pytest.mark.parametrize("F,Q,tail", [(1, 0, 0), (1, 20, 37), (2, 5, 200), (0, 20, 0), (0, 5, 11)])
 def test_lm_head_schedule_branches(F, Q, tail):
     """The product's schedule gives each XCD's GX workgroups F whole rounds
     of tiles and Q tiles left over; when 2 Q <= GX the leftovers run as half
-    tiles, otherwise whole.  V is derived from the device's compute units so
-    that each case is met (no leftovers; leftovers run whole; half tiles
-    after two rounds; leftovers only), with a ragged last tile.  Integer
-    inputs make every logit exact and tie often, so the greedy tokens (ties
-    to the lowest index) and the bf16 logits must equal the oracle's."""
+    tiles (128 rows each), otherwise whole.  V is derived from the device's
+    compute units so that each case is met (no leftovers; leftovers run
+    whole; half tiles after two rounds; whole leftovers only; half tiles
+    only), with a ragged last tile, and the 136 rows reach into both halves
+    of a row tile.  Integer inputs make every logit exact and tie often, so
+    the greedy tokens (ties to the lowest index) and the bf16 logits must
+    equal the oracle's."""
     n_cu = torch.cuda.get_device_properties(0).multi_processor_count
     GX = max(1, n_cu // 8)  # workgroups per XCD of a k_lmhead launch
     Q = min(Q, GX - 1)
     n_vt = 8 * (GX * F + Q)
     if n_vt == 0:
         pytest.skip("no tiles for this device")
-    V, H, B, K = n_vt * 256 - tail, 64, 2, 2
+    V, H, B, K = n_vt * LM_TILE_TOKENS - tail, 64, 17, 7
     _print_case(f"lm head schedule F={F} Q={Q} GX={GX} V={V}")
     hb, wb = _int_inputs(B * (K + 1), V, H, seed=V + F)
     L = oracle.lm_head_logits(hb, wb).reshape(B, K + 1, V)

@@ -16,11 +16,9 @@
 // each looping over (256 rows, 320 tokens) tiles (see the schedule below).
 // A tile spans 256 rows so that, for up to 256 rows (a batch of 32 sequences
 // of 8 positions), every unembedding row is read from memory by one
-// workgroup only.  What bounds how fast a compute unit is fed is not HBM but
-// its L1's limit on requests in flight, so the bytes a tile pulls in per
-// token it covers are what count: every tile re-reads the hidden states
-// (from L2), and 320 tokens, the widest tile whose accumulators fit the
-// registers of 8 waves, spread that re-read over the most tokens.  A tile
+// workgroup only.  Every tile re-reads the hidden states (from L2), and 320
+// tokens, the widest tile whose accumulators fit the registers of 8 waves,
+// spread that re-read over the most tokens.  A tile
 // walks the hidden dimension in 32-wide steps through a ring of four LDS
 // stages that the loads fill directly (global_load_lds_dwordx4: no registers
 // hold loaded data), so three steps are in flight while the fourth

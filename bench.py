@@ -531,7 +531,8 @@ def main():
     g_tok, g_num = out_t.cpu().numpy(), out_n.cpu().numpy()
 
     src_hash = kernel_source_hash()
-    kernel = "k_row_argmax" if greedy else "k_row"
+    # greedy batches below 512 sequences run in one launch (argmax and prefix)
+    kernel = ("k_greedy_rows" if w.B < 512 else "k_row_argmax") if greedy else "k_row"
     achieved = ideal / (k_ms * 1e-3) / 1e9
     workload = w.name + ("-point" if point else ("-ragged" if ragged else ""))
     traffic = traffic_from_profiles(workload, src_hash, kernel)

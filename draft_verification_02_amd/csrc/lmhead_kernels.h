@@ -36,6 +36,7 @@
 #include <type_traits>
 
 #include "device_common.h"
+#include "seq_kernels.h"
 
 namespace sv {
 
@@ -351,10 +352,9 @@ __global__ void __launch_bounds__(kLmThreads, kLmPerCU) k_lmhead(LmArgs a) {
     }
 }
 
-__global__ void __launch_bounds__(256) k_lmhead_merge(LmArgs a) {
-    __shared__ float s_v[4];
-    __shared__ int s_i[4];
-    const int row = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+// A row's argmax over its tile parts (thread 0 returns it; 256 threads).
+__device__ __forceinline__ int lm_merge_row(const LmArgs& a, int row, float* s_v, int* s_i) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const LmPart* p = a.part + (size_t)row * (2 * a.n_vt);
     float bv = -INFINITY;
     int bi = INT32_MAX;
@@ -385,8 +385,27 @@ __global__ void __launch_bounds__(256) k_lmhead_merge(LmArgs a) {
                 bv = s_v[w2];
                 bi = s_i[w2];
             }
-        a.gidx[row] = bi;
     }
+    return bi;
+}
+
+__global__ void __launch_bounds__(256) k_lmhead_merge(LmArgs a) {
+    __shared__ float s_v[4];
+    __shared__ int s_i[4];
+    const int row = blockIdx.x;
+    const int bi = lm_merge_row(a, row, s_v, s_i);
+    if (threadIdx.x == 0) a.gidx[row] = bi;
+}
+
+// The merge with the greedy prefix match folded in (fewer than kSplitRows
+// sequences): the last of a sequence's rows to be merged writes its outputs.
+__global__ void __launch_bounds__(256) k_lmhead_merge_greedy(LmArgs a, GreedyArgs g) {
+    __shared__ float s_v[4];
+    __shared__ int s_i[4];
+    __shared__ GreedyShared S;
+    const int row = blockIdx.x;
+    const int bi = lm_merge_row(a, row, s_v, s_i);
+    greedy_arrive(g, row, bi, S);
 }
 
 }  // namespace sv

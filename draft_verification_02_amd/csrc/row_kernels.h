@@ -1831,7 +1831,7 @@ __global__ void __launch_bounds__(kRB, 4) k_row(RowArgs a) {
 // k_row_argmax: lowest-index argmax of a target row (greedy mode).
 // ---------------------------------------------------------------------------
 template <int DT>
-__device__ __forceinline__ void argmax_body(const Shape& sh, int row, int32_t* gidx, u64* s_red) {
+__device__ __forceinline__ int32_t argmax_body(const Shape& sh, int row, u64* s_red) {
     const char* rowp = row_ptr(sh, row);
     const RowStream<DT> st(rowp, sh.V);
     constexpr int NL = RowStream<DT>::NL;
@@ -1861,7 +1861,7 @@ __device__ __forceinline__ void argmax_body(const Shape& sh, int row, int32_t* g
     const u64 key = bidx < 0 ? 0ull
                              : (((u64)fkey(best) << 32) | (u64)(0xFFFFFFFFu - (uint32_t)bidx));
     const u64 k = rb_max_u64(key, s_red);
-    if (threadIdx.x == 0) gidx[row] = (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
+    return (int32_t)(0xFFFFFFFFu - (uint32_t)(k & 0xFFFFFFFFull));
 }
 
 __global__ void __launch_bounds__(kRB) k_row_argmax(Shape sh, int32_t* gidx) {
@@ -1869,10 +1869,8 @@ __global__ void __launch_bounds__(kRB) k_row_argmax(Shape sh, int32_t* gidx) {
     const int row = blockIdx.x;
     clear_counters(sh);
     if (!row_live(sh, row)) return;
-    if (sh.tdt == DT_BF16)
-        argmax_body<DT_BF16>(sh, row, gidx, s_red);
-    else
-        argmax_body<DT_F32>(sh, row, gidx, s_red);
+    const int32_t g = sh.tdt == DT_BF16 ? argmax_body<DT_BF16>(sh, row, s_red) : argmax_body<DT_F32>(sh, row, s_red);
+    if (threadIdx.x == 0) gidx[row] = g;
 }
 
 }  // namespace sv

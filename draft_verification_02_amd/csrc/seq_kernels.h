@@ -951,6 +951,103 @@ __global__ void k_greedy_prefix(Shape sh, const int32_t* gidx, int32_t* out_toke
     count_accepts(sh, b, j);
 }
 
+// Greedy verification in one launch (drafted sequences, fewer than
+// kSplitRows of them).  Each workgroup takes one target row's lowest-index
+// argmax, stores it with an agent-scope store, waits for the store and counts
+// its row on the sequence's counter; the last of the sequence's live rows to
+// arrive matches the prefix (the greedy rule of "DFlash", section 4: the
+// longest run of drafted tokens equal to the target's argmax, then the
+// target's token at the first mismatch, or the bonus token after the last
+// draft) and writes the outputs.  When acceptance counts are asked for, the
+// last sequence to finish counts the batch's totals per position and writes
+// them (no clearing, no atomics on them).  The counters are zero between
+// calls: each last arrival resets its own.
+struct GreedyArgs {
+    Shape sh;
+    int32_t* gidx;        // [n_trows] row argmaxes
+    int32_t* out_tokens;  // [B][K+1]
+    int32_t* out_num;     // [B]
+    unsigned* cnt;        // B sequence counters, then the batch counter, kCntStride apart
+};
+
+struct GreedyShared {
+    int flag, j;
+    int jb[kSplitRows];
+};
+
+// The row's part, for the whole workgroup: store the argmax am of row `row`
+// (of sequence b), count it, and, in the last live row of the sequence to
+// arrive, write the sequence's outputs (and, in the last sequence, the
+// batch's acceptance counts).
+__device__ __forceinline__ void greedy_arrive(const GreedyArgs& g, int row, int32_t am, GreedyShared& S) {
+    const Shape& sh = g.sh;
+    const int K = sh.K, b = row / (K + 1), Kb = seq_len(sh, b);
+    const int nt = (int)blockDim.x;
+    if (threadIdx.x == 0) {
+        st_agent(&g.gidx[row], am);
+        wait_stores();
+        S.flag = __hip_atomic_fetch_add(&g.cnt[(size_t)b * kCntStride], 1u, __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT) == (unsigned)Kb;
+        S.j = Kb;
+    }
+    __syncthreads();
+    if (!S.flag) return;
+    // the first position k < K_b whose drafted token differs from the argmax
+    const int32_t* d = sh.tokens + (size_t)b * K;
+    const int32_t* gi = g.gidx + (size_t)b * (K + 1);
+    for (int k0 = 0; k0 < Kb; k0 += nt) {
+        const int k = k0 + (int)threadIdx.x;
+        if (k < Kb && d[k] != ld_agent(&gi[k])) atomicMin(&S.j, k);
+        __syncthreads();
+        if (S.j < Kb) break;
+    }
+    const int j = S.j;
+    const int32_t gj = ld_agent(&gi[j]);
+    int32_t* out = g.out_tokens + (size_t)b * (K + 1);
+    for (int k = threadIdx.x; k <= K; k += nt) out[k] = k < j ? d[k] : (k == j ? gj : -1);
+    const bool counts = sh.tested || sh.accepted;
+    __syncthreads();  // every thread has read S.j
+    if (threadIdx.x == 0) {
+        g.cnt[(size_t)b * kCntStride] = 0u;
+        if (counts) {
+            st_agent(&g.out_num[b], j);
+            wait_stores();
+            S.flag = __hip_atomic_fetch_add(&g.cnt[(size_t)sh.B * kCntStride], 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) == (unsigned)(sh.B - 1);
+        } else {
+            g.out_num[b] = j;
+            S.flag = 0;
+        }
+    }
+    __syncthreads();
+    if (!S.flag) return;
+    // the batch's last sequence: tests ran at positions k <= j_b, k < K_b,
+    // and accepted at k < j_b
+    for (int bb = threadIdx.x; bb < sh.B; bb += nt) S.jb[bb] = ld_agent(&g.out_num[bb]);
+    __syncthreads();
+    for (int k = threadIdx.x; k < K; k += nt) {
+        int t = 0, ac = 0;
+        for (int bb = 0; bb < sh.B; ++bb) {
+            const int jb = S.jb[bb];
+            t += k < min(jb + 1, seq_len(sh, bb)) ? 1 : 0;
+            ac += k < jb ? 1 : 0;
+        }
+        if (sh.tested) sh.tested[k] = t;
+        if (sh.accepted) sh.accepted[k] = ac;
+    }
+    if (threadIdx.x == 0) g.cnt[(size_t)sh.B * kCntStride] = 0u;
+}
+
+__global__ void __launch_bounds__(kRB) k_greedy_rows(GreedyArgs g) {
+    __shared__ u64 s_red[kRW];
+    __shared__ GreedyShared S;
+    const Shape& sh = g.sh;
+    const int row = blockIdx.x;
+    if (!row_live(sh, row)) return;
+    const int32_t am = sh.tdt == DT_BF16 ? argmax_body<DT_BF16>(sh, row, s_red) : argmax_body<DT_F32>(sh, row, s_red);
+    greedy_arrive(g, row, am, S);
+}
+
 // Copy row records to the caller's stats arrays.
 __global__ void k_copy_stats(const RowRec* rec, int n_trows, int n_drows, spec_row_stats_t* tstats,
                              spec_row_stats_t* dstats) {

@@ -25,8 +25,9 @@ using namespace sv;
 // token-tree walks.  Every kernel writes what it later reads within the same
 // call.  The draw's arrival counters are cleared by the row kernel before the
 // draw runs; the split rows' counters, which the row kernel itself counts
-// with, sit at offset 0 of every layout, are zero when the memory is fresh
-// and are left at zero by the part that merges.
+// with (and the single-launch greedy kernel its sequences and batch), sit at
+// offset 0 of every layout, are zero when the memory is fresh and are left at
+// zero by the workgroup that counts last.
 struct Caps {
     size_t rows = 0;         // row records (and split-row partials)
     size_t lists = 0;        // target rows with stored kept lists
@@ -247,6 +248,15 @@ int run_greedy(const void* target, const int32_t* tokens, int B, int K, int V, i
     void *evb, *eva;
     take_events(&evb, &eva);
     if (evb && hipEventRecord(static_cast<hipEvent_t>(evb), stream) != hipSuccess) return SPEC_E_LAUNCH;
+    if (B < kSplitRows) {
+        // one launch: the last row of each sequence to finish writes its
+        // outputs, counted on the split rows' counters (zero between calls)
+        const GreedyArgs ga{sh, ws->gidx, out_tokens, out_num, ws->part_cnt};
+        hipLaunchKernelGGL(k_greedy_rows, dim3(n_trows), dim3(kRB), 0, stream, ga);
+        if ((rc = launch_status())) return rc;
+        if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
+        return SPEC_OK;
+    }
     hipLaunchKernelGGL(k_row_argmax, dim3(n_trows), dim3(kRB), 0, stream, sh, ws->gidx);
     if ((rc = launch_status())) return rc;
     if (eva && hipEventRecord(static_cast<hipEvent_t>(eva), stream) != hipSuccess) return SPEC_E_LAUNCH;
@@ -662,10 +672,16 @@ int spec_verify_greedy_hidden(const void* hidden, const void* w_unembed, const i
     la.part = static_cast<LmPart*>(ws->chunks);
     la.gidx = ws->gidx;
     if ((rc = launch_lm(LM_ARGMAX, la, ws->n_cu, st))) return rc;
-    hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)R), dim3(256), 0, st, la);
-    if ((rc = launch_status())) return rc;
     const Shape sh{nullptr, nullptr, draft_tokens, B, K, V, SPEC_DTYPE_BF16, 0, 2, 0, (int)R, 0, nullptr, nullptr,
                    nullptr};
+    if (B < kSplitRows) {
+        // the last merged row of each sequence writes its outputs
+        const GreedyArgs ga{sh, ws->gidx, out_tokens, out_num_accepted, ws->part_cnt};
+        hipLaunchKernelGGL(k_lmhead_merge_greedy, dim3((unsigned)R), dim3(256), 0, st, la, ga);
+        return launch_status();
+    }
+    hipLaunchKernelGGL(k_lmhead_merge, dim3((unsigned)R), dim3(256), 0, st, la);
+    if ((rc = launch_status())) return rc;
     hipLaunchKernelGGL(k_greedy_prefix, dim3((unsigned)ceil_div(B, 256)), dim3(256), 0, st, sh,
                        (const int32_t*)ws->gidx, out_tokens, out_num_accepted);
     return launch_status();

@@ -62,7 +62,8 @@ def _check(B, K, V, H, seed, seqs=None, agree=0.8):
 
 
 @pytest.mark.parametrize("B,K,V,H", [(4, 3, 1000, 64), (7, 20, 1, 8), (3, 5, 129, 32), (5, 4, 127, 40),
-                                     (2, 0, 5000, 256), (9, 15, 2049, 128)])
+                                     (2, 0, 5000, 256), (9, 15, 2049, 128),
+                                     (511, 1, 300, 64), (512, 1, 300, 64)])
 def test_hidden_greedy_small(B, K, V, H):
     _print_case(f"hidden greedy B={B} K={K} V={V} H={H}")
     print("near ties", _check(B, K, V, H, seed=B * 100 + V + H))

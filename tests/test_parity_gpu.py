@@ -210,6 +210,30 @@ def test_greedy_edge_cases():
             check_greedy(w)
 
 
+@pytest.mark.parametrize("B", [1, 511, 512, 600])
+def test_greedy_batches_around_the_single_launch_limit(B):
+    """Greedy verification runs in one launch below 512 sequences (the last
+    row of each sequence to finish writes its outputs, the last sequence the
+    acceptance counts) and in two launches from 512 on: both give the
+    oracle's tokens, and the ragged call's counters match their definition,
+    on two calls in a row (the arrival counters must be left at zero)."""
+    from parity import check_ragged
+    _print_case(f"greedy B={B}")
+    rng = np.random.default_rng(B)
+    K, V = 3, 700
+    x = rng.integers(-4, 5, size=(B, K + 1, V)).astype(np.float32)  # ties
+    g = x.argmax(-1).astype(np.int32)
+    toks = g[:, :K].copy()
+    miss = rng.random((B, K)) < 0.3
+    toks[miss] = (toks[miss] + 1) % V
+    for tgt in (x, wl.f32_to_bf16_bits(x)):
+        w = wl.Workload("g", B, K, V, tgt, None, toks, 0.0, 0, 1.0, 0)
+        check_greedy(w)
+        check_greedy(w, via_verify=True)
+        check_ragged(w, _lens(B, K, B + 1))
+        check_ragged(w, _lens(B, K, B + 2))
+
+
 def test_unaligned_rows():
     """bf16 rows of odd length start at 2-byte offsets: element-wise load path."""
     _print_case("unaligned")

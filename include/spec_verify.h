@@ -344,9 +344,11 @@ int spec_rng_uniforms(uint64_t seed, int B, int K, double* u_accept,
 
 /*
  * Measurement hook: when both are non-NULL hipEvent_t handles, the next
- * sampling-mode call records `before` on its stream just before launching its
- * streaming (dominant) kernel and `after` just after it; the hook is then
- * cleared.  Passing NULLs clears it.  Not thread-safe with concurrent calls.
+ * verification call on logits (sampling or greedy) records `before` on its
+ * stream just before launching its streaming (dominant) kernel and `after`
+ * just after it (for greedy calls below 512 sequences that kernel also
+ * writes the outputs); the hook is then cleared.  Passing NULLs clears it.
+ * Not thread-safe with concurrent calls.
  */
 int spec_profile_events(void* before, void* after);
 

@@ -418,20 +418,27 @@ def bench_hidden(args, torch, binding, wl, sample=False):
 
 
 def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap = argparse.ArgumentParser(description="Throughput of batched speculative-decoding verification on one "
+                                             "GPU; prints one JSON line.")
+    ap.add_argument("--gpus", type=int, default=1, help="GPUs (only 1 is supported)")
+    ap.add_argument("--steps", type=int, default=200, help="timed steps (one call each)")
+    ap.add_argument("--warmup", type=int, default=20, help="untimed steps before the settle phase")
     ap.add_argument("--no-settle", dest="settle", action="store_false",
                     help="skip the untimed settle phase after the warmup steps")
-    ap.add_argument("--config", type=int, default=3)
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload 1..5: 1 tiny (B1 K4 V1000), 2 single stream (B1 K15 V151936), "
+                         "3 concurrent batch (B32 K7 V151936, the headline), 4 greedy (B64 K15), "
+                         "5 large batch (B256 K4 V262144)")
     ap.add_argument("--mode", choices=["general", "point", "ragged", "tree", "hidden", "hidden-sample"],
                     default="general",
                     help="general: spec_verify with draft logits (the headline); point: "
-                         "spec_verify_point with point-mass drafts")
+                         "spec_verify_point with point-mass drafts; ragged: spec_verify_ragged with "
+                         "per-sequence draft lengths; tree: spec_verify_tree over 44-node token trees; "
+                         "hidden: spec_verify_greedy_hidden; hidden-sample: spec_verify_hidden "
+                         "(the hidden modes use the concurrent-batch shape)")
     ap.add_argument("--sets", type=int, default=0, help="input copies rotated (0: auto)")
     ap.add_argument("--cpu-seqs", type=int, default=0, help="sequences of the CPU baseline (0: auto)")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the CPU oracle's timing")
     ap.add_argument("--copy-probe", type=int, default=0,
                     help="only run a plain device copy of this many bytes (3 times), for "
                          "calibrating HBM traffic counters, then exit")
